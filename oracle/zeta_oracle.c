@@ -1,0 +1,283 @@
+/*
+ * zeta_oracle.c -- plain, slow CPU definition of ZETA causal top-k attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the GPU path is checked
+ * against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load it; the product path never calls it, and it shares no code, header, table or
+ * helper with the HIP kernels.
+ *
+ * Source: "ZETA: Leveraging Z-order Curves for Efficient Top-k Attention"
+ *   [R]  the authors' rebuttal page (paperhub.cn/paper/j9VVzueEbG)
+ *   [S]  the AI-written summary page (atlas.scime.ai, paper 83158)
+ *   [A]  the arXiv abstract page (fugumt.com, 2501.14577v2)
+ *
+ * Everything is written as the plain definition: each query scans its whole causal
+ * prefix, orders it with qsort and keeps the first k; all floating point is fp64.
+ * Where the pages leave a step open, the reading taken is stated at the function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------ */
+/* Step 1: quantise one coordinate.
+ * [R] answer W2/A2 ("Clarification of Binary Expansion and Precision"): every coordinate
+ * is normalised onto a fixed interval and discretised onto a grid of equal cells.
+ * Reading taken: fixed interval [-4, 4), 1024 cells (10 bits), cell width 1/128:
+ *     cell = floor((x + 4) * 128), clamped to [0, 1023];  NaN -> cell 0.
+ * Evaluated as floor(128 x) + 512, which is exact in double (128 x is an exact scaling),
+ * so no intermediate rounding can move a value across a cell edge.                        */
+int32_t oracle_cell(float x)
+{
+    if (isnan(x)) return 0;
+    double t = floor(128.0 * (double)x) + 512.0;
+    if (t < 0.0) return 0;
+    if (t > 1023.0) return 1023;
+    return (int32_t)t;
+}
+
+/* Step 2: bit interleave.  [R] answer W2/A2: the Z-order value interleaves the bits of the
+ * per-axis cells.  Reading taken: bit b of axis a lands on bit 3b + a of the code, so axis
+ * 0 holds the lowest bit of every triple (30-bit code for three 10-bit cells).            */
+uint32_t oracle_interleave(int32_t c0, int32_t c1, int32_t c2)
+{
+    const int32_t c[3] = {c0, c1, c2};
+    uint32_t z = 0;
+    for (int b = 0; b < 10; ++b)
+        for (int a = 0; a < 3; ++a)
+            if ((c[a] >> b) & 1) z |= 1u << (3 * b + a);
+    return z;
+}
+
+/* Z-order codes of `rows` three-dimensional points (row-major [rows][3]).                */
+void oracle_encode(const float *x, int64_t rows, uint32_t *z)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        z[r] = oracle_interleave(oracle_cell(x[3 * r + 0]), oracle_cell(x[3 * r + 1]),
+                                 oracle_cell(x[3 * r + 2]));
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Step 3: exact causal selection.
+ * [R] answers W3/A3 and W2/A2 ("Clarification"): queries and keys live on the 1-D Z-order
+ * line, and a query's top-k are the keys nearest to it on that line; [A] and [S]
+ * ("Problem"): under the causal mask query i may only use keys j <= i.
+ * Reading taken (exact form of "nearest on the line"):
+ *     order every j in [0, i] by (|zq_i - zk_j|, j) lexicographically, take the first
+ *     m = min(k, i + 1); idx[r] is the r-th of them for r < m and -1 for r >= m.
+ * |zq - zk| is the absolute difference of the two unsigned codes.  The selection key is
+ * packed as (|dz| << 32) | j so that one integer comparison is the lexicographic one.     */
+static int cmp_u64(const void *a, const void *b)
+{
+    uint64_t x = *(const uint64_t *)a, y = *(const uint64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* rows[t] = flat query row (bh * N + i); zq, zk hold all B*H*N codes; idx is [nrows][K]. */
+void oracle_select_codes(int64_t N, int64_t K, const uint32_t *zq, const uint32_t *zk,
+                         int64_t nrows, const int64_t *rows, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        uint64_t *keys = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            int64_t row = rows[t];
+            int64_t bh = row / N, i = row % N;
+            const uint32_t *zkh = zk + bh * N;
+            uint32_t z = zq[row];
+            for (int64_t j = 0; j <= i; ++j) {
+                uint64_t dz = z > zkh[j] ? (uint64_t)(z - zkh[j]) : (uint64_t)(zkh[j] - z);
+                keys[j] = (dz << 32) | (uint64_t)j;
+            }
+            qsort(keys, (size_t)(i + 1), sizeof(uint64_t), cmp_u64);
+            int64_t m = K < i + 1 ? K : i + 1;
+            for (int64_t r = 0; r < K; ++r)
+                idx[t * K + r] = r < m ? (int32_t)(keys[r] & 0xffffffffu) : -1;
+        }
+        free(keys);
+    }
+}
+
+/* Selection from the raw fp32 points: encode both sides, then select.                    */
+void oracle_select(int64_t BH, int64_t N, int64_t K, const float *q, const float *k,
+                   int64_t nrows, const int64_t *rows, int32_t *idx)
+{
+    uint32_t *zq = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(BH * N));
+    uint32_t *zk = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(BH * N));
+    oracle_encode(q, BH * N, zq);
+    oracle_encode(k, BH * N, zk);
+    oracle_select_codes(N, K, zq, zk, nrows, rows, idx);
+    free(zq);
+    free(zk);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Value access: v is fp32, or bf16 carried as raw 16-bit patterns (exact widening).      */
+static double value_at(const void *v, int v_bf16, int64_t off)
+{
+    if (v_bf16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)v)[off] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)v)[off];
+}
+
+/* Squared Euclidean distance of the raw (unquantised) fp32 points, in fp64.
+ * [R] answer W3/A3 ("Justification for Euclidean Distance Claim"): similarity is the
+ * Euclidean distance between query and key, not a dot product.                           */
+static double sqdist(const float *a, const float *b)
+{
+    double s = 0.0;
+    for (int c = 0; c < 3; ++c) {
+        double d = (double)a[c] - (double)b[c];
+        s += d * d;
+    }
+    return s;
+}
+
+/* Steps 4-5: Adaptive Cauchy-softmax over the selected set, then the weighted sum.
+ * [R] answer W2/A2 ("Discussion on its robustness"): the Cauchy kernel carries a trainable
+ * scale gamma (gamma = 1 gives the static Student-t kernel):
+ *     s_ij = 1 / (1 + ||q_i - k_j||^2 / gamma_h^2),   a_ij = s_ij / sum_j' s_ij',
+ *     o_i  = sum_j a_ij v_j          (sums over the selected j only).
+ * gamma is one value per head, shared over the batch.  `rows` lists flat query rows; idx,
+ * out and (optionally) weights are laid out per listed row.                               */
+void oracle_forward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
+                    const float *q, const float *k, const void *v, const float *gamma,
+                    int64_t nrows, const int64_t *rows, const int32_t *idx,
+                    double *out, double *weights)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < nrows; ++t) {
+        int64_t row = rows[t];
+        int64_t bh = row / N;
+        double g = (double)gamma[bh % H];
+        double s[K > 0 ? K : 1];
+        double S = 0.0;
+        for (int64_t r = 0; r < K; ++r) {
+            int32_t j = idx[t * K + r];
+            s[r] = 0.0;
+            if (j < 0) continue;
+            double d = sqdist(q + 3 * row, k + 3 * (bh * N + j));
+            s[r] = 1.0 / (1.0 + d / (g * g));
+            S += s[r];
+        }
+        for (int64_t c = 0; c < dv; ++c) out[t * dv + c] = 0.0;
+        for (int64_t r = 0; r < K; ++r) {
+            int32_t j = idx[t * K + r];
+            double a = j < 0 ? 0.0 : s[r] / S;
+            if (weights) weights[t * K + r] = a;
+            if (j < 0) continue;
+            for (int64_t c = 0; c < dv; ++c)
+                out[t * dv + c] += a * value_at(v, v_bf16, (bh * N + j) * dv + c);
+        }
+    }
+}
+
+/* Step 6: gradients of the forward above with the selection held fixed.
+ * [R] answers W3/A3 and Q2 describe forward+backward as the training cost, and gamma is
+ * trained ("Discussion on its robustness"), so dq, dk, dv and dgamma are all needed.
+ * Chain rule of o_i = sum_r a_ir v_r with a_ir = s_ir / S_i, s_ir = 1/(1 + d_ir/gamma^2):
+ *     g_ir  = dO_i . v_r                     (dL/da_ir)
+ *     D_i   = sum_r a_ir g_ir
+ *     dL/ds_ir = (g_ir - D_i) / S_i
+ *     ds/dd    = -s^2 / gamma^2,   ds/dgamma = 2 d s^2 / gamma^3
+ *     c_ir  = a_ir s_ir (g_ir - D_i)
+ *     dq_i  = -(2/gamma^2) sum_r c_ir (q_i - k_r)
+ *     dk_r += (2/gamma^2) c_ir (q_i - k_r)
+ *     dv_r += a_ir dO_i
+ *     dgamma_h += (2/gamma^3) c_ir d_ir
+ * dq is written per listed row ([nrows][3]); dk ([B*H*N][3]), dv ([B*H*N][dv]) and
+ * dgamma ([H]) are accumulated (the caller zeroes them), so listing every query row that
+ * can select a key gives that key's complete gradient.  Runs sequentially.               */
+void oracle_backward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
+                     const float *q, const float *k, const void *v, const float *gamma,
+                     const void *dout, int64_t nrows, const int64_t *rows,
+                     const int32_t *idx, double *dq, double *dk, double *dvout,
+                     double *dgamma)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *d = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *gr = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    for (int64_t t = 0; t < nrows; ++t) {
+        int64_t row = rows[t];
+        int64_t bh = row / N, h = bh % H;
+        double g = (double)gamma[h];
+        const float *qi = q + 3 * row;
+        double S = 0.0;
+        for (int64_t r = 0; r < K; ++r) {
+            int32_t j = idx[t * K + r];
+            s[r] = d[r] = gr[r] = 0.0;
+            if (j < 0) continue;
+            int64_t col = bh * N + j;
+            d[r] = sqdist(qi, k + 3 * col);
+            s[r] = 1.0 / (1.0 + d[r] / (g * g));
+            S += s[r];
+            double acc = 0.0;
+            for (int64_t c = 0; c < dv; ++c)
+                acc += value_at(dout, v_bf16, row * dv + c) * value_at(v, v_bf16, col * dv + c);
+            gr[r] = acc;
+        }
+        double D = 0.0;
+        for (int64_t r = 0; r < K; ++r)
+            if (idx[t * K + r] >= 0) D += (s[r] / S) * gr[r];
+        double dqi[3] = {0.0, 0.0, 0.0};
+        for (int64_t r = 0; r < K; ++r) {
+            int32_t j = idx[t * K + r];
+            if (j < 0) continue;
+            int64_t col = bh * N + j;
+            double a = s[r] / S;
+            double c = a * s[r] * (gr[r] - D);
+            for (int e = 0; e < 3; ++e) {
+                double diff = (double)qi[e] - (double)k[3 * col + e];
+                dqi[e] += -(2.0 / (g * g)) * c * diff;
+                dk[3 * col + e] += (2.0 / (g * g)) * c * diff;
+            }
+            for (int64_t cc = 0; cc < dv; ++cc)
+                dvout[col * dv + cc] += a * value_at(dout, v_bf16, row * dv + cc);
+            dgamma[h] += (2.0 / (g * g * g)) * c * d[r];
+        }
+        for (int e = 0; e < 3; ++e) dq[3 * t + e] = dqi[e];
+    }
+    free(s);
+    free(d);
+    free(gr);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Rounding of an fp64 result to bf16 (round to nearest, ties to even), as raw bits.
+ * Used to state what "the exact result in the output dtype" is for bf16 outputs.          */
+uint16_t oracle_bf16_bits(double x)
+{
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0) return sign;
+    int e;
+    frexp(ax, &e);                       /* ax = m * 2^e, m in [0.5, 1)          */
+    int qexp = e - 8;                    /* 8 significant bits in bf16           */
+    if (qexp < -133) qexp = -133;        /* bf16 subnormal spacing is 2^-133     */
+    double r = nearbyint(ldexp(ax, -qexp)) ;
+    double val = ldexp(r, qexp);
+    if (val >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float f = (float)val;                /* exact: val has <= 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (bits >> 16));
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
