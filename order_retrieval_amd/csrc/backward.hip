@@ -1,0 +1,456 @@
+// backward.hip -- gradients of the Cauchy-weighted top-k attention with the selection fixed.
+//
+// "ZETA: Leveraging Z-order Curves for Efficient Top-k Attention", rebuttal page: answers
+// W3/A3 and Q2 time the forward+backward pass used for training; answer W2/A2 ("Discussion
+// on its robustness") makes gamma trainable.  With s = 1/(1 + d/gamma^2), a = s/S,
+// g_ij = dO_i . v_j, D_i = sum_j a_ij g_ij and c_ij = a_ij s_ij (g_ij - D_i):
+//     dq_i = -(2/gamma^2) sum_j c_ij (q_i - k_j)        dv_j = sum_i a_ij dO_i
+//     dk_j =  (2/gamma^2) sum_i c_ij (q_i - k_j)        dgamma = (2/gamma^3) sum c_ij d_ij
+//
+// Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
+//   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij, dq_i and the
+//      query's dgamma term;
+//   2. selection transpose: stable LSD radix sort (8-bit digits) of the valid (j, pair id)
+//      pairs of every (b,h) by j; pair ids stay ascending inside a key's segment;
+//   3. segment starts offs[j] from the sorted keys;
+//   4. per-key pass: each key reduces its segment in ascending query order (dv, dk);
+//   5. dgamma: fixed-order reduction per head over the batch and the queries.
+#include "zeta_internal.hpp"
+#include "vec_io.hpp"
+
+namespace zeta {
+
+constexpr int kRadixThreads = 256;
+constexpr int kRadixItems = 16;
+constexpr int kRadixTile = kRadixThreads * kRadixItems;
+constexpr int kMaxGroups = 256 / 8;  // groups per workgroup (at least 8 lanes per group)
+
+// A selection slot r of query i is a pair when r < min(topk, i+1); its key is clamped into
+// [0, i], so an index tensor that is not a valid selection still never leads outside the
+// buffers (the result is then meaningless but defined).
+__device__ __forceinline__ int64_t clamp_index(int32_t j, int64_t i) {
+    return j < 0 ? 0 : (j > i ? i : j);
+}
+
+__device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64_t e, int topk,
+                                          uint32_t& key) {
+    const uint32_t i = static_cast<uint32_t>(e) / static_cast<uint32_t>(topk);
+    const uint32_t r = static_cast<uint32_t>(e) - i * static_cast<uint32_t>(topk);
+    if (r > i) return false;  // slot beyond min(topk, i+1)
+    key = static_cast<uint32_t>(clamp_index(idx[e], i));
+    return true;
+}
+
+__device__ __forceinline__ float group_sum(float x, int G) {
+    for (int off = G >> 1; off > 0; off >>= 1) x += __shfl_xor(x, off, G);
+    return x;
+}
+
+// ---------------------------------------------------------------------------- 1. queries
+template <bool BF16, int CPL>
+__global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ gamma, const int32_t* __restrict__ idx,
+    const void* __restrict__ dout, int64_t rows, int64_t N, int64_t H, int dv, int topk,
+    int glog, float* __restrict__ A, float* __restrict__ Cc, float* __restrict__ dq,
+    float* __restrict__ dg_row) {
+    using IO = VecIO<BF16>;
+    using T = typename IO::elem_t;
+    constexpr int E = IO::kElems;
+    __shared__ float2 sh[kMaxGroups][kMaxTopK];
+    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = gtid >> glog;
+    const int G = 1 << glog;
+    const int lane = static_cast<int>(gtid & (G - 1));
+    const int grp = threadIdx.x >> glog;
+    if (row >= rows) return;
+    const int chunks = dv / E;
+    const int64_t bh = row / N;
+    const int64_t i = row - bh * N;
+    const float g = gamma[bh % H];
+    const float inv_g2 = 1.0f / (g * g);
+    const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
+    const int m = static_cast<int>(i + 1 < topk ? i + 1 : topk);
+    const int32_t* ir = idx + row * topk;
+    const float* kh = k + bh * N * 3;
+    const T* vh = static_cast<const T*>(v) + bh * N * dv;
+
+    float go[CPL][E];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + c * G;
+        if (ch < chunks) {
+            IO::load(static_cast<const T*>(dout) + row * dv + ch * E, go[c]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
+        }
+    }
+
+    float S = 0.0f, Tsum = 0.0f;
+#pragma unroll 4
+    for (int r = 0; r < m; ++r) {
+        const int64_t j = clamp_index(ir[r], i);
+        const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
+        const float d = d0 * d0 + d1 * d1 + d2 * d2;
+        const float s = 1.0f / (1.0f + d * inv_g2);
+        float part = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = lane + c * G;
+            if (ch < chunks) {
+                float x[E];
+                IO::load(vh + j * dv + ch * E, x);
+#pragma unroll
+                for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
+            }
+        }
+        const float gr = group_sum(part, G);
+        S += s;
+        Tsum += s * gr;
+        if ((r & (G - 1)) == lane) sh[grp][r] = make_float2(s, gr);
+    }
+    const float inv_S = 1.0f / S;
+    const float D = Tsum * inv_S;
+
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
+    for (int r = lane; r < m; r += G) {
+        const float2 sg = sh[grp][r];
+        const int64_t j = clamp_index(ir[r], i);
+        const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
+        const float d = d0 * d0 + d1 * d1 + d2 * d2;
+        const float a = sg.x * inv_S;
+        const float c = a * sg.x * (sg.y - D);
+        A[row * topk + r] = a;
+        Cc[row * topk + r] = c;
+        a0 += c * d0;
+        a1 += c * d1;
+        a2 += c * d2;
+        ag += c * d;
+    }
+    a0 = group_sum(a0, G);
+    a1 = group_sum(a1, G);
+    a2 = group_sum(a2, G);
+    ag = group_sum(ag, G);
+    if (lane == 0) {
+        const float f = -2.0f * inv_g2;
+        dq[3 * row] = f * a0;
+        dq[3 * row + 1] = f * a1;
+        dq[3 * row + 2] = f * a2;
+        dg_row[row] = 2.0f * inv_g2 / g * ag;
+    }
+}
+
+// ---------------------------------------------------------------------------- 2. transpose
+// Digit counts of one tile of items.  Pass 0 reads the selection itself (-1 slots are not
+// pairs); later passes read the previous pass's keys (all valid).
+__global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ keys_in, int64_t items,
+    int64_t in_stride, int shift, int64_t tiles, int topk, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[256];
+    const int64_t bh = blockIdx.y;
+    cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    for (int it = 0; it < kRadixItems; ++it) {
+        const int64_t e = t0 + it * kRadixThreads + threadIdx.x;
+        if (e < items) {
+            uint32_t key = 0;
+            bool valid;
+            if (idx) {
+                valid = pair_item(idx + bh * in_stride, e, topk, key);
+            } else {
+                valid = true;
+                key = keys_in[bh * in_stride + e];
+            }
+            if (valid) atomicAdd(&cnt[(key >> shift) & 255u], 1u);
+        }
+    }
+    __syncthreads();
+    hist[(bh * 256 + threadIdx.x) * tiles + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Exclusive scan of one (b,h, digit) row of per-tile counts (in place) and its total.
+__global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restrict__ hist,
+                                                             int64_t tiles,
+                                                             uint32_t* __restrict__ totals) {
+    const int64_t rowid = static_cast<int64_t>(blockIdx.y) * 256 + blockIdx.x;
+    uint32_t* h = hist + rowid * tiles;
+    const int lane = threadIdx.x;
+    const int64_t per = (tiles + 63) / 64;
+    const int64_t b0 = lane * per;
+    const int64_t b1 = b0 + per < tiles ? b0 + per : tiles;
+    uint32_t local = 0;
+    for (int64_t t = b0; t < b1; ++t) local += h[t];
+    uint32_t incl = local;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    uint32_t run = incl - local;
+    for (int64_t t = b0; t < b1; ++t) {
+        const uint32_t c = h[t];
+        h[t] = run;
+        run += c;
+    }
+    if (lane == 63) totals[rowid] = incl;
+}
+
+// Stable scatter of one tile: items are ranked in (iteration, wave, lane) order, which is
+// their input order, so equal digits keep their relative order.
+__global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ keys_in,
+    const uint32_t* __restrict__ vals_in, int64_t items, int64_t in_stride, int shift,
+    int64_t tiles, int topk, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals,
+    int64_t P, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    __shared__ uint32_t base[256];
+    __shared__ uint32_t scan[256];
+    __shared__ uint32_t wcnt[4][256];
+    __shared__ uint32_t wpre[4][256];
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+
+    scan[tid] = totals[bh * 256 + tid];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan of the totals
+        const uint32_t y = tid >= off ? scan[tid - off] : 0u;
+        __syncthreads();
+        scan[tid] += y;
+        __syncthreads();
+    }
+    base[tid] = scan[tid] - totals[bh * 256 + tid] + hist[(bh * 256 + tid) * tiles + blockIdx.x];
+    uint32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    for (int it = 0; it < kRadixItems; ++it) {
+        const int64_t e = t0 + it * kRadixThreads + tid;
+        bool valid = false;
+        uint32_t key = 0, val = 0;
+        if (e < items) {
+            if (idx) {
+                valid = pair_item(idx + bh * in_stride, e, topk, key);
+                val = static_cast<uint32_t>(e);
+            } else {
+                valid = true;
+                key = keys_in[bh * in_stride + e];
+                val = vals_in[bh * in_stride + e];
+            }
+        }
+        const uint32_t digit = valid ? (key >> shift) & 255u : 0u;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (digit >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        if (!valid) peers = 0;
+        const uint32_t rank = __popcll(peers & lt);
+        if (valid && (peers & lt) == 0) wcnt[wave][digit] = __popcll(peers);
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            wpre[w][tid] = run;
+            run += wcnt[w][tid];
+            wcnt[w][tid] = 0;
+        }
+        __syncthreads();
+        if (valid) {
+            const uint32_t pos = base[digit] + wpre[wave][digit] + rank;
+            keys_out[bh * P + pos] = key;
+            vals_out[bh * P + pos] = val;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- 3. offsets
+__global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint32_t* __restrict__ keys,
+                                                                    int64_t P, int64_t N,
+                                                                    uint32_t* __restrict__ offs) {
+    const int64_t bh = blockIdx.y;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= P) return;
+    const uint32_t* kh = keys + bh * P;
+    uint32_t* oh = offs + bh * (N + 1);
+    const int64_t kk = kh[t];
+    const int64_t lo = t == 0 ? 0 : static_cast<int64_t>(kh[t - 1]) + 1;
+    for (int64_t jj = lo; jj <= kk; ++jj) oh[jj] = static_cast<uint32_t>(t);
+    if (t == P - 1)
+        for (int64_t jj = kk + 1; jj <= N; ++jj) oh[jj] = static_cast<uint32_t>(P);
+}
+
+// ---------------------------------------------------------------------------- 4. keys
+template <bool BF16, int CPL>
+__global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
+    const void* __restrict__ dout, const float* __restrict__ A, const float* __restrict__ Cc,
+    const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ offs, int64_t rows,
+    int64_t N, int64_t H, int dv, int topk, int glog, int64_t P, float* __restrict__ dk,
+    void* __restrict__ dvout) {
+    using IO = VecIO<BF16>;
+    using T = typename IO::elem_t;
+    constexpr int E = IO::kElems;
+    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = gtid >> glog;
+    const int G = 1 << glog;
+    const int lane = static_cast<int>(gtid & (G - 1));
+    if (row >= rows) return;
+    const int chunks = dv / E;
+    const int64_t bh = row / N;
+    const int64_t j = row - bh * N;
+    const float g = gamma[bh % H];
+    const float inv_g2 = 1.0f / (g * g);
+    const float k0 = k[3 * row], k1 = k[3 * row + 1], k2 = k[3 * row + 2];
+    const uint32_t seg0 = offs[bh * (N + 1) + j], seg1 = offs[bh * (N + 1) + j + 1];
+    const uint32_t* ph = pairs + bh * P;
+    const float* Ah = A + bh * N * topk;
+    const float* Ch = Cc + bh * N * topk;
+    const float* qh = q + bh * N * 3;
+    const T* doh = static_cast<const T*>(dout) + bh * N * dv;
+
+    float acc[CPL][E];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+#pragma unroll 4
+    for (uint32_t t = seg0; t < seg1; ++t) {
+        const uint32_t pid = ph[t];
+        const int64_t i = pid / static_cast<uint32_t>(topk);
+        const float a = Ah[pid], c = Ch[pid];
+        s0 += c * (qh[3 * i] - k0);
+        s1 += c * (qh[3 * i + 1] - k1);
+        s2 += c * (qh[3 * i + 2] - k2);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int ch = lane + cc * G;
+            if (ch < chunks) {
+                float x[E];
+                IO::load(doh + i * dv + ch * E, x);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[cc][e] += a * x[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + c * G;
+        if (ch < chunks) IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
+    }
+    if (lane == 0) {
+        const float f = 2.0f * inv_g2;
+        dk[3 * row] = f * s0;
+        dk[3 * row + 1] = f * s1;
+        dk[3 * row + 2] = f * s2;
+    }
+}
+
+// ---------------------------------------------------------------------------- 5. dgamma
+__global__ void __launch_bounds__(256) zeta_dgamma_reduce_kernel(const float* __restrict__ dg_row,
+                                                                  int64_t B, int64_t H, int64_t N,
+                                                                  float* __restrict__ dgamma) {
+    __shared__ float red[256];
+    const int64_t h = blockIdx.x;
+    float acc = 0.0f;
+    for (int64_t b = 0; b < B; ++b) {
+        const float* p = dg_row + (b * H + h) * N;
+        for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += p[i];
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dgamma[h] = red[0];
+}
+
+// ---------------------------------------------------------------------------- host
+size_t bwd_pairs_per_head(int64_t N, int topk) {
+    if (N <= topk) return static_cast<size_t>(N * (N + 1) / 2);
+    return static_cast<size_t>(int64_t(topk) * (topk + 1) / 2 + (N - topk) * topk);
+}
+
+int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
+
+template <bool BF16, int CPL>
+static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk, int glog,
+                               const float* q, const float* k, const void* v, const float* gamma,
+                               const int32_t* idx, const void* dout, float* dq, float* dk,
+                               void* dvout, float* dgamma, const BwdBuffers& ws,
+                               const StageEvents& marks, hipStream_t s) {
+    const int64_t rows = BH * N;
+    marks.record(0, s);
+    const int64_t gblocks = ((rows << glog) + 255) / 256;
+    hipLaunchKernelGGL((zeta_bwd_query_kernel<BF16, CPL>), dim3(static_cast<unsigned>(gblocks)),
+                       dim3(256), 0, s, q, k, v, gamma, idx, dout, rows, N, H, dv, topk, glog,
+                       ws.A, ws.C, dq, ws.dg_row);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    marks.record(1, s);
+
+    int bits = 0;
+    while ((int64_t(1) << bits) < N) ++bits;
+    const int passes = bits <= 8 ? 1 : (bits + 7) / 8;
+    const int64_t raw_items = N * topk;
+    uint32_t* kin = nullptr;
+    uint32_t* vin = nullptr;
+    for (int p = 0; p < passes; ++p) {
+        const bool first = p == 0;
+        const int64_t items = first ? raw_items : ws.P;
+        const int64_t stride = first ? raw_items : ws.P;
+        const int64_t tiles = bwd_tiles_per_head(items);
+        uint32_t* kout = (p & 1) ? ws.key1 : ws.key0;
+        uint32_t* vout = (p & 1) ? ws.val1 : ws.val0;
+        const int32_t* pidx = first ? idx : nullptr;
+        dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
+        hipLaunchKernelGGL(zeta_radix_hist_kernel, grid, dim3(kRadixThreads), 0, s, pidx, kin,
+                           items, stride, 8 * p, tiles, topk, ws.hist);
+        hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64),
+                           0, s, ws.hist, tiles, ws.totals);
+        hipLaunchKernelGGL(zeta_radix_scatter_kernel, grid, dim3(kRadixThreads), 0, s, pidx, kin,
+                           vin, items, stride, 8 * p, tiles, topk, ws.hist, ws.totals, ws.P, kout,
+                           vout);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        kin = kout;
+        vin = vout;
+    }
+    hipLaunchKernelGGL(zeta_segment_offsets_kernel,
+                       dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
+                       dim3(256), 0, s, kin, ws.P, N, ws.offs);
+    marks.record(2, s);
+    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(gblocks)),
+                       dim3(256), 0, s, q, k, gamma, dout, ws.A, ws.C, vin, ws.offs, rows, N, H, dv,
+                       topk, glog, ws.P, dk, dvout);
+    marks.record(3, s);
+    hipLaunchKernelGGL(zeta_dgamma_reduce_kernel, dim3(static_cast<unsigned>(H)), dim3(256), 0, s,
+                       ws.dg_row, BH / H, H, N, dgamma);
+    marks.record(4, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
+                      const float* q, const float* k, const void* v, const float* gamma,
+                      const int32_t* idx, const void* dout, float* dq, float* dk, void* dvout,
+                      float* dgamma, const BwdBuffers& ws, const StageEvents& marks,
+                      hipStream_t s) {
+    if (BH * N <= 0) return hipSuccess;
+    const int chunks = static_cast<int>(dv / (bf16 ? 8 : 4));
+    const int glog = group_log2(chunks);
+    const int cpl = (chunks + (1 << glog) - 1) >> glog;
+    if (bf16)
+        return cpl == 1 ? launch_bwd_t<true, 1>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s)
+                        : launch_bwd_t<true, 2>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+    return cpl == 1 ? launch_bwd_t<false, 1>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s)
+                    : launch_bwd_t<false, 2>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+}
+
+}  // namespace zeta

@@ -1,0 +1,179 @@
+// tree.hip -- per-(b,h) merge-sort tree of the key codes.
+//
+// "ZETA: Leveraging Z-order Curves for Efficient Top-k Attention", rebuttal page, answers
+// W3/A3 and W2/A2 ("Clarification"): keys are sorted along the Z-order line so that a
+// query finds its neighbours by binary search around its insertion position.  Under the
+// causal mask a query i may only see keys j <= i, so instead of one sort the keys are kept
+// sorted per aligned power-of-two block of positions: level l holds every block
+// [m 2^l, (m+1) 2^l) sorted (the last block possibly shorter).  Any prefix [0, i] is the
+// union of at most log2(N)+1 such blocks.
+//
+// Two trees are built from the same codes with different packed keys, both sorted as plain
+// ascending uint64:
+//   asc : (code << 32) | j          -> code ascending, j ascending
+//   desc: (code << 32) | ~j         -> code ascending, j descending
+// The selection kernel walks the asc tree forward (codes >= the query) and the desc tree
+// backward (codes < the query), so both walks meet equal codes in ascending j order.
+//
+// Build: levels 0..10 inside one workgroup per 1024-entry tile (LDS rank merge: each entry
+// moves to its own index plus its rank in the sibling block; keys are unique, so this is
+// an exact merge), then one merge-path launch per higher level (streaming: 8 B read and
+// 8 B written per entry and tree).
+#include "zeta_internal.hpp"
+
+namespace zeta {
+
+constexpr int kTileLog = 10;
+constexpr int kTile = 1 << kTileLog;
+constexpr int kMergeTile = 2048;  // merged outputs per workgroup, 8 per thread
+
+__device__ __forceinline__ int lds_lower_bound(const uint64_t* a, int n, uint64_t x) {
+    int lo = 0;
+    while (n > 0) {
+        int half = n >> 1;
+        if (a[lo + half] < x) {
+            lo += half + 1;
+            n -= half + 1;
+        } else {
+            n = half;
+        }
+    }
+    return lo;
+}
+
+__global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const uint32_t* __restrict__ zk,
+                                                              uint64_t* __restrict__ asc,
+                                                              uint64_t* __restrict__ desc,
+                                                              int64_t N, int levels, int top) {
+    __shared__ uint64_t buf[2][2][kTile];  // [tree][ping-pong][entry]
+    const int64_t bh = blockIdx.y;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
+    const int n = static_cast<int>(N - base < kTile ? N - base : kTile);
+    const uint32_t* zrow = zk + bh * N + base;
+    uint64_t* tA = asc + bh * levels * N + base;
+    uint64_t* tD = desc + bh * levels * N + base;
+
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        const uint32_t j = static_cast<uint32_t>(base + e);
+        const uint64_t c = static_cast<uint64_t>(zrow[e]) << 32;
+        const uint64_t ka = c | j, kd = c | static_cast<uint32_t>(~j);
+        buf[0][0][e] = ka;
+        buf[1][0][e] = kd;
+        tA[e] = ka;
+        tD[e] = kd;
+    }
+    __syncthreads();
+
+    int cur = 0;
+    for (int l = 0; l < top; ++l) {
+        const int s = 1 << l;
+        for (int e = threadIdx.x; e < n; e += blockDim.x) {
+            const int run0 = e & ~(2 * s - 1);
+            const bool inB = (e & s) != 0;
+            const int own = e - run0 - (inB ? s : 0);
+            const int sib0 = inB ? run0 : run0 + s;
+            int sibLen = n - sib0;
+            sibLen = sibLen < 0 ? 0 : (sibLen > s ? s : sibLen);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint64_t x = buf[t][cur][e];
+                const int r = lds_lower_bound(&buf[t][cur][sib0], sibLen, x);
+                buf[t][cur ^ 1][run0 + own + r] = x;
+            }
+        }
+        __syncthreads();
+        cur ^= 1;
+        uint64_t* oA = tA + static_cast<int64_t>(l + 1) * N;
+        uint64_t* oD = tD + static_cast<int64_t>(l + 1) * N;
+        for (int e = threadIdx.x; e < n; e += blockDim.x) {
+            oA[e] = buf[0][cur][e];
+            oD[e] = buf[1][cur][e];
+        }
+    }
+}
+
+// Number of A entries among the first d outputs of merge(A, B) (keys unique).
+__device__ __forceinline__ int diag_split(const uint64_t* A, int na, const uint64_t* B, int nb,
+                                          int d) {
+    int lo = d - nb > 0 ? d - nb : 0;
+    int hi = d < na ? d : na;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (A[mid] < B[d - 1 - mid])
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// Level l -> l+1 for l >= kTileLog: merge sibling blocks of 2^l entries (merge path).
+__global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restrict__ asc,
+                                                               uint64_t* __restrict__ desc,
+                                                               int64_t N, int levels, int l) {
+    __shared__ uint64_t seg[kMergeTile];
+    __shared__ int split[2];
+    const int64_t bh = blockIdx.y;
+    uint64_t* T = (blockIdx.z ? desc : asc) + bh * levels * N;
+    const uint64_t* src = T + static_cast<int64_t>(l) * N;
+    uint64_t* dst = T + static_cast<int64_t>(l + 1) * N;
+    const int64_t s = int64_t(1) << l;
+    const int64_t o0 = static_cast<int64_t>(blockIdx.x) * kMergeTile;
+    if (o0 >= N) return;
+    const int64_t run0 = o0 & ~(2 * s - 1);
+    const int na = static_cast<int>(N - run0 < s ? N - run0 : s);
+    int64_t nbl = N - run0 - s;
+    const int nb = static_cast<int>(nbl < 0 ? 0 : (nbl > s ? s : nbl));
+    const uint64_t* A = src + run0;
+    const uint64_t* B = src + run0 + s;
+    const int d0 = static_cast<int>(o0 - run0);
+    const int d1 = d0 + kMergeTile < na + nb ? d0 + kMergeTile : na + nb;
+
+    if (threadIdx.x < 2) split[threadIdx.x] = diag_split(A, na, B, nb, threadIdx.x ? d1 : d0);
+    __syncthreads();
+    const int a0 = split[0], a1 = split[1];
+    const int b0 = d0 - a0, b1 = d1 - a1;
+    const int ca = a1 - a0, cb = b1 - b0;
+    for (int e = threadIdx.x; e < ca + cb; e += blockDim.x)
+        seg[e] = e < ca ? A[a0 + e] : B[b0 + e - ca];
+    __syncthreads();
+
+    const uint64_t* sa = seg;
+    const uint64_t* sb = seg + ca;
+    const int t0 = threadIdx.x * 8;
+    if (t0 >= ca + cb) return;
+    int ia = diag_split(sa, ca, sb, cb, t0);
+    int ib = t0 - ia;
+    uint64_t* out = dst + run0 + d0 + t0;
+    const int cnt = ca + cb - t0 < 8 ? ca + cb - t0 : 8;
+    for (int u = 0; u < cnt; ++u) {
+        uint64_t x;
+        if (ib >= cb || (ia < ca && sa[ia] < sb[ib]))
+            x = sa[ia++];
+        else
+            x = sb[ib++];
+        out[u] = x;
+    }
+}
+
+hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
+                             uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
+    if (BH <= 0 || N <= 0) return hipSuccess;
+    const int top_tile = levels - 1 < kTileLog ? levels - 1 : kTileLog;
+    dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
+    hipLaunchKernelGGL(zeta_tree_tile_kernel, grid, dim3(256), 0, s, zk, tree_asc, tree_desc,
+                       N, levels, top_tile);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int l = top_tile; l + 1 < levels; ++l) {
+        dim3 g(static_cast<unsigned>((N + kMergeTile - 1) / kMergeTile),
+               static_cast<unsigned>(BH), 2);
+        hipLaunchKernelGGL(zeta_tree_merge_kernel, g, dim3(256), 0, s, tree_asc, tree_desc, N,
+                           levels, l);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace zeta

@@ -1,0 +1,305 @@
+// zeta_api.hip -- the C ABI of include/zeta.h: validation, workspace plan, launch order.
+//
+// Everything is validated on the host before the first launch; the library allocates
+// nothing (scratch lives in the caller's workspace) and never synchronises the stream.
+#include <stdio.h>
+
+#include <string>
+
+#include "zeta.h"
+#include "zeta_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local zeta::StageEvents g_marks;
+
+zeta_status fail(zeta_status st, const char* msg) {
+    g_last_error = msg;
+    return st;
+}
+
+zeta_status fail_hip(const char* what, hipError_t e) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+    g_last_error = buf;
+    return ZETA_ERR_HIP;
+}
+
+int levels_of(int64_t N) {
+    int l = 0;
+    while ((int64_t(2) << l) <= N) ++l;
+    return l + 1;
+}
+
+size_t align_up(size_t x) { return (x + zeta::kAlign - 1) & ~(zeta::kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+zeta_status check_shape(const zeta_shape* sh) {
+    if (!sh) return fail(ZETA_ERR_INVALID_ARGUMENT, "shape is NULL");
+    if (sh->B < 1 || sh->H < 1 || sh->N < 1)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "B, H and N must be >= 1");
+    if (sh->topk < 1) return fail(ZETA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+    if (sh->topk > zeta::kMaxTopK) return fail(ZETA_ERR_UNSUPPORTED, "topk above ZETA_MAX_TOPK");
+    if (sh->dv < 8 || sh->dv % 8 != 0)
+        return fail(ZETA_ERR_UNSUPPORTED, "dv must be a positive multiple of 8");
+    if (sh->dv > zeta::kMaxDv) return fail(ZETA_ERR_UNSUPPORTED, "dv above ZETA_MAX_DV");
+    if (sh->v_dtype != ZETA_F32 && sh->v_dtype != ZETA_BF16)
+        return fail(ZETA_ERR_UNSUPPORTED, "v_dtype must be ZETA_F32 or ZETA_BF16");
+    if (sh->reserved != 0) return fail(ZETA_ERR_INVALID_ARGUMENT, "reserved must be 0");
+    if (sh->N >= (int64_t(1) << 30)) return fail(ZETA_ERR_UNSUPPORTED, "N must be < 2^30");
+    const int64_t lim = int64_t(1) << 31;
+    if (sh->B > lim || sh->H > lim || sh->B * sh->H > lim / sh->N ||
+        sh->B * sh->H * sh->N > (lim - 1) / sh->topk)
+        return fail(ZETA_ERR_UNSUPPORTED, "B*H*N*topk must be < 2^31");
+    return ZETA_OK;
+}
+
+zeta_status preflight() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip("no usable HIP device", e);
+    return ZETA_OK;
+}
+
+struct FwdPlan {
+    size_t zq, zk, tasc, tdesc, total;
+};
+
+FwdPlan plan_fwd(const zeta_shape* sh) {
+    const int64_t BHN = sh->B * sh->H * sh->N;
+    const int L = levels_of(sh->N);
+    FwdPlan p{};
+    size_t off = 0;
+    p.zq = off;
+    off += align_up(sizeof(uint32_t) * BHN);
+    p.zk = off;
+    off += align_up(sizeof(uint32_t) * BHN);
+    p.tasc = off;
+    off += align_up(sizeof(uint64_t) * BHN * L);
+    p.tdesc = off;
+    off += align_up(sizeof(uint64_t) * BHN * L);
+    p.total = off;
+    return p;
+}
+
+struct BwdPlan {
+    size_t A, C, dg, k0, v0, k1, v1, hist, totals, offs, total;
+    int64_t P, tiles;
+};
+
+BwdPlan plan_bwd(const zeta_shape* sh) {
+    const int64_t BH = sh->B * sh->H, N = sh->N, K = sh->topk;
+    BwdPlan p{};
+    p.P = static_cast<int64_t>(zeta::bwd_pairs_per_head(N, static_cast<int>(K)));
+    p.tiles = zeta::bwd_tiles_per_head(N * K);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    p.A = take(sizeof(float) * BH * N * K);
+    p.C = take(sizeof(float) * BH * N * K);
+    p.dg = take(sizeof(float) * BH * N);
+    p.k0 = take(sizeof(uint32_t) * BH * p.P);
+    p.v0 = take(sizeof(uint32_t) * BH * p.P);
+    p.k1 = take(sizeof(uint32_t) * BH * p.P);
+    p.v1 = take(sizeof(uint32_t) * BH * p.P);
+    p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
+    p.totals = take(sizeof(uint32_t) * BH * 256);
+    p.offs = take(sizeof(uint32_t) * BH * (N + 1));
+    p.total = off;
+    return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+zeta_status check_ws(void* ws, size_t have, size_t need) {
+    if (!ws) return fail(ZETA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned(ws, zeta::kAlign))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (have < need) return fail(ZETA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+    return ZETA_OK;
+}
+
+zeta_status check_qk(const float* q, const float* k) {
+    if (!q || !k) return fail(ZETA_ERR_INVALID_ARGUMENT, "q or k is NULL");
+    if (!aligned(q, 4) || !aligned(k, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "q and k must be 4-byte aligned");
+    return ZETA_OK;
+}
+
+zeta_status run_select(const zeta_shape* sh, const float* q, const float* k, int32_t* idx, void* ws,
+                       hipStream_t s) {
+    const FwdPlan p = plan_fwd(sh);
+    const int64_t BH = sh->B * sh->H, N = sh->N, BHN = BH * N;
+    const int L = levels_of(N);
+    uint32_t* zq = at<uint32_t>(ws, p.zq);
+    uint32_t* zk = at<uint32_t>(ws, p.zk);
+    uint64_t* ta = at<uint64_t>(ws, p.tasc);
+    uint64_t* td = at<uint64_t>(ws, p.tdesc);
+    g_marks.record(0, s);
+    hipError_t e = zeta::launch_encode(q, BHN, zq, s);
+    if (e != hipSuccess) return fail_hip("encode launch", e);
+    e = zeta::launch_encode(k, BHN, zk, s);
+    if (e != hipSuccess) return fail_hip("encode launch", e);
+    g_marks.record(1, s);
+    e = zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
+    if (e != hipSuccess) return fail_hip("tree launch", e);
+    g_marks.record(2, s);
+    e = zeta::launch_select(BH, N, L, static_cast<int>(sh->topk), zq, ta, td, idx, s);
+    if (e != hipSuccess) return fail_hip("select launch", e);
+    g_marks.record(3, s);
+    return ZETA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zeta_workspace_bytes(const zeta_shape* shape, int32_t kind) {
+    if (check_shape(shape) != ZETA_OK) return 0;
+    switch (kind) {
+        case ZETA_WS_SELECT:
+        case ZETA_WS_FWD:
+            return plan_fwd(shape).total;
+        case ZETA_WS_BWD:
+            return plan_bwd(shape).total;
+        default:
+            g_last_error = "unknown workspace kind";
+            return 0;
+    }
+}
+
+int32_t zeta_tree_levels(int64_t N) { return N < 1 ? 0 : levels_of(N); }
+
+zeta_status zeta_encode(const float* x, int64_t rows, uint32_t* codes, void* stream) {
+    g_last_error.clear();
+    if (rows < 0) return fail(ZETA_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+    if (rows == 0) return ZETA_OK;
+    if (!x || !codes) return fail(ZETA_ERR_INVALID_ARGUMENT, "x or codes is NULL");
+    if (!aligned(x, 4) || !aligned(codes, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "x and codes must be 4-byte aligned");
+    zeta_status st = preflight();
+    if (st != ZETA_OK) return st;
+    hipError_t e = zeta::launch_encode(x, rows, codes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZETA_OK : fail_hip("encode launch", e);
+}
+
+zeta_status zeta_build_tree(int64_t BH, int64_t N, const uint32_t* zk, uint64_t* tree_asc,
+                            uint64_t* tree_desc, void* stream) {
+    g_last_error.clear();
+    if (BH < 1 || N < 1) return fail(ZETA_ERR_INVALID_ARGUMENT, "BH and N must be >= 1");
+    if (N >= (int64_t(1) << 30) || BH > (int64_t(1) << 31) / N)
+        return fail(ZETA_ERR_UNSUPPORTED, "BH*N must be < 2^31 and N < 2^30");
+    if (!zk || !tree_asc || !tree_desc) return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(zk, 4) || !aligned(tree_asc, 8) || !aligned(tree_desc, 8))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    zeta_status st = preflight();
+    if (st != ZETA_OK) return st;
+    hipError_t e = zeta::launch_build_tree(BH, N, levels_of(N), zk, tree_asc, tree_desc,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZETA_OK : fail_hip("tree launch", e);
+}
+
+zeta_status zeta_select(const zeta_shape* shape, const float* q, const float* k, int32_t* idx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    zeta_status st = check_shape(shape);
+    if (st != ZETA_OK) return st;
+    if ((st = check_qk(q, k)) != ZETA_OK) return st;
+    if (!idx || !aligned(idx, 4)) return fail(ZETA_ERR_INVALID_ARGUMENT, "idx NULL or misaligned");
+    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape).total)) != ZETA_OK) return st;
+    if ((st = preflight()) != ZETA_OK) return st;
+    return run_select(shape, q, k, idx, workspace, static_cast<hipStream_t>(stream));
+}
+
+zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
+                     const float* gamma, void* out, int32_t* idx, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    zeta_status st = check_shape(shape);
+    if (st != ZETA_OK) return st;
+    if ((st = check_qk(q, k)) != ZETA_OK) return st;
+    if (!v || !gamma || !out || !idx) return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(v, 16) || !aligned(out, 16))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "v and out must be 16-byte aligned");
+    if (!aligned(gamma, 4) || !aligned(idx, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "gamma and idx must be 4-byte aligned");
+    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape).total)) != ZETA_OK) return st;
+    if ((st = preflight()) != ZETA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = run_select(shape, q, k, idx, workspace, s)) != ZETA_OK) return st;
+    hipError_t e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
+                                       static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16,
+                                       q, k, v, gamma, idx, out, s);
+    if (e != hipSuccess) return fail_hip("gather launch", e);
+    g_marks.record(4, s);
+    return ZETA_OK;
+}
+
+zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
+                     const float* gamma, const int32_t* idx, const void* dout, float* dq,
+                     float* dk, void* dv, float* dgamma, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    zeta_status st = check_shape(shape);
+    if (st != ZETA_OK) return st;
+    if ((st = check_qk(q, k)) != ZETA_OK) return st;
+    if (!v || !gamma || !idx || !dout || !dq || !dk || !dv || !dgamma)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(v, 16) || !aligned(dout, 16) || !aligned(dv, 16))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "v, dout and dv must be 16-byte aligned");
+    if (!aligned(gamma, 4) || !aligned(idx, 4) || !aligned(dq, 4) || !aligned(dk, 4) ||
+        !aligned(dgamma, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    const BwdPlan p = plan_bwd(shape);
+    if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
+    if ((st = preflight()) != ZETA_OK) return st;
+    zeta::BwdBuffers b{};
+    b.A = at<float>(workspace, p.A);
+    b.C = at<float>(workspace, p.C);
+    b.dg_row = at<float>(workspace, p.dg);
+    b.key0 = at<uint32_t>(workspace, p.k0);
+    b.val0 = at<uint32_t>(workspace, p.v0);
+    b.key1 = at<uint32_t>(workspace, p.k1);
+    b.val1 = at<uint32_t>(workspace, p.v1);
+    b.hist = at<uint32_t>(workspace, p.hist);
+    b.totals = at<uint32_t>(workspace, p.totals);
+    b.offs = at<uint32_t>(workspace, p.offs);
+    b.P = p.P;
+    b.tiles = p.tiles;
+    hipError_t e = zeta::launch_bwd(shape->B * shape->H, shape->H, shape->N, shape->dv,
+                                    static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16, q, k,
+                                    v, gamma, idx, dout, dq, dk, dv, dgamma, b, g_marks,
+                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZETA_OK : fail_hip("backward launch", e);
+}
+
+zeta_status zeta_set_stage_events(void* const* events, int32_t count) {
+    g_last_error.clear();
+    if (count < 0) return fail(ZETA_ERR_INVALID_ARGUMENT, "count must be >= 0");
+    g_marks.ev = count > 0 ? events : nullptr;
+    g_marks.n = events ? count : 0;
+    return ZETA_OK;
+}
+
+const char* zeta_status_string(zeta_status status) {
+    switch (status) {
+        case ZETA_OK: return "ZETA_OK";
+        case ZETA_ERR_INVALID_ARGUMENT: return "ZETA_ERR_INVALID_ARGUMENT";
+        case ZETA_ERR_UNSUPPORTED: return "ZETA_ERR_UNSUPPORTED";
+        case ZETA_ERR_WORKSPACE_TOO_SMALL: return "ZETA_ERR_WORKSPACE_TOO_SMALL";
+        case ZETA_ERR_HIP: return "ZETA_ERR_HIP";
+        default: return "unknown zeta_status";
+    }
+}
+
+const char* zeta_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

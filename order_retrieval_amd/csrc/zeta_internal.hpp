@@ -1,0 +1,70 @@
+// zeta_internal.hpp -- shared declarations of the HIP kernels' launchers and device helpers.
+// Internal to libzeta.so; the public surface is include/zeta.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zeta {
+
+constexpr int kMaxTopK = 64;
+constexpr int kMaxDv = 512;
+constexpr size_t kAlign = 256;
+
+// ----------------------------------------------------------------------------- device
+// bf16 is carried as raw 16-bit patterns; widening is exact, narrowing rounds to nearest
+// even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Optional events recorded between the stages of one call (measurement hook).
+struct StageEvents {
+    void* const* ev = nullptr;
+    int n = 0;
+    void record(int stage, hipStream_t s) const {
+        if (stage < n && ev[stage]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[stage]), s);
+    }
+};
+
+// ----------------------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launches (hipSuccess when nothing was launched).
+hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t s);
+hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
+                             uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
+hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, const uint32_t* zq,
+                         const uint64_t* tree_asc, const uint64_t* tree_desc, int32_t* idx,
+                         hipStream_t s);
+hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
+                         const float* q, const float* k, const void* v, const float* gamma,
+                         const int32_t* idx, void* out, hipStream_t s);
+
+struct BwdBuffers {
+    float* A;         // [BHN][topk] normalised weights a_ij
+    float* C;         // [BHN][topk] pair coefficients c_ij
+    float* dg_row;    // [BHN] per-query dgamma contributions
+    uint32_t* key0;   // [BH][P] radix-sort ping-pong keys
+    uint32_t* val0;   // [BH][P] radix-sort ping-pong values
+    uint32_t* key1;
+    uint32_t* val1;
+    uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
+    uint32_t* totals; // [BH][256] digit totals
+    uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
+    int64_t P;        // valid pairs per (b,h)
+    int64_t tiles;    // radix tiles per (b,h)
+};
+size_t bwd_pairs_per_head(int64_t N, int topk);
+int64_t bwd_tiles_per_head(int64_t P);
+hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
+                      const float* q, const float* k, const void* v, const float* gamma,
+                      const int32_t* idx, const void* dout, float* dq, float* dk, void* dvout,
+                      float* dgamma, const BwdBuffers& ws, const StageEvents& marks,
+                      hipStream_t s);
+
+}  // namespace zeta

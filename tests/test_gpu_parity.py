@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer results (codes, tree levels, selected indices) must match bit for bit; floating
+point within the tolerance rule in gpu_common.  Small workloads are compared in full; the
+full-size ones on sampled rows that the oracle computes one by one, plus properties that
+hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from order_retrieval_amd import inputs
+from order_retrieval_amd import zeta as Z
+from gpu_common import (assert_close, device_inputs, log, sample_rows, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+CFG = inputs.CONFIGS
+
+
+def W(name, B, H, N, dv, topk, vt=inputs.F32, dist="normal", gamma=None, seed=0,
+      backward=False):
+    return inputs.Workload(name, B, H, N, dv, topk, vt, dist, gamma, seed, backward)
+
+
+# ----------------------------------------------------------------------------- encode
+
+
+@pytest.mark.parametrize("name", list(CFG)[:4])
+def test_encode_bit_exact(name):
+    w = CFG[name]
+    log(f"encode {name}")
+    x = inputs.make_inputs(w)
+    for key in ("q", "k"):
+        got = to_np(Z.zeta_encode(to_dev(x[key]))).view(np.uint32)
+        np.testing.assert_array_equal(got, oracle.encode(x[key]))
+
+
+def test_encode_special_values_and_ragged_rows():
+    vals = np.array([np.nan, np.inf, -np.inf, 4.0, -4.0, 3.9999998, -4.0000005, 0.0, -0.0,
+                     -1e-30, 1e-30, -1e-9, 1e30, -1e30, 2.5, -3.9921875], dtype=np.float32)
+    rng = np.random.default_rng(1)
+    for rows in (1, 2, 3, 4, 5, 7, 1001):
+        x = vals[rng.integers(0, vals.size, size=(rows, 3))]
+        got = to_np(Z.zeta_encode(to_dev(x))).view(np.uint32)
+        np.testing.assert_array_equal(got, oracle.encode(x))
+    # every cell edge and the fp32 value just below it, on every axis
+    m = np.arange(1, 1024)
+    edges = (-4.0 + m / 128.0).astype(np.float32)
+    below = np.nextafter(edges, np.float32(-np.inf), dtype=np.float32)
+    pts = np.stack([np.concatenate([edges, below])] * 3, axis=1)
+    pts[:, 1] = np.roll(pts[:, 1], 17)
+    pts[:, 2] = np.roll(pts[:, 2], 501)
+    pts = np.ascontiguousarray(pts)
+    np.testing.assert_array_equal(to_np(Z.zeta_encode(to_dev(pts))).view(np.uint32),
+                                  oracle.encode(pts))
+
+
+def test_encode_unaligned_input_view():
+    x = np.random.default_rng(2).standard_normal((1000, 3)).astype(np.float32)
+    t = to_dev(x.reshape(-1))
+    view = t[3:].view(999, 3)  # 12-byte offset: the scalar path
+    got = to_np(Z.zeta_encode(view)).view(np.uint32)
+    np.testing.assert_array_equal(got, oracle.encode(x[1:]))
+
+
+# ----------------------------------------------------------------------------- tree
+
+
+def _expected_levels(codes: np.ndarray, N: int, levels: int):
+    """Every aligned block of 2^l positions, sorted: the defining property of a level."""
+    j = np.arange(N, dtype=np.uint64)
+    c = codes.astype(np.uint64) << np.uint64(32)
+    asc = c | j
+    desc = c | (np.uint64(0xFFFFFFFF) - j)
+    out_a, out_d = [], []
+    for l in range(levels):
+        s = 1 << l
+        full = (N // s) * s
+        ea = np.concatenate([np.sort(asc[:full].reshape(-1, s), axis=1).reshape(-1),
+                             np.sort(asc[full:])])
+        ed = np.concatenate([np.sort(desc[:full].reshape(-1, s), axis=1).reshape(-1),
+                             np.sort(desc[full:])])
+        out_a.append(ea)
+        out_d.append(ed)
+    return np.stack(out_a), np.stack(out_d)
+
+
+@pytest.mark.parametrize("BH,N,dist", [(1, 1, "normal"), (2, 2, "normal"), (1, 3, "discrete"),
+                                       (3, 1000, "normal"), (2, 1024, "discrete"),
+                                       (2, 1025, "normal"), (2, 2049, "clustered"),
+                                       (1, 4097, "discrete"), (8, 4096, "normal"),
+                                       (1, 20000, "clustered"), (2, 65536, "normal")])
+def test_tree_levels_are_sorted_blocks(BH, N, dist):
+    log(f"tree BH={BH} N={N} {dist}")
+    w = W("t", 1, BH, N, 8, 1, dist=dist, seed=N)
+    x = inputs.make_inputs(w)
+    zk = oracle.encode(x["k"]).reshape(BH, N)
+    asc, desc = Z.zeta_build_tree(to_dev(zk.view(np.int32)))
+    asc, desc = to_np(asc).view(np.uint64), to_np(desc).view(np.uint64)
+    L = Z.zeta_tree_levels(N)
+    for bh in range(BH):
+        ea, ed = _expected_levels(zk[bh], N, L)
+        np.testing.assert_array_equal(asc[bh], ea)
+        np.testing.assert_array_equal(desc[bh], ed)
+
+
+# ----------------------------------------------------------------------------- select
+
+
+def _select_and_compare(w, rows=None):
+    x = inputs.make_inputs(w)
+    idx = to_np(Z.zeta_select(to_dev(x["q"]), to_dev(x["k"]), w.topk)).reshape(-1, w.topk)
+    ref = oracle.select(x["q"], x["k"], w.topk, rows=rows)
+    got = idx if rows is None else idx[rows]
+    if not np.array_equal(got, ref):
+        bad = np.nonzero((got != ref).any(axis=1))[0]
+        r = bad[0]
+        raise AssertionError(f"{len(bad)} rows differ; first row {r if rows is None else rows[r]}:"
+                             f" gpu {got[r].tolist()} ref {ref[r].tolist()}")
+    return x, idx
+
+
+@pytest.mark.parametrize("name", ["tiny", "multihead"])
+def test_select_bit_exact_full(name):
+    log(f"select full {name}")
+    _select_and_compare(CFG[name])
+
+
+@pytest.mark.parametrize("name", ["clustered", "long_fwd"])
+def test_select_bit_exact_sampled(name):
+    w = CFG[name]
+    rows = sample_rows(w, 1500, seed=3)
+    log(f"select sampled {name}: {rows.size} rows")
+    _select_and_compare(w, rows)
+
+
+@pytest.mark.parametrize("B,H,N,topk,dist", [
+    (1, 1, 1, 1, "normal"), (1, 2, 1, 5, "normal"), (2, 1, 2, 1, "normal"),
+    (1, 1, 3, 2, "discrete"), (1, 2, 40, 64, "normal"), (1, 1, 100, 64, "clustered"),
+    (2, 2, 1000, 32, "normal"), (1, 3, 4097, 16, "normal"), (1, 1, 2049, 48, "clustered"),
+    (2, 3, 3000, 32, "discrete"), (1, 2, 3000, 64, "constant"), (1, 2, 2500, 1, "normal"),
+    (1, 1, 1500, 5, "discrete"), (3, 1, 777, 7, "clustered"), (1, 1, 5000, 3, "normal"),
+    (1, 1, 1100, 33, "discrete"), (1, 1, 2000, 2, "constant"), (1, 1, 1030, 16, "discrete"),
+])
+def test_select_edge_shapes(B, H, N, topk, dist):
+    log(f"select edge B={B} H={H} N={N} k={topk} {dist}")
+    _select_and_compare(W("e", B, H, N, 8, topk, dist=dist, seed=N + topk))
+
+
+def test_select_nonfinite_inputs():
+    w = W("e", 1, 2, 600, 8, 12, seed=9)
+    x = inputs.make_inputs(w)
+    rng = np.random.default_rng(4)
+    for key in ("q", "k"):
+        flat = x[key].reshape(-1)
+        pos = rng.integers(0, flat.size, size=200)
+        flat[pos] = np.array([np.nan, np.inf, -np.inf, 1e30], dtype=np.float32)[pos % 4]
+    idx = to_np(Z.zeta_select(to_dev(x["q"]), to_dev(x["k"]), w.topk)).reshape(-1, w.topk)
+    np.testing.assert_array_equal(idx, oracle.select(x["q"], x["k"], w.topk))
+
+
+def test_select_prefix_causality():
+    w = W("c", 1, 2, 3000, 8, 32, dist="clustered", seed=5)
+    x = inputs.make_inputs(w)
+    full = to_np(Z.zeta_select(to_dev(x["q"]), to_dev(x["k"]), 32))
+    n2 = 1777
+    part = to_np(Z.zeta_select(to_dev(np.ascontiguousarray(x["q"][:, :, :n2])),
+                               to_dev(np.ascontiguousarray(x["k"][:, :, :n2])), 32))
+    np.testing.assert_array_equal(full[:, :, :n2], part)
+
+
+# ----------------------------------------------------------------------------- forward
+
+
+def _forward_check(w, rows=None):
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    out, idx = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+    torch.cuda.synchronize()
+    out = to_np(out).reshape(-1, w.dv)
+    idx = to_np(idx).reshape(-1, w.topk)
+    ref_idx = oracle.select(x["q"], x["k"], w.topk, rows=rows)
+    got_idx = idx if rows is None else idx[rows]
+    np.testing.assert_array_equal(got_idx, ref_idx)
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["gamma"], ref_idx,
+                         w.v_dtype == inputs.BF16, rows=rows)
+    got = out if rows is None else out[rows]
+    assert_close(got, ref, w.v_dtype, f"o {w.name}", bf16_output=w.v_dtype == inputs.BF16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "multihead"])
+def test_forward_full(name):
+    log(f"forward full {name}")
+    _forward_check(CFG[name])
+
+
+@pytest.mark.parametrize("name", ["clustered", "long_fwd"])
+def test_forward_sampled(name):
+    w = CFG[name]
+    rows = sample_rows(w, 1200, seed=5)
+    log(f"forward sampled {name}: {rows.size} rows")
+    _forward_check(w, rows)
+
+
+@pytest.mark.parametrize("N,dv,topk,vt,dist", [
+    (1, 8, 1, inputs.F32, "normal"), (1, 8, 4, inputs.BF16, "normal"),
+    (50, 24, 64, inputs.F32, "normal"), (300, 512, 16, inputs.F32, "clustered"),
+    (300, 512, 16, inputs.BF16, "normal"), (700, 136, 5, inputs.BF16, "discrete"),
+    (1025, 8, 32, inputs.BF16, "constant"), (2000, 64, 48, inputs.F32, "discrete"),
+    (999, 256, 32, inputs.BF16, "clustered"), (64, 40, 64, inputs.F32, "normal"),
+])
+def test_forward_edge_shapes(N, dv, topk, vt, dist):
+    log(f"forward edge N={N} dv={dv} k={topk} {vt} {dist}")
+    _forward_check(W("fe", 2, 2, N, dv, topk, vt, dist, seed=N + dv))
+
+
+def test_forward_gamma_one_is_student_t():
+    w = W("g1", 1, 3, 500, 32, 16, gamma=1.0, seed=8)
+    _forward_check(w)
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def _bwd_full_check(w):
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    bf = w.v_dtype == inputs.BF16
+    out, idx = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+    dq, dk, dv, dg = Z.zeta_bwd(d["q"], d["k"], d["v"], d["gamma"], idx, d["dout"])
+    torch.cuda.synchronize()
+    ref_idx = oracle.select(x["q"], x["k"], w.topk)
+    np.testing.assert_array_equal(to_np(idx).reshape(-1, w.topk), ref_idx)
+    rq, rk, rv, rg = oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], ref_idx, bf)
+    assert_close(to_np(dq).reshape(-1, 3), rq, w.v_dtype, f"dq {w.name}")
+    assert_close(to_np(dk), rk, w.v_dtype, f"dk {w.name}")
+    assert_close(to_np(dv), rv, w.v_dtype, f"dv {w.name}", bf16_output=bf)
+    assert_close(to_np(dg), rg, w.v_dtype, f"dgamma {w.name}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "multihead"])
+def test_backward_full(name):
+    w = CFG[name]
+    log(f"backward full {name}")
+    _bwd_full_check(inputs.Workload(**{**w.__dict__, "backward": True}))
+
+
+@pytest.mark.parametrize("B,H,N,dv,topk,vt,dist", [
+    (1, 1, 1, 8, 1, inputs.F32, "normal"), (2, 2, 3, 8, 4, inputs.BF16, "normal"),
+    (1, 2, 40, 24, 64, inputs.F32, "normal"), (2, 3, 600, 64, 32, inputs.BF16, "clustered"),
+    (1, 2, 300, 512, 16, inputs.F32, "discrete"), (2, 1, 1025, 136, 5, inputs.BF16, "normal"),
+    (1, 1, 2000, 32, 64, inputs.F32, "constant"), (3, 2, 700, 8, 1, inputs.F32, "clustered"),
+    (1, 1, 4500, 64, 33, inputs.F32, "normal"),
+])
+def test_backward_edge_shapes(B, H, N, dv, topk, vt, dist):
+    log(f"backward edge B={B} H={H} N={N} dv={dv} k={topk} {vt} {dist}")
+    _bwd_full_check(W("be", B, H, N, dv, topk, vt, dist, seed=N * 3 + topk, backward=True))
+
+
+def _bwd_sampled_check(w, n_rows=600, tail=256):
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    bf = w.v_dtype == inputs.BF16
+    out, idx = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+    dq, dk, dv, dg = Z.zeta_bwd(d["q"], d["k"], d["v"], d["gamma"], idx, d["dout"])
+    torch.cuda.synchronize()
+    idx = to_np(idx).reshape(-1, w.topk)
+    dq, dk, dv, dg = (to_np(t) for t in (dq, dk, dv, dg))
+    BH, N = w.B * w.H, w.N
+    # dq is per query: check sampled rows
+    rows = sample_rows(w, n_rows, seed=11)
+    ridx = oracle.select(x["q"], x["k"], w.topk, rows=rows)
+    np.testing.assert_array_equal(idx[rows], ridx)
+    rq, _, _, _ = oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], ridx, bf,
+                                  rows=rows)
+    assert_close(dq.reshape(-1, 3)[rows], rq, w.v_dtype, f"dq {w.name} sampled")
+    # keys in the last `tail` positions are selected only by queries in the same tail, so
+    # running the oracle over every tail query gives their complete gradients
+    trows = np.array([bh * N + i for bh in range(BH) for i in range(N - tail, N)], np.int64)
+    tidx = oracle.select(x["q"], x["k"], w.topk, rows=trows)
+    np.testing.assert_array_equal(idx[trows], tidx)
+    _, rk, rv, _ = oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], tidx, bf,
+                                   rows=trows)
+    sel = np.zeros((BH, N), dtype=bool)
+    sel[:, N - tail:] = True
+    assert_close(dk.reshape(BH, N, 3)[sel], rk.reshape(BH, N, 3)[sel], w.v_dtype,
+                 f"dk {w.name} tail keys")
+    assert_close(dv.reshape(BH, N, w.dv)[sel], rv.reshape(BH, N, w.dv)[sel], w.v_dtype,
+                 f"dv {w.name} tail keys", bf16_output=bf)
+    # identities that hold at any size (fp64 sums of the GPU results)
+    q64 = x["q"].astype(np.float64).reshape(-1, 3)
+    k64 = x["k"].astype(np.float64).reshape(-1, 3)
+    dq64, dk64 = dq.astype(np.float64).reshape(-1, 3), dk.astype(np.float64).reshape(-1, 3)
+    scale = np.abs(dq64).sum() + np.abs(dk64).sum()
+    trans = np.abs(dq64.sum(0) + dk64.sum(0)).max()
+    hom = abs((q64 * dq64).sum() + (k64 * dk64).sum() +
+              (x["gamma"].astype(np.float64) * dg.astype(np.float64)).sum())
+    homs = np.abs(q64 * dq64).sum() + np.abs(k64 * dk64).sum()
+    log(f"  translation {trans:.3e} (scale {scale:.3e}); homogeneity {hom:.3e} (scale {homs:.3e})")
+    assert trans <= 1e-5 * scale and hom <= 1e-5 * homs
+    dout64 = (inputs.bf16_bits_to_f32(x["dout"]) if bf else x["dout"]).astype(np.float64)
+    colsum_ref = dout64.reshape(BH, N, w.dv).sum(1)
+    colsum = dv.astype(np.float64).reshape(BH, N, w.dv).sum(1)
+    tol = (2e-2 * np.sqrt(N)) if bf else 1e-3
+    assert np.abs(colsum - colsum_ref).max() <= tol, np.abs(colsum - colsum_ref).max()
+
+
+@pytest.mark.parametrize("name", ["clustered", "long_fwd_bwd"])
+def test_backward_sampled(name):
+    w = CFG[name]
+    log(f"backward sampled {name}")
+    _bwd_sampled_check(inputs.Workload(**{**w.__dict__, "backward": True}))
+
+
+# ----------------------------------------------------------------------------- properties
+
+
+def test_bitwise_deterministic():
+    w = W("det", 2, 4, 8192, 64, 32, inputs.BF16, "clustered", seed=21, backward=True)
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    res = []
+    for _ in range(2):
+        out, idx = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+        g = Z.zeta_bwd(d["q"], d["k"], d["v"], d["gamma"], idx, d["dout"])
+        torch.cuda.synchronize()
+        res.append([to_np(t).copy() for t in (out, idx, *g)])
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_autograd_wrapper_matches_direct_calls():
+    w = W("ag", 1, 2, 700, 16, 8, seed=13, backward=True)
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    q, k, v, g = (d[n].clone().requires_grad_() for n in ("q", "k", "v", "gamma"))
+    out, idx = Z.zeta_attention(q, k, v, g, w.topk)
+    out.backward(d["dout"])
+    out2, idx2 = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+    grads = Z.zeta_bwd(d["q"], d["k"], d["v"], d["gamma"], idx2, d["dout"])
+    assert torch.equal(out, out2) and torch.equal(idx, idx2)
+    for a, b in zip((q.grad, k.grad, v.grad, g.grad), grads):
+        assert torch.equal(a, b)
+
+
+def test_error_paths_leave_outputs_untouched():
+    w = W("err", 1, 1, 64, 8, 4, seed=1)
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    shape = Z.make_shape(1, 1, 64, 8, 4, Z.ZETA_F32)
+    ws = Z.workspace(shape, Z.ZETA_WS_FWD, torch.device("cuda", 0))
+    out = torch.full((1, 1, 64, 8), 7.0, device="cuda")
+    idx = torch.full((1, 1, 64, 4), 9, dtype=torch.int32, device="cuda")
+    with pytest.raises(Z.ZetaError) as e:
+        Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], 4, ws=ws[: ws.numel() - 1], out=out, idx=idx)
+    assert e.value.status == Z.ZETA_ERR_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(idx == 9)
