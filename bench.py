@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZETA causal top-k attention hot path on one MI355X.
+
+A step is one zeta_fwd (encode, tree build, select, Cauchy gather) plus one zeta_bwd
+(per-query pass, selection transpose, per-key pass, dgamma) on the 65536-token workload
+B=1, H=8, N=65536, d_K=3, d_V=128, k=32 with bf16 v and dO (seeded synthetic inputs,
+already resident in HBM when the timed region starts).  Prints one JSON line.
+
+Kernel durations come from HIP events that the library records on its launch stream
+between stages (zeta_set_stage_events), inside the timed steps.  The CPU baseline is the
+oracle timed on a bounded random sample of query rows and scaled to the full step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from order_retrieval_amd import inputs  # noqa: E402
+
+METRIC = "ms per ZETA fwd (and fwd+bwd) at N=65536,H=8; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PAGES_CONTEXT = {"zeta_fwd_ms": 85.8, "zeta_fwd_bwd_ms": 608.2, "flash_fwd_ms": 805.3,
+                 "flash_fwd_bwd_ms": 7044.1, "hardware": "not stated on the pages"}
+FWD_STAGES = ["encode", "tree", "select", "gather"]
+BWD_STAGES = ["bwd_query", "bwd_transpose", "bwd_key", "bwd_dgamma"]
+SINGLE_KERNEL = {"select": "zeta_select_kernel", "gather": "zeta_cauchy_gather_kernel",
+                 "bwd_query": "zeta_bwd_query_kernel", "bwd_key": "zeta_bwd_key_kernel"}
+KERNEL_SOURCE = {"select": "select.hip", "gather": "gather.hip", "bwd_query": "backward.hip",
+                 "bwd_key": "backward.hip"}
+
+
+# ----------------------------------------------------------------------------- bytes
+def valid_slots(w: inputs.Workload) -> np.ndarray:
+    """m_i = min(k, i+1): selected keys of query i (same for every (b,h))."""
+    return np.minimum(np.arange(w.N, dtype=np.int64) + 1, w.topk)
+
+
+def select_run_bytes(w: inputs.Workload) -> float:
+    """Per (b,h): for every query, the sorted runs of its causal prefix (set bits of i+1):
+    a binary search (floor(log2 s)+1 probes of 8 B) and two k-wide windows (<= s entries of
+    8 B) per run, plus the query code (4 B) and the written index row (4k B)."""
+    i1 = np.arange(1, w.N + 1, dtype=np.int64)
+    total = np.zeros(w.N, dtype=np.float64)
+    for l in range(int(np.log2(w.N)) + 1):
+        s = 1 << l
+        has = (i1 >> l) & 1
+        total += has * (8.0 * (l + 1) + 8.0 * min(2 * w.topk, s))
+    return float((total + 4 + 4 * w.topk).sum())
+
+
+def kernel_bytes(w: inputs.Workload) -> dict:
+    """Algorithmic bytes per launch of each kernel (every gathered row counted as read)."""
+    BH = w.B * w.H
+    vb = 2 if w.v_dtype == inputs.BF16 else 4
+    row = w.dv * vb
+    m = valid_slots(w).astype(np.float64)
+    pairs = float(m.sum())  # per (b,h)
+    levels = int(np.log2(w.N)) + 1
+    tile_levels = min(levels - 1, 10)
+    b = {}
+    b["encode"] = BH * w.N * (2 * 12 + 2 * 4)
+    b["tree"] = BH * w.N * (4 + 2 * 8 * (tile_levels + 1) + 2 * 16 * (levels - 1 - tile_levels))
+    b["select"] = BH * select_run_bytes(w)
+    b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + row).sum())
+    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 8 * m + 16).sum())
+    bits = int(np.ceil(np.log2(w.N))) if w.N > 1 else 0
+    passes = 1 if bits <= 8 else -(-bits // 8)
+    # pass 0 reads the index rows twice (histogram, scatter) and writes (key, pair) once;
+    # every further pass reads keys (histogram) and (key, pair) and writes (key, pair);
+    # the segment starts read the sorted keys and write N+1 offsets
+    b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 20 * pairs +
+                               4 * pairs + 4 * (w.N + 1))
+    b["bwd_key"] = BH * (w.N * (8 + 12 + 12 + row) + pairs * (4 + 4 + 4 + 12 + row))
+    b["bwd_dgamma"] = BH * w.N * 4.0
+    return b
+
+
+# ----------------------------------------------------------------------------- HIP events
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded (shared with libzeta)."""
+
+    def __init__(self, runtime_path: str):
+        self.lib = ctypes.CDLL(runtime_path)
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int):
+        evs = (ctypes.c_void_p * n)()
+        for t in range(n):
+            h = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            evs[t] = h
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for h in evs:
+            self.lib.hipEventDestroy(h)
+
+
+# ----------------------------------------------------------------------------- counters
+def stored_traffic(stage: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/*_counters.json), used
+    only while the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_long_fwd_bwd_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "order_retrieval_amd", "csrc", KERNEL_SOURCE[stage])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(w: inputs.Workload, x: dict, target_s: float, seed: int = 0) -> dict:
+    import oracle
+
+    bf = w.v_dtype == inputs.BF16
+    total = w.B * w.H * w.N
+    rng = np.random.default_rng(seed)
+
+    def run(count):
+        rows = np.sort(rng.choice(total, size=count, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        idx = oracle.select(x["q"], x["k"], w.topk, rows=rows)
+        oracle.forward(x["q"], x["k"], x["v"], x["gamma"], idx, bf, rows=rows)
+        oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], idx, bf, rows=rows)
+        return time.perf_counter() - t0
+
+    # the oracle's backward zeroes full-size dk/dv arrays on every call, so calibrate the
+    # sample size from the cost difference of two probe sizes (marginal cost per row)
+    p1, p2 = min(256, total), min(2048, total)
+    t1, t2 = run(p1), run(p2)
+    per_row = max((t2 - t1) / max(p2 - p1, 1), 1e-7)
+    count = int(min(total, max(p2, (target_s - t1) / per_row)))
+    t = run(count)
+    return {"value": round(t / count * total * 1e3, 1), "unit": "ms", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": (f"{count} uniformly drawn query rows of the same workload (select + forward "
+                       f"+ backward contributions, {t:.1f} s), scaled by {total}/{count}; "
+                       f"selection and forward use all threads, backward runs on one")}
+
+
+# ----------------------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_fwd_bwd", choices=sorted(inputs.CONFIGS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the (b,h) slices "
+              "are independent and each GPU would run this same kernel sequence on its heads.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from order_retrieval_amd import zeta as Z
+
+    w = inputs.CONFIGS[args.workload]
+    w = inputs.Workload(**{**w.__dict__, "backward": True})
+    x = inputs.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    bf = w.v_dtype == inputs.BF16
+
+    def to_dev(a, as_bf16=False):
+        if as_bf16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, gamma = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["gamma"])
+    v, dout = to_dev(x["v"], bf), to_dev(x["dout"], bf)
+    shape = Z.make_shape(w.B, w.H, w.N, w.dv, w.topk, Z.ZETA_BF16 if bf else Z.ZETA_F32)
+    ws_f = Z.workspace(shape, Z.ZETA_WS_FWD, dev)
+    ws_b = Z.workspace(shape, Z.ZETA_WS_BWD, dev)
+    out = torch.empty_like(v)
+    idx = torch.empty((w.B, w.H, w.N, w.topk), dtype=torch.int32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty((w.H,), dtype=torch.float32, device=dev))
+    lib = Z.load_library()
+    torch.cuda.synchronize()
+    hip = HipEvents(Z.hip_runtimes_mapped()[0])
+
+    def step(ev_f=None, ev_b=None):
+        if ev_f is not None:
+            lib.zeta_set_stage_events(ev_f, len(ev_f))
+        Z.zeta_fwd(q, k, v, gamma, w.topk, ws=ws_f, out=out, idx=idx)
+        if ev_b is not None:
+            lib.zeta_set_stage_events(ev_b, len(ev_b))
+        Z.zeta_bwd(q, k, v, gamma, idx, dout, ws=ws_b, grads=grads)
+        lib.zeta_set_stage_events(None, 0)
+
+    for _ in range(args.warmup):
+        step()
+    ev = [(hip.create(5), hip.create(5)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(*ev[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+
+    stages = {n: [] for n in FWD_STAGES + BWD_STAGES}
+    for evf, evb in ev:
+        for s, n in enumerate(FWD_STAGES):
+            stages[n].append(hip.elapsed_ms(evf[s], evf[s + 1]))
+        for s, n in enumerate(BWD_STAGES):
+            stages[n].append(hip.elapsed_ms(evb[s], evb[s + 1]))
+    stage_ms = {n: float(np.mean(t)) for n, t in stages.items()}
+    fwd_ms = sum(stage_ms[n] for n in FWD_STAGES)
+    bwd_ms = sum(stage_ms[n] for n in BWD_STAGES)
+    for evf, evb in ev:
+        hip.destroy(evf)
+        hip.destroy(evb)
+
+    # forward alone, for the forward-only figure
+    fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    fs.record()
+    for _ in range(args.steps):
+        Z.zeta_fwd(q, k, v, gamma, w.topk, ws=ws_f, out=out, idx=idx)
+    fe.record()
+    torch.cuda.synchronize()
+    fwd_only_ms = fs.elapsed_time(fe) / args.steps
+
+    kb = kernel_bytes(w)
+    dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
+    achieved = kb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    fwd_bytes = sum(kb[n] for n in FWD_STAGES)
+    step_bytes = sum(kb.values())
+    rows = w.B * w.H * w.N
+    result = {
+        "metric": METRIC,
+        "value": round(step_ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} H{w.H} N{w.N} dK3 dV{w.dv} k{w.topk}, "
+                               f"v/dO {w.v_dtype}, forward+backward",
+                   "B": w.B, "H": w.H, "N": w.N, "d_K": 3, "d_V": w.dv, "topk": w.topk,
+                   "v_dtype": w.v_dtype, "seed": w.seed},
+        "fwd_ms": round(fwd_only_ms, 4),
+        "fwd_bwd_ms": round(step_ms, 4),
+        "queries_per_s_fwd": round(rows / (fwd_only_ms * 1e-3), 1),
+        "queries_per_s_fwd_bwd": round(rows / (step_ms * 1e-3), 1),
+        "fwd_algorithmic_GBs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+        "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_GBs": round(step_bytes / ((fwd_ms + bwd_ms) * 1e-3) / 1e9, 1),
+        "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()},
+        "stage_algorithmic_bytes": {n: int(b) for n, b in kb.items()},
+        "roofline": {"bound": "hbm", "kernel": SINGLE_KERNEL[dom], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(dom)},
+        "wall_s_timed": round(wall, 3),
+        "pages_context": PAGES_CONTEXT,
+        "input_sha256": inputs.digest(x),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

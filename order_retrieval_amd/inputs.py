@@ -12,8 +12,8 @@ Recipe (numpy PCG64 via ``default_rng(seed)``; draw order q, k, v, gamma, dout):
                    Z-order cell, which exercises the tie rule.
 * ``discrete``  -- every coordinate drawn from a small fixed set of values, so that codes
                    collide heavily (tie-heavy test inputs).
-* v, dout ~ N(0, 1); bf16 values are the round-to-nearest-even of the fp32 draw and are
-  carried as raw uint16 bit patterns.
+* v, dout ~ N(0, 1) drawn directly in fp32; bf16 values are the round-to-nearest-even of
+  the fp32 draw and are carried as raw uint16 bit patterns.
 * gamma: a fixed value, or U[0.5, 2.0] per head.
 """
 
@@ -65,10 +65,17 @@ DISCRETE_VALUES = np.array([-1.0, -0.25, 0.0, 0.5, 2.0], dtype=np.float64)
 
 
 def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    """Round finite fp32 values to bf16 (nearest, ties to even); uint16 bit patterns.
+
+    uint32 arithmetic cannot overflow here: finite fp32 bit patterns are at most
+    0xFF7FFFFF, so adding at most 0x8000 stays below 2^32."""
+    b = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = b >> 16
+    lsb &= 1
+    b += 0x7FFF
+    b += lsb
+    b >>= 16
+    return b.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -101,7 +108,7 @@ def _qk(rng: np.random.Generator, w: Workload) -> tuple[np.ndarray, np.ndarray]:
 
 
 def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(shape).astype(np.float32)
+    x = rng.standard_normal(shape, dtype=np.float32)
     if dtype == BF16:
         return fp32_to_bf16_bits(x)
     if dtype == F32:
