@@ -10,10 +10,11 @@
 // Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
 //   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij, dq_i and the
 //      query's dgamma term;
-//   2. selection transpose: stable LSD radix sort (8-bit digits) of the valid (j, pair id)
-//      pairs of every (b,h) by j; pair ids stay ascending inside a key's segment;
+//   2. selection transpose: stable LSD radix sort (8-bit digits) of the pairs of every (b,h)
+//      by j, carrying 16-byte records {j, i, a_ij, c_ij}; queries stay ascending inside a
+//      key's segment;
 //   3. segment starts offs[j] from the sorted keys;
-//   4. per-key pass: each key reduces its segment in ascending query order (dv, dk);
+//   4. per-key pass: each key reduces its segment in a fixed order (dv, dk);
 //   5. dgamma: fixed-order reduction per head over the batch and the queries.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
@@ -141,31 +142,58 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     }
 }
 
+
 // ---------------------------------------------------------------------------- 2. transpose
-// Digit counts of one tile of items.  Pass 0 reads the selection itself (-1 slots are not
-// pairs); later passes read the previous pass's keys (all valid).
+// Every pair travels through the sort as one 16-byte record {j, i, a_ij, c_ij}.  Pass 0
+// reads the selection and the per-pair coefficients in pair order (coalesced) and builds the
+// records; later passes move records.  The key kernel then reads each key's pairs as one
+// contiguous run of records.
+template <bool FIRST>
+__device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
+                                          const float* __restrict__ A,
+                                          const float* __restrict__ Cc,
+                                          const uint4* __restrict__ rin, int64_t e, int topk,
+                                          uint4& rec) {
+    if (FIRST) {
+        uint32_t key;
+        if (!pair_item(idx, e, topk, key)) return false;
+        rec = make_uint4(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(topk),
+                         __float_as_uint(A[e]), __float_as_uint(Cc[e]));
+        return true;
+    }
+    rec = rin[e];
+    return true;
+}
+
+// Digit counts of one tile of items.
+template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ keys_in, int64_t items,
+    const int32_t* __restrict__ idx, const uint4* __restrict__ rin, int64_t items,
     int64_t in_stride, int shift, int64_t tiles, int topk, uint32_t* __restrict__ hist) {
     __shared__ uint32_t cnt[256];
     const int64_t bh = blockIdx.y;
     cnt[threadIdx.x] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    uint32_t keys[kRadixItems];
+    bool valid[kRadixItems];
+#pragma unroll
     for (int it = 0; it < kRadixItems; ++it) {
         const int64_t e = t0 + it * kRadixThreads + threadIdx.x;
+        valid[it] = false;
+        keys[it] = 0;
         if (e < items) {
-            uint32_t key = 0;
-            bool valid;
-            if (idx) {
-                valid = pair_item(idx + bh * in_stride, e, topk, key);
-            } else {
-                valid = true;
-                key = keys_in[bh * in_stride + e];
+            if (FIRST)
+                valid[it] = pair_item(idx + bh * in_stride, e, topk, keys[it]);
+            else {
+                valid[it] = true;
+                keys[it] = rin[bh * in_stride + e].x;
             }
-            if (valid) atomicAdd(&cnt[(key >> shift) & 255u], 1u);
         }
     }
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it)
+        if (valid[it]) atomicAdd(&cnt[(keys[it] >> shift) & 255u], 1u);
     __syncthreads();
     hist[(bh * 256 + threadIdx.x) * tiles + blockIdx.x] = cnt[threadIdx.x];
 }
@@ -197,12 +225,14 @@ __global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restric
 }
 
 // Stable scatter of one tile: items are ranked in (iteration, wave, lane) order, which is
-// their input order, so equal digits keep their relative order.
+// their input order, so equal digits keep their relative order.  All of the tile's items
+// are loaded before the ranking starts, so their loads overlap.
+template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ keys_in,
-    const uint32_t* __restrict__ vals_in, int64_t items, int64_t in_stride, int shift,
-    int64_t tiles, int topk, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals,
-    int64_t P, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out) {
+    const int32_t* __restrict__ idx, const float* __restrict__ A, const float* __restrict__ Cc,
+    const uint4* __restrict__ rin, int64_t items, int64_t in_stride, int shift, int64_t tiles,
+    int topk, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int64_t P,
+    uint4* __restrict__ rout) {
     __shared__ uint32_t base[256];
     __shared__ uint32_t scan[256];
     __shared__ uint32_t wcnt[4][256];
@@ -211,11 +241,25 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+
+    uint4 rec[kRadixItems];
+    uint32_t okmask = 0;
+    {
+        const int64_t off = bh * in_stride;
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) {
+            const int64_t e = t0 + it * kRadixThreads + tid;
+            rec[it] = make_uint4(0, 0, 0, 0);
+            if (e < items && load_pair<FIRST>(idx + off, A + off, Cc + off, rin + off, e, topk, rec[it]))
+                okmask |= 1u << it;
+        }
+    }
 
     scan[tid] = totals[bh * 256 + tid];
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan of the totals
-        const uint32_t y = tid >= off ? scan[tid - off] : 0u;
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan of the totals
+        const uint32_t y = tid >= o ? scan[tid - o] : 0u;
         __syncthreads();
         scan[tid] += y;
         __syncthreads();
@@ -227,22 +271,11 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     __syncthreads();
 
     const uint64_t lt = (1ull << lane) - 1ull;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    uint4* out = rout + bh * P;
+#pragma unroll
     for (int it = 0; it < kRadixItems; ++it) {
-        const int64_t e = t0 + it * kRadixThreads + tid;
-        bool valid = false;
-        uint32_t key = 0, val = 0;
-        if (e < items) {
-            if (idx) {
-                valid = pair_item(idx + bh * in_stride, e, topk, key);
-                val = static_cast<uint32_t>(e);
-            } else {
-                valid = true;
-                key = keys_in[bh * in_stride + e];
-                val = vals_in[bh * in_stride + e];
-            }
-        }
-        const uint32_t digit = valid ? (key >> shift) & 255u : 0u;
+        const bool valid = (okmask >> it) & 1u;
+        const uint32_t digit = valid ? (rec[it].x >> shift) & 255u : 0u;
         uint64_t peers = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -261,46 +294,46 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
             wcnt[w][tid] = 0;
         }
         __syncthreads();
-        if (valid) {
-            const uint32_t pos = base[digit] + wpre[wave][digit] + rank;
-            keys_out[bh * P + pos] = key;
-            vals_out[bh * P + pos] = val;
-        }
+        if (valid) out[base[digit] + wpre[wave][digit] + rank] = rec[it];
     }
 }
 
 // ---------------------------------------------------------------------------- 3. offsets
-__global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint32_t* __restrict__ keys,
+__global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint4* __restrict__ recs,
                                                                     int64_t P, int64_t N,
                                                                     uint32_t* __restrict__ offs) {
     const int64_t bh = blockIdx.y;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= P) return;
-    const uint32_t* kh = keys + bh * P;
+    const uint4* rh = recs + bh * P;
     uint32_t* oh = offs + bh * (N + 1);
-    const int64_t kk = kh[t];
-    const int64_t lo = t == 0 ? 0 : static_cast<int64_t>(kh[t - 1]) + 1;
+    const int64_t kk = rh[t].x;
+    const int64_t lo = t == 0 ? 0 : static_cast<int64_t>(rh[t - 1].x) + 1;
     for (int64_t jj = lo; jj <= kk; ++jj) oh[jj] = static_cast<uint32_t>(t);
     if (t == P - 1)
         for (int64_t jj = kk + 1; jj <= N; ++jj) oh[jj] = static_cast<uint32_t>(P);
 }
 
 // ---------------------------------------------------------------------------- 4. keys
+// One wavefront per key.  The wavefront is split into sub-groups of G lanes (one value row
+// per sub-group); sub-group s takes pairs s, s+S, s+2S, ... of the key's segment, and the S
+// partial sums are combined with a fixed butterfly, so the summation order is fixed.
 template <bool BF16, int CPL>
 __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
-    const void* __restrict__ dout, const float* __restrict__ A, const float* __restrict__ Cc,
-    const uint32_t* __restrict__ pairs, const uint32_t* __restrict__ offs, int64_t rows,
-    int64_t N, int64_t H, int dv, int topk, int glog, int64_t P, float* __restrict__ dk,
-    void* __restrict__ dvout) {
+    const void* __restrict__ dout, const uint4* __restrict__ recs,
+    const uint32_t* __restrict__ offs, int64_t rows, int64_t N, int64_t H, int dv, int glog,
+    int64_t P, float* __restrict__ dk, void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
-    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t row = gtid >> glog;
-    const int G = 1 << glog;
-    const int lane = static_cast<int>(gtid & (G - 1));
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= rows) return;
+    const int lane64 = threadIdx.x & 63;
+    const int G = 1 << glog;
+    const int S = 64 >> glog;
+    const int sub = lane64 >> glog;
+    const int lane = lane64 & (G - 1);
     const int chunks = dv / E;
     const int64_t bh = row / N;
     const int64_t j = row - bh * N;
@@ -308,9 +341,7 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const float inv_g2 = 1.0f / (g * g);
     const float k0 = k[3 * row], k1 = k[3 * row + 1], k2 = k[3 * row + 2];
     const uint32_t seg0 = offs[bh * (N + 1) + j], seg1 = offs[bh * (N + 1) + j + 1];
-    const uint32_t* ph = pairs + bh * P;
-    const float* Ah = A + bh * N * topk;
-    const float* Ch = Cc + bh * N * topk;
+    const uint4* rh = recs + bh * P;
     const float* qh = q + bh * N * 3;
     const T* doh = static_cast<const T*>(dout) + bh * N * dv;
 
@@ -320,11 +351,11 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-#pragma unroll 4
-    for (uint32_t t = seg0; t < seg1; ++t) {
-        const uint32_t pid = ph[t];
-        const int64_t i = pid / static_cast<uint32_t>(topk);
-        const float a = Ah[pid], c = Ch[pid];
+#pragma unroll 2
+    for (uint32_t t = seg0 + sub; t < seg1; t += S) {
+        const uint4 rec = rh[t];
+        const int64_t i = rec.y;
+        const float a = __uint_as_float(rec.z), c = __uint_as_float(rec.w);
         s0 += c * (qh[3 * i] - k0);
         s1 += c * (qh[3 * i + 1] - k1);
         s2 += c * (qh[3 * i + 2] - k2);
@@ -339,33 +370,55 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
             }
         }
     }
+    for (int off = G; off < 64; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + c * G;
-        if (ch < chunks) IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[c][e] += __shfl_xor(acc[c][e], off, 64);
+        s0 += __shfl_xor(s0, off, 64);
+        s1 += __shfl_xor(s1, off, 64);
+        s2 += __shfl_xor(s2, off, 64);
     }
-    if (lane == 0) {
-        const float f = 2.0f * inv_g2;
-        dk[3 * row] = f * s0;
-        dk[3 * row + 1] = f * s1;
-        dk[3 * row + 2] = f * s2;
+    if (sub == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = lane + c * G;
+            if (ch < chunks) IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
+        }
+        if (lane == 0) {
+            const float f = 2.0f * inv_g2;
+            dk[3 * row] = f * s0;
+            dk[3 * row + 1] = f * s1;
+            dk[3 * row + 2] = f * s2;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
-__global__ void __launch_bounds__(256) zeta_dgamma_reduce_kernel(const float* __restrict__ dg_row,
-                                                                  int64_t B, int64_t H, int64_t N,
-                                                                  float* __restrict__ dgamma) {
-    __shared__ float red[256];
+// One workgroup per head; every thread keeps 8 independent partial sums (so 8 loads are in
+// flight), combined in a fixed order, then a fixed LDS tree.
+constexpr int kDgThreads = 1024;
+__global__ void __launch_bounds__(kDgThreads) zeta_dgamma_reduce_kernel(
+    const float* __restrict__ dg_row, int64_t B, int64_t H, int64_t N, float* __restrict__ dgamma) {
+    __shared__ float red[kDgThreads];
     const int64_t h = blockIdx.x;
-    float acc = 0.0f;
-    for (int64_t b = 0; b < B; ++b) {
-        const float* p = dg_row + (b * H + h) * N;
-        for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += p[i];
+    const int64_t total = B * N;
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
+    for (int64_t f0 = threadIdx.x; f0 < total; f0 += 8 * kDgThreads) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t f = f0 + u * kDgThreads;
+            if (f < total) {
+                const int64_t b = f / N, i = f - b * N;
+                acc[u] += dg_row[(b * H + h) * N + i];
+            }
+        }
     }
-    red[threadIdx.x] = acc;
+    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
+    for (int w = kDgThreads / 2; w > 0; w >>= 1) {
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
@@ -379,6 +432,20 @@ size_t bwd_pairs_per_head(int64_t N, int topk) {
 }
 
 int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
+
+template <bool FIRST>
+static void radix_pass(int64_t BH, const int32_t* idx, const float* A, const float* Cc,
+                       const uint4* rin, int64_t items, int64_t stride, int shift, int topk,
+                       const BwdBuffers& ws, uint4* rout, hipStream_t s) {
+    const int64_t tiles = bwd_tiles_per_head(items);
+    dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
+    hipLaunchKernelGGL(zeta_radix_hist_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
+                       items, stride, shift, tiles, topk, ws.hist);
+    hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64), 0, s,
+                       ws.hist, tiles, ws.totals);
+    hipLaunchKernelGGL(zeta_radix_scatter_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, A,
+                       Cc, rin, items, stride, shift, tiles, topk, ws.hist, ws.totals, ws.P, rout);
+}
 
 template <bool BF16, int CPL>
 static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk, int glog,
@@ -399,40 +466,26 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
     const int passes = bits <= 8 ? 1 : (bits + 7) / 8;
-    const int64_t raw_items = N * topk;
-    uint32_t* kin = nullptr;
-    uint32_t* vin = nullptr;
-    for (int p = 0; p < passes; ++p) {
-        const bool first = p == 0;
-        const int64_t items = first ? raw_items : ws.P;
-        const int64_t stride = first ? raw_items : ws.P;
-        const int64_t tiles = bwd_tiles_per_head(items);
-        uint32_t* kout = (p & 1) ? ws.key1 : ws.key0;
-        uint32_t* vout = (p & 1) ? ws.val1 : ws.val0;
-        const int32_t* pidx = first ? idx : nullptr;
-        dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
-        hipLaunchKernelGGL(zeta_radix_hist_kernel, grid, dim3(kRadixThreads), 0, s, pidx, kin,
-                           items, stride, 8 * p, tiles, topk, ws.hist);
-        hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64),
-                           0, s, ws.hist, tiles, ws.totals);
-        hipLaunchKernelGGL(zeta_radix_scatter_kernel, grid, dim3(kRadixThreads), 0, s, pidx, kin,
-                           vin, items, stride, 8 * p, tiles, topk, ws.hist, ws.totals, ws.P, kout,
-                           vout);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        kin = kout;
-        vin = vout;
+    radix_pass<true>(BH, idx, ws.A, ws.C, nullptr, N * topk, N * topk, 0, topk, ws, ws.rec0, s);
+    uint4* cur = ws.rec0;
+    for (int p = 1; p < passes; ++p) {
+        uint4* nxt = (p & 1) ? ws.rec1 : ws.rec0;
+        radix_pass<false>(BH, nullptr, nullptr, nullptr, cur, ws.P, ws.P, 8 * p, topk, ws, nxt, s);
+        cur = nxt;
     }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(zeta_segment_offsets_kernel,
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
-                       dim3(256), 0, s, kin, ws.P, N, ws.offs);
+                       dim3(256), 0, s, cur, ws.P, N, ws.offs);
     marks.record(2, s);
-    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(gblocks)),
-                       dim3(256), 0, s, q, k, gamma, dout, ws.A, ws.C, vin, ws.offs, rows, N, H, dv,
-                       topk, glog, ws.P, dk, dvout);
+    const int64_t kblocks = (rows + 3) / 4;
+    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(kblocks)),
+                       dim3(256), 0, s, q, k, gamma, dout, cur, ws.offs, rows, N, H, dv, glog, ws.P,
+                       dk, dvout);
     marks.record(3, s);
-    hipLaunchKernelGGL(zeta_dgamma_reduce_kernel, dim3(static_cast<unsigned>(H)), dim3(256), 0, s,
-                       ws.dg_row, BH / H, H, N, dgamma);
+    hipLaunchKernelGGL(zeta_dgamma_reduce_kernel, dim3(static_cast<unsigned>(H)), dim3(kDgThreads),
+                       0, s, ws.dg_row, BH / H, H, N, dgamma);
     marks.record(4, s);
     return hipGetLastError();
 }

@@ -85,7 +85,7 @@ FwdPlan plan_fwd(const zeta_shape* sh) {
 }
 
 struct BwdPlan {
-    size_t A, C, dg, k0, v0, k1, v1, hist, totals, offs, total;
+    size_t A, C, dg, r0, r1, hist, totals, offs, total;
     int64_t P, tiles;
 };
 
@@ -103,10 +103,8 @@ BwdPlan plan_bwd(const zeta_shape* sh) {
     p.A = take(sizeof(float) * BH * N * K);
     p.C = take(sizeof(float) * BH * N * K);
     p.dg = take(sizeof(float) * BH * N);
-    p.k0 = take(sizeof(uint32_t) * BH * p.P);
-    p.v0 = take(sizeof(uint32_t) * BH * p.P);
-    p.k1 = take(sizeof(uint32_t) * BH * p.P);
-    p.v1 = take(sizeof(uint32_t) * BH * p.P);
+    p.r0 = take(16 * BH * p.P);
+    p.r1 = take(16 * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
@@ -265,10 +263,8 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     b.A = at<float>(workspace, p.A);
     b.C = at<float>(workspace, p.C);
     b.dg_row = at<float>(workspace, p.dg);
-    b.key0 = at<uint32_t>(workspace, p.k0);
-    b.val0 = at<uint32_t>(workspace, p.v0);
-    b.key1 = at<uint32_t>(workspace, p.k1);
-    b.val1 = at<uint32_t>(workspace, p.v1);
+    b.rec0 = at<uint4>(workspace, p.r0);
+    b.rec1 = at<uint4>(workspace, p.r1);
     b.hist = at<uint32_t>(workspace, p.hist);
     b.totals = at<uint32_t>(workspace, p.totals);
     b.offs = at<uint32_t>(workspace, p.offs);

@@ -49,10 +49,8 @@ struct BwdBuffers {
     float* A;         // [BHN][topk] normalised weights a_ij
     float* C;         // [BHN][topk] pair coefficients c_ij
     float* dg_row;    // [BHN] per-query dgamma contributions
-    uint32_t* key0;   // [BH][P] radix-sort ping-pong keys
-    uint32_t* val0;   // [BH][P] radix-sort ping-pong values
-    uint32_t* key1;
-    uint32_t* val1;
+    uint4* rec0;      // [BH][P] radix-sort ping-pong records {j, i, a, c}
+    uint4* rec1;
     uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
     uint32_t* totals; // [BH][256] digit totals
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
