@@ -33,8 +33,8 @@ METRIC = "ms per ZETA fwd (and fwd+bwd) at N=65536,H=8; achieved HBM GB/s vs pea
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PAGES_CONTEXT = {"zeta_fwd_ms": 85.8, "zeta_fwd_bwd_ms": 608.2, "flash_fwd_ms": 805.3,
                  "flash_fwd_bwd_ms": 7044.1, "hardware": "not stated on the pages"}
-FWD_STAGES = ["encode", "tree", "select", "gather"]
-BWD_STAGES = ["bwd_query", "bwd_transpose", "bwd_key", "bwd_dgamma"]
+FWD_STAGES = ["encode", "tree", "select", "order", "gather"]
+BWD_STAGES = ["bwd_order", "bwd_query", "bwd_transpose", "bwd_key", "bwd_dgamma"]
 SINGLE_KERNEL = {"select": "zeta_select_kernel", "gather": "zeta_cauchy_gather_kernel",
                  "bwd_query": "zeta_bwd_query_kernel", "bwd_key": "zeta_bwd_key_kernel"}
 KERNEL_SOURCE = {"select": "select.hip", "gather": "gather.hip", "bwd_query": "backward.hip",
@@ -73,8 +73,11 @@ def kernel_bytes(w: inputs.Workload) -> dict:
     b["encode"] = BH * w.N * (2 * 12 + 2 * 4)
     b["tree"] = BH * w.N * (4 + 2 * 8 * (tile_levels + 1) + 2 * 16 * (levels - 1 - tile_levels))
     b["select"] = BH * select_run_bytes(w)
-    b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + row).sum())
-    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 8 * m + 16).sum())
+    # processing order: bucket histogram and scatter read the codes, the order is written
+    b["order"] = BH * w.N * (4 + 4 + 4)
+    b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + 4 + row).sum())
+    b["bwd_order"] = BH * w.N * (2 * 12 + 2 * 4 + 2 * 12)
+    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 8 * m + 16 + 4).sum())
     bits = int(np.ceil(np.log2(w.N))) if w.N > 1 else 0
     passes = 1 if bits <= 8 else -(-bits // 8)
     # pass 0 reads the index rows twice (histogram, scatter) and writes (key, pair) once;
@@ -82,7 +85,7 @@ def kernel_bytes(w: inputs.Workload) -> dict:
     # the segment starts read the sorted keys and write N+1 offsets
     b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 20 * pairs +
                                4 * pairs + 4 * (w.N + 1))
-    b["bwd_key"] = BH * (w.N * (8 + 12 + 12 + row) + pairs * (4 + 4 + 4 + 12 + row))
+    b["bwd_key"] = BH * (w.N * (4 + 8 + 12 + 12 + row) + pairs * (16 + 12 + row))
     b["bwd_dgamma"] = BH * w.N * 4.0
     return b
 
@@ -175,6 +178,8 @@ def main() -> int:
     ap.add_argument("--workload", default="long_fwd_bwd", choices=sorted(inputs.CONFIGS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device-to-device copies (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -184,6 +189,18 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        # known-size plain copies: the HBM counters of this kernel give the scale factor
+        # between counter readings and bytes (1 GiB read + 1 GiB written per copy)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": src.numel() * 4,
+                          "copies": 5}), flush=True)
+        return 0
 
     from order_retrieval_amd import zeta as Z
 
@@ -222,7 +239,8 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    ev = [(hip.create(5), hip.create(5)) for _ in range(args.steps)]
+    ev = [(hip.create(len(FWD_STAGES) + 1), hip.create(len(BWD_STAGES) + 1))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()

@@ -114,8 +114,9 @@ zeta_status zeta_fwd(const zeta_shape *shape, const float *q, const float *k, co
  *     dk_j =  (2/gamma^2) sum_i c_ij (q_i - k_j)          dk: [B,H,N,3] fp32
  *     dv_j =  sum_i a_ij dO_i                             dv: [B,H,N,dv] v_dtype
  *     dgamma_h = (2/gamma_h^3) sum_{b,i,j} c_ij d_ij      dgamma: [H] fp32
- * Sums over i for a key run over the pairs that selected it in ascending i, so results are
- * bitwise reproducible (no floating-point atomics).  dout: [B,H,N,dv] v_dtype.
+ * Every sum runs in a fixed order (a key's pairs are sorted by query, then reduced by a
+ * fixed butterfly), so results are bitwise reproducible: no floating-point atomics.
+ * dout: [B,H,N,dv] v_dtype.
  * idx is expected to be the selection zeta_fwd returned: slot r of query i is used when
  * r < min(topk, i+1), and its entry is clamped into [0, i]; later slots are ignored.  An
  * index tensor that is not a valid selection therefore gives meaningless but bounded
@@ -131,9 +132,10 @@ zeta_status zeta_bwd(const zeta_shape *shape, const float *q, const float *k, co
  * stream before its first launch and events[s] after stage s, for as many stages as the
  * call has and `count` allows:
  *   zeta_select, zeta_fwd: 1 encode (q and k), 2 tree build, 3 select kernel,
- *                          4 gather kernel (zeta_fwd only);
- *   zeta_bwd:              1 per-query kernel, 2 selection transpose (radix passes and
- *                          segment starts), 3 per-key kernel, 4 dgamma reduction.
+ *                          4 query processing order, 5 gather kernel (4, 5: zeta_fwd only);
+ *   zeta_bwd:              1 encode and processing orders, 2 per-query kernel,
+ *                          3 selection transpose (radix passes and segment starts),
+ *                          4 per-key kernel, 5 dgamma reduction.
  * events = NULL or count = 0 turns recording off.  The events stay owned by the caller and
  * must outlive the calls that record them.                                               */
 zeta_status zeta_set_stage_events(void *const *events, int32_t count);

@@ -15,7 +15,7 @@
 //      key's segment;
 //   3. segment starts offs[j] from the sorted keys;
 //   4. per-key pass: each key reduces its segment in a fixed order (dv, dk);
-//   5. dgamma: fixed-order reduction per head over the batch and the queries.
+//   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
 
@@ -24,7 +24,6 @@ namespace zeta {
 constexpr int kRadixThreads = 256;
 constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;
-constexpr int kMaxGroups = 256 / 8;  // groups per workgroup (at least 8 lanes per group)
 
 // A selection slot r of query i is a pair when r < min(topk, i+1); its key is clamped into
 // [0, i], so an index tensor that is not a valid selection still never leads outside the
@@ -48,26 +47,32 @@ __device__ __forceinline__ float group_sum(float x, int G) {
 }
 
 // ---------------------------------------------------------------------------- 1. queries
-template <bool BF16, int CPL>
+// Slot r of a query belongs to lane r % G of its group (register r / G): the owner loads the
+// index and key row and computes s, the distance terms, and later a, c and the dq / dgamma
+// terms of its slots.  The value rows are taken in slot order with the index broadcast from
+// the owner, so a batch of row loads does not wait on memory; g = dO . v is reduced over the
+// group with a xor butterfly and kept by the slot's owner.
+template <bool BF16, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
-    const void* __restrict__ dout, int64_t rows, int64_t N, int64_t H, int dv, int topk,
-    int glog, float* __restrict__ A, float* __restrict__ Cc, float* __restrict__ dq,
-    float* __restrict__ dg_row) {
+    const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t rows, int64_t N,
+    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd, float* __restrict__ A,
+    float* __restrict__ Cc, float* __restrict__ dq, float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
-    __shared__ float2 sh[kMaxGroups][kMaxTopK];
-    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t row = gtid >> glog;
+    const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
+    if (tile >= tiles) return;
+    const int64_t gtid = tile * blockDim.x + threadIdx.x;
+    const int64_t t = gtid >> glog;  // position in the processing order
     const int G = 1 << glog;
     const int lane = static_cast<int>(gtid & (G - 1));
-    const int grp = threadIdx.x >> glog;
-    if (row >= rows) return;
+    if (t >= rows) return;
     const int chunks = dv / E;
-    const int64_t bh = row / N;
-    const int64_t i = row - bh * N;
+    const int64_t bh = t / N;
+    const int64_t i = order ? static_cast<int64_t>(order[t]) : t - bh * N;
+    const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
@@ -88,46 +93,68 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         }
     }
 
-    float S = 0.0f, Tsum = 0.0f;
-#pragma unroll 4
-    for (int r = 0; r < m; ++r) {
-        const int64_t j = clamp_index(ir[r], i);
-        const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
-        const float d = d0 * d0 + d1 * d1 + d2 * d2;
-        const float s = 1.0f / (1.0f + d * inv_g2);
-        float part = 0.0f;
+    int32_t jo[U];
+    float so[U], dx[U], dy[U], dz[U], gg[U];
+    float ssum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + c * G;
-            if (ch < chunks) {
-                float x[E];
-                IO::load(vh + j * dv + ch * E, x);
-#pragma unroll
-                for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
-            }
+    for (int u = 0; u < U; ++u) {
+        const int r = lane + u * G;
+        jo[u] = 0;
+        so[u] = dx[u] = dy[u] = dz[u] = gg[u] = 0.0f;
+        if (r < m) {
+            const int32_t j = static_cast<int32_t>(clamp_index(ir[r], i));
+            jo[u] = j;
+            dx[u] = q0 - kh[3 * j];
+            dy[u] = q1 - kh[3 * j + 1];
+            dz[u] = q2 - kh[3 * j + 2];
+            so[u] = 1.0f / (1.0f + (dx[u] * dx[u] + dy[u] * dy[u] + dz[u] * dz[u]) * inv_g2);
+            ssum += so[u];
         }
-        const float gr = group_sum(part, G);
-        S += s;
-        Tsum += s * gr;
-        if ((r & (G - 1)) == lane) sh[grp][r] = make_float2(s, gr);
     }
+    const float S = group_sum(ssum, G);
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int n = m - u * G < G ? m - u * G : G;
+#pragma unroll 4
+        for (int sl = 0; sl < n; ++sl) {
+            const int64_t j = __shfl(jo[u], sl, G);
+            float part = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + c * G;
+                if (ch < chunks) {
+                    float x[E];
+                    IO::load(vh + j * dv + ch * E, x);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
+                }
+            }
+            const float gr = group_sum(part, G);
+            if (sl == lane) gg[u] = gr;
+        }
+    }
+
+    float tsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) tsum += so[u] * gg[u];
     const float inv_S = 1.0f / S;
-    const float D = Tsum * inv_S;
+    const float D = group_sum(tsum, G) * inv_S;
 
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
-    for (int r = lane; r < m; r += G) {
-        const float2 sg = sh[grp][r];
-        const int64_t j = clamp_index(ir[r], i);
-        const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
-        const float d = d0 * d0 + d1 * d1 + d2 * d2;
-        const float a = sg.x * inv_S;
-        const float c = a * sg.x * (sg.y - D);
-        A[row * topk + r] = a;
-        Cc[row * topk + r] = c;
-        a0 += c * d0;
-        a1 += c * d1;
-        a2 += c * d2;
-        ag += c * d;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = lane + u * G;
+        if (r < m) {
+            const float a = so[u] * inv_S;
+            const float c = a * so[u] * (gg[u] - D);
+            A[row * topk + r] = a;
+            Cc[row * topk + r] = c;
+            a0 += c * dx[u];
+            a1 += c * dy[u];
+            a2 += c * dz[u];
+            ag += c * (dx[u] * dx[u] + dy[u] * dy[u] + dz[u] * dz[u]);
+        }
     }
     a0 = group_sum(a0, G);
     a1 = group_sum(a1, G);
@@ -141,7 +168,6 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         dg_row[row] = 2.0f * inv_g2 / g * ag;
     }
 }
-
 
 // ---------------------------------------------------------------------------- 2. transpose
 // Every pair travels through the sort as one 16-byte record {j, i, a_ij, c_ij}.  Pass 0
@@ -315,20 +341,26 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint4* 
 }
 
 // ---------------------------------------------------------------------------- 4. keys
-// One wavefront per key.  The wavefront is split into sub-groups of G lanes (one value row
-// per sub-group); sub-group s takes pairs s, s+S, s+2S, ... of the key's segment, and the S
-// partial sums are combined with a fixed butterfly, so the summation order is fixed.
+// One wavefront per key.  The key's records are taken 64 at a time, one per lane: each lane
+// adds its record's dk term and keeps (i, a) for the others.  The wavefront's sub-groups of G
+// lanes (one value row each) then take every S-th record of the batch (S = 64/G), with i and
+// a broadcast from the owning lane, so a batch of dO row loads does not wait on memory.  The
+// partial sums are combined with fixed butterflies, so the summation order is fixed.
 template <bool BF16, int CPL>
 __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
     const void* __restrict__ dout, const uint4* __restrict__ recs,
-    const uint32_t* __restrict__ offs, int64_t rows, int64_t N, int64_t H, int dv, int glog,
-    int64_t P, float* __restrict__ dk, void* __restrict__ dvout) {
+    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ order, int64_t rows,
+    int64_t N, int64_t H, int dv, int glog, int64_t P, int64_t tiles, int64_t per_xcd,
+    float* __restrict__ dk, void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
+    if (tile >= tiles) return;
+    const int64_t t = tile * (blockDim.x >> 6) + (threadIdx.x >> 6);  // position in the order
+    if (t >= rows) return;
+    const int64_t row = order ? (t / N) * N + order[t] : t;
     const int lane64 = threadIdx.x & 63;
     const int G = 1 << glog;
     const int S = 64 >> glog;
@@ -351,22 +383,35 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-#pragma unroll 2
-    for (uint32_t t = seg0 + sub; t < seg1; t += S) {
-        const uint4 rec = rh[t];
-        const int64_t i = rec.y;
-        const float a = __uint_as_float(rec.z), c = __uint_as_float(rec.w);
-        s0 += c * (qh[3 * i] - k0);
-        s1 += c * (qh[3 * i + 1] - k1);
-        s2 += c * (qh[3 * i + 2] - k2);
+    for (uint32_t base = seg0; base < seg1; base += 64) {
+        const int cnt = seg1 - base < 64u ? static_cast<int>(seg1 - base) : 64;
+        uint32_t io = 0;
+        float ao = 0.0f;
+        if (lane64 < cnt) {
+            const uint4 rec = rh[base + lane64];
+            io = rec.y;
+            ao = __uint_as_float(rec.z);
+            const float c = __uint_as_float(rec.w);
+            s0 += c * (qh[3 * io] - k0);
+            s1 += c * (qh[3 * io + 1] - k1);
+            s2 += c * (qh[3 * io + 2] - k2);
+        }
+        // the loop is uniform over the wavefront so that every lane takes part in the
+        // shuffles (a lane that has left a loop does not supply data to them)
+#pragma unroll 4
+        for (int pp0 = 0; pp0 < cnt; pp0 += S) {
+            const int pp = pp0 + sub;
+            const int64_t i = __shfl(io, pp & 63, 64);
+            const float a = __shfl(ao, pp & 63, 64);
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-            const int ch = lane + cc * G;
-            if (ch < chunks) {
-                float x[E];
-                IO::load(doh + i * dv + ch * E, x);
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int ch = lane + cc * G;
+                if (pp < cnt && ch < chunks) {
+                    float x[E];
+                    IO::load(doh + i * dv + ch * E, x);
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[cc][e] += a * x[e];
+                    for (int e = 0; e < E; ++e) acc[cc][e] += a * x[e];
+                }
             }
         }
     }
@@ -375,6 +420,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[c][e] += __shfl_xor(acc[c][e], off, 64);
+    }
+    for (int off = 1; off < 64; off <<= 1) {
         s0 += __shfl_xor(s0, off, 64);
         s1 += __shfl_xor(s1, off, 64);
         s2 += __shfl_xor(s2, off, 64);
@@ -395,35 +442,47 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
-// One workgroup per head; every thread keeps 8 independent partial sums (so 8 loads are in
-// flight), combined in a fixed order, then a fixed LDS tree.
-constexpr int kDgThreads = 1024;
-__global__ void __launch_bounds__(kDgThreads) zeta_dgamma_reduce_kernel(
-    const float* __restrict__ dg_row, int64_t B, int64_t H, int64_t N, float* __restrict__ dgamma) {
-    __shared__ float red[kDgThreads];
-    const int64_t h = blockIdx.x;
+// Two fixed-order levels: workgroups sum chunks of kDgChunk per-query terms of a head (8
+// loads in flight per thread, then an LDS tree), and one wavefront per head sums the chunk
+// partials in chunk order.
+constexpr int kDgChunk = 2048;
+__global__ void __launch_bounds__(256) zeta_dgamma_partial_kernel(const float* __restrict__ dg_row,
+                                                                   int64_t B, int64_t H, int64_t N,
+                                                                   int64_t chunks,
+                                                                   float* __restrict__ part) {
+    __shared__ float red[256];
+    const int64_t h = blockIdx.y;
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kDgChunk;
     const int64_t total = B * N;
-    float acc[8];
+    float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-    for (int64_t f0 = threadIdx.x; f0 < total; f0 += 8 * kDgThreads) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t f = f0 + u * kDgThreads;
-            if (f < total) {
-                const int64_t b = f / N, i = f - b * N;
-                acc[u] += dg_row[(b * H + h) * N + i];
-            }
+    for (int u = 0; u < kDgChunk / 256; ++u) {
+        const int64_t f = f0 + u * 256 + threadIdx.x;
+        if (f < total) {
+            const int64_t b = f / N, i = f - b * N;
+            acc += dg_row[(b * H + h) * N + i];
         }
     }
-    red[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    red[threadIdx.x] = acc;
     __syncthreads();
-    for (int w = kDgThreads / 2; w > 0; w >>= 1) {
+    for (int w = 128; w > 0; w >>= 1) {
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) dgamma[h] = red[0];
+    if (threadIdx.x == 0) part[h * chunks + blockIdx.x] = red[0];
 }
+
+__global__ void __launch_bounds__(64) zeta_dgamma_final_kernel(const float* __restrict__ part,
+                                                                int64_t chunks,
+                                                                float* __restrict__ dgamma) {
+    const int64_t h = blockIdx.x;
+    float acc = 0.0f;
+    for (int64_t c = threadIdx.x; c < chunks; c += 64) acc += part[h * chunks + c];
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (threadIdx.x == 0) dgamma[h] = acc;
+}
+
+int64_t dgamma_chunks(int64_t B, int64_t N) { return (B * N + kDgChunk - 1) / kDgChunk; }
 
 // ---------------------------------------------------------------------------- host
 size_t bwd_pairs_per_head(int64_t N, int topk) {
@@ -455,13 +514,23 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
                                const StageEvents& marks, hipStream_t s) {
     const int64_t rows = BH * N;
     marks.record(0, s);
-    const int64_t gblocks = ((rows << glog) + 255) / 256;
-    hipLaunchKernelGGL((zeta_bwd_query_kernel<BF16, CPL>), dim3(static_cast<unsigned>(gblocks)),
-                       dim3(256), 0, s, q, k, v, gamma, idx, dout, rows, N, H, dv, topk, glog,
-                       ws.A, ws.C, dq, ws.dg_row);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_encode(q, rows, ws.zq, s);
+    if (e == hipSuccess) e = launch_order(BH, N, ws.zq, ws.perm_q, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
+    const int64_t gtiles = ((rows << glog) + 255) / 256;
+    const int64_t gper = xcd_per(gtiles);
+    const int u = (topk + (1 << glog) - 1) >> glog;  // slots per lane (<= 8)
+    auto qk = u <= 1 ? zeta_bwd_query_kernel<BF16, CPL, 1>
+            : u <= 2 ? zeta_bwd_query_kernel<BF16, CPL, 2>
+            : u <= 4 ? zeta_bwd_query_kernel<BF16, CPL, 4>
+                     : zeta_bwd_query_kernel<BF16, CPL, 8>;
+    hipLaunchKernelGGL(qk, dim3(static_cast<unsigned>(gper * kXcds)), dim3(256), 0, s, q, k, v,
+                       gamma, idx, dout, ws.perm_q, rows, N, H, dv, topk, glog, gtiles, gper, ws.A,
+                       ws.C, dq, ws.dg_row);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    marks.record(2, s);
 
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
@@ -478,15 +547,20 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     hipLaunchKernelGGL(zeta_segment_offsets_kernel,
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
                        dim3(256), 0, s, cur, ws.P, N, ws.offs);
-    marks.record(2, s);
-    const int64_t kblocks = (rows + 3) / 4;
-    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(kblocks)),
-                       dim3(256), 0, s, q, k, gamma, dout, cur, ws.offs, rows, N, H, dv, glog, ws.P,
-                       dk, dvout);
     marks.record(3, s);
-    hipLaunchKernelGGL(zeta_dgamma_reduce_kernel, dim3(static_cast<unsigned>(H)), dim3(kDgThreads),
-                       0, s, ws.dg_row, BH / H, H, N, dgamma);
+    const int64_t ktiles = (rows + 3) / 4;
+    const int64_t kper = xcd_per(ktiles);
+    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(kper * kXcds)),
+                       dim3(256), 0, s, q, k, gamma, dout, cur, ws.offs, nullptr, rows, N, H, dv,
+                       glog, ws.P, ktiles, kper, dk, dvout);
     marks.record(4, s);
+    const int64_t dch = dgamma_chunks(BH / H, N);
+    hipLaunchKernelGGL(zeta_dgamma_partial_kernel,
+                       dim3(static_cast<unsigned>(dch), static_cast<unsigned>(H)), dim3(256), 0, s,
+                       ws.dg_row, BH / H, H, N, dch, ws.dg_part);
+    hipLaunchKernelGGL(zeta_dgamma_final_kernel, dim3(static_cast<unsigned>(H)), dim3(64), 0, s,
+                       ws.dg_part, dch, dgamma);
+    marks.record(5, s);
     return hipGetLastError();
 }
 

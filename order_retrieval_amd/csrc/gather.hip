@@ -8,31 +8,40 @@
 // over the k selected keys only ("the use of the top-k tokens for attention" in W3/A3).
 //
 // HBM-bound gather: per query k value rows of dv elements (k * dv * |v| bytes) dominate.
+// Queries are taken in Z-order buckets (order.hip) with an XCD-aware tile mapping, so the
+// rows that concurrent queries select overlap and are served from L2.
 // A group of G lanes (a power of two, G * 16 B >= one row) owns one query; each lane keeps
 // fp32 accumulators for its 16-byte chunk(s) of the row, so every selected row is read with
-// one coalesced 16 B-per-lane load.  Weights are computed redundantly by the G lanes from
-// the raw fp32 q, k (their loads hit the same cache lines).  The output is rounded once to
-// the value dtype.
+// one coalesced 16 B-per-lane load.  The output is rounded once to the value dtype.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
 
 namespace zeta {
 
-template <bool BF16, int CPL>
+// Slot r of a query belongs to lane r % G of its group (register r / G): the owner loads
+// the index and the key row and computes the weight, so the group's index and key loads
+// are all in flight at once.  The value rows are then taken in slot order, the index and
+// weight of each slot broadcast from its owner with a cross-lane shuffle, so a batch of
+// row loads does not wait on any memory load.
+template <bool BF16, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ gamma, const int32_t* __restrict__ idx, void* __restrict__ out,
-    int64_t rows, int64_t N, int64_t H, int dv, int topk, int glog) {
+    const float* __restrict__ gamma, const int32_t* __restrict__ idx,
+    const uint32_t* __restrict__ order, void* __restrict__ out, int64_t rows, int64_t N,
+    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd) {
     using IO = VecIO<BF16>;
     constexpr int E = IO::kElems;
-    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t row = gtid >> glog;
+    const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
+    if (tile >= tiles) return;
+    const int64_t gtid = tile * blockDim.x + threadIdx.x;
+    const int64_t t = gtid >> glog;  // position in the processing order
     const int lane = static_cast<int>(gtid & ((1 << glog) - 1));
-    if (row >= rows) return;
+    if (t >= rows) return;
     const int G = 1 << glog;
     const int chunks = dv / E;
-    const int64_t bh = row / N;
-    const int64_t i = row - bh * N;
+    const int64_t bh = t / N;
+    const int64_t i = order ? static_cast<int64_t>(order[t]) : t - bh * N;
+    const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
@@ -41,33 +50,52 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* kh = k + bh * N * 3;
     const typename IO::elem_t* vh = static_cast<const typename IO::elem_t*>(v) + bh * N * dv;
 
+    int32_t jo[U];
+    float so[U];
+    float ssum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = lane + u * G;
+        jo[u] = 0;
+        so[u] = 0.0f;
+        if (r < m) {
+            // the selection guarantees 0 <= j <= i; clamping keeps every access in bounds
+            const int32_t jr = ir[r];
+            const int32_t j = jr < 0 ? 0 : (jr > i ? static_cast<int32_t>(i) : jr);
+            const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
+            jo[u] = j;
+            so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
+            ssum += so[u];
+        }
+    }
+    for (int off = G >> 1; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, G);
+
     float acc[CPL][E];
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
-    float S = 0.0f;
-
-#pragma unroll 4
-    for (int r = 0; r < m; ++r) {
-        const int64_t j = ir[r];
-        const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
-        const float d = d0 * d0 + d1 * d1 + d2 * d2;
-        const float s = 1.0f / (1.0f + d * inv_g2);
-        S += s;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + c * G;
-            if (ch < chunks) {
-                float x[E];
-                IO::load(vh + j * dv + ch * E, x);
+    for (int u = 0; u < U; ++u) {
+        const int n = m - u * G < G ? m - u * G : G;  // slots owned at register u
+#pragma unroll 8
+        for (int sl = 0; sl < n; ++sl) {
+            const int64_t j = __shfl(jo[u], sl, G);
+            const float s = __shfl(so[u], sl, G);
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[c][e] += s * x[e];
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + c * G;
+                if (ch < chunks) {
+                    float x[E];
+                    IO::load(vh + j * dv + ch * E, x);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[c][e] += s * x[e];
+                }
             }
         }
     }
 
-    const float inv_S = 1.0f / S;
+    const float inv_S = 1.0f / ssum;
     typename IO::elem_t* orow = static_cast<typename IO::elem_t*>(out) + row * dv;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -81,31 +109,45 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     }
 }
 
-template <bool BF16, int CPL>
+template <bool BF16, int CPL, int U>
 static hipError_t launch_gather_t(int64_t rows, int64_t N, int64_t H, int dv, int topk, int glog,
                                   const float* q, const float* k, const void* v,
-                                  const float* gamma, const int32_t* idx, void* out,
-                                  hipStream_t s) {
+                                  const float* gamma, const int32_t* idx, const uint32_t* order,
+                                  void* out, hipStream_t s) {
     const int64_t threads = rows << glog;
-    const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((zeta_cauchy_gather_kernel<BF16, CPL>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, q, k, v, gamma, idx, out, rows, N, H, dv, topk, glog);
+    const int64_t tiles = (threads + 255) / 256;
+    const int64_t per = xcd_per(tiles);
+    hipLaunchKernelGGL((zeta_cauchy_gather_kernel<BF16, CPL, U>),
+                       dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v, gamma, idx,
+                       order, out, rows, N, H, dv, topk, glog, tiles, per);
     return hipGetLastError();
+}
+
+template <bool BF16, int CPL>
+static hipError_t launch_gather_u(int64_t rows, int64_t N, int64_t H, int dv, int topk, int glog,
+                                  const float* q, const float* k, const void* v,
+                                  const float* gamma, const int32_t* idx, const uint32_t* order,
+                                  void* out, hipStream_t s) {
+    const int u = (topk + (1 << glog) - 1) >> glog;  // slots per lane (<= 8: G >= 8, k <= 64)
+    if (u <= 1) return launch_gather_t<BF16, CPL, 1>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    if (u <= 2) return launch_gather_t<BF16, CPL, 2>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    if (u <= 4) return launch_gather_t<BF16, CPL, 4>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    return launch_gather_t<BF16, CPL, 8>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
 }
 
 hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
                          const float* q, const float* k, const void* v, const float* gamma,
-                         const int32_t* idx, void* out, hipStream_t s) {
+                         const int32_t* idx, const uint32_t* order, void* out, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const int chunks = static_cast<int>(dv / (bf16 ? 8 : 4));
     const int glog = group_log2(chunks);
     const int cpl = (chunks + (1 << glog) - 1) >> glog;
     if (bf16)
-        return cpl == 1 ? launch_gather_t<true, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, out, s)
-                        : launch_gather_t<true, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, out, s);
-    return cpl == 1 ? launch_gather_t<false, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, out, s)
-                    : launch_gather_t<false, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, out, s);
+        return cpl == 1 ? launch_gather_u<true, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s)
+                        : launch_gather_u<true, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    return cpl == 1 ? launch_gather_u<false, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s)
+                    : launch_gather_u<false, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s);
 }
 
 }  // namespace zeta

@@ -40,17 +40,32 @@ __device__ __forceinline__ void bitonic_sort_bitonic(uint64_t (&a)[K]) {
     }
 }
 
+// Candidates of a walk are loaded kChunk at a time, so that only kChunk of them are live in
+// registers next to the running top-K (more resident wavefronts hide more latency).
+#ifndef ZETA_SELECT_CHUNK
+#define ZETA_SELECT_CHUNK 8
+#endif
+constexpr int kChunk = ZETA_SELECT_CHUNK;
+constexpr int kSearchGroup = 4;  // runs whose binary searches advance in lock-step
+
 // Keys with code >= zq, walking the asc run forward from p: key = e - (zq << 32).
 template <int K>
 __device__ __forceinline__ void merge_right(uint64_t (&best)[K], const uint64_t* __restrict__ run,
                                             int64_t p, int64_t s, uint64_t target) {
     if (p >= s) return;
     if (run[p] - target >= best[K - 1]) return;
+    constexpr int CH = kChunk < K ? kChunk : K;
 #pragma unroll
-    for (int t = 0; t < K; ++t) {
-        const int64_t pos = p + (K - 1 - t);
-        const uint64_t c = pos < s ? run[pos] - target : ~0ull;
-        best[t] = c < best[t] ? c : best[t];
+    for (int c0 = 0; c0 < K; c0 += CH) {
+        uint64_t c[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int64_t pos = p + (K - 1 - (c0 + u));
+            c[u] = pos < s ? run[pos] - target : ~0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) best[c0 + u] = c[u] < best[c0 + u] ? c[u] : best[c0 + u];
+        if (CH < K) __builtin_amdgcn_sched_barrier(0);
     }
     bitonic_sort_bitonic<K>(best);
 }
@@ -63,11 +78,18 @@ __device__ __forceinline__ void merge_left(uint64_t (&best)[K], const uint64_t* 
     if (p <= 0) return;
     const uint64_t top = target | 0xffffffffull;
     if (top - run[p - 1] >= best[K - 1]) return;
+    constexpr int CH = kChunk < K ? kChunk : K;
 #pragma unroll
-    for (int t = 0; t < K; ++t) {
-        const int64_t pos = p - K + t;  // candidate number K-1-t of the walk
-        const uint64_t c = pos >= 0 ? top - run[pos] : ~0ull;
-        best[t] = c < best[t] ? c : best[t];
+    for (int c0 = 0; c0 < K; c0 += CH) {
+        uint64_t c[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int64_t pos = p - K + (c0 + u);  // candidate number K-1-t of the walk
+            c[u] = pos >= 0 ? top - run[pos] : ~0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) best[c0 + u] = c[u] < best[c0 + u] ? c[u] : best[c0 + u];
+        if (CH < K) __builtin_amdgcn_sched_barrier(0);
     }
     bitonic_sort_bitonic<K>(best);
 }
@@ -90,20 +112,47 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
 #pragma unroll
     for (int t = 0; t < K; ++t) best[t] = ~0ull;
 
-    const int64_t m = i + 1;
-    for (int l = levels - 1; l >= 0; --l) {
-        if (!((m >> l) & 1)) continue;
-        const int64_t start = (m >> (l + 1)) << (l + 1);
-        const int64_t s = int64_t(1) << l;
-        const uint64_t* ra = hA + static_cast<int64_t>(l) * N + start;
-        const uint64_t* rd = hD + static_cast<int64_t>(l) * N + start;
-        // lower_bound of the query code in the run (first entry with code >= zq)
-        int64_t p = 0;
-        for (int64_t step = s >> 1; step > 0; step >>= 1)
-            if (ra[p + step - 1] < target) p += step;
-        if (ra[p] < target) p += 1;
-        merge_right<K>(best, ra, p, s, target);
-        merge_left<K>(best, rd, p, target);
+    // The runs are the set bits of i+1, largest first.  They are taken kSearchGroup at a
+    // time: their lower_bound searches (first entry with code >= zq) advance together, so
+    // the probes of different runs are independent loads in flight at once.
+    const uint64_t m = static_cast<uint64_t>(i) + 1;
+    uint64_t rem = m;
+    while (rem) {
+        int lv[kSearchGroup];
+        int64_t pos[kSearchGroup];
+        const uint64_t* ra[kSearchGroup];
+        const uint64_t* rd[kSearchGroup];
+#pragma unroll
+        for (int g = 0; g < kSearchGroup; ++g) {
+            lv[g] = -1;
+            pos[g] = 0;
+            ra[g] = hA;
+            rd[g] = hD;
+            if (rem) {
+                const int l = 63 - __clzll(rem);
+                rem ^= uint64_t(1) << l;
+                const int64_t start = static_cast<int64_t>((m >> (l + 1)) << (l + 1));
+                lv[g] = l;
+                ra[g] = hA + static_cast<int64_t>(l) * N + start;
+                rd[g] = hD + static_cast<int64_t>(l) * N + start;
+            }
+        }
+        for (int64_t step = (int64_t(1) << lv[0]) >> 1; step > 0; step >>= 1) {
+#pragma unroll
+            for (int g = 0; g < kSearchGroup; ++g)
+                if (lv[g] >= 0 && step < (int64_t(1) << lv[g]) && ra[g][pos[g] + step - 1] < target)
+                    pos[g] += step;
+        }
+#pragma unroll
+        for (int g = 0; g < kSearchGroup; ++g)
+            if (lv[g] >= 0 && ra[g][pos[g]] < target) pos[g] += 1;
+#pragma unroll
+        for (int g = 0; g < kSearchGroup; ++g) {
+            if (lv[g] >= 0) {
+                merge_right<K>(best, ra[g], pos[g], int64_t(1) << lv[g], target);
+                merge_left<K>(best, rd[g], pos[g], target);
+            }
+        }
     }
 
     int32_t* out = idx + row * topk;

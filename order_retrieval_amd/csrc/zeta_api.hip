@@ -64,7 +64,7 @@ zeta_status preflight() {
 }
 
 struct FwdPlan {
-    size_t zq, zk, tasc, tdesc, total;
+    size_t zq, zk, tasc, tdesc, perm, total;
 };
 
 FwdPlan plan_fwd(const zeta_shape* sh) {
@@ -80,12 +80,14 @@ FwdPlan plan_fwd(const zeta_shape* sh) {
     off += align_up(sizeof(uint64_t) * BHN * L);
     p.tdesc = off;
     off += align_up(sizeof(uint64_t) * BHN * L);
+    p.perm = off;
+    off += align_up(sizeof(uint32_t) * BHN);
     p.total = off;
     return p;
 }
 
 struct BwdPlan {
-    size_t A, C, dg, r0, r1, hist, totals, offs, total;
+    size_t A, C, dg, dgp, r0, r1, hist, totals, offs, zq, pq, total;
     int64_t P, tiles;
 };
 
@@ -103,11 +105,14 @@ BwdPlan plan_bwd(const zeta_shape* sh) {
     p.A = take(sizeof(float) * BH * N * K);
     p.C = take(sizeof(float) * BH * N * K);
     p.dg = take(sizeof(float) * BH * N);
+    p.dgp = take(sizeof(float) * sh->H * zeta::dgamma_chunks(sh->B, N));
     p.r0 = take(16 * BH * p.P);
     p.r1 = take(16 * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
+    p.zq = take(sizeof(uint32_t) * BH * N);
+    p.pq = take(sizeof(uint32_t) * BH * N);
     p.total = off;
     return p;
 }
@@ -233,11 +238,17 @@ zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, co
     if ((st = preflight()) != ZETA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = run_select(shape, q, k, idx, workspace, s)) != ZETA_OK) return st;
-    hipError_t e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
-                                       static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16,
-                                       q, k, v, gamma, idx, out, s);
-    if (e != hipSuccess) return fail_hip("gather launch", e);
+    const FwdPlan p = plan_fwd(shape);
+    uint32_t* perm = at<uint32_t>(workspace, p.perm);
+    hipError_t e = zeta::launch_order(shape->B * shape->H, shape->N, at<uint32_t>(workspace, p.zq),
+                                      perm, s);
+    if (e != hipSuccess) return fail_hip("order launch", e);
     g_marks.record(4, s);
+    e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
+                            static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16, q, k, v,
+                            gamma, idx, perm, out, s);
+    if (e != hipSuccess) return fail_hip("gather launch", e);
+    g_marks.record(5, s);
     return ZETA_OK;
 }
 
@@ -263,11 +274,14 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     b.A = at<float>(workspace, p.A);
     b.C = at<float>(workspace, p.C);
     b.dg_row = at<float>(workspace, p.dg);
+    b.dg_part = at<float>(workspace, p.dgp);
     b.rec0 = at<uint4>(workspace, p.r0);
     b.rec1 = at<uint4>(workspace, p.r1);
     b.hist = at<uint32_t>(workspace, p.hist);
     b.totals = at<uint32_t>(workspace, p.totals);
     b.offs = at<uint32_t>(workspace, p.offs);
+    b.zq = at<uint32_t>(workspace, p.zq);
+    b.perm_q = at<uint32_t>(workspace, p.pq);
     b.P = p.P;
     b.tiles = p.tiles;
     hipError_t e = zeta::launch_bwd(shape->B * shape->H, shape->H, shape->N, shape->dv,

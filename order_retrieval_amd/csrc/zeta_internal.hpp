@@ -24,6 +24,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Workgroups of a launch are dispatched round-robin over the 8 XCDs of an MI355X.  Kernels
+// that gather rows map the hardware block index to a logical tile so that each XCD walks
+// one contiguous eighth of the tiles in order: its L2 then serves one slice of the
+// processing order.  Launch kXcds * per_xcd blocks (per_xcd = ceil(tiles / kXcds)); blocks
+// whose tile is >= tiles exit.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t block, int64_t per_xcd) {
+    return (block % kXcds) * per_xcd + block / kXcds;
+}
+inline int64_t xcd_per(int64_t tiles) { return (tiles + kXcds - 1) / kXcds; }
+
 // Optional events recorded between the stages of one call (measurement hook).
 struct StageEvents {
     void* const* ev = nullptr;
@@ -43,22 +54,29 @@ hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, const uint
                          hipStream_t s);
 hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
                          const float* q, const float* k, const void* v, const float* gamma,
-                         const int32_t* idx, void* out, hipStream_t s);
+                         const int32_t* idx, const uint32_t* order, void* out, hipStream_t s);
+// Processing order: per (b,h), positions bucketed by the top code bits (order.hip).
+hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
+                        hipStream_t s);
 
 struct BwdBuffers {
     float* A;         // [BHN][topk] normalised weights a_ij
     float* C;         // [BHN][topk] pair coefficients c_ij
     float* dg_row;    // [BHN] per-query dgamma contributions
+    float* dg_part;   // [H][dgamma_chunks] partial sums
     uint4* rec0;      // [BH][P] radix-sort ping-pong records {j, i, a, c}
     uint4* rec1;
     uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
     uint32_t* totals; // [BH][256] digit totals
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
+    uint32_t* zq;     // [BHN] query codes
+    uint32_t* perm_q; // [BHN] query processing order
     int64_t P;        // valid pairs per (b,h)
     int64_t tiles;    // radix tiles per (b,h)
 };
 size_t bwd_pairs_per_head(int64_t N, int topk);
 int64_t bwd_tiles_per_head(int64_t P);
+int64_t dgamma_chunks(int64_t B, int64_t N);
 hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
                       const float* q, const float* k, const void* v, const float* gamma,
                       const int32_t* idx, const void* dout, float* dq, float* dk, void* dvout,
