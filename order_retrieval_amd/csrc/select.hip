@@ -15,21 +15,68 @@
 // global top-k is among the first k of one of those two walks in its own run, so merging
 // the first k of every walk gives the exact answer.
 //
-// Each thread owns one query and keeps its running top-K (K = next power of two >= k) as a
-// sorted array of packed keys (|dz| << 32) | j in registers.  A walk's K candidates are
-// merged with one bitonic step: elementwise min against the reversed candidates leaves a
-// bitonic sequence of the K smallest, which log2(K) compare-exchange stages sort.  A walk
-// whose first candidate is not better than the current K-th is skipped.
+// The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
+// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = K/16 for K >= 32, so
+// every lane holds 16 entries in registers; L = 1 below).  A walk's K candidates are merged
+// with one bitonic step: elementwise min against the reversed candidates (each lane loads
+// its own contiguous block of the walk) leaves a bitonic sequence of the K smallest, which
+// log2(K) compare-exchange stages sort; the stages whose stride spans lanes exchange values
+// with DPP quad permutes.  A walk whose first candidate is not better than the current K-th
+// is skipped.  The binary searches of up to kSearchGroup runs advance in lock-step, so their
+// probes are independent loads in flight together.
 #include "zeta_internal.hpp"
 
 namespace zeta {
 
-template <int K>
-__device__ __forceinline__ void bitonic_sort_bitonic(uint64_t (&a)[K]) {
+constexpr int kSearchGroup = 2;  // runs whose binary searches advance in lock-step
+constexpr int kChunk = 8;        // candidates of a walk loaded per step (register budget)
+
+// Value of the lane `lane ^ D` of the same quad (D = 1 or 2).
+template <int D>
+__device__ __forceinline__ uint64_t quad_xor(uint64_t x) {
+    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF,
+                                            0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)), ctrl,
+                                            0xF, 0xF, false);
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Value of the last lane of this query's lane group (L = 1, 2 or 4 lanes in a quad).
+template <int L>
+__device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
+    if constexpr (L == 1) {
+        return x;
+    } else {
+        constexpr int ctrl = L == 2 ? 0xF5 : 0xFF;  // quad_perm [1,1,3,3] / [3,3,3,3]
+        const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl,
+                                                0xF, 0xF, false);
+        const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)),
+                                                ctrl, 0xF, 0xF, false);
+        return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    }
+}
+
+// Cross-lane compare-exchange stage with partner lane ^ D: the lower lane keeps minima.
+template <int E, int D>
+__device__ __forceinline__ void cross_stage(uint64_t (&a)[E], bool keep_min) {
 #pragma unroll
-    for (int stride = K / 2; stride > 0; stride >>= 1) {
+    for (int u = 0; u < E; ++u) {
+        const uint64_t y = quad_xor<D>(a[u]);
+        const bool lt = y < a[u];
+        a[u] = (lt == keep_min) ? y : a[u];
+    }
+}
+
+// Sort the bitonic sequence held as L lanes x E registers (lane-major) ascending.
+template <int E, int L>
+__device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
+    if constexpr (L == 4) cross_stage<E, 2>(a, (lane & 2) == 0);
+    if constexpr (L >= 2) cross_stage<E, 1>(a, (lane & 1) == 0);
 #pragma unroll
-        for (int t = 0; t < K; ++t) {
+    for (int stride = E / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
             if ((t & stride) == 0) {
                 const uint64_t x = a[t], y = a[t + stride];
                 const bool sw = y < x;
@@ -40,134 +87,125 @@ __device__ __forceinline__ void bitonic_sort_bitonic(uint64_t (&a)[K]) {
     }
 }
 
-// Candidates of a walk are loaded kChunk at a time, so that only kChunk of them are live in
-// registers next to the running top-K (more resident wavefronts hide more latency).
-#ifndef ZETA_SELECT_CHUNK
-#define ZETA_SELECT_CHUNK 8
-#endif
-constexpr int kChunk = ZETA_SELECT_CHUNK;
-constexpr int kSearchGroup = 4;  // runs whose binary searches advance in lock-step
-
-// Keys with code >= zq, walking the asc run forward from p: key = e - (zq << 32).
-template <int K>
-__device__ __forceinline__ void merge_right(uint64_t (&best)[K], const uint64_t* __restrict__ run,
-                                            int64_t p, int64_t s, uint64_t target) {
-    if (p >= s) return;
-    if (run[p] - target >= best[K - 1]) return;
-    constexpr int CH = kChunk < K ? kChunk : K;
-#pragma unroll
-    for (int c0 = 0; c0 < K; c0 += CH) {
-        uint64_t c[CH];
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int64_t pos = p + (K - 1 - (c0 + u));
-            c[u] = pos < s ? run[pos] - target : ~0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < CH; ++u) best[c0 + u] = c[u] < best[c0 + u] ? c[u] : best[c0 + u];
-        if (CH < K) __builtin_amdgcn_sched_barrier(0);
-    }
-    bitonic_sort_bitonic<K>(best);
-}
-
-// Keys with code < zq, walking the desc run backward from p-1:
-// e = (code << 32) | ~j  ->  key = ((zq - code) << 32) | j = (target | 0xffffffff) - e.
-template <int K>
-__device__ __forceinline__ void merge_left(uint64_t (&best)[K], const uint64_t* __restrict__ run,
-                                           int64_t p, uint64_t target) {
-    if (p <= 0) return;
+// Merge one walk into the running top-K.  Candidate c (0 = first) of the walk sits at run
+// position p + c (right walk, asc tree, key = e - target) or p - 1 - c (left walk, desc
+// tree, key = (target | 0xffffffff) - e).  Lane `lane` of the query holds list entries
+// [lane*E, lane*E + E) and pairs them with candidates K-1-t, i.e. its own block of E.
+template <int K, int L, bool RIGHT>
+__device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
+                                           int64_t roff, int64_t p, int64_t s, uint64_t target,
+                                           int lane) {
+    const uint64_t* run = tree + roff;
+    constexpr int E = K / L;
     const uint64_t top = target | 0xffffffffull;
-    if (top - run[p - 1] >= best[K - 1]) return;
-    constexpr int CH = kChunk < K ? kChunk : K;
+    // skip when the walk is empty or its first candidate does not beat the current K-th
+    const bool empty = RIGHT ? p >= s : p <= 0;
+    const uint64_t first = empty ? ~0ull : (RIGHT ? run[p] - target : top - run[p - 1]);
+    const uint64_t kth = from_last_lane<L>(best[E - 1]);
+    if (first >= kth) return;
+    constexpr int CH = kChunk < E ? kChunk : E;
+    // One base pointer per walk and lane; the E candidates sit at constant offsets from it
+    // (immediate offsets of the loads, so no per-candidate address is kept in registers).
+    // Right walk: entry u of this lane is run[b - u], valid while b - u < s.
+    // Left walk:  entry u of this lane is run[b + u], valid while b + u >= 0.
+    const int64_t b = RIGHT ? p + (K - 1 - lane * E) : p - K + lane * E;
+    const uint64_t* wp = run + b;
+    const int64_t lim = RIGHT ? b - s : -b;  // right: valid iff u > lim; left: valid iff u >= lim
 #pragma unroll
-    for (int c0 = 0; c0 < K; c0 += CH) {
+    for (int u0 = 0; u0 < E; u0 += CH) {
         uint64_t c[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int64_t pos = p - K + (c0 + u);  // candidate number K-1-t of the walk
-            c[u] = pos >= 0 ? top - run[pos] : ~0ull;
+        for (int v = 0; v < CH; ++v) {
+            const int u = u0 + v;
+            if (RIGHT)
+                c[v] = u > lim ? wp[-u] - target : ~0ull;
+            else
+                c[v] = u >= lim ? top - wp[u] : ~0ull;
         }
 #pragma unroll
-        for (int u = 0; u < CH; ++u) best[c0 + u] = c[u] < best[c0 + u] ? c[u] : best[c0 + u];
-        if (CH < K) __builtin_amdgcn_sched_barrier(0);
+        for (int v = 0; v < CH; ++v) best[u0 + v] = c[v] < best[u0 + v] ? c[v] : best[u0 + v];
+        if (CH < E) __builtin_amdgcn_sched_barrier(0);
     }
-    bitonic_sort_bitonic<K>(best);
+    bitonic_clean<E, L>(best, lane);
 }
 
-template <int K>
+template <int K, int L>
 __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __restrict__ zq,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            int64_t rows, int64_t N, int levels,
                                                            int topk, int32_t* __restrict__ idx) {
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (row >= rows) return;
+    constexpr int E = K / L;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = g / L;
+    const int lane = static_cast<int>(g % L);
+    if (row >= rows) return;  // uniform over the L lanes of a query
     const int64_t bh = row / N;
     const int64_t i = row - bh * N;
     const uint64_t target = static_cast<uint64_t>(zq[row]) << 32;
     const uint64_t* hA = tree_asc + bh * levels * N;
     const uint64_t* hD = tree_desc + bh * levels * N;
 
-    uint64_t best[K];
+    uint64_t best[E];
 #pragma unroll
-    for (int t = 0; t < K; ++t) best[t] = ~0ull;
+    for (int t = 0; t < E; ++t) best[t] = ~0ull;
 
-    // The runs are the set bits of i+1, largest first.  They are taken kSearchGroup at a
-    // time: their lower_bound searches (first entry with code >= zq) advance together, so
-    // the probes of different runs are independent loads in flight at once.
+    // The runs are the set bits of i+1, largest first, taken kSearchGroup at a time: their
+    // lower_bound searches (first entry with code >= zq) advance together.
     const uint64_t m = static_cast<uint64_t>(i) + 1;
     uint64_t rem = m;
     while (rem) {
+        // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
+        // offsets (not pointers) keep every access a global-memory access
         int lv[kSearchGroup];
         int64_t pos[kSearchGroup];
-        const uint64_t* ra[kSearchGroup];
-        const uint64_t* rd[kSearchGroup];
+        int64_t roff[kSearchGroup];
 #pragma unroll
-        for (int g = 0; g < kSearchGroup; ++g) {
-            lv[g] = -1;
-            pos[g] = 0;
-            ra[g] = hA;
-            rd[g] = hD;
+        for (int gi = 0; gi < kSearchGroup; ++gi) {
+            lv[gi] = -1;
+            pos[gi] = 0;
+            roff[gi] = 0;
             if (rem) {
                 const int l = 63 - __clzll(rem);
                 rem ^= uint64_t(1) << l;
-                const int64_t start = static_cast<int64_t>((m >> (l + 1)) << (l + 1));
-                lv[g] = l;
-                ra[g] = hA + static_cast<int64_t>(l) * N + start;
-                rd[g] = hD + static_cast<int64_t>(l) * N + start;
+                lv[gi] = l;
+                roff[gi] = static_cast<int64_t>(l) * N + static_cast<int64_t>((m >> (l + 1)) << (l + 1));
             }
         }
         for (int64_t step = (int64_t(1) << lv[0]) >> 1; step > 0; step >>= 1) {
 #pragma unroll
-            for (int g = 0; g < kSearchGroup; ++g)
-                if (lv[g] >= 0 && step < (int64_t(1) << lv[g]) && ra[g][pos[g] + step - 1] < target)
-                    pos[g] += step;
+            for (int gi = 0; gi < kSearchGroup; ++gi)
+                if (lv[gi] >= 0 && step < (int64_t(1) << lv[gi]) &&
+                    hA[roff[gi] + pos[gi] + step - 1] < target)
+                    pos[gi] += step;
         }
 #pragma unroll
-        for (int g = 0; g < kSearchGroup; ++g)
-            if (lv[g] >= 0 && ra[g][pos[g]] < target) pos[g] += 1;
+        for (int gi = 0; gi < kSearchGroup; ++gi)
+            if (lv[gi] >= 0 && hA[roff[gi] + pos[gi]] < target) pos[gi] += 1;
 #pragma unroll
-        for (int g = 0; g < kSearchGroup; ++g) {
-            if (lv[g] >= 0) {
-                merge_right<K>(best, ra[g], pos[g], int64_t(1) << lv[g], target);
-                merge_left<K>(best, rd[g], pos[g], target);
+        for (int gi = 0; gi < kSearchGroup; ++gi) {
+            if (lv[gi] >= 0) {
+                const int64_t s = int64_t(1) << lv[gi];
+                merge_walk<K, L, true>(best, hA, roff[gi], pos[gi], s, target, lane);
+                merge_walk<K, L, false>(best, hD, roff[gi], pos[gi], s, target, lane);
             }
         }
     }
 
-    int32_t* out = idx + row * topk;
+    int32_t* out = idx + row * topk + lane * E;
 #pragma unroll
-    for (int t = 0; t < K; ++t)
-        if (t < topk) out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(static_cast<uint32_t>(best[t]));
+    for (int t = 0; t < E; ++t)
+        if (lane * E + t < topk)
+            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(static_cast<uint32_t>(best[t]));
 }
 
-template <int K>
+template <int K, int L>
 static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, const uint32_t* zq,
                                   const uint64_t* ta, const uint64_t* td, int32_t* idx,
                                   hipStream_t s) {
-    const int64_t blocks = (rows + 255) / 256;
-    hipLaunchKernelGGL(zeta_select_kernel<K>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       zq, ta, td, rows, N, levels, topk, idx);
+    const int64_t blocks = (rows * L + 255) / 256;
+    hipLaunchKernelGGL((zeta_select_kernel<K, L>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       s, zq, ta, td, rows, N, levels, topk, idx);
     return hipGetLastError();
 }
 
@@ -176,13 +214,15 @@ hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, const uint
                          hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
-    if (topk <= 1) return launch_select_k<1>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    if (topk <= 2) return launch_select_k<2>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    if (topk <= 4) return launch_select_k<4>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    if (topk <= 8) return launch_select_k<8>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    if (topk <= 16) return launch_select_k<16>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    if (topk <= 32) return launch_select_k<32>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
-    return launch_select_k<64>(rows, N, levels, topk, zq, tree_asc, tree_desc, idx, s);
+    const auto* ta = tree_asc;
+    const auto* td = tree_desc;
+    if (topk <= 1) return launch_select_k<1, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
+    if (topk <= 32) return launch_select_k<32, 2>(rows, N, levels, topk, zq, ta, td, idx, s);
+    return launch_select_k<64, 4>(rows, N, levels, topk, zq, ta, td, idx, s);
 }
 
 }  // namespace zeta
