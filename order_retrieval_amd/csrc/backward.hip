@@ -8,16 +8,20 @@
 //     dk_j =  (2/gamma^2) sum_i c_ij (q_i - k_j)        dgamma = (2/gamma^3) sum c_ij d_ij
 //
 // Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
-//   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij, dq_i and the
-//      query's dgamma term;
+//   1. per-query pass: recompute s, gather v rows for g, write the query's 1/S_i and D_i,
+//      dq_i and the query's dgamma term;
 //   2. selection transpose: stable LSD radix sort (8-bit digits) of the pairs of every (b,h)
-//      by j, carrying 16-byte records {j, i, a_ij, c_ij}; queries stay ascending inside a
-//      key's segment;
+//      by j, carrying 8-byte records {j, i}; queries stay ascending inside a key's segment;
 //   3. segment starts offs[j] from the sorted keys;
-//   4. per-key pass: each key reduces its segment in a fixed order (dv, dk);
+//   4. per-key pass: each key recomputes s_ij, g_ij = dO_i . v_j (it reads the dO_i rows for
+//      dv_j anyway), a_ij and c_ij from the query's 1/S_i and D_i, and reduces its segment
+//      in a fixed order (dv, dk);
 //   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
+// Recomputing a and c on the key side keeps the sorted records at 8 bytes (half of what
+// carrying a and c would take) and saves writing and re-reading two per-pair arrays.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
+#include "xlane.hpp"
 
 namespace zeta {
 
@@ -41,10 +45,6 @@ __device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64
     return true;
 }
 
-__device__ __forceinline__ float group_sum(float x, int G) {
-    for (int off = G >> 1; off > 0; off >>= 1) x += __shfl_xor(x, off, G);
-    return x;
-}
 
 // ---------------------------------------------------------------------------- 1. queries
 // Slot r of a query belongs to lane r % G of its group (register r / G): the owner loads the
@@ -57,8 +57,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd, float* __restrict__ A,
-    float* __restrict__ Cc, float* __restrict__ dq, float* __restrict__ dg_row) {
+    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd,
+    float2* __restrict__ qstat, float* __restrict__ dq, float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -148,8 +148,6 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         if (r < m) {
             const float a = so[u] * inv_S;
             const float c = a * so[u] * (gg[u] - D);
-            A[row * topk + r] = a;
-            Cc[row * topk + r] = c;
             a0 += c * dx[u];
             a1 += c * dy[u];
             a2 += c * dz[u];
@@ -166,25 +164,22 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         dq[3 * row + 1] = f * a1;
         dq[3 * row + 2] = f * a2;
         dg_row[row] = 2.0f * inv_g2 / g * ag;
+        qstat[row] = make_float2(inv_S, D);
     }
 }
 
 // ---------------------------------------------------------------------------- 2. transpose
-// Every pair travels through the sort as one 16-byte record {j, i, a_ij, c_ij}.  Pass 0
-// reads the selection and the per-pair coefficients in pair order (coalesced) and builds the
-// records; later passes move records.  The key kernel then reads each key's pairs as one
-// contiguous run of records.
+// Every pair travels through the sort as one 8-byte record {j, i}.  Pass 0 reads the
+// selection in pair order (coalesced) and builds the records; later passes move records.
+// The key kernel then reads each key's pairs as one contiguous run of records.
 template <bool FIRST>
 __device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
-                                          const float* __restrict__ A,
-                                          const float* __restrict__ Cc,
-                                          const uint4* __restrict__ rin, int64_t e, int topk,
-                                          uint4& rec) {
+                                          const uint2* __restrict__ rin, int64_t e, int topk,
+                                          uint2& rec) {
     if (FIRST) {
         uint32_t key;
         if (!pair_item(idx, e, topk, key)) return false;
-        rec = make_uint4(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(topk),
-                         __float_as_uint(A[e]), __float_as_uint(Cc[e]));
+        rec = make_uint2(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(topk));
         return true;
     }
     rec = rin[e];
@@ -194,7 +189,7 @@ __device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
 // Digit counts of one tile of items.
 template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
-    const int32_t* __restrict__ idx, const uint4* __restrict__ rin, int64_t items,
+    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t items,
     int64_t in_stride, int shift, int64_t tiles, int topk, uint32_t* __restrict__ hist) {
     __shared__ uint32_t cnt[256];
     const int64_t bh = blockIdx.y;
@@ -255,10 +250,9 @@ __global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restric
 // are loaded before the ranking starts, so their loads overlap.
 template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ A, const float* __restrict__ Cc,
-    const uint4* __restrict__ rin, int64_t items, int64_t in_stride, int shift, int64_t tiles,
-    int topk, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int64_t P,
-    uint4* __restrict__ rout) {
+    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t items,
+    int64_t in_stride, int shift, int64_t tiles, int topk, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ totals, int64_t P, uint2* __restrict__ rout) {
     __shared__ uint32_t base[256];
     __shared__ uint32_t scan[256];
     __shared__ uint32_t wcnt[4][256];
@@ -269,15 +263,15 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int lane = tid & 63;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
 
-    uint4 rec[kRadixItems];
+    uint2 rec[kRadixItems];
     uint32_t okmask = 0;
     {
         const int64_t off = bh * in_stride;
 #pragma unroll
         for (int it = 0; it < kRadixItems; ++it) {
             const int64_t e = t0 + it * kRadixThreads + tid;
-            rec[it] = make_uint4(0, 0, 0, 0);
-            if (e < items && load_pair<FIRST>(idx + off, A + off, Cc + off, rin + off, e, topk, rec[it]))
+            rec[it] = make_uint2(0, 0);
+            if (e < items && load_pair<FIRST>(idx + off, rin + off, e, topk, rec[it]))
                 okmask |= 1u << it;
         }
     }
@@ -297,7 +291,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     __syncthreads();
 
     const uint64_t lt = (1ull << lane) - 1ull;
-    uint4* out = rout + bh * P;
+    uint2* out = rout + bh * P;
 #pragma unroll
     for (int it = 0; it < kRadixItems; ++it) {
         const bool valid = (okmask >> it) & 1u;
@@ -325,13 +319,13 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
 }
 
 // ---------------------------------------------------------------------------- 3. offsets
-__global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint4* __restrict__ recs,
+__global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* __restrict__ recs,
                                                                     int64_t P, int64_t N,
                                                                     uint32_t* __restrict__ offs) {
     const int64_t bh = blockIdx.y;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (t >= P) return;
-    const uint4* rh = recs + bh * P;
+    const uint2* rh = recs + bh * P;
     uint32_t* oh = offs + bh * (N + 1);
     const int64_t kk = rh[t].x;
     const int64_t lo = t == 0 ? 0 : static_cast<int64_t>(rh[t - 1].x) + 1;
@@ -341,104 +335,168 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint4* 
 }
 
 // ---------------------------------------------------------------------------- 4. keys
-// One wavefront per key.  The key's records are taken 64 at a time, one per lane: each lane
-// adds its record's dk term and keeps (i, a) for the others.  The wavefront's sub-groups of G
-// lanes (one value row each) then take every S-th record of the batch (S = 64/G), with i and
-// a broadcast from the owning lane, so a batch of dO row loads does not wait on memory.  The
-// partial sums are combined with fixed butterflies, so the summation order is fixed.
+// One 16-lane row (a DPP row) per key j, four keys per wavefront.  A key's pairs are a
+// contiguous run of records, taken kKeyBatch at a time: lane l of the row owns records l and
+// 16 + l of the batch, loads their q_i and the query's {1/S_i, D_i} and forms s_ij, a_ij and
+// a_ij s_ij.  The row then walks the batch's records in order: i and a_ij come from the owning
+// lane by a DPP row broadcast, every lane loads its chunks of the dO_i row (the loads of
+// kKeyLoads records are issued together), adds a_ij dO_i to its chunks of dv_j and its part
+// of g_ij = dO_i . v_j, and a DPP butterfly over the row completes g_ij, which the owning lane
+// keeps for c_ij and the dk term.  No LDS traffic; the trip counts are uniform over the
+// wavefront (the longest of its four keys) and a key's sums run in a fixed order.
+constexpr int kKeyRow = 16;               // lanes per key
+constexpr int kKeyRecs = 2;               // records per lane per batch
+constexpr int kKeyBatch = kKeyRow * kKeyRecs;
+constexpr int kKeyLoads = 4;              // records whose dO loads are issued together
+
+template <bool BF16, int CPL, int U0>
+__device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* __restrict__ doh,
+                                            int dv, const int (&coff)[CPL], uint32_t io,
+                                            float ao, int lrow, int left, float (&vj)[CPL][VecIO<BF16>::kElems],
+                                            float (&acc)[CPL][VecIO<BF16>::kElems], float& gmine) {
+    using IO = VecIO<BF16>;
+    using R = typename IO::raw_t;
+    constexpr int E = IO::kElems;
+    R raw[kKeyLoads][CPL];
+    static_for<0, kKeyLoads>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int64_t i = row_bcast<U0 + u>(io);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) raw[u][c] = IO::load_raw(doh + i * dv + coff[c]);
+    });
+    static_for<0, kKeyLoads>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const float a = row_bcast<U0 + u>(ao);
+        float part = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float x[E];
+            IO::unpack(raw[u][c], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) part += x[e] * vj[c][e];
+            if (U0 + u < left) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[c][e] += a * x[e];
+            }
+        }
+        const float g = group_sum(part, kKeyRow);
+        if (lrow == U0 + u) gmine = g;
+    });
+}
+
 template <bool BF16, int CPL>
 __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
-    const void* __restrict__ dout, const uint4* __restrict__ recs,
-    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ order, int64_t rows,
-    int64_t N, int64_t H, int dv, int glog, int64_t P, int64_t tiles, int64_t per_xcd,
-    float* __restrict__ dk, void* __restrict__ dvout) {
+    const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ gamma, const void* __restrict__ dout,
+    const float2* __restrict__ qstat, const uint2* __restrict__ recs,
+    const uint32_t* __restrict__ offs, int64_t rows, int64_t N, int64_t H, int dv, int64_t P,
+    int64_t tiles, int64_t per_xcd, float* __restrict__ dk, void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
-    if (tile >= tiles) return;
-    const int64_t t = tile * (blockDim.x >> 6) + (threadIdx.x >> 6);  // position in the order
-    if (t >= rows) return;
-    const int64_t row = order ? (t / N) * N + order[t] : t;
+    if (tile >= tiles) return;  // uniform over the workgroup
     const int lane64 = threadIdx.x & 63;
-    const int G = 1 << glog;
-    const int S = 64 >> glog;
-    const int sub = lane64 >> glog;
-    const int lane = lane64 & (G - 1);
+    const int lrow = lane64 & (kKeyRow - 1);
+    const int64_t key = tile * (blockDim.x / kKeyRow) + threadIdx.x / kKeyRow;
+    const bool live = key < rows;
+    const int64_t row = live ? key : rows - 1;  // a row past the end reads a real key, stores nothing
     const int chunks = dv / E;
     const int64_t bh = row / N;
     const int64_t j = row - bh * N;
-    const float g = gamma[bh % H];
-    const float inv_g2 = 1.0f / (g * g);
+    const float gm = gamma[bh % H];
+    const float inv_g2 = 1.0f / (gm * gm);
     const float k0 = k[3 * row], k1 = k[3 * row + 1], k2 = k[3 * row + 2];
-    const uint32_t seg0 = offs[bh * (N + 1) + j], seg1 = offs[bh * (N + 1) + j + 1];
-    const uint4* rh = recs + bh * P;
+    const uint32_t seg0 = offs[bh * (N + 1) + j];
+    const int cnt = live ? static_cast<int>(offs[bh * (N + 1) + j + 1] - seg0) : 0;
+    const uint2* rh = recs + bh * P + seg0;
     const float* qh = q + bh * N * 3;
+    const float2* sh = qstat + bh * N;
     const T* doh = static_cast<const T*>(dout) + bh * N * dv;
 
-    float acc[CPL][E];
+    float vj[CPL][E], acc[CPL][E];
+    int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet vj = 0)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lrow + c * kKeyRow;
+        coff[c] = (ch < chunks ? ch : chunks - 1) * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
+        for (int e = 0; e < E; ++e) vj[c][e] = acc[c][e] = 0.0f;
+        if (ch < chunks) IO::load(static_cast<const T*>(v) + row * dv + ch * E, vj[c]);
+    }
+    // the longest of the wavefront's four keys sets the trip counts
+    int most = cnt;
+    most = max(most, __shfl_xor(most, 16, 64));
+    most = max(most, __shfl_xor(most, 32, 64));
+
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-    for (uint32_t base = seg0; base < seg1; base += 64) {
-        const int cnt = seg1 - base < 64u ? static_cast<int>(seg1 - base) : 64;
-        uint32_t io = 0;
-        float ao = 0.0f;
-        if (lane64 < cnt) {
-            const uint4 rec = rh[base + lane64];
-            io = rec.y;
-            ao = __uint_as_float(rec.z);
-            const float c = __uint_as_float(rec.w);
-            s0 += c * (qh[3 * io] - k0);
-            s1 += c * (qh[3 * io + 1] - k1);
-            s2 += c * (qh[3 * io + 2] - k2);
-        }
-        // the loop is uniform over the wavefront so that every lane takes part in the
-        // shuffles (a lane that has left a loop does not supply data to them)
-#pragma unroll 4
-        for (int pp0 = 0; pp0 < cnt; pp0 += S) {
-            const int pp = pp0 + sub;
-            const int64_t i = __shfl(io, pp & 63, 64);
-            const float a = __shfl(ao, pp & 63, 64);
+    for (int base = 0; base < most; base += kKeyBatch) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const int ch = lane + cc * G;
-                if (pp < cnt && ch < chunks) {
-                    float x[E];
-                    IO::load(doh + i * dv + ch * E, x);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[cc][e] += a * x[e];
-                }
+        for (int r = 0; r < kKeyRecs; ++r) {
+            const int first = base + r * kKeyRow;  // the batch's records r*16 .. r*16+15
+            if (first >= most) break;               // uniform
+            const int p = first + lrow;
+            const bool own = p < cnt;
+            // records past the key's run name query 0 (inside the buffers) and carry a = 0
+            const uint32_t io = own ? rh[p].y : 0u;
+            const float dx = qh[3 * io] - k0, dy = qh[3 * io + 1] - k1, dz = qh[3 * io + 2] - k2;
+            const float2 st = sh[io];
+            const float sv = 1.0f / (1.0f + (dx * dx + dy * dy + dz * dz) * inv_g2);
+            const float ao = own ? sv * st.x : 0.0f;
+            const int left = cnt - first;  // records of this key from position `first` on
+            float gmine = 0.0f;
+            key_records<BF16, CPL, 0>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            if (first + 4 < most)
+                key_records<BF16, CPL, 4>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            if (first + 8 < most)
+                key_records<BF16, CPL, 8>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            if (first + 12 < most)
+                key_records<BF16, CPL, 12>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            if (own) {
+                const float c = ao * sv * (gmine - st.y);
+                s0 += c * dx;
+                s1 += c * dy;
+                s2 += c * dz;
             }
         }
     }
-    for (int off = G; off < 64; off <<= 1) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[c][e] += __shfl_xor(acc[c][e], off, 64);
-    }
-    for (int off = 1; off < 64; off <<= 1) {
-        s0 += __shfl_xor(s0, off, 64);
-        s1 += __shfl_xor(s1, off, 64);
-        s2 += __shfl_xor(s2, off, 64);
-    }
-    if (sub == 0) {
+    s0 = group_sum(s0, kKeyRow);
+    s1 = group_sum(s1, kKeyRow);
+    s2 = group_sum(s2, kKeyRow);
+    if (live) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + c * G;
+            const int ch = lrow + c * kKeyRow;
             if (ch < chunks) IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
         }
-        if (lane == 0) {
+        if (lrow == 0) {
+            // dk_j = (2/gamma^2) sum_i c_ij (q_i - k_j)
             const float f = 2.0f * inv_g2;
             dk[3 * row] = f * s0;
             dk[3 * row + 1] = f * s1;
             dk[3 * row + 2] = f * s2;
         }
     }
+}
+
+template <bool BF16>
+static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, const float* q,
+                             const float* k, const void* v, const float* gamma, const void* dout,
+                             const BwdBuffers& ws, const uint2* recs, float* dk, void* dvout,
+                             hipStream_t s) {
+    const int64_t rows = BH * N;
+    const int chunks = dv / VecIO<BF16>::kElems;
+    const int cpl = (chunks + kKeyRow - 1) / kKeyRow;
+    const int64_t tiles = (rows + (256 / kKeyRow) - 1) / (256 / kKeyRow);
+    const int64_t per = xcd_per(tiles);
+    auto kern = cpl <= 1 ? zeta_bwd_key_kernel<BF16, 1>
+              : cpl <= 2 ? zeta_bwd_key_kernel<BF16, 2>
+              : cpl <= 4 ? zeta_bwd_key_kernel<BF16, 4>
+                         : zeta_bwd_key_kernel<BF16, BF16 ? 4 : 8>;  // bf16 rows have <= 64 chunks
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
+                       gamma, dout, ws.qstat, recs, ws.offs, rows, N, H, dv, ws.P, tiles, per, dk,
+                       dvout);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
@@ -493,17 +551,17 @@ size_t bwd_pairs_per_head(int64_t N, int topk) {
 int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
 
 template <bool FIRST>
-static void radix_pass(int64_t BH, const int32_t* idx, const float* A, const float* Cc,
-                       const uint4* rin, int64_t items, int64_t stride, int shift, int topk,
-                       const BwdBuffers& ws, uint4* rout, hipStream_t s) {
+static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t items,
+                       int64_t stride, int shift, int topk, const BwdBuffers& ws, uint2* rout,
+                       hipStream_t s) {
     const int64_t tiles = bwd_tiles_per_head(items);
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
     hipLaunchKernelGGL(zeta_radix_hist_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
                        items, stride, shift, tiles, topk, ws.hist);
     hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64), 0, s,
                        ws.hist, tiles, ws.totals);
-    hipLaunchKernelGGL(zeta_radix_scatter_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, A,
-                       Cc, rin, items, stride, shift, tiles, topk, ws.hist, ws.totals, ws.P, rout);
+    hipLaunchKernelGGL(zeta_radix_scatter_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
+                       items, stride, shift, tiles, topk, ws.hist, ws.totals, ws.P, rout);
 }
 
 template <bool BF16, int CPL>
@@ -526,8 +584,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
             : u <= 4 ? zeta_bwd_query_kernel<BF16, CPL, 4>
                      : zeta_bwd_query_kernel<BF16, CPL, 8>;
     hipLaunchKernelGGL(qk, dim3(static_cast<unsigned>(gper * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, dout, ws.perm_q, rows, N, H, dv, topk, glog, gtiles, gper, ws.A,
-                       ws.C, dq, ws.dg_row);
+                       gamma, idx, dout, ws.perm_q, rows, N, H, dv, topk, glog, gtiles, gper,
+                       ws.qstat, dq, ws.dg_row);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     marks.record(2, s);
@@ -535,11 +593,11 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
     const int passes = bits <= 8 ? 1 : (bits + 7) / 8;
-    radix_pass<true>(BH, idx, ws.A, ws.C, nullptr, N * topk, N * topk, 0, topk, ws, ws.rec0, s);
-    uint4* cur = ws.rec0;
+    radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, topk, ws, ws.rec0, s);
+    uint2* cur = ws.rec0;
     for (int p = 1; p < passes; ++p) {
-        uint4* nxt = (p & 1) ? ws.rec1 : ws.rec0;
-        radix_pass<false>(BH, nullptr, nullptr, nullptr, cur, ws.P, ws.P, 8 * p, topk, ws, nxt, s);
+        uint2* nxt = (p & 1) ? ws.rec1 : ws.rec0;
+        radix_pass<false>(BH, nullptr, cur, ws.P, ws.P, 8 * p, topk, ws, nxt, s);
         cur = nxt;
     }
     e = hipGetLastError();
@@ -548,11 +606,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
                        dim3(256), 0, s, cur, ws.P, N, ws.offs);
     marks.record(3, s);
-    const int64_t ktiles = (rows + 3) / 4;
-    const int64_t kper = xcd_per(ktiles);
-    hipLaunchKernelGGL((zeta_bwd_key_kernel<BF16, CPL>), dim3(static_cast<unsigned>(kper * kXcds)),
-                       dim3(256), 0, s, q, k, gamma, dout, cur, ws.offs, nullptr, rows, N, H, dv,
-                       glog, ws.P, ktiles, kper, dk, dvout);
+    e = launch_key<BF16>(BH, H, N, dv, q, k, v, gamma, dout, ws, cur, dk, dvout, s);
+    if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);
     hipLaunchKernelGGL(zeta_dgamma_partial_kernel,

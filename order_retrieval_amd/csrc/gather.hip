@@ -15,6 +15,7 @@
 // one coalesced 16 B-per-lane load.  The output is rounded once to the value dtype.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
+#include "xlane.hpp"
 
 namespace zeta {
 
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
             ssum += so[u];
         }
     }
-    for (int off = G >> 1; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, G);
+    ssum = group_sum(ssum, G);
 
     float acc[CPL][E];
 #pragma unroll

@@ -1,0 +1,54 @@
+// xlane.hpp -- cross-lane sums inside a wavefront.
+#pragma once
+
+#include <type_traits>
+
+#include "zeta_internal.hpp"
+
+namespace zeta {
+
+// x from another lane of the same 16-lane row, by a DPP pattern (a modifier of the VALU
+// instruction that reads it, no LDS round trip).  Every lane is active where these are used.
+template <int CTRL>
+__device__ __forceinline__ float dpp_take(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane l of an 8-lane half-row takes lane 7-l
+constexpr int kDppMirror = 0x140;      // lane l of a 16-lane row takes lane 15-l
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, each I a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Every lane of a 16-lane row takes lane L of that row (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+    return dpp_take<0x150 + L>(x);
+}
+template <int L>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x150 + L, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G a power of two, 8 <= G <= 64).  Each step adds the
+// partner block's partial sum: partners xor 1 and xor 2 inside a quad, then the mirrored
+// quad of the half-row and the mirrored half of the row, then xor 16 and xor 32 across rows.
+// Since a + b == b + a exactly, every lane of a group ends with the same bits.
+__device__ __forceinline__ float group_sum(float x, int G) {
+    x += dpp_take<kDppXor1>(x);
+    x += dpp_take<kDppXor2>(x);
+    x += dpp_take<kDppHalfMirror>(x);
+    if (G > 8) x += dpp_take<kDppMirror>(x);
+    for (int off = 16; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace zeta

@@ -87,7 +87,7 @@ FwdPlan plan_fwd(const zeta_shape* sh) {
 }
 
 struct BwdPlan {
-    size_t A, C, dg, dgp, r0, r1, hist, totals, offs, zq, pq, total;
+    size_t qs, dg, dgp, r0, r1, hist, totals, offs, zq, pq, total;
     int64_t P, tiles;
 };
 
@@ -102,12 +102,11 @@ BwdPlan plan_bwd(const zeta_shape* sh) {
         off += align_up(bytes);
         return at;
     };
-    p.A = take(sizeof(float) * BH * N * K);
-    p.C = take(sizeof(float) * BH * N * K);
+    p.qs = take(2 * sizeof(float) * BH * N);
     p.dg = take(sizeof(float) * BH * N);
     p.dgp = take(sizeof(float) * sh->H * zeta::dgamma_chunks(sh->B, N));
-    p.r0 = take(16 * BH * p.P);
-    p.r1 = take(16 * BH * p.P);
+    p.r0 = take(8 * BH * p.P);
+    p.r1 = take(8 * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
@@ -271,12 +270,11 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
     zeta::BwdBuffers b{};
-    b.A = at<float>(workspace, p.A);
-    b.C = at<float>(workspace, p.C);
+    b.qstat = at<float2>(workspace, p.qs);
     b.dg_row = at<float>(workspace, p.dg);
     b.dg_part = at<float>(workspace, p.dgp);
-    b.rec0 = at<uint4>(workspace, p.r0);
-    b.rec1 = at<uint4>(workspace, p.r1);
+    b.rec0 = at<uint2>(workspace, p.r0);
+    b.rec1 = at<uint2>(workspace, p.r1);
     b.hist = at<uint32_t>(workspace, p.hist);
     b.totals = at<uint32_t>(workspace, p.totals);
     b.offs = at<uint32_t>(workspace, p.offs);

@@ -60,12 +60,11 @@ hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* 
                         hipStream_t s);
 
 struct BwdBuffers {
-    float* A;         // [BHN][topk] normalised weights a_ij
-    float* C;         // [BHN][topk] pair coefficients c_ij
+    float2* qstat;    // [BHN] per-query {1/S_i, D_i}
     float* dg_row;    // [BHN] per-query dgamma contributions
     float* dg_part;   // [H][dgamma_chunks] partial sums
-    uint4* rec0;      // [BH][P] radix-sort ping-pong records {j, i, a, c}
-    uint4* rec1;
+    uint2* rec0;      // [BH][P] radix-sort ping-pong records {j, i}
+    uint2* rec1;
     uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
     uint32_t* totals; // [BH][256] digit totals
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list

@@ -308,6 +308,13 @@ def _bwd_sampled_check(w, n_rows=600, tail=256):
     assert np.abs(colsum - colsum_ref).max() <= tol, np.abs(colsum - colsum_ref).max()
 
 
+def test_backward_beyond_two_byte_keys():
+    # N > 65536: the selection transpose takes the all-bytes radix path
+    w = W("lsd", 1, 1, 70000, 8, 8, inputs.BF16, "normal", seed=17, backward=True)
+    log("backward N=70000 (three radix passes)")
+    _bwd_sampled_check(w, n_rows=300, tail=128)
+
+
 @pytest.mark.parametrize("name", ["clustered", "long_fwd_bwd"])
 def test_backward_sampled(name):
     w = CFG[name]
