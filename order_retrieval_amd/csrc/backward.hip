@@ -47,50 +47,83 @@ __device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64
 
 
 // ---------------------------------------------------------------------------- 1. queries
-// Slot r of a query belongs to lane r % G of its group (register r / G): the owner loads the
-// index and key row and computes s, the distance terms, and later a, c and the dq / dgamma
-// terms of its slots.  The value rows are taken in slot order with the index broadcast from
-// the owner, so a batch of row loads does not wait on memory; g = dO . v is reduced over the
-// group with a xor butterfly and kept by the slot's owner.
+// One 16-lane row (a DPP row) per query i, four queries per wavefront, taken in the Z-order
+// processing order.  Lane l owns slots l, 16 + l, ...: it loads their indices and key rows
+// and forms s, the distance terms and later a, c and the dq / dgamma terms.  The row keeps
+// its chunks of dO_i in registers and walks the slots in order: the index comes from the
+// owning lane by a DPP row broadcast, every lane loads its chunks of the v_j row (the loads
+// of kRowLoads slots are issued together) and a DPP butterfly over the row completes
+// g_ij = dO_i . v_j, which the owning lane keeps.
+constexpr int kRowLanes = 16;  // lanes per query or key
+constexpr int kRowLoads = 4;   // rows whose loads are issued together
+
+template <bool BF16, int CPL, int L0>
+__device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
+                                            int dv, const int (&coff)[CPL], int32_t jo,
+                                            const float (&go)[CPL][VecIO<BF16>::kElems],
+                                            int lrow, float& gmine) {
+    using IO = VecIO<BF16>;
+    using R = typename IO::raw_t;
+    constexpr int E = IO::kElems;
+    R raw[kRowLoads][CPL];
+    static_for<0, kRowLoads>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
+        const int64_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + j * dv + coff[c]);
+    });
+    static_for<0, kRowLoads>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
+        float part = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float x[E];
+            IO::unpack(raw[w][c], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
+        }
+        const float g = group_sum(part, kRowLanes);
+        if (lrow == L0 + w) gmine = g;
+    });
+}
+
 template <bool BF16, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd,
-    float2* __restrict__ qstat, float* __restrict__ dq, float* __restrict__ dg_row) {
+    int64_t H, int dv, int topk, int64_t tiles, int64_t per_xcd, float2* __restrict__ qstat,
+    float* __restrict__ dq, float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
-    if (tile >= tiles) return;
-    const int64_t gtid = tile * blockDim.x + threadIdx.x;
-    const int64_t t = gtid >> glog;  // position in the processing order
-    const int G = 1 << glog;
-    const int lane = static_cast<int>(gtid & (G - 1));
-    if (t >= rows) return;
+    if (tile >= tiles) return;  // uniform over the workgroup
+    const int lrow = threadIdx.x & (kRowLanes - 1);
+    const int64_t t = tile * (blockDim.x / kRowLanes) + threadIdx.x / kRowLanes;
+    const bool live = t < rows;
+    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real query, stores nothing
     const int chunks = dv / E;
-    const int64_t bh = t / N;
-    const int64_t i = order ? static_cast<int64_t>(order[t]) : t - bh * N;
+    const int64_t bh = tt / N;
+    const int64_t i = order ? static_cast<int64_t>(order[tt]) : tt - bh * N;
     const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
-    const int m = static_cast<int>(i + 1 < topk ? i + 1 : topk);
+    const int m = live ? static_cast<int>(i + 1 < topk ? i + 1 : topk) : 0;
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
     float go[CPL][E];
+    int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet go = 0)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + c * G;
-        if (ch < chunks) {
-            IO::load(static_cast<const T*>(dout) + row * dv + ch * E, go[c]);
-        } else {
+        const int ch = lrow + c * kRowLanes;
+        coff[c] = (ch < chunks ? ch : chunks - 1) * E;
 #pragma unroll
-            for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
-        }
+        for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
+        if (ch < chunks) IO::load(static_cast<const T*>(dout) + row * dv + ch * E, go[c]);
     }
 
     int32_t jo[U];
@@ -98,8 +131,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     float ssum = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lane + u * G;
-        jo[u] = 0;
+        const int r = lrow + u * kRowLanes;
+        jo[u] = 0;  // slots past m name key 0 (inside the buffers) and are never summed
         so[u] = dx[u] = dy[u] = dz[u] = gg[u] = 0.0f;
         if (r < m) {
             const int32_t j = static_cast<int32_t>(clamp_index(ir[r], i));
@@ -111,41 +144,34 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
             ssum += so[u];
         }
     }
-    const float S = group_sum(ssum, G);
+    const float S = group_sum(ssum, kRowLanes);
+    // the longest selection among the wavefront's four queries sets the trip count
+    int most = m;
+    most = max(most, __shfl_xor(most, 16, 64));
+    most = max(most, __shfl_xor(most, 32, 64));
 
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int n = m - u * G < G ? m - u * G : G;
-#pragma unroll 4
-        for (int sl = 0; sl < n; ++sl) {
-            const int64_t j = __shfl(jo[u], sl, G);
-            float part = 0.0f;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int ch = lane + c * G;
-                if (ch < chunks) {
-                    float x[E];
-                    IO::load(vh + j * dv + ch * E, x);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
-                }
-            }
-            const float gr = group_sum(part, G);
-            if (sl == lane) gg[u] = gr;
+    static_for<0, U>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u * kRowLanes < most) {
+            static_for<0, kRowLanes / kRowLoads>([&](auto bc) {
+                constexpr int b = decltype(bc)::value;
+                if (u * kRowLanes + b * kRowLoads < most)
+                    query_slots<BF16, CPL, b * kRowLoads>(vh, dv, coff, jo[u], go, lrow, gg[u]);
+            });
         }
-    }
+    });
 
     float tsum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) tsum += so[u] * gg[u];
+    for (int u = 0; u < U; ++u)
+        if (lrow + u * kRowLanes < m) tsum += so[u] * gg[u];
     const float inv_S = 1.0f / S;
-    const float D = group_sum(tsum, G) * inv_S;
+    const float D = group_sum(tsum, kRowLanes) * inv_S;
 
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lane + u * G;
-        if (r < m) {
+        if (lrow + u * kRowLanes < m) {
             const float a = so[u] * inv_S;
             const float c = a * so[u] * (gg[u] - D);
             a0 += c * dx[u];
@@ -154,11 +180,11 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
             ag += c * (dx[u] * dx[u] + dy[u] * dy[u] + dz[u] * dz[u]);
         }
     }
-    a0 = group_sum(a0, G);
-    a1 = group_sum(a1, G);
-    a2 = group_sum(a2, G);
-    ag = group_sum(ag, G);
-    if (lane == 0) {
+    a0 = group_sum(a0, kRowLanes);
+    a1 = group_sum(a1, kRowLanes);
+    a2 = group_sum(a2, kRowLanes);
+    ag = group_sum(ag, kRowLanes);
+    if (live && lrow == 0) {
         const float f = -2.0f * inv_g2;
         dq[3 * row] = f * a0;
         dq[3 * row + 1] = f * a1;
@@ -166,6 +192,37 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         dg_row[row] = 2.0f * inv_g2 / g * ag;
         qstat[row] = make_float2(inv_S, D);
     }
+}
+
+template <bool BF16, int CPL>
+static hipError_t launch_query_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
+                                 const float* q, const float* k, const void* v, const float* gamma,
+                                 const int32_t* idx, const void* dout, const uint32_t* order,
+                                 float2* qstat, float* dq, float* dg_row, hipStream_t s) {
+    const int64_t tiles = (rows + (256 / kRowLanes) - 1) / (256 / kRowLanes);
+    const int64_t per = xcd_per(tiles);
+    const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane (<= 4)
+    auto kern = u <= 1 ? zeta_bwd_query_kernel<BF16, CPL, 1>
+              : u <= 2 ? zeta_bwd_query_kernel<BF16, CPL, 2>
+                       : zeta_bwd_query_kernel<BF16, CPL, 4>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
+                       gamma, idx, dout, order, rows, N, H, dv, topk, tiles, per, qstat, dq, dg_row);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_query(int64_t rows, int64_t N, int64_t H, int dv, int topk,
+                               const float* q, const float* k, const void* v, const float* gamma,
+                               const int32_t* idx, const void* dout, const uint32_t* order,
+                               float2* qstat, float* dq, float* dg_row, hipStream_t s) {
+    const int cpl = (dv / VecIO<BF16>::kElems + kRowLanes - 1) / kRowLanes;
+    if (cpl <= 1)
+        return launch_query_c<BF16, 1>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+    if (cpl <= 2)
+        return launch_query_c<BF16, 2>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+    if (BF16 || cpl <= 4)  // bf16 rows have <= 64 chunks
+        return launch_query_c<BF16, 4>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+    return launch_query_c<BF16, BF16 ? 4 : 8>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
 }
 
 // ---------------------------------------------------------------------------- 2. transpose
@@ -344,10 +401,10 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* 
 // of g_ij = dO_i . v_j, and a DPP butterfly over the row completes g_ij, which the owning lane
 // keeps for c_ij and the dk term.  No LDS traffic; the trip counts are uniform over the
 // wavefront (the longest of its four keys) and a key's sums run in a fixed order.
-constexpr int kKeyRow = 16;               // lanes per key
+constexpr int kKeyRow = kRowLanes;        // lanes per key
 constexpr int kKeyRecs = 2;               // records per lane per batch
 constexpr int kKeyBatch = kKeyRow * kKeyRecs;
-constexpr int kKeyLoads = 4;              // records whose dO loads are issued together
+constexpr int kKeyLoads = kRowLoads;      // records whose dO loads are issued together
 
 template <bool BF16, int CPL, int U0>
 __device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* __restrict__ doh,
@@ -564,8 +621,8 @@ static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t
                        items, stride, shift, tiles, topk, ws.hist, ws.totals, ws.P, rout);
 }
 
-template <bool BF16, int CPL>
-static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk, int glog,
+template <bool BF16>
+static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk,
                                const float* q, const float* k, const void* v, const float* gamma,
                                const int32_t* idx, const void* dout, float* dq, float* dk,
                                void* dvout, float* dgamma, const BwdBuffers& ws,
@@ -576,17 +633,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     if (e == hipSuccess) e = launch_order(BH, N, ws.zq, ws.perm_q, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
-    const int64_t gtiles = ((rows << glog) + 255) / 256;
-    const int64_t gper = xcd_per(gtiles);
-    const int u = (topk + (1 << glog) - 1) >> glog;  // slots per lane (<= 8)
-    auto qk = u <= 1 ? zeta_bwd_query_kernel<BF16, CPL, 1>
-            : u <= 2 ? zeta_bwd_query_kernel<BF16, CPL, 2>
-            : u <= 4 ? zeta_bwd_query_kernel<BF16, CPL, 4>
-                     : zeta_bwd_query_kernel<BF16, CPL, 8>;
-    hipLaunchKernelGGL(qk, dim3(static_cast<unsigned>(gper * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, dout, ws.perm_q, rows, N, H, dv, topk, glog, gtiles, gper,
-                       ws.qstat, dq, ws.dg_row);
-    e = hipGetLastError();
+    e = launch_query<BF16>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, ws.perm_q, ws.qstat,
+                           dq, ws.dg_row, s);
     if (e != hipSuccess) return e;
     marks.record(2, s);
 
@@ -625,14 +673,9 @@ hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bo
                       float* dgamma, const BwdBuffers& ws, const StageEvents& marks,
                       hipStream_t s) {
     if (BH * N <= 0) return hipSuccess;
-    const int chunks = static_cast<int>(dv / (bf16 ? 8 : 4));
-    const int glog = group_log2(chunks);
-    const int cpl = (chunks + (1 << glog) - 1) >> glog;
     if (bf16)
-        return cpl == 1 ? launch_bwd_t<true, 1>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s)
-                        : launch_bwd_t<true, 2>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
-    return cpl == 1 ? launch_bwd_t<false, 1>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s)
-                    : launch_bwd_t<false, 2>(BH, H, N, (int)dv, topk, glog, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+        return launch_bwd_t<true>(BH, H, N, (int)dv, topk, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+    return launch_bwd_t<false>(BH, H, N, (int)dv, topk, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
 }
 
 }  // namespace zeta

@@ -10,53 +10,86 @@
 // HBM-bound gather: per query k value rows of dv elements (k * dv * |v| bytes) dominate.
 // Queries are taken in Z-order buckets (order.hip) with an XCD-aware tile mapping, so the
 // rows that concurrent queries select overlap and are served from L2.
-// A group of G lanes (a power of two, G * 16 B >= one row) owns one query; each lane keeps
-// fp32 accumulators for its 16-byte chunk(s) of the row, so every selected row is read with
-// one coalesced 16 B-per-lane load.  The output is rounded once to the value dtype.
+// Each lane keeps fp32 accumulators for its 16-byte chunk(s) of the row, so every selected
+// row is read with coalesced 16 B-per-lane loads.  The output is rounded once to the value
+// dtype.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
 #include "xlane.hpp"
 
 namespace zeta {
 
-// Slot r of a query belongs to lane r % G of its group (register r / G): the owner loads
-// the index and the key row and computes the weight, so the group's index and key loads
-// are all in flight at once.  The value rows are then taken in slot order, the index and
-// weight of each slot broadcast from its owner with a cross-lane shuffle, so a batch of
-// row loads does not wait on any memory load.
+// One 16-lane row (a DPP row) per query, four queries per wavefront.  Lane l owns slots l,
+// 16 + l, ...: it loads their indices and key rows and computes the weights, so all of the
+// row's index and key loads are in flight at once.  The row then walks the slots in order:
+// index and weight come from the owning lane by a DPP row broadcast, every lane loads its
+// 16-byte chunk(s) of the value row (the loads of kGatherLoads slots are issued together,
+// none waits on another load) and accumulates in fp32.
+constexpr int kGatherLanes = 16;
+constexpr int kGatherLoads = 4;
+
+template <bool BF16, int CPL, int L0>
+__device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
+                                             int dv, const int (&coff)[CPL], int32_t jo, float so,
+                                             int left, float (&acc)[CPL][VecIO<BF16>::kElems]) {
+    using IO = VecIO<BF16>;
+    using R = typename IO::raw_t;
+    constexpr int E = IO::kElems;
+    R raw[kGatherLoads][CPL];
+    static_for<0, kGatherLoads>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
+        const int64_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + j * dv + coff[c]);
+    });
+    static_for<0, kGatherLoads>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
+        const float s = row_bcast<L0 + w>(so);
+        if (L0 + w < left) {  // slots past the selection read key 0's row and add nothing
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                float x[E];
+                IO::unpack(raw[w][c], x);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[c][e] += s * x[e];
+            }
+        }
+    });
+}
+
 template <bool BF16, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ order, void* __restrict__ out, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int glog, int64_t tiles, int64_t per_xcd) {
+    int64_t H, int dv, int topk, int64_t tiles, int64_t per_xcd) {
     using IO = VecIO<BF16>;
+    using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
-    if (tile >= tiles) return;
-    const int64_t gtid = tile * blockDim.x + threadIdx.x;
-    const int64_t t = gtid >> glog;  // position in the processing order
-    const int lane = static_cast<int>(gtid & ((1 << glog) - 1));
-    if (t >= rows) return;
-    const int G = 1 << glog;
+    if (tile >= tiles) return;  // uniform over the workgroup
+    const int lrow = threadIdx.x & (kGatherLanes - 1);
+    const int64_t t = tile * (blockDim.x / kGatherLanes) + threadIdx.x / kGatherLanes;
+    const bool live = t < rows;
+    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real query, stores nothing
     const int chunks = dv / E;
-    const int64_t bh = t / N;
-    const int64_t i = order ? static_cast<int64_t>(order[t]) : t - bh * N;
+    const int64_t bh = tt / N;
+    const int64_t i = order ? static_cast<int64_t>(order[tt]) : tt - bh * N;
     const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
-    const int m = static_cast<int>(i + 1 < topk ? i + 1 : topk);  // valid slots
+    const int m = live ? static_cast<int>(i + 1 < topk ? i + 1 : topk) : 0;  // valid slots
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
-    const typename IO::elem_t* vh = static_cast<const typename IO::elem_t*>(v) + bh * N * dv;
+    const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
     int32_t jo[U];
     float so[U];
     float ssum = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lane + u * G;
+        const int r = lrow + u * kGatherLanes;
         jo[u] = 0;
         so[u] = 0.0f;
         if (r < m) {
@@ -69,71 +102,63 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
             ssum += so[u];
         }
     }
-    ssum = group_sum(ssum, G);
+    ssum = group_sum(ssum, kGatherLanes);
+    // the longest selection among the wavefront's four queries sets the trip count
+    int most = m;
+    most = max(most, __shfl_xor(most, 16, 64));
+    most = max(most, __shfl_xor(most, 32, 64));
 
     float acc[CPL][E];
+    int coff[CPL];  // element offset of the lane's chunks (clamped; never stored past the row)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lrow + c * kGatherLanes;
+        coff[c] = (ch < chunks ? ch : chunks - 1) * E;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
+    }
+    static_for<0, U>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if (u * kGatherLanes < most) {
+            static_for<0, kGatherLanes / kGatherLoads>([&](auto bc) {
+                constexpr int b = decltype(bc)::value;
+                if (u * kGatherLanes + b * kGatherLoads < most)
+                    gather_slots<BF16, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u],
+                                                             m - u * kGatherLanes, acc);
+            });
+        }
+    });
+
+    if (live) {
+        const float inv_S = 1.0f / ssum;
+        T* orow = static_cast<T*>(out) + row * dv;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int n = m - u * G < G ? m - u * G : G;  // slots owned at register u
-#pragma unroll 8
-        for (int sl = 0; sl < n; ++sl) {
-            const int64_t j = __shfl(jo[u], sl, G);
-            const float s = __shfl(so[u], sl, G);
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = lrow + c * kGatherLanes;
+            if (ch < chunks) {
+                float x[E];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int ch = lane + c * G;
-                if (ch < chunks) {
-                    float x[E];
-                    IO::load(vh + j * dv + ch * E, x);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[c][e] += s * x[e];
-                }
+                for (int e = 0; e < E; ++e) x[e] = acc[c][e] * inv_S;
+                IO::store(orow + ch * E, x);
             }
         }
     }
-
-    const float inv_S = 1.0f / ssum;
-    typename IO::elem_t* orow = static_cast<typename IO::elem_t*>(out) + row * dv;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + c * G;
-        if (ch < chunks) {
-            float x[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = acc[c][e] * inv_S;
-            IO::store(orow + ch * E, x);
-        }
-    }
-}
-
-template <bool BF16, int CPL, int U>
-static hipError_t launch_gather_t(int64_t rows, int64_t N, int64_t H, int dv, int topk, int glog,
-                                  const float* q, const float* k, const void* v,
-                                  const float* gamma, const int32_t* idx, const uint32_t* order,
-                                  void* out, hipStream_t s) {
-    const int64_t threads = rows << glog;
-    const int64_t tiles = (threads + 255) / 256;
-    const int64_t per = xcd_per(tiles);
-    hipLaunchKernelGGL((zeta_cauchy_gather_kernel<BF16, CPL, U>),
-                       dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v, gamma, idx,
-                       order, out, rows, N, H, dv, topk, glog, tiles, per);
-    return hipGetLastError();
 }
 
 template <bool BF16, int CPL>
-static hipError_t launch_gather_u(int64_t rows, int64_t N, int64_t H, int dv, int topk, int glog,
+static hipError_t launch_gather_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
                                   const float* q, const float* k, const void* v,
                                   const float* gamma, const int32_t* idx, const uint32_t* order,
                                   void* out, hipStream_t s) {
-    const int u = (topk + (1 << glog) - 1) >> glog;  // slots per lane (<= 8: G >= 8, k <= 64)
-    if (u <= 1) return launch_gather_t<BF16, CPL, 1>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
-    if (u <= 2) return launch_gather_t<BF16, CPL, 2>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
-    if (u <= 4) return launch_gather_t<BF16, CPL, 4>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
-    return launch_gather_t<BF16, CPL, 8>(rows, N, H, dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    const int64_t tiles = (rows + (256 / kGatherLanes) - 1) / (256 / kGatherLanes);
+    const int64_t per = xcd_per(tiles);
+    const int u = (topk + kGatherLanes - 1) / kGatherLanes;  // slots per lane (<= 4)
+    auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, CPL, 1>
+              : u <= 2 ? zeta_cauchy_gather_kernel<BF16, CPL, 2>
+                       : zeta_cauchy_gather_kernel<BF16, CPL, 4>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
+                       gamma, idx, order, out, rows, N, H, dv, topk, tiles, per);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
@@ -141,14 +166,16 @@ hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk,
                          const int32_t* idx, const uint32_t* order, void* out, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
-    const int chunks = static_cast<int>(dv / (bf16 ? 8 : 4));
-    const int glog = group_log2(chunks);
-    const int cpl = (chunks + (1 << glog) - 1) >> glog;
-    if (bf16)
-        return cpl == 1 ? launch_gather_u<true, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s)
-                        : launch_gather_u<true, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s);
-    return cpl == 1 ? launch_gather_u<false, 1>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s)
-                    : launch_gather_u<false, 2>(rows, N, H, (int)dv, topk, glog, q, k, v, gamma, idx, order, out, s);
+    const int cpl = static_cast<int>((dv / (bf16 ? 8 : 4) + kGatherLanes - 1) / kGatherLanes);
+    if (bf16) {  // bf16 rows have <= 64 chunks
+        if (cpl <= 1) return launch_gather_c<true, 1>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+        if (cpl <= 2) return launch_gather_c<true, 2>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+        return launch_gather_c<true, 4>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+    }
+    if (cpl <= 1) return launch_gather_c<false, 1>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 2) return launch_gather_c<false, 2>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 4) return launch_gather_c<false, 4>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+    return launch_gather_c<false, 8>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
 }
 
 }  // namespace zeta

@@ -59,12 +59,4 @@ struct VecIO<false> {
     }
 };
 
-// log2 of the lanes that share one value row: the next power of two >= the row's 16-byte
-// chunks, at least 8 and at most 64 (one wavefront).
-inline int group_log2(int chunks) {
-    int g = 3;
-    while ((1 << g) < chunks && g < 6) ++g;
-    return g;
-}
-
 }  // namespace zeta
