@@ -14,7 +14,9 @@ oracle timed on a bounded random sample of query rows and scaled to the full ste
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
 import hashlib
 import json
 import os
@@ -143,6 +145,116 @@ def stored_traffic(stage: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- reports
+def kernel_base(name: str) -> str:
+    """zeta::zeta_select_kernel<32, 2>(...) -> zeta_select_kernel."""
+    base = name.split("(")[0].split("<")[0]
+    return base.replace("void ", "").split("::")[-1].strip()
+
+
+def counter_means(path: str, counter: str) -> dict:
+    """Mean counter value per dispatch of each kernel in a rocprofv3 --pmc csv output dir."""
+    files = glob.glob(os.path.join(path, "*counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    vals: dict = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(kernel_base(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+COUNTER_CMDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- "
+    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- "
+    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o copy_fetch -- "
+    "python3 bench.py --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o copy_write -- "
+    "python3 bench.py --copy-calibration",
+]
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+
+
+def counters_summary(d: str, workload: str) -> None:
+    """HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE passes, each scaled
+    by what the same counter reads for a plain 1 GiB device copy; writes
+    profiles/<stage>_<workload>_counters.json (keyed to the kernel source's sha256) and a
+    markdown table of every kernel."""
+    copy_bytes = float(1 << 30)
+    cf = counter_means(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
+    cw = counter_means(os.path.join(d, "copy_write"), "WRITE_SIZE")
+    copy_name = next(k for k in cf if "copyBuffer" in k or "copy" in k.lower())
+    fscale = copy_bytes / (cf[copy_name] * 1024.0)
+    wscale = copy_bytes / (cw[copy_name] * 1024.0)
+    fetch = counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    cmds = [c.format(d=d) for c in COUNTER_CMDS]
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    lines = [f"# HBM traffic per launch, {workload} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands (each pass its own run, from the repository root):", ""]
+    lines += [f"    {c}" for c in cmds] + [f"    python3 bench.py --counters-summary {d}", ""]
+    lines += [f"Copy calibration: a 1 GiB device copy reads {cf[copy_name]:.0f} KiB (FETCH_SIZE) and "
+              f"writes {cw[copy_name]:.0f} KiB (WRITE_SIZE): scale {fscale:.3f} and {wscale:.3f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch (scaled) |",
+              "|---|---|---|---|"]
+    for kname in sorted(fetch, key=lambda n: -fetch[n]):
+        if not kname.startswith("zeta_"):
+            continue
+        hb = fetch[kname] * 1024 * fscale + write.get(kname, 0.0) * 1024 * wscale
+        lines.append(f"| {kname} | {fetch[kname]:.0f} | {write.get(kname, 0.0):.0f} | {hb / 1e6:.1f} |")
+    for stage, kname in SINGLE_KERNEL.items():
+        if kname not in fetch:
+            continue
+        src = os.path.join(ROOT, "order_retrieval_amd", "csrc", KERNEL_SOURCE[stage])
+        rec = {"kernel": kname, "workload": workload,
+               "fetch_kib": fetch[kname], "write_kib": write.get(kname, 0.0),
+               "fetch_scale": fscale, "write_scale": wscale,
+               "hbm_bytes_per_launch": int(fetch[kname] * 1024 * fscale +
+                                           write.get(kname, 0.0) * 1024 * wscale),
+               "source": KERNEL_SOURCE[stage],
+               "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+               "commands": cmds}
+        with open(os.path.join(prof, f"{stage}_{workload}_counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    with open(os.path.join(prof, f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def trace_summary(d: str, workload: str) -> None:
+    """Per-kernel durations from a rocprofv3 --kernel-trace --stats run, next to the bench line
+    the same run printed (its stage_ms come from HIP events on the launch stream)."""
+    stats = glob.glob(os.path.join(d, "*kernel_stats.csv"))
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(stats[0])))
+    bench_line = None
+    log = os.path.join(d, "run.log")
+    if os.path.exists(log):
+        for ln in open(log):
+            if ln.startswith("{"):
+                bench_line = json.loads(ln)
+    lines = [f"# Kernel durations, {workload} (rocprofv3 --kernel-trace --stats)", "",
+             "Command (from the repository root; stdout to run.log in the same folder):", "",
+             f"    {TRACE_CMD.format(d=d)}", f"    python3 bench.py --trace-summary {d}", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    if bench_line is not None:
+        lines += ["", "Stage times the same run measured with HIP events (ms per launch):", "",
+                  "    " + json.dumps(bench_line["stage_ms"]),
+                  "", f"fwd+bwd step: {bench_line['value']} ms; roofline: "
+                  + json.dumps(bench_line["roofline"])]
+    with open(os.path.join(ROOT, "profiles", f"kernels_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(w: inputs.Workload, x: dict, target_s: float, seed: int = 0) -> dict:
     import oracle
@@ -184,7 +296,17 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (counter calibration)")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="write profiles/*_counters.json from rocprofv3 --pmc outputs under DIR")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write profiles/kernels_<workload>.md from a rocprofv3 kernel-trace run")
     args = ap.parse_args()
+    if args.counters_summary:
+        counters_summary(args.counters_summary, args.workload)
+        return 0
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.workload)
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the (b,h) slices "

@@ -13,7 +13,7 @@
 //   2. selection transpose: stable LSD radix sort (8-bit digits) of the pairs of every (b,h)
 //      by j, carrying 8-byte records {j, i}; queries stay ascending inside a key's segment;
 //   3. segment starts offs[j] from the sorted keys;
-//   4. per-key pass: each key recomputes s_ij, g_ij = dO_i . v_j (it reads the dO_i rows for
+//   4. per-key pass (keys in Z-order): each key recomputes s_ij, g_ij = dO_i . v_j (it reads the dO_i rows for
 //      dv_j anyway), a_ij and c_ij from the query's 1/S_i and D_i, and reduces its segment
 //      in a fixed order (dv, dk);
 //   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
@@ -392,7 +392,9 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* 
 }
 
 // ---------------------------------------------------------------------------- 4. keys
-// One 16-lane row (a DPP row) per key j, four keys per wavefront.  A key's pairs are a
+// One 16-lane row (a DPP row) per key j, four keys per wavefront, keys taken in their Z-order
+// processing order: the queries that selected a key are near it on the curve, so keys that
+// run together read overlapping dO rows and L2 serves the repeats.  A key's pairs are a
 // contiguous run of records, taken kKeyBatch at a time: lane l of the row owns records l and
 // 16 + l of the batch, loads their q_i and the query's {1/S_i, D_i} and forms s_ij, a_ij and
 // a_ij s_ij.  The row then walks the batch's records in order: i and a_ij come from the owning
@@ -446,8 +448,9 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const void* __restrict__ dout,
     const float2* __restrict__ qstat, const uint2* __restrict__ recs,
-    const uint32_t* __restrict__ offs, int64_t rows, int64_t N, int64_t H, int dv, int64_t P,
-    int64_t tiles, int64_t per_xcd, float* __restrict__ dk, void* __restrict__ dvout) {
+    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ order, int64_t rows,
+    int64_t N, int64_t H, int dv, int64_t P, int64_t tiles, int64_t per_xcd,
+    float* __restrict__ dk, void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -455,9 +458,10 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     if (tile >= tiles) return;  // uniform over the workgroup
     const int lane64 = threadIdx.x & 63;
     const int lrow = lane64 & (kKeyRow - 1);
-    const int64_t key = tile * (blockDim.x / kKeyRow) + threadIdx.x / kKeyRow;
-    const bool live = key < rows;
-    const int64_t row = live ? key : rows - 1;  // a row past the end reads a real key, stores nothing
+    const int64_t t = tile * (blockDim.x / kKeyRow) + threadIdx.x / kKeyRow;  // processing order
+    const bool live = t < rows;
+    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real key, stores nothing
+    const int64_t row = order ? (tt / N) * N + order[tt] : tt;
     const int chunks = dv / E;
     const int64_t bh = row / N;
     const int64_t j = row - bh * N;
@@ -539,8 +543,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
 template <bool BF16>
 static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, const float* q,
                              const float* k, const void* v, const float* gamma, const void* dout,
-                             const BwdBuffers& ws, const uint2* recs, float* dk, void* dvout,
-                             hipStream_t s) {
+                             const BwdBuffers& ws, const uint2* recs, const uint32_t* order,
+                             float* dk, void* dvout, hipStream_t s) {
     const int64_t rows = BH * N;
     const int chunks = dv / VecIO<BF16>::kElems;
     const int cpl = (chunks + kKeyRow - 1) / kKeyRow;
@@ -551,8 +555,8 @@ static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, const flo
               : cpl <= 4 ? zeta_bwd_key_kernel<BF16, 4>
                          : zeta_bwd_key_kernel<BF16, BF16 ? 4 : 8>;  // bf16 rows have <= 64 chunks
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, dout, ws.qstat, recs, ws.offs, rows, N, H, dv, ws.P, tiles, per, dk,
-                       dvout);
+                       gamma, dout, ws.qstat, recs, ws.offs, order, rows, N, H, dv, ws.P, tiles,
+                       per, dk, dvout);
     return hipGetLastError();
 }
 
@@ -630,7 +634,9 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     const int64_t rows = BH * N;
     marks.record(0, s);
     hipError_t e = launch_encode(q, rows, ws.zq, s);
-    if (e == hipSuccess) e = launch_order(BH, N, ws.zq, ws.perm_q, s);
+    if (e == hipSuccess) e = launch_order(BH, N, ws.zq, ws.perm_q, ws.ohist, s);
+    if (e == hipSuccess) e = launch_encode(k, rows, ws.zk, s);
+    if (e == hipSuccess) e = launch_order(BH, N, ws.zk, ws.perm_k, ws.ohist, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
     e = launch_query<BF16>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, ws.perm_q, ws.qstat,
@@ -654,7 +660,7 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
                        dim3(256), 0, s, cur, ws.P, N, ws.offs);
     marks.record(3, s);
-    e = launch_key<BF16>(BH, H, N, dv, q, k, v, gamma, dout, ws, cur, dk, dvout, s);
+    e = launch_key<BF16>(BH, H, N, dv, q, k, v, gamma, dout, ws, cur, ws.perm_k, dk, dvout, s);
     if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);

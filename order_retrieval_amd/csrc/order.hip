@@ -1,15 +1,16 @@
 // order.hip -- Z-order processing order for the row-gathering kernels.
 //
-// Queries whose codes are close select largely the same keys (their neighbourhoods on the
-// Z-order line overlap), so processing queries bucketed by the high bits of their code
-// makes the value rows that concurrent workgroups read overlap, and an XCD's L2 can serve
-// them.  (Keys in the per-key backward pass stay in position order: their records are then
-// read as one stream, which measured faster than a code order.)
+// Queries (or keys) whose codes are close select largely the same rows (their neighbourhoods
+// on the Z-order line overlap), so processing them bucketed by the high bits of their code
+// makes the rows that concurrent workgroups read overlap, and an XCD's L2 can serve them.
+// Buckets are fine (12 bits) because normally distributed points crowd the centre cells.
 //
 // The order only schedules work: every query or key is still computed exactly once and
 // independently, so results do not depend on it.  It is a counting sort by the top
-// kOrderBits code bits per (b,h) (order inside a bucket is arbitrary), built with LDS
-// integer atomics only.
+// kOrderBits code bits per (b,h) over tiles of kOrderTile positions: per-tile bucket counts
+// (tile-major), one scan per (b,h) in (bucket, tile) order, and a scatter that places a
+// tile's positions after the earlier tiles' positions of the same bucket (order inside a
+// tile's bucket comes from LDS atomics and is arbitrary).
 #include "zeta_internal.hpp"
 
 namespace zeta {
@@ -17,78 +18,130 @@ namespace zeta {
 constexpr int kOrderBits = 12;
 constexpr int kOrderBuckets = 1 << kOrderBits;
 constexpr int kOrderShift = 30 - kOrderBits;  // codes are < 2^30
-
-// One workgroup per (b,h): bucket counts, their exclusive scan and the scatter all run in
-// LDS (LDS atomics are cheap even on the crowded buckets near the centre of the code range).
 constexpr int kOrderThreads = 1024;
-__global__ void __launch_bounds__(kOrderThreads) zeta_order_kernel(const uint32_t* __restrict__ codes,
-                                                                    int64_t N,
-                                                                    uint32_t* __restrict__ perm) {
+constexpr int kOrderPer = kOrderBuckets / kOrderThreads;  // buckets per thread (4: one uint4)
+constexpr int kOrderItems = 4;
+constexpr int kOrderTile = kOrderThreads * kOrderItems;
+static_assert(kOrderPer == 4, "counts move as uint4");
+
+int64_t order_tiles(int64_t N) { return (N + kOrderTile - 1) / kOrderTile; }
+size_t order_scratch_words(int64_t BH, int64_t N) {
+    return static_cast<size_t>(BH * kOrderBuckets * order_tiles(N));
+}
+
+__device__ __forceinline__ uint32_t order_bucket(uint32_t code) {
+    return (code >> kOrderShift) & (kOrderBuckets - 1);
+}
+
+// Bucket counts of one tile: hist[bh][tile][bucket].
+__global__ void __launch_bounds__(kOrderThreads) zeta_order_hist_kernel(
+    const uint32_t* __restrict__ codes, int64_t N, int64_t tiles, uint4* __restrict__ hist) {
     __shared__ uint32_t cnt[kOrderBuckets];
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kOrderPer; ++u) cnt[tid * kOrderPer + u] = 0;
+    __syncthreads();
+    const uint32_t* c = codes + bh * N;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kOrderTile;
+    uint32_t bk[kOrderItems];
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it) {
+        const int64_t e = t0 + it * kOrderThreads + tid;
+        bk[it] = e < N ? order_bucket(c[e]) : kOrderBuckets;
+    }
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it)
+        if (bk[it] < kOrderBuckets) atomicAdd(&cnt[bk[it]], 1u);
+    __syncthreads();
+    hist[(bh * tiles + blockIdx.x) * kOrderThreads + tid] =
+        make_uint4(cnt[tid * 4], cnt[tid * 4 + 1], cnt[tid * 4 + 2], cnt[tid * 4 + 3]);
+}
+
+// Per (b,h): exclusive scan in (bucket, tile) order, in place.  Thread t owns buckets
+// 4t .. 4t+3; the tiles' counts of those buckets are one coalesced uint4 per tile.
+__global__ void __launch_bounds__(kOrderThreads) zeta_order_scan_kernel(uint4* __restrict__ hist,
+                                                                         int64_t tiles) {
     __shared__ uint32_t part[kOrderThreads];
-    constexpr int per = kOrderBuckets / kOrderThreads;
-    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    uint4* h = hist + static_cast<int64_t>(blockIdx.x) * tiles * kOrderThreads + tid;
+    uint32_t tot[kOrderPer] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int64_t t = 0; t < tiles; ++t) {
+        const uint4 x = h[t * kOrderThreads];
+        tot[0] += x.x;
+        tot[1] += x.y;
+        tot[2] += x.z;
+        tot[3] += x.w;
+    }
+    const uint32_t mine = tot[0] + tot[1] + tot[2] + tot[3];
+    part[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kOrderThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+        const uint32_t y = tid >= off ? part[tid - off] : 0u;
+        __syncthreads();
+        part[tid] += y;
+        __syncthreads();
+    }
+    uint32_t run[kOrderPer];
+    run[0] = part[tid] - mine;
+    run[1] = run[0] + tot[0];
+    run[2] = run[1] + tot[1];
+    run[3] = run[2] + tot[2];
+#pragma unroll 4
+    for (int64_t t = 0; t < tiles; ++t) {
+        const uint4 x = h[t * kOrderThreads];
+        h[t * kOrderThreads] = make_uint4(run[0], run[1], run[2], run[3]);
+        run[0] += x.x;
+        run[1] += x.y;
+        run[2] += x.z;
+        run[3] += x.w;
+    }
+}
+
+// Places every position of a tile at its bucket's next free slot.
+__global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
+    const uint32_t* __restrict__ codes, int64_t N, int64_t tiles, const uint4* __restrict__ hist,
+    uint32_t* __restrict__ perm) {
+    __shared__ uint32_t base[kOrderBuckets];
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const uint4 b4 = hist[(bh * tiles + blockIdx.x) * kOrderThreads + tid];
+    base[tid * 4] = b4.x;
+    base[tid * 4 + 1] = b4.y;
+    base[tid * 4 + 2] = b4.z;
+    base[tid * 4 + 3] = b4.w;
+    __syncthreads();
     const uint32_t* c = codes + bh * N;
     uint32_t* out = perm + bh * N;
-    constexpr int B8 = 8;  // codes loaded per thread before their atomics (loads in flight)
-    for (int b = threadIdx.x; b < kOrderBuckets; b += kOrderThreads) cnt[b] = 0;
-    __syncthreads();
-    for (int64_t e0 = threadIdx.x; e0 < N; e0 += B8 * kOrderThreads) {
-        uint32_t bk[B8];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kOrderTile;
+    uint32_t bk[kOrderItems];
 #pragma unroll
-        for (int u = 0; u < B8; ++u) {
-            const int64_t e = e0 + u * kOrderThreads;
-            bk[u] = e < N ? (c[e] >> kOrderShift) & (kOrderBuckets - 1) : kOrderBuckets;
-        }
-#pragma unroll
-        for (int u = 0; u < B8; ++u)
-            if (bk[u] < kOrderBuckets) atomicAdd(&cnt[bk[u]], 1u);
+    for (int it = 0; it < kOrderItems; ++it) {
+        const int64_t e = t0 + it * kOrderThreads + tid;
+        bk[it] = e < N ? order_bucket(c[e]) : kOrderBuckets;
     }
-    __syncthreads();
-    uint32_t v[per];
-    uint32_t sum = 0;
 #pragma unroll
-    for (int u = 0; u < per; ++u) {
-        v[u] = cnt[threadIdx.x * per + u];
-        sum += v[u];
-    }
-    part[threadIdx.x] = sum;
-    __syncthreads();
-    for (int off = 1; off < kOrderThreads; off <<= 1) {
-        const uint32_t y = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
-        __syncthreads();
-        part[threadIdx.x] += y;
-        __syncthreads();
-    }
-    uint32_t run = part[threadIdx.x] - sum;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-        cnt[threadIdx.x * per + u] = run;
-        run += v[u];
-    }
-    __syncthreads();
-    for (int64_t e0 = threadIdx.x; e0 < N; e0 += B8 * kOrderThreads) {
-        uint32_t bk[B8];
-#pragma unroll
-        for (int u = 0; u < B8; ++u) {
-            const int64_t e = e0 + u * kOrderThreads;
-            bk[u] = e < N ? (c[e] >> kOrderShift) & (kOrderBuckets - 1) : kOrderBuckets;
-        }
-#pragma unroll
-        for (int u = 0; u < B8; ++u) {
-            if (bk[u] < kOrderBuckets) {
-                const uint32_t pos = atomicAdd(&cnt[bk[u]], 1u);
-                out[pos] = static_cast<uint32_t>(e0 + u * kOrderThreads);
-            }
+    for (int it = 0; it < kOrderItems; ++it) {
+        if (bk[it] < kOrderBuckets) {
+            const uint32_t pos = atomicAdd(&base[bk[it]], 1u);
+            out[pos] = static_cast<uint32_t>(t0 + it * kOrderThreads + tid);
         }
     }
 }
 
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
-                        hipStream_t s) {
+                        uint32_t* scratch, hipStream_t s) {
     if (BH <= 0 || N <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zeta_order_kernel, dim3(static_cast<unsigned>(BH)), dim3(kOrderThreads), 0, s,
-                       codes, N, perm);
+    const int64_t tiles = order_tiles(N);
+    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
+    uint4* hist = reinterpret_cast<uint4*>(scratch);  // the workspace carve is 256-byte aligned
+    hipLaunchKernelGGL(zeta_order_hist_kernel, grid, dim3(kOrderThreads), 0, s, codes, N, tiles,
+                       hist);
+    hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(BH)), dim3(kOrderThreads),
+                       0, s, hist, tiles);
+    hipLaunchKernelGGL(zeta_order_scatter_kernel, grid, dim3(kOrderThreads), 0, s, codes, N, tiles,
+                       hist, perm);
     return hipGetLastError();
 }
 

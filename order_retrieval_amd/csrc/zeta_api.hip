@@ -64,7 +64,7 @@ zeta_status preflight() {
 }
 
 struct FwdPlan {
-    size_t zq, zk, tasc, tdesc, perm, total;
+    size_t zq, zk, tasc, tdesc, perm, ohist, total;
 };
 
 FwdPlan plan_fwd(const zeta_shape* sh) {
@@ -82,12 +82,14 @@ FwdPlan plan_fwd(const zeta_shape* sh) {
     off += align_up(sizeof(uint64_t) * BHN * L);
     p.perm = off;
     off += align_up(sizeof(uint32_t) * BHN);
+    p.ohist = off;
+    off += align_up(sizeof(uint32_t) * zeta::order_scratch_words(sh->B * sh->H, sh->N));
     p.total = off;
     return p;
 }
 
 struct BwdPlan {
-    size_t qs, dg, dgp, r0, r1, hist, totals, offs, zq, pq, total;
+    size_t qs, dg, dgp, r0, r1, hist, totals, offs, zq, pq, zk, pk, ohist, total;
     int64_t P, tiles;
 };
 
@@ -112,6 +114,9 @@ BwdPlan plan_bwd(const zeta_shape* sh) {
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
     p.zq = take(sizeof(uint32_t) * BH * N);
     p.pq = take(sizeof(uint32_t) * BH * N);
+    p.zk = take(sizeof(uint32_t) * BH * N);
+    p.pk = take(sizeof(uint32_t) * BH * N);
+    p.ohist = take(sizeof(uint32_t) * zeta::order_scratch_words(BH, N));
     p.total = off;
     return p;
 }
@@ -240,7 +245,7 @@ zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, co
     const FwdPlan p = plan_fwd(shape);
     uint32_t* perm = at<uint32_t>(workspace, p.perm);
     hipError_t e = zeta::launch_order(shape->B * shape->H, shape->N, at<uint32_t>(workspace, p.zq),
-                                      perm, s);
+                                      perm, at<uint32_t>(workspace, p.ohist), s);
     if (e != hipSuccess) return fail_hip("order launch", e);
     g_marks.record(4, s);
     e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
@@ -280,6 +285,9 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     b.offs = at<uint32_t>(workspace, p.offs);
     b.zq = at<uint32_t>(workspace, p.zq);
     b.perm_q = at<uint32_t>(workspace, p.pq);
+    b.zk = at<uint32_t>(workspace, p.zk);
+    b.perm_k = at<uint32_t>(workspace, p.pk);
+    b.ohist = at<uint32_t>(workspace, p.ohist);
     b.P = p.P;
     b.tiles = p.tiles;
     hipError_t e = zeta::launch_bwd(shape->B * shape->H, shape->H, shape->N, shape->dv,

@@ -56,8 +56,10 @@ hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk,
                          const float* q, const float* k, const void* v, const float* gamma,
                          const int32_t* idx, const uint32_t* order, void* out, hipStream_t s);
 // Processing order: per (b,h), positions bucketed by the top code bits (order.hip).
+// scratch: order_scratch_words(BH, N) words.
+size_t order_scratch_words(int64_t BH, int64_t N);
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
-                        hipStream_t s);
+                        uint32_t* scratch, hipStream_t s);
 
 struct BwdBuffers {
     float2* qstat;    // [BHN] per-query {1/S_i, D_i}
@@ -70,6 +72,9 @@ struct BwdBuffers {
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
     uint32_t* zq;     // [BHN] query codes
     uint32_t* perm_q; // [BHN] query processing order
+    uint32_t* zk;     // [BHN] key codes
+    uint32_t* perm_k; // [BHN] key processing order
+    uint32_t* ohist;  // order_scratch_words(BH, N) words for the processing orders
     int64_t P;        // valid pairs per (b,h)
     int64_t tiles;    // radix tiles per (b,h)
 };
