@@ -51,6 +51,17 @@ def _load():
                                        p, p, p]
         lib.oracle_backward.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, p, p, p, p, i64,
                                         p, p, p, p, p, p]
+        lib.oracle_cell12.argtypes = [ctypes.c_float]
+        lib.oracle_cell12.restype = ctypes.c_int32
+        lib.oracle_interleave36.argtypes = [ctypes.c_int32] * 3
+        lib.oracle_interleave36.restype = ctypes.c_uint64
+        lib.oracle_encode_ex.argtypes = [p, i64, ctypes.c_int, p, p]
+        lib.oracle_select_codes64.argtypes = [i64, i64, ctypes.c_int, p, p, i64, p, p]
+        lib.oracle_chunk_len.argtypes = [i64, i64]
+        lib.oracle_chunk_len.restype = i64
+        lib.oracle_select_chunked.argtypes = [i64, i64, i64, p, p, i64, p, p]
+        lib.oracle_select_multi.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, p, i64, p, p]
+        lib.oracle_euclid_topk.argtypes = [i64, i64, ctypes.c_int, p, p, i64, p, p]
         lib.oracle_bf16_bits.argtypes = [ctypes.c_double]
         lib.oracle_bf16_bits.restype = ctypes.c_uint16
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -108,6 +119,79 @@ def select(q: np.ndarray, k: np.ndarray, topk: int, rows=None) -> np.ndarray:
     r = _rows(rows, B * H * N)
     idx = np.empty((r.size, topk), dtype=np.int32)
     _load().oracle_select(B * H, N, topk, _ptr(q), _ptr(k), r.size, _ptr(r), _ptr(idx))
+    return idx
+
+
+def cell12(x: float) -> int:
+    return int(_load().oracle_cell12(float(x)))
+
+
+def interleave36(c0: int, c1: int, c2: int) -> int:
+    return int(_load().oracle_interleave36(c0, c1, c2))
+
+
+def encode_ex(x: np.ndarray, bits: int = 10, perm=(0, 1, 2)) -> np.ndarray:
+    """Z-order codes (uint64) with `bits` (10 or 12) per axis, axis a from coordinate perm[a]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    z = np.empty(x.shape[:-1], dtype=np.uint64)
+    pm = np.ascontiguousarray(perm, dtype=np.int32)
+    _load().oracle_encode_ex(_ptr(x), x.size // 3, int(bits), _ptr(pm), _ptr(z))
+    return z
+
+
+def select_codes64(zq, zk, N: int, topk: int, causal: bool = True, rows=None) -> np.ndarray:
+    """Exact top-k by (|zq-zk|, j) over uint64 codes, causal (j <= i) or not (j < N)."""
+    zq = np.ascontiguousarray(zq, dtype=np.uint64).reshape(-1)
+    zk = np.ascontiguousarray(zk, dtype=np.uint64).reshape(-1)
+    r = _rows(rows, zq.size)
+    idx = np.empty((r.size, topk), dtype=np.int32)
+    _load().oracle_select_codes64(N, topk, int(causal), _ptr(zq), _ptr(zk), r.size, _ptr(r),
+                                  _ptr(idx))
+    return idx
+
+
+def select_ex(q, k, topk: int, bits: int = 10, causal: bool = True, rows=None) -> np.ndarray:
+    """Exact selection from fp32 points with `bits` per axis, causal or not."""
+    N = q.shape[-2]
+    return select_codes64(encode_ex(q, bits), encode_ex(k, bits), N, topk, causal, rows)
+
+
+def chunk_len(N: int, chunks: int) -> int:
+    return int(_load().oracle_chunk_len(N, chunks))
+
+
+def select_chunked(zq, zk, N: int, topk: int, chunks: int, rows=None) -> np.ndarray:
+    """The chunked causal search (window around the insertion position in each chunk)."""
+    zq = np.ascontiguousarray(zq, dtype=np.uint32).reshape(-1)
+    zk = np.ascontiguousarray(zk, dtype=np.uint32).reshape(-1)
+    r = _rows(rows, zq.size)
+    idx = np.empty((r.size, topk), dtype=np.int32)
+    _load().oracle_select_chunked(N, topk, chunks, _ptr(zq), _ptr(zk), r.size, _ptr(r),
+                                  _ptr(idx))
+    return idx
+
+
+def select_multi(q, k, topk: int, curves: int, causal: bool = True, rows=None) -> np.ndarray:
+    """Several curves (3 or 6 axis orders), each its own top-(topk // curves), merged."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    B, H, N, _ = q.shape
+    r = _rows(rows, B * H * N)
+    idx = np.empty((r.size, topk), dtype=np.int32)
+    _load().oracle_select_multi(B * H, N, topk, curves, int(causal), _ptr(q), _ptr(k), r.size,
+                                _ptr(r), _ptr(idx))
+    return idx
+
+
+def euclid_topk(q, k, topk: int, causal: bool = True, rows=None) -> np.ndarray:
+    """Exact Euclidean top-k of the raw points by (d^2, j) (recall diagnostic)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    B, H, N, _ = q.shape
+    r = _rows(rows, B * H * N)
+    idx = np.empty((r.size, topk), dtype=np.int32)
+    _load().oracle_euclid_topk(N, topk, int(causal), _ptr(q), _ptr(k), r.size, _ptr(r),
+                               _ptr(idx))
     return idx
 
 

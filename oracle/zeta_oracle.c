@@ -117,6 +117,242 @@ void oracle_select(int64_t BH, int64_t N, int64_t K, const float *q, const float
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* Variants of the selection: the pages' own 12-bit precision, axis permutations (several
+ * curves), the unmasked case and the chunked causal search.  Codes are carried as uint64
+ * so that 36-bit codes fit; candidates are compared as (|dz|, j) pairs.                   */
+
+/* 12-bit quantiser.  [R] answer W2/A2 ("Clarification of Binary Expansion and Precision"):
+ * a grid of 4096 cells per coordinate, i.e. 12 bits.  Reading taken: the same fixed
+ * interval [-4, 4) as the 10-bit form, cell width 1/512:
+ *     cell = floor((x + 4) * 512), clamped to [0, 4095];  NaN -> cell 0,
+ * evaluated as floor(512 x) + 2048 (512 x is an exact scaling in double).                */
+int32_t oracle_cell12(float x)
+{
+    if (isnan(x)) return 0;
+    double c = floor(512.0 * (double)x) + 2048.0;
+    if (c < 0.0) return 0;
+    if (c > 4095.0) return 4095;
+    return (int32_t)c;
+}
+
+/* Interleave of three 12-bit cells.  [R] answer W2/A2: three 12-bit components interleave
+ * into a 36-bit value that fits in a 64-bit integer.  Bit b of axis a -> bit 3b + a.       */
+uint64_t oracle_interleave36(int32_t c0, int32_t c1, int32_t c2)
+{
+    int32_t c[3] = {c0, c1, c2};
+    uint64_t z = 0;
+    for (int b = 0; b < 12; ++b)
+        for (int a = 0; a < 3; ++a)
+            z |= (uint64_t)((c[a] >> b) & 1) << (3 * b + a);
+    return z;
+}
+
+/* Codes of `rows` points with `bits` (10 or 12) bits per axis, axis a of the code taken from
+ * coordinate perm[a].  [R] ("Interleaving the bits from different dimensions ..."): the
+ * several-curve variant feeds the coordinates to the curve in permuted orders, e.g.
+ * (K2, K3, K1); perm = {0, 1, 2} is the plain code.                                       */
+void oracle_encode_ex(const float *x, int64_t rows, int bits, const int32_t *perm, uint64_t *z)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *p = x + 3 * r;
+        if (bits == 12)
+            z[r] = oracle_interleave36(oracle_cell12(p[perm[0]]), oracle_cell12(p[perm[1]]),
+                                       oracle_cell12(p[perm[2]]));
+        else
+            z[r] = (uint64_t)oracle_interleave(oracle_cell(p[perm[0]]), oracle_cell(p[perm[1]]),
+                                               oracle_cell(p[perm[2]]));
+    }
+}
+
+typedef struct {
+    uint64_t d;  /* |dz| (or, for the Euclidean diagnostic, the bits of d^2 >= 0) */
+    int64_t j;
+} cand_t;
+
+static int cmp_cand(const void *a, const void *b)
+{
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->d != y->d) return x->d < y->d ? -1 : 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static uint64_t absdiff64(uint64_t a, uint64_t b) { return a > b ? a - b : b - a; }
+
+/* Exact selection over uint64 codes.  causal = 1: keys j in [0, i] (as oracle_select_codes);
+ * causal = 0: every key of the sequence, j in [0, N) -- the unmasked case of the same
+ * problem ([S] "Problem": the causal mask is what rules out one search for the whole
+ * sequence; without it every query searches the one sorted key sequence).  The first
+ * min(K, number of keys) of (|dz|, j) ascending; -1 padding.                              */
+void oracle_select_codes64(int64_t N, int64_t K, int causal, const uint64_t *zq,
+                           const uint64_t *zk, int64_t nrows, const int64_t *rows, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            int64_t row = rows[t];
+            int64_t bh = row / N, i = row % N;
+            int64_t n = causal ? i + 1 : N;
+            for (int64_t j = 0; j < n; ++j) {
+                c[j].d = absdiff64(zq[row], zk[bh * N + j]);
+                c[j].j = j;
+            }
+            qsort(c, (size_t)n, sizeof(cand_t), cmp_cand);
+            for (int64_t r = 0; r < K; ++r) idx[t * K + r] = r < n ? (int32_t)c[r].j : -1;
+        }
+        free(c);
+    }
+}
+
+/* Chunk length of the chunked search: the smallest power of two L with L * C >= N, so the
+ * sequence splits into ceil(N / L) <= C aligned chunks of L positions (the last one
+ * possibly shorter).                                                                      */
+int64_t oracle_chunk_len(int64_t N, int64_t C)
+{
+    int64_t want = (N + C - 1) / C, L = 1;
+    while (L < want) L <<= 1;
+    return L;
+}
+
+static int cmp_code_j(const void *a, const void *b)
+{
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->d != y->d) return x->d < y->d ? -1 : 1;  /* here d holds the key's code */
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+/* The pages' chunked causal search.  [S] "Approach": keys are sorted and chunked so that
+ * every query retrieves its top-k in parallel under the causal mask; [R] answer W2/A2
+ * ("Details about experiments"): 4 to 32 chunks depending on the sequence length;
+ * ("Clarification"): a query's binary search finds its insertion position in the sorted
+ * keys and the keys in the window centred there are taken as its nearest neighbours.
+ * The pages do not print the chunking steps; the plainest reading, taken here:
+ *   - the positions split into aligned chunks of L = oracle_chunk_len(N, C) positions;
+ *   - each chunk's keys are sorted by (code, j);
+ *   - query i searches every chunk c <= i / L: p = number of the chunk's keys with code
+ *     < zq_i, and the window is the w = min(K, chunk size) consecutive sorted entries
+ *     starting at p - floor(K / 2), shifted to lie inside the chunk;
+ *   - the causal mask then drops window keys with j > i (only the query's own chunk
+ *     holds any);
+ *   - the result is the first min(K, candidates) candidates by (|dz|, j), -1 padded.
+ * Windows of different chunks never share a key, so no candidate repeats.                */
+void oracle_select_chunked(int64_t N, int64_t K, int64_t C, const uint32_t *zq,
+                           const uint32_t *zk, int64_t nrows, const int64_t *rows, int32_t *idx)
+{
+    int64_t L = oracle_chunk_len(N, C);
+#pragma omp parallel
+    {
+        cand_t *chunk = (cand_t *)malloc(sizeof(cand_t) * (size_t)L);
+        cand_t *cand = (cand_t *)malloc(sizeof(cand_t) * (size_t)(N + K));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            int64_t row = rows[t];
+            int64_t bh = row / N, i = row % N;
+            uint64_t z = zq[row];
+            int64_t nc = 0;
+            for (int64_t c = 0; c <= i / L; ++c) {
+                int64_t lo = c * L, hi = lo + L < N ? lo + L : N, n = hi - lo;
+                for (int64_t j = lo; j < hi; ++j) {
+                    chunk[j - lo].d = zk[bh * N + j];
+                    chunk[j - lo].j = j;
+                }
+                qsort(chunk, (size_t)n, sizeof(cand_t), cmp_code_j);
+                int64_t p = 0;
+                while (p < n && chunk[p].d < z) ++p;
+                int64_t w = K < n ? K : n;
+                int64_t w0 = p - K / 2;
+                if (w0 > n - w) w0 = n - w;
+                if (w0 < 0) w0 = 0;
+                for (int64_t e = w0; e < w0 + w; ++e) {
+                    if (chunk[e].j > i) continue;  /* causal mask */
+                    cand[nc].d = absdiff64(z, chunk[e].d);
+                    cand[nc].j = chunk[e].j;
+                    ++nc;
+                }
+            }
+            qsort(cand, (size_t)nc, sizeof(cand_t), cmp_cand);
+            for (int64_t r = 0; r < K; ++r) idx[t * K + r] = r < nc ? (int32_t)cand[r].j : -1;
+        }
+        free(chunk);
+        free(cand);
+    }
+}
+
+/* Several curves.  [R] ("Interleaving the bits from different dimensions would more-or-less
+ * remove the asymmetry"): 3 curves with the coordinates in the orders (K1,K2,K3),
+ * (K2,K3,K1), (K3,K1,K2), or 6 curves with all six orders (K1,K2,K3), (K1,K3,K2),
+ * (K2,K3,K1), (K2,K1,K3), (K3,K1,K2), (K3,K2,K1); every curve collects k // P tokens.
+ * Reading taken: curve p selects its own exact top-(K / P) (causal or not) on its codes;
+ * the result lists curve 0's picks, then each later curve's picks that are not yet listed,
+ * each curve in its own (|dz|, j) order; the rest of the K slots are -1.                  */
+static const int32_t kPerm3[3][3] = {{0, 1, 2}, {1, 2, 0}, {2, 0, 1}};
+static const int32_t kPerm6[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 2, 0},
+                                     {1, 0, 2}, {2, 0, 1}, {2, 1, 0}};
+
+void oracle_select_multi(int64_t BH, int64_t N, int64_t K, int64_t P, int causal,
+                         const float *q, const float *k, int64_t nrows, const int64_t *rows,
+                         int32_t *idx)
+{
+    int64_t per = K / P;
+    uint64_t *zq = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(BH * N));
+    uint64_t *zk = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(BH * N));
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nrows * (per > 0 ? per : 1)));
+    for (int64_t t = 0; t < nrows * K; ++t) idx[t] = -1;
+    int64_t *fill = (int64_t *)calloc((size_t)nrows, sizeof(int64_t));
+    for (int64_t c = 0; c < P && per > 0; ++c) {
+        const int32_t *perm = P == 3 ? kPerm3[c] : kPerm6[c];
+        oracle_encode_ex(q, BH * N, 10, perm, zq);
+        oracle_encode_ex(k, BH * N, 10, perm, zk);
+        oracle_select_codes64(N, per, causal, zq, zk, nrows, rows, sel);
+        for (int64_t t = 0; t < nrows; ++t) {
+            for (int64_t r = 0; r < per; ++r) {
+                int32_t j = sel[t * per + r];
+                if (j < 0) continue;
+                int dup = 0;
+                for (int64_t e = 0; e < fill[t]; ++e)
+                    if (idx[t * K + e] == j) dup = 1;
+                if (!dup) idx[t * K + fill[t]++] = j;
+            }
+        }
+    }
+    free(zq);
+    free(zk);
+    free(sel);
+    free(fill);
+}
+
+/* Recall diagnostic: the exact Euclidean top-K of the raw points, ordered by (d^2, j)
+ * (fp64 squared distances), causal or not.  [R] answer W3/A3 ("Justification for
+ * Euclidean Distance Claim") and [A] (top-k of the most relevant tokens): the Z-order
+ * selection stands in for this set.                                                       */
+static double sqdist(const float *a, const float *b);
+void oracle_euclid_topk(int64_t N, int64_t K, int causal, const float *q, const float *k,
+                        int64_t nrows, const int64_t *rows, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)N);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            int64_t row = rows[t];
+            int64_t bh = row / N, i = row % N;
+            int64_t n = causal ? i + 1 : N;
+            for (int64_t j = 0; j < n; ++j) {
+                double d = sqdist(q + 3 * row, k + 3 * (bh * N + j));
+                uint64_t bits;
+                memcpy(&bits, &d, sizeof bits);  /* order of non-negative doubles */
+                c[j].d = bits;
+                c[j].j = j;
+            }
+            qsort(c, (size_t)n, sizeof(cand_t), cmp_cand);
+            for (int64_t r = 0; r < K; ++r) idx[t * K + r] = r < n ? (int32_t)c[r].j : -1;
+        }
+        free(c);
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Value access: v is fp32, or bf16 carried as raw 16-bit patterns (exact widening).      */
 static double value_at(const void *v, int v_bf16, int64_t off)
 {
@@ -148,7 +384,9 @@ static double sqdist(const float *a, const float *b)
  *     s_ij = 1 / (1 + ||q_i - k_j||^2 / gamma_h^2),   a_ij = s_ij / sum_j' s_ij',
  *     o_i  = sum_j a_ij v_j          (sums over the selected j only).
  * gamma is one value per head, shared over the batch.  `rows` lists flat query rows; idx,
- * out and (optionally) weights are laid out per listed row.                               */
+ * out and (optionally) weights are laid out per listed row.  Slots with idx < 0 are not
+ * selected.  Reading taken for an empty selection (possible with the chunked search, whose
+ * windows can miss every key j <= i): the output is zero and no gradient flows.           */
 void oracle_forward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
                     const float *q, const float *k, const void *v, const float *gamma,
                     int64_t nrows, const int64_t *rows, const int32_t *idx,
@@ -161,6 +399,7 @@ void oracle_forward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
         double g = (double)gamma[bh % H];
         double s[K > 0 ? K : 1];
         double S = 0.0;
+        int64_t nsel = 0;
         for (int64_t r = 0; r < K; ++r) {
             int32_t j = idx[t * K + r];
             s[r] = 0.0;
@@ -168,8 +407,14 @@ void oracle_forward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
             double d = sqdist(q + 3 * row, k + 3 * (bh * N + j));
             s[r] = 1.0 / (1.0 + d / (g * g));
             S += s[r];
+            ++nsel;
         }
         for (int64_t c = 0; c < dv; ++c) out[t * dv + c] = 0.0;
+        if (nsel == 0) {  /* empty selection: zero output */
+            if (weights)
+                for (int64_t r = 0; r < K; ++r) weights[t * K + r] = 0.0;
+            continue;
+        }
         for (int64_t r = 0; r < K; ++r) {
             int32_t j = idx[t * K + r];
             double a = j < 0 ? 0.0 : s[r] / S;
@@ -212,6 +457,7 @@ void oracle_backward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
         double g = (double)gamma[h];
         const float *qi = q + 3 * row;
         double S = 0.0;
+        for (int e = 0; e < 3; ++e) dq[3 * t + e] = 0.0;
         for (int64_t r = 0; r < K; ++r) {
             int32_t j = idx[t * K + r];
             s[r] = d[r] = gr[r] = 0.0;
@@ -225,6 +471,9 @@ void oracle_backward(int64_t H, int64_t N, int64_t K, int64_t dv, int v_bf16,
                 acc += value_at(dout, v_bf16, row * dv + c) * value_at(v, v_bf16, col * dv + c);
             gr[r] = acc;
         }
+        int64_t nsel = 0;
+        for (int64_t r = 0; r < K; ++r) nsel += idx[t * K + r] >= 0;
+        if (nsel == 0) continue;  /* empty selection: no gradient */
         double D = 0.0;
         for (int64_t r = 0; r < K; ++r)
             if (idx[t * K + r] >= 0) D += (s[r] / S) * gr[r];
