@@ -118,13 +118,78 @@ zeta_status zeta_fwd(const zeta_shape *shape, const float *q, const float *k, co
  * fixed butterfly), so results are bitwise reproducible: no floating-point atomics.
  * dout: [B,H,N,dv] v_dtype.
  * idx is expected to be the selection zeta_fwd returned: slot r of query i is used when
- * r < min(topk, i+1), and its entry is clamped into [0, i]; later slots are ignored.  An
- * index tensor that is not a valid selection therefore gives meaningless but bounded
- * results (no access outside the buffers).                                               */
+ * r < min(topk, i+1) and its entry is >= 0, and the entry is clamped to at most i; other
+ * slots are ignored.  An index tensor that is not a valid selection therefore gives
+ * meaningless but bounded results (no access outside the buffers).                      */
 zeta_status zeta_bwd(const zeta_shape *shape, const float *q, const float *k, const void *v,
                      const float *gamma, const int32_t *idx, const void *dout, float *dq,
                      float *dk, void *dv, float *dgamma, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Selection variants (the _ex calls).  NULL options = the exact causal selection with
+ * 10-bit cells, i.e. the calls above.
+ *
+ *   ZETA_SELECT_EXACT    exact top-k by (|dz|, j), as zeta_select; with causal = 0 every
+ *                        key j < N competes for every query (the unmasked form of the same
+ *                        problem, [S] "Problem": the causal mask is what prevents one
+ *                        search over the whole sorted sequence).
+ *   ZETA_SELECT_CHUNKED  the pages' chunked causal search ([S] "Approach": sort and chunk
+ *                        the keys; [R] answer W2/A2 "Details about experiments": 4-32
+ *                        chunks; "Clarification": the window centred at the query's
+ *                        insertion position).  Reading taken: chunks are the aligned blocks
+ *                        of L positions, L the smallest power of two with L * chunks >= N;
+ *                        each chunk's keys sorted by (code, j); for every chunk up to the
+ *                        query's own, the min(k, chunk size) sorted entries starting
+ *                        floor(k/2) before the insertion position (shifted to lie inside
+ *                        the chunk); keys j > i dropped; the first k candidates by
+ *                        (|dz|, j).  An approximation of the exact selection: a query may
+ *                        get fewer than min(k, i+1) keys (-1 slots anywhere after the
+ *                        picks) or none.  causal must be 1.
+ *   ZETA_SELECT_CURVES   several Z-order curves ([R], on the asymmetry of interleaving):
+ *                        curves = 3 takes the coordinate orders (K1,K2,K3), (K2,K3,K1),
+ *                        (K3,K1,K2); curves = 6 all six orders (K1,K2,K3), (K1,K3,K2),
+ *                        (K2,K3,K1), (K2,K1,K3), (K3,K1,K2), (K3,K2,K1).  Each curve takes
+ *                        its exact top-(k / curves); idx lists curve 0's picks, then each
+ *                        later curve's picks not listed yet; -1 in the remaining slots.
+ *
+ * A query with no selected key outputs zero and passes no gradient.  zeta_bwd_ex uses only
+ * `causal` from the options: slot r of query i is used when r < min(k, i+1) (causal) or
+ * r < min(k, N) and idx >= 0; entries are clamped to the last usable key.
+ * The stage events of zeta_set_stage_events keep their meaning; with several curves stages
+ * 1 and 2 cover the first curve and stage 3 the remaining curves and the merge.            */
+#define ZETA_MAX_CHUNKS 1024
+
+typedef enum zeta_select_mode {
+    ZETA_SELECT_EXACT = 0,
+    ZETA_SELECT_CHUNKED = 1,
+    ZETA_SELECT_CURVES = 2
+} zeta_select_mode;
+
+typedef struct zeta_select_opts {
+    int32_t mode;     /* zeta_select_mode                                                   */
+    int32_t causal;   /* 1: keys j <= i;  0: every key j < N (EXACT and CURVES only)        */
+    int32_t bits;     /* bits per axis of the codes: 10 (12: ZETA_ERR_UNSUPPORTED for now)   */
+    int32_t chunks;   /* CHUNKED: number of chunks C, 1 <= C <= ZETA_MAX_CHUNKS              */
+    int32_t curves;   /* CURVES: 3 or 6 (and topk >= curves)                                */
+    int32_t reserved; /* must be 0                                                          */
+} zeta_select_opts;
+
+/* As the calls without _ex, for the selection variant in `opts` (NULL = exact, causal,
+ * 10 bits).  Invalid options: ZETA_ERR_INVALID_ARGUMENT or ZETA_ERR_UNSUPPORTED (and 0
+ * from zeta_workspace_bytes_ex).                                                          */
+size_t zeta_workspace_bytes_ex(const zeta_shape *shape, const zeta_select_opts *opts,
+                               int32_t kind);
+zeta_status zeta_select_ex(const zeta_shape *shape, const zeta_select_opts *opts,
+                           const float *q, const float *k, int32_t *idx, void *workspace,
+                           size_t workspace_bytes, void *stream);
+zeta_status zeta_fwd_ex(const zeta_shape *shape, const zeta_select_opts *opts, const float *q,
+                        const float *k, const void *v, const float *gamma, void *out,
+                        int32_t *idx, void *workspace, size_t workspace_bytes, void *stream);
+zeta_status zeta_bwd_ex(const zeta_shape *shape, const zeta_select_opts *opts, const float *q,
+                        const float *k, const void *v, const float *gamma, const int32_t *idx,
+                        const void *dout, float *dq, float *dk, void *dv, float *dgamma,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Measurement hook (for timing individual kernels from the caller).  Hands this thread a
  * list of `count` hipEvent_t handles (created by the caller, with timing enabled).  Every

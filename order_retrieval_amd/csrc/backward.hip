@@ -29,19 +29,29 @@ constexpr int kRadixThreads = 256;
 constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;
 
-// A selection slot r of query i is a pair when r < min(topk, i+1); its key is clamped into
-// [0, i], so an index tensor that is not a valid selection still never leads outside the
-// buffers (the result is then meaningless but defined).
-__device__ __forceinline__ int64_t clamp_index(int32_t j, int64_t i) {
-    return j < 0 ? 0 : (j > i ? i : j);
+// A selection slot r of query i is a pair when r < min(topk, keys the query may use) (i+1
+// under the causal mask, else N) and it holds an index >= 0; the index is clamped to the
+// last usable key, so an index tensor that is not a valid selection still never leads
+// outside the buffers (the result is then meaningless but defined).
+__device__ __forceinline__ int64_t clamp_index(int32_t j, int64_t jmax) {
+    return j < 0 ? 0 : (j > jmax ? jmax : j);
 }
 
-__device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64_t e, int topk,
-                                          uint32_t& key) {
-    const uint32_t i = static_cast<uint32_t>(e) / static_cast<uint32_t>(topk);
-    const uint32_t r = static_cast<uint32_t>(e) - i * static_cast<uint32_t>(topk);
-    if (r > i) return false;  // slot beyond min(topk, i+1)
-    key = static_cast<uint32_t>(clamp_index(idx[e], i));
+struct PairSpec {
+    int topk;
+    int causal;
+    int64_t N;
+};
+
+__device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64_t e,
+                                          const PairSpec& ps, uint32_t& key) {
+    const uint32_t i = static_cast<uint32_t>(e) / static_cast<uint32_t>(ps.topk);
+    const uint32_t r = static_cast<uint32_t>(e) - i * static_cast<uint32_t>(ps.topk);
+    const int64_t nk = ps.causal ? static_cast<int64_t>(i) + 1 : ps.N;
+    if (r >= nk) return false;  // slot beyond min(topk, nk)
+    const int32_t j = idx[e];
+    if (j < 0) return false;    // no selection in this slot
+    key = static_cast<uint32_t>(clamp_index(j, nk - 1));
     return true;
 }
 
@@ -68,9 +78,10 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
     R raw[kRowLoads][CPL];
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
-        const int64_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+        const int32_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+        const int64_t jr = j < 0 ? 0 : j;  // an empty slot reads key 0's row; its g is unused
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + j * dv + coff[c]);
+        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + jr * dv + coff[c]);
     });
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
@@ -92,8 +103,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int64_t tiles, int64_t per_xcd, float2* __restrict__ qstat,
-    float* __restrict__ dq, float* __restrict__ dg_row) {
+    int64_t H, int dv, int topk, int causal, int64_t tiles, int64_t per_xcd,
+    float2* __restrict__ qstat, float* __restrict__ dq, float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -110,7 +121,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
-    const int m = live ? static_cast<int>(i + 1 < topk ? i + 1 : topk) : 0;
+    const int64_t nk = causal ? i + 1 : N;  // keys the query may use
+    const int m = live ? static_cast<int>(nk < topk ? nk : topk) : 0;
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
@@ -128,15 +140,17 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
 
     int32_t jo[U];
     float so[U], dx[U], dy[U], dz[U], gg[U];
-    float ssum = 0.0f;
+    float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int r = lrow + u * kRowLanes;
-        jo[u] = 0;  // slots past m name key 0 (inside the buffers) and are never summed
+        jo[u] = -1;  // not selected: never summed
         so[u] = dx[u] = dy[u] = dz[u] = gg[u] = 0.0f;
-        if (r < m) {
-            const int32_t j = static_cast<int32_t>(clamp_index(ir[r], i));
+        const int32_t jr = r < m ? ir[r] : -1;
+        if (jr >= 0) {
+            const int32_t j = static_cast<int32_t>(clamp_index(jr, nk - 1));
             jo[u] = j;
+            nsel += 1.0f;
             dx[u] = q0 - kh[3 * j];
             dy[u] = q1 - kh[3 * j + 1];
             dz[u] = q2 - kh[3 * j + 2];
@@ -145,6 +159,7 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         }
     }
     const float S = group_sum(ssum, kRowLanes);
+    nsel = group_sum(nsel, kRowLanes);
     // the longest selection among the wavefront's four queries sets the trip count
     int most = m;
     most = max(most, __shfl_xor(most, 16, 64));
@@ -164,14 +179,14 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     float tsum = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (lrow + u * kRowLanes < m) tsum += so[u] * gg[u];
-    const float inv_S = 1.0f / S;
+        if (jo[u] >= 0) tsum += so[u] * gg[u];
+    const float inv_S = nsel > 0.0f ? 1.0f / S : 0.0f;  // an empty selection passes no gradient
     const float D = group_sum(tsum, kRowLanes) * inv_S;
 
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (lrow + u * kRowLanes < m) {
+        if (jo[u] >= 0) {
             const float a = so[u] * inv_S;
             const float c = a * so[u] * (gg[u] - D);
             a0 += c * dx[u];
@@ -196,9 +211,10 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
 
 template <bool BF16, int CPL>
 static hipError_t launch_query_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
-                                 const float* q, const float* k, const void* v, const float* gamma,
-                                 const int32_t* idx, const void* dout, const uint32_t* order,
-                                 float2* qstat, float* dq, float* dg_row, hipStream_t s) {
+                                 int causal, const float* q, const float* k, const void* v,
+                                 const float* gamma, const int32_t* idx, const void* dout,
+                                 const uint32_t* order, float2* qstat, float* dq, float* dg_row,
+                                 hipStream_t s) {
     const int64_t tiles = (rows + (256 / kRowLanes) - 1) / (256 / kRowLanes);
     const int64_t per = xcd_per(tiles);
     const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane (<= 4)
@@ -206,23 +222,24 @@ static hipError_t launch_query_c(int64_t rows, int64_t N, int64_t H, int dv, int
               : u <= 2 ? zeta_bwd_query_kernel<BF16, CPL, 2>
                        : zeta_bwd_query_kernel<BF16, CPL, 4>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, dout, order, rows, N, H, dv, topk, tiles, per, qstat, dq, dg_row);
+                       gamma, idx, dout, order, rows, N, H, dv, topk, causal, tiles, per, qstat, dq,
+                       dg_row);
     return hipGetLastError();
 }
 
 template <bool BF16>
-static hipError_t launch_query(int64_t rows, int64_t N, int64_t H, int dv, int topk,
+static hipError_t launch_query(int64_t rows, int64_t N, int64_t H, int dv, int topk, int causal,
                                const float* q, const float* k, const void* v, const float* gamma,
                                const int32_t* idx, const void* dout, const uint32_t* order,
                                float2* qstat, float* dq, float* dg_row, hipStream_t s) {
     const int cpl = (dv / VecIO<BF16>::kElems + kRowLanes - 1) / kRowLanes;
     if (cpl <= 1)
-        return launch_query_c<BF16, 1>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_c<BF16, 1>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
     if (cpl <= 2)
-        return launch_query_c<BF16, 2>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_c<BF16, 2>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
     if (BF16 || cpl <= 4)  // bf16 rows have <= 64 chunks
-        return launch_query_c<BF16, 4>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
-    return launch_query_c<BF16, BF16 ? 4 : 8>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_c<BF16, 4>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+    return launch_query_c<BF16, BF16 ? 4 : 8>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
 }
 
 // ---------------------------------------------------------------------------- 2. transpose
@@ -231,25 +248,28 @@ static hipError_t launch_query(int64_t rows, int64_t N, int64_t H, int dv, int t
 // The key kernel then reads each key's pairs as one contiguous run of records.
 template <bool FIRST>
 __device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
-                                          const uint2* __restrict__ rin, int64_t e, int topk,
-                                          uint2& rec) {
+                                          const uint2* __restrict__ rin, int64_t e,
+                                          const PairSpec& ps, uint2& rec) {
     if (FIRST) {
         uint32_t key;
-        if (!pair_item(idx, e, topk, key)) return false;
-        rec = make_uint2(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(topk));
+        if (!pair_item(idx, e, ps, key)) return false;
+        rec = make_uint2(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(ps.topk));
         return true;
     }
     rec = rin[e];
     return true;
 }
 
-// Digit counts of one tile of items.
+// Digit counts of one tile of items.  Pass 0 takes every selection slot (items = N * topk)
+// and keeps the pairs; later passes take the first counts[bh] records.
 template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
-    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t items,
-    int64_t in_stride, int shift, int64_t tiles, int topk, uint32_t* __restrict__ hist) {
+    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t slots,
+    const uint32_t* __restrict__ counts, int64_t in_stride, int shift, int64_t tiles,
+    PairSpec ps, uint32_t* __restrict__ hist) {
     __shared__ uint32_t cnt[256];
     const int64_t bh = blockIdx.y;
+    const int64_t items = FIRST ? slots : static_cast<int64_t>(counts[bh]);
     cnt[threadIdx.x] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
@@ -262,7 +282,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
         keys[it] = 0;
         if (e < items) {
             if (FIRST)
-                valid[it] = pair_item(idx + bh * in_stride, e, topk, keys[it]);
+                valid[it] = pair_item(idx + bh * in_stride, e, ps, keys[it]);
             else {
                 valid[it] = true;
                 keys[it] = rin[bh * in_stride + e].x;
@@ -304,12 +324,14 @@ __global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restric
 
 // Stable scatter of one tile: items are ranked in (iteration, wave, lane) order, which is
 // their input order, so equal digits keep their relative order.  All of the tile's items
-// are loaded before the ranking starts, so their loads overlap.
+// are loaded before the ranking starts, so their loads overlap.  Pass 0 also records the
+// number of pairs of each (b,h) in counts[bh] (the sum of the digit totals).
 template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
-    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t items,
-    int64_t in_stride, int shift, int64_t tiles, int topk, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ totals, int64_t P, uint2* __restrict__ rout) {
+    const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t slots,
+    uint32_t* __restrict__ counts, int64_t in_stride, int shift, int64_t tiles, PairSpec ps,
+    const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int64_t P,
+    uint2* __restrict__ rout) {
     __shared__ uint32_t base[256];
     __shared__ uint32_t scan[256];
     __shared__ uint32_t wcnt[4][256];
@@ -319,6 +341,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    const int64_t items = FIRST ? slots : static_cast<int64_t>(counts[bh]);
 
     uint2 rec[kRadixItems];
     uint32_t okmask = 0;
@@ -328,7 +351,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
         for (int it = 0; it < kRadixItems; ++it) {
             const int64_t e = t0 + it * kRadixThreads + tid;
             rec[it] = make_uint2(0, 0);
-            if (e < items && load_pair<FIRST>(idx + off, rin + off, e, topk, rec[it]))
+            if (e < items && load_pair<FIRST>(idx + off, rin + off, e, ps, rec[it]))
                 okmask |= 1u << it;
         }
     }
@@ -342,6 +365,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
         __syncthreads();
     }
     base[tid] = scan[tid] - totals[bh * 256 + tid] + hist[(bh * 256 + tid) * tiles + blockIdx.x];
+    if (FIRST && blockIdx.x == 0 && tid == 255) counts[bh] = scan[255];
     uint32_t run = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
@@ -376,19 +400,27 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
 }
 
 // ---------------------------------------------------------------------------- 3. offsets
+// offs[j] = first record of key j (records sorted by key), offs[N] = number of pairs.
 __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* __restrict__ recs,
+                                                                    const uint32_t* __restrict__ counts,
                                                                     int64_t P, int64_t N,
                                                                     uint32_t* __restrict__ offs) {
     const int64_t bh = blockIdx.y;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= P) return;
-    const uint2* rh = recs + bh * P;
+    const int64_t cnt = counts[bh];
     uint32_t* oh = offs + bh * (N + 1);
+    if (cnt == 0) {  // no pairs: every segment empty
+        if (t == 0)
+            for (int64_t jj = 0; jj <= N; ++jj) oh[jj] = 0;
+        return;
+    }
+    if (t >= cnt) return;
+    const uint2* rh = recs + bh * P;
     const int64_t kk = rh[t].x;
     const int64_t lo = t == 0 ? 0 : static_cast<int64_t>(rh[t - 1].x) + 1;
     for (int64_t jj = lo; jj <= kk; ++jj) oh[jj] = static_cast<uint32_t>(t);
-    if (t == P - 1)
-        for (int64_t jj = kk + 1; jj <= N; ++jj) oh[jj] = static_cast<uint32_t>(P);
+    if (t == cnt - 1)
+        for (int64_t jj = kk + 1; jj <= N; ++jj) oh[jj] = static_cast<uint32_t>(cnt);
 }
 
 // ---------------------------------------------------------------------------- 4. keys
@@ -604,29 +636,32 @@ __global__ void __launch_bounds__(64) zeta_dgamma_final_kernel(const float* __re
 int64_t dgamma_chunks(int64_t B, int64_t N) { return (B * N + kDgChunk - 1) / kDgChunk; }
 
 // ---------------------------------------------------------------------------- host
-size_t bwd_pairs_per_head(int64_t N, int topk) {
+size_t bwd_pairs_per_head(int64_t N, int topk, bool causal) {
+    if (!causal) return static_cast<size_t>(N * (N < topk ? N : topk));
     if (N <= topk) return static_cast<size_t>(N * (N + 1) / 2);
     return static_cast<size_t>(int64_t(topk) * (topk + 1) / 2 + (N - topk) * topk);
 }
 
 int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
 
+// items: slots of pass 0 (N * topk), else the upper bound P of the pairs per (b,h) (the
+// grid size; the kernels stop at the device-side count).
 template <bool FIRST>
 static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t items,
-                       int64_t stride, int shift, int topk, const BwdBuffers& ws, uint2* rout,
-                       hipStream_t s) {
+                       int64_t stride, int shift, const PairSpec& ps, const BwdBuffers& ws,
+                       uint2* rout, hipStream_t s) {
     const int64_t tiles = bwd_tiles_per_head(items);
     dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(BH));
     hipLaunchKernelGGL(zeta_radix_hist_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
-                       items, stride, shift, tiles, topk, ws.hist);
+                       items, ws.counts, stride, shift, tiles, ps, ws.hist);
     hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64), 0, s,
                        ws.hist, tiles, ws.totals);
     hipLaunchKernelGGL(zeta_radix_scatter_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
-                       items, stride, shift, tiles, topk, ws.hist, ws.totals, ws.P, rout);
+                       items, ws.counts, stride, shift, tiles, ps, ws.hist, ws.totals, ws.P, rout);
 }
 
 template <bool BF16>
-static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk,
+static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int topk, bool causal,
                                const float* q, const float* k, const void* v, const float* gamma,
                                const int32_t* idx, const void* dout, float* dq, float* dk,
                                void* dvout, float* dgamma, const BwdBuffers& ws,
@@ -639,7 +674,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     if (e == hipSuccess) e = launch_order(BH, N, ws.zk, ws.perm_k, ws.ohist, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
-    e = launch_query<BF16>(rows, N, H, dv, topk, q, k, v, gamma, idx, dout, ws.perm_q, ws.qstat,
+    e = launch_query<BF16>(rows, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,
+                           ws.perm_q, ws.qstat,
                            dq, ws.dg_row, s);
     if (e != hipSuccess) return e;
     marks.record(2, s);
@@ -647,18 +683,19 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
     const int passes = bits <= 8 ? 1 : (bits + 7) / 8;
-    radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, topk, ws, ws.rec0, s);
+    const PairSpec ps{topk, causal ? 1 : 0, N};
+    radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
     uint2* cur = ws.rec0;
     for (int p = 1; p < passes; ++p) {
         uint2* nxt = (p & 1) ? ws.rec1 : ws.rec0;
-        radix_pass<false>(BH, nullptr, cur, ws.P, ws.P, 8 * p, topk, ws, nxt, s);
+        radix_pass<false>(BH, nullptr, cur, ws.P, ws.P, 8 * p, ps, ws, nxt, s);
         cur = nxt;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(zeta_segment_offsets_kernel,
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
-                       dim3(256), 0, s, cur, ws.P, N, ws.offs);
+                       dim3(256), 0, s, cur, ws.counts, ws.P, N, ws.offs);
     marks.record(3, s);
     e = launch_key<BF16>(BH, H, N, dv, q, k, v, gamma, dout, ws, cur, ws.perm_k, dk, dvout, s);
     if (e != hipSuccess) return e;
@@ -673,15 +710,15 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
+hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal, bool bf16,
                       const float* q, const float* k, const void* v, const float* gamma,
                       const int32_t* idx, const void* dout, float* dq, float* dk, void* dvout,
                       float* dgamma, const BwdBuffers& ws, const StageEvents& marks,
                       hipStream_t s) {
     if (BH * N <= 0) return hipSuccess;
     if (bf16)
-        return launch_bwd_t<true>(BH, H, N, (int)dv, topk, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
-    return launch_bwd_t<false>(BH, H, N, (int)dv, topk, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+        return launch_bwd_t<true>(BH, H, N, (int)dv, topk, causal, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
+    return launch_bwd_t<false>(BH, H, N, (int)dv, topk, causal, q, k, v, gamma, idx, dout, dq, dk, dvout, dgamma, ws, marks, s);
 }
 
 }  // namespace zeta

@@ -33,10 +33,24 @@ __device__ __forceinline__ uint32_t morton3(float x0, float x1, float x2) {
     return spread3(cell10(x0)) | (spread3(cell10(x1)) << 1) | (spread3(cell10(x2)) << 2);
 }
 
+// Coordinate `a` of the curve's axis order: axis a reads coordinate (perm >> 2a) & 3.
+__device__ __forceinline__ float axis_of(float x0, float x1, float x2, int perm, int a) {
+    const int c = (perm >> (2 * a)) & 3;
+    return c == 0 ? x0 : (c == 1 ? x1 : x2);
+}
+
+__device__ __forceinline__ uint32_t morton3p(float x0, float x1, float x2, int perm) {
+    return morton3(axis_of(x0, x1, x2, perm, 0), axis_of(x0, x1, x2, perm, 1),
+                   axis_of(x0, x1, x2, perm, 2));
+}
+
+// perm packs the curve's coordinate order (several-curve variant, rebuttal page on the
+// asymmetry of interleaving: the coordinates are fed to the curve in a permuted order);
+// kPermIdentity = axis a reads coordinate a.
 __global__ void __launch_bounds__(256) zeta_morton_encode_kernel(const float* __restrict__ x,
                                                                   int64_t rows,
                                                                   uint32_t* __restrict__ z,
-                                                                  int vec_ok) {
+                                                                  int vec_ok, int perm) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t r0 = t * 4;
     if (r0 >= rows) return;
@@ -44,26 +58,31 @@ __global__ void __launch_bounds__(256) zeta_morton_encode_kernel(const float* __
         const float4* xv = reinterpret_cast<const float4*>(x) + 3 * t;
         float4 a = xv[0], b = xv[1], c = xv[2];
         uint4 o;
-        o.x = morton3(a.x, a.y, a.z);
-        o.y = morton3(a.w, b.x, b.y);
-        o.z = morton3(b.z, b.w, c.x);
-        o.w = morton3(c.y, c.z, c.w);
+        o.x = morton3p(a.x, a.y, a.z, perm);
+        o.y = morton3p(a.w, b.x, b.y, perm);
+        o.z = morton3p(b.z, b.w, c.x, perm);
+        o.w = morton3p(c.y, c.z, c.w, perm);
         *reinterpret_cast<uint4*>(z + r0) = o;
     } else {
         for (int64_t r = r0; r < rows && r < r0 + 4; ++r)
-            z[r] = morton3(x[3 * r], x[3 * r + 1], x[3 * r + 2]);
+            z[r] = morton3p(x[3 * r], x[3 * r + 1], x[3 * r + 2], perm);
     }
 }
 
-hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t s) {
+hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z,
+                              hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const int vec_ok = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
                         (reinterpret_cast<uintptr_t>(z) & 15u) == 0);
     const int64_t threads = (rows + 3) / 4;
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(zeta_morton_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                       0, s, x, rows, z, vec_ok);
+                       0, s, x, rows, z, vec_ok, perm);
     return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t s) {
+    return launch_encode_perm(x, rows, kPermIdentity, z, s);
 }
 
 }  // namespace zeta

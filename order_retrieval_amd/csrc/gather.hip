@@ -21,7 +21,10 @@ namespace zeta {
 
 // One 16-lane row (a DPP row) per query, four queries per wavefront.  Lane l owns slots l,
 // 16 + l, ...: it loads their indices and key rows and computes the weights, so all of the
-// row's index and key loads are in flight at once.  The row then walks the slots in order:
+// row's index and key loads are in flight at once.  A slot is selected when it lies within
+// min(k, keys the query may use) and holds an index >= 0 (the exact selection fills all of
+// them; the chunked and several-curve selections can leave -1 there); a query with no
+// selected slot outputs zero.  The row then walks the slots in order:
 // index and weight come from the owning lane by a DPP row broadcast, every lane loads its
 // 16-byte chunk(s) of the value row (the loads of kGatherLoads slots are issued together,
 // none waits on another load) and accumulates in fp32.
@@ -31,21 +34,23 @@ constexpr int kGatherLoads = 4;
 template <bool BF16, int CPL, int L0>
 __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
                                              int dv, const int (&coff)[CPL], int32_t jo, float so,
-                                             int left, float (&acc)[CPL][VecIO<BF16>::kElems]) {
+                                             float (&acc)[CPL][VecIO<BF16>::kElems]) {
     using IO = VecIO<BF16>;
     using R = typename IO::raw_t;
     constexpr int E = IO::kElems;
     R raw[kGatherLoads][CPL];
+    int32_t jw[kGatherLoads];
     static_for<0, kGatherLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
-        const int64_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+        jw[w] = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
+        const int64_t jr = jw[w] < 0 ? 0 : jw[w];  // an empty slot reads key 0's row, adds nothing
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + j * dv + coff[c]);
+        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + jr * dv + coff[c]);
     });
     static_for<0, kGatherLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         const float s = row_bcast<L0 + w>(so);
-        if (L0 + w < left) {  // slots past the selection read key 0's row and add nothing
+        if (jw[w] >= 0) {  // slot selected
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 float x[E];
@@ -62,7 +67,7 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ order, void* __restrict__ out, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int64_t tiles, int64_t per_xcd) {
+    int64_t H, int dv, int topk, int causal, int64_t tiles, int64_t per_xcd) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -79,30 +84,35 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
     const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
-    const int m = live ? static_cast<int>(i + 1 < topk ? i + 1 : topk) : 0;  // valid slots
+    // slots that may hold a selection: min(k, keys the query may use); empty ones hold -1
+    const int64_t nk = causal ? i + 1 : N;
+    const int m = live ? static_cast<int>(nk < topk ? nk : topk) : 0;
+    const int64_t jmax = nk - 1;
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
     int32_t jo[U];
     float so[U];
-    float ssum = 0.0f;
+    float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int r = lrow + u * kGatherLanes;
-        jo[u] = 0;
+        jo[u] = -1;
         so[u] = 0.0f;
-        if (r < m) {
-            // the selection guarantees 0 <= j <= i; clamping keeps every access in bounds
-            const int32_t jr = ir[r];
-            const int32_t j = jr < 0 ? 0 : (jr > i ? static_cast<int32_t>(i) : jr);
+        const int32_t jr = r < m ? ir[r] : -1;
+        if (jr >= 0) {
+            // a selection has j <= jmax; clamping keeps every access in bounds
+            const int32_t j = jr > jmax ? static_cast<int32_t>(jmax) : jr;
             const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
             jo[u] = j;
             so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
             ssum += so[u];
+            nsel += 1.0f;
         }
     }
     ssum = group_sum(ssum, kGatherLanes);
+    nsel = group_sum(nsel, kGatherLanes);
     // the longest selection among the wavefront's four queries sets the trip count
     int most = m;
     most = max(most, __shfl_xor(most, 16, 64));
@@ -123,14 +133,13 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
             static_for<0, kGatherLanes / kGatherLoads>([&](auto bc) {
                 constexpr int b = decltype(bc)::value;
                 if (u * kGatherLanes + b * kGatherLoads < most)
-                    gather_slots<BF16, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u],
-                                                             m - u * kGatherLanes, acc);
+                    gather_slots<BF16, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u], acc);
             });
         }
     });
 
     if (live) {
-        const float inv_S = 1.0f / ssum;
+        const float inv_S = nsel > 0.0f ? 1.0f / ssum : 0.0f;  // an empty selection outputs 0
         T* orow = static_cast<T*>(out) + row * dv;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -147,7 +156,7 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
 
 template <bool BF16, int CPL>
 static hipError_t launch_gather_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
-                                  const float* q, const float* k, const void* v,
+                                  int causal, const float* q, const float* k, const void* v,
                                   const float* gamma, const int32_t* idx, const uint32_t* order,
                                   void* out, hipStream_t s) {
     const int64_t tiles = (rows + (256 / kGatherLanes) - 1) / (256 / kGatherLanes);
@@ -157,25 +166,27 @@ static hipError_t launch_gather_c(int64_t rows, int64_t N, int64_t H, int dv, in
               : u <= 2 ? zeta_cauchy_gather_kernel<BF16, CPL, 2>
                        : zeta_cauchy_gather_kernel<BF16, CPL, 4>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, order, out, rows, N, H, dv, topk, tiles, per);
+                       gamma, idx, order, out, rows, N, H, dv, topk, causal, tiles, per);
     return hipGetLastError();
 }
 
-hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
-                         const float* q, const float* k, const void* v, const float* gamma,
-                         const int32_t* idx, const uint32_t* order, void* out, hipStream_t s) {
+hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal,
+                         bool bf16, const float* q, const float* k, const void* v,
+                         const float* gamma, const int32_t* idx, const uint32_t* order, void* out,
+                         hipStream_t s) {
+    const int cz = causal ? 1 : 0;
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const int cpl = static_cast<int>((dv / (bf16 ? 8 : 4) + kGatherLanes - 1) / kGatherLanes);
     if (bf16) {  // bf16 rows have <= 64 chunks
-        if (cpl <= 1) return launch_gather_c<true, 1>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
-        if (cpl <= 2) return launch_gather_c<true, 2>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
-        return launch_gather_c<true, 4>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+        if (cpl <= 1) return launch_gather_c<true, 1>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+        if (cpl <= 2) return launch_gather_c<true, 2>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+        return launch_gather_c<true, 4>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
     }
-    if (cpl <= 1) return launch_gather_c<false, 1>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
-    if (cpl <= 2) return launch_gather_c<false, 2>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
-    if (cpl <= 4) return launch_gather_c<false, 4>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
-    return launch_gather_c<false, 8>(rows, N, H, (int)dv, topk, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 1) return launch_gather_c<false, 1>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 2) return launch_gather_c<false, 2>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 4) return launch_gather_c<false, 4>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+    return launch_gather_c<false, 8>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
 }
 
 }  // namespace zeta

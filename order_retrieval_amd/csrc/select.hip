@@ -134,7 +134,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            int64_t rows, int64_t N, int levels,
-                                                           int topk, int32_t* __restrict__ idx) {
+                                                           int topk, int causal,
+                                                           int32_t* __restrict__ idx) {
     constexpr int E = K / L;
     const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t row = g / L;
@@ -150,9 +151,10 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
 #pragma unroll
     for (int t = 0; t < E; ++t) best[t] = ~0ull;
 
-    // The runs are the set bits of i+1, largest first, taken kSearchGroup at a time: their
-    // lower_bound searches (first entry with code >= zq) advance together.
-    const uint64_t m = static_cast<uint64_t>(i) + 1;
+    // The runs are the set bits of the number of usable keys (i+1 under the causal mask,
+    // else N), largest first, taken kSearchGroup at a time: their lower_bound searches
+    // (first entry with code >= zq) advance together.
+    const uint64_t m = causal ? static_cast<uint64_t>(i) + 1 : static_cast<uint64_t>(N);
     uint64_t rem = m;
     while (rem) {
         // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
@@ -200,29 +202,192 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
 }
 
 template <int K, int L>
-static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, const uint32_t* zq,
-                                  const uint64_t* ta, const uint64_t* td, int32_t* idx,
-                                  hipStream_t s) {
+static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, int causal,
+                                  const uint32_t* zq, const uint64_t* ta, const uint64_t* td,
+                                  int32_t* idx, hipStream_t s) {
     const int64_t blocks = (rows * L + 255) / 256;
     hipLaunchKernelGGL((zeta_select_kernel<K, L>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       s, zq, ta, td, rows, N, levels, topk, idx);
+                       s, zq, ta, td, rows, N, levels, topk, causal, idx);
     return hipGetLastError();
 }
 
-hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, const uint32_t* zq,
-                         const uint64_t* tree_asc, const uint64_t* tree_desc, int32_t* idx,
-                         hipStream_t s) {
+hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
+                         const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
+                         int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const auto* ta = tree_asc;
     const auto* td = tree_desc;
-    if (topk <= 1) return launch_select_k<1, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
-    if (topk <= 2) return launch_select_k<2, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
-    if (topk <= 4) return launch_select_k<4, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
-    if (topk <= 8) return launch_select_k<8, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1>(rows, N, levels, topk, zq, ta, td, idx, s);
-    if (topk <= 32) return launch_select_k<32, 2>(rows, N, levels, topk, zq, ta, td, idx, s);
-    return launch_select_k<64, 4>(rows, N, levels, topk, zq, ta, td, idx, s);
+    const int c = causal ? 1 : 0;
+    if (topk <= 1) return launch_select_k<1, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 32) return launch_select_k<32, 2>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    return launch_select_k<64, 4>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+}
+
+// ---------------------------------------------------------------------------- chunked
+// The pages' chunked causal search (summary page, "Approach": keys sorted and chunked so all
+// queries search in parallel under the causal mask; rebuttal page, answer W2/A2: 4 to 32
+// chunks, and the window centred at the query's insertion position in the sorted keys).
+// Chunks are the aligned blocks of 2^lvl positions, i.e. one level of the merge-sort tree
+// (ascending (code, j)).  For every chunk up to the query's own: lower_bound p of zq, the
+// window of min(k, n) sorted entries from p - floor(k/2) shifted inside the chunk, keys
+// j > i dropped.  A window is in (code, j) order, which is not (|dz|, j) order inside a
+// group of equal codes below zq, so its candidates are bitonic-sorted (descending) across
+// the query's lanes and then merged into the running top-K like a walk.
+
+// One compare-exchange layer of a bitonic sort of the K = E*L entries (entry x = lane*E + t)
+// for block size K2 and stride J; DESC sorts descending.
+template <int E, int L, int K2, int J, bool DESC>
+__device__ __forceinline__ void sort_layer(uint64_t (&a)[E], int lane) {
+    if constexpr (J >= E) {
+        const int x = lane * E;
+        const bool up = ((x & K2) == 0) != DESC;
+        cross_stage<E, J / E>(a, up == ((x & J) == 0));
+    } else {
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            if ((t & J) == 0) {
+                const int x = lane * E + t;
+                const bool up = ((x & K2) == 0) != DESC;
+                const uint64_t p = a[t], q = a[t + J];
+                const bool sw = up ? (q < p) : (p < q);
+                a[t] = sw ? q : p;
+                a[t + J] = sw ? p : q;
+            }
+        }
+    }
+    if constexpr (J > 1) sort_layer<E, L, K2, J / 2, DESC>(a, lane);
+}
+
+template <int E, int L, int K2, bool DESC>
+__device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
+    if constexpr (K2 <= E * L) {  // a single entry (K = 1) needs no layer
+        sort_layer<E, L, K2, K2 / 2, DESC>(a, lane);
+        if constexpr (K2 < E * L) sort_blocks<E, L, K2 * 2, DESC>(a, lane);
+    }
+}
+
+template <int K, int L>
+__global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
+    const uint32_t* __restrict__ zq, const uint64_t* __restrict__ tree_asc, int64_t rows,
+    int64_t N, int levels, int lvl, int topk, int32_t* __restrict__ idx) {
+    constexpr int E = K / L;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = g / L;
+    const int lane = static_cast<int>(g % L);
+    if (row >= rows) return;  // uniform over the L lanes of a query
+    const int64_t bh = row / N;
+    const int64_t i = row - bh * N;
+    const uint32_t z = zq[row];
+    const uint64_t target = static_cast<uint64_t>(z) << 32;
+    const uint64_t* run = tree_asc + bh * levels * N + static_cast<int64_t>(lvl) * N;
+    const int64_t len = int64_t(1) << lvl;
+
+    uint64_t best[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) best[t] = ~0ull;
+
+    for (int64_t c = 0; c <= i >> lvl; ++c) {
+        const int64_t lo = c * len;
+        const int64_t n = N - lo < len ? N - lo : len;
+        int64_t p = 0;  // lower_bound of zq in run[lo .. lo + n)
+        for (int64_t step = len >> 1; step > 0; step >>= 1)
+            if (p + step <= n && run[lo + p + step - 1] < target) p += step;
+        if (p < n && run[lo + p] < target) p += 1;
+        const int64_t w = topk < n ? topk : n;  // window of k entries (K pads k to a power of 2)
+        int64_t w0 = p - topk / 2;
+        if (w0 > n - w) w0 = n - w;
+        if (w0 < 0) w0 = 0;
+        uint64_t cand[E];
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            const int64_t u = lane * E + t;
+            cand[t] = ~0ull;
+            if (u < w) {
+                const uint64_t e = run[lo + w0 + u];
+                const uint32_t j = static_cast<uint32_t>(e);
+                const uint32_t code = static_cast<uint32_t>(e >> 32);
+                const uint64_t dz = code > z ? code - z : z - code;
+                if (j <= i) cand[t] = (dz << 32) | j;  // causal mask
+            }
+        }
+        sort_blocks<E, L, 2, true>(cand, lane);
+#pragma unroll
+        for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
+        bitonic_clean<E, L>(best, lane);
+    }
+
+    int32_t* out = idx + row * topk + lane * E;
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+        if (lane * E + t < topk)
+            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(static_cast<uint32_t>(best[t]));
+}
+
+template <int K, int L>
+static hipError_t launch_chunked_k(int64_t rows, int64_t N, int levels, int lvl, int topk,
+                                   const uint32_t* zq, const uint64_t* ta, int32_t* idx,
+                                   hipStream_t s) {
+    const int64_t blocks = (rows * L + 255) / 256;
+    hipLaunchKernelGGL((zeta_select_chunked_kernel<K, L>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, zq, ta, rows, N, levels, lvl, topk, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
+                                 const uint32_t* zq, const uint64_t* ta, int32_t* idx,
+                                 hipStream_t s) {
+    const int64_t rows = BH * N;
+    if (rows <= 0) return hipSuccess;
+    if (topk <= 1) return launch_chunked_k<1, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 2) return launch_chunked_k<2, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 4) return launch_chunked_k<4, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 8) return launch_chunked_k<8, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 16) return launch_chunked_k<16, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 32) return launch_chunked_k<32, 2>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    return launch_chunked_k<64, 4>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+}
+
+// ---------------------------------------------------------------------------- curves
+// Several curves (rebuttal page, on the asymmetry of interleaving: 3 or 6 coordinate orders,
+// each collecting k // P tokens).  sel[c] holds curve c's exact top-per; the result lists
+// curve 0's picks, then each later curve's picks not listed yet, in curve order, and -1 in
+// the remaining slots.  One thread per query; a pick is a repeat when an earlier curve
+// picked it (a curve's own picks are distinct).
+__global__ void __launch_bounds__(256) zeta_curves_merge_kernel(const int32_t* __restrict__ sel,
+                                                                 int64_t rows, int curves, int per,
+                                                                 int topk,
+                                                                 int32_t* __restrict__ idx) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    int32_t* out = idx + row * topk;
+    int pos = 0;
+    for (int c = 0; c < curves; ++c) {
+        const int32_t* mine = sel + (static_cast<int64_t>(c) * rows + row) * per;
+        for (int r = 0; r < per; ++r) {
+            const int32_t j = mine[r];
+            if (j < 0) continue;
+            bool seen = false;
+            for (int c2 = 0; c2 < c && !seen; ++c2) {
+                const int32_t* other = sel + (static_cast<int64_t>(c2) * rows + row) * per;
+                for (int r2 = 0; r2 < per; ++r2) seen = seen || other[r2] == j;
+            }
+            if (!seen) out[pos++] = j;
+        }
+    }
+    for (; pos < topk; ++pos) out[pos] = -1;
+}
+
+hipError_t launch_curves_merge(int64_t rows, int curves, int per, int topk, const int32_t* sel,
+                               int32_t* idx, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zeta_curves_merge_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)),
+                       dim3(256), 0, s, sel, rows, curves, per, topk, idx);
+    return hipGetLastError();
 }
 
 }  // namespace zeta

@@ -63,40 +63,119 @@ zeta_status preflight() {
     return ZETA_OK;
 }
 
-struct FwdPlan {
-    size_t zq, zk, tasc, tdesc, perm, ohist, total;
+// Resolved selection options (NULL options = exact, causal, 10 bits per axis).
+struct Opts {
+    int mode = ZETA_SELECT_EXACT;
+    bool causal = true;
+    int bits = 10;
+    int chunks = 0;
+    int curves = 0;
 };
 
-FwdPlan plan_fwd(const zeta_shape* sh) {
-    const int64_t BHN = sh->B * sh->H * sh->N;
+zeta_status resolve_opts(const zeta_select_opts* o, const zeta_shape* sh, Opts& r) {
+    r = Opts{};
+    if (!o) return ZETA_OK;
+    if (o->reserved != 0) return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.reserved must be 0");
+    if (o->causal != 0 && o->causal != 1)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.causal must be 0 or 1");
+    r.causal = o->causal == 1;
+    r.mode = o->mode;
+    r.bits = o->bits;
+    r.chunks = o->chunks;
+    r.curves = o->curves;
+    if (r.bits != 10 && r.bits != 12)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.bits must be 10 or 12");
+    if (r.bits == 12) return fail(ZETA_ERR_UNSUPPORTED, "12-bit codes are not available yet");
+    switch (r.mode) {
+        case ZETA_SELECT_EXACT:
+            break;
+        case ZETA_SELECT_CHUNKED:
+            if (!r.causal)
+                return fail(ZETA_ERR_UNSUPPORTED, "the chunked search is a causal search");
+            if (r.chunks < 1 || r.chunks > ZETA_MAX_CHUNKS)
+                return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.chunks must be in [1, ZETA_MAX_CHUNKS]");
+            break;
+        case ZETA_SELECT_CURVES:
+            if (r.curves != 3 && r.curves != 6)
+                return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.curves must be 3 or 6");
+            if (sh->topk < r.curves)
+                return fail(ZETA_ERR_INVALID_ARGUMENT, "topk must be >= opts.curves");
+            break;
+        default:
+            return fail(ZETA_ERR_INVALID_ARGUMENT, "unknown opts.mode");
+    }
+    return ZETA_OK;
+}
+
+// log2 of the chunk length: the smallest power of two L with L * chunks >= N.
+int chunk_level(int64_t N, int chunks) {
+    const int64_t want = (N + chunks - 1) / chunks;
+    int l = 0;
+    while ((int64_t(1) << l) < want) ++l;
+    return l;
+}
+
+// Tree levels a selection needs: every level of the exact search, and for the chunked
+// search also the chunk level (which is above the top level when 2^lvl > N).
+int tree_levels(const zeta_shape* sh, const Opts& o) {
     const int L = levels_of(sh->N);
+    if (o.mode == ZETA_SELECT_CHUNKED) {
+        const int need = chunk_level(sh->N, o.chunks) + 1;
+        return need > L ? need : L;
+    }
+    return L;
+}
+
+// Curve coordinate orders of the several-curve variant (rebuttal page, on the asymmetry of
+// interleaving): 3 curves (K1,K2,K3), (K2,K3,K1), (K3,K1,K2); 6 curves in the order
+// (K1,K2,K3), (K1,K3,K2), (K2,K3,K1), (K2,K1,K3), (K3,K1,K2), (K3,K2,K1).
+int curve_perm(int curves, int c) {
+    static constexpr int k3[3] = {zeta::perm_code(0, 1, 2), zeta::perm_code(1, 2, 0),
+                                  zeta::perm_code(2, 0, 1)};
+    static constexpr int k6[6] = {zeta::perm_code(0, 1, 2), zeta::perm_code(0, 2, 1),
+                                  zeta::perm_code(1, 2, 0), zeta::perm_code(1, 0, 2),
+                                  zeta::perm_code(2, 0, 1), zeta::perm_code(2, 1, 0)};
+    return curves == 3 ? k3[c] : k6[c];
+}
+
+struct FwdPlan {
+    size_t zq, zk, tasc, tdesc, perm, ohist, sel, total;
+    int levels;
+};
+
+FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
+    const int64_t BHN = sh->B * sh->H * sh->N;
     FwdPlan p{};
+    p.levels = tree_levels(sh, o);
     size_t off = 0;
-    p.zq = off;
-    off += align_up(sizeof(uint32_t) * BHN);
-    p.zk = off;
-    off += align_up(sizeof(uint32_t) * BHN);
-    p.tasc = off;
-    off += align_up(sizeof(uint64_t) * BHN * L);
-    p.tdesc = off;
-    off += align_up(sizeof(uint64_t) * BHN * L);
-    p.perm = off;
-    off += align_up(sizeof(uint32_t) * BHN);
-    p.ohist = off;
-    off += align_up(sizeof(uint32_t) * zeta::order_scratch_words(sh->B * sh->H, sh->N));
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    p.zq = take(sizeof(uint32_t) * BHN);
+    p.zk = take(sizeof(uint32_t) * BHN);
+    p.tasc = take(sizeof(uint64_t) * BHN * p.levels);
+    p.tdesc = take(sizeof(uint64_t) * BHN * p.levels);
+    p.perm = take(sizeof(uint32_t) * BHN);
+    p.ohist = take(sizeof(uint32_t) * zeta::order_scratch_words(sh->B * sh->H, sh->N));
+    // several curves: each curve's picks, [curves][BHN][topk / curves]
+    p.sel = take(o.mode == ZETA_SELECT_CURVES
+                     ? sizeof(int32_t) * BHN * static_cast<size_t>(sh->topk / o.curves) * o.curves
+                     : 0);
     p.total = off;
     return p;
 }
 
 struct BwdPlan {
-    size_t qs, dg, dgp, r0, r1, hist, totals, offs, zq, pq, zk, pk, ohist, total;
+    size_t qs, dg, dgp, r0, r1, hist, totals, counts, offs, zq, pq, zk, pk, ohist, total;
     int64_t P, tiles;
 };
 
-BwdPlan plan_bwd(const zeta_shape* sh) {
+BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
     const int64_t BH = sh->B * sh->H, N = sh->N, K = sh->topk;
     BwdPlan p{};
-    p.P = static_cast<int64_t>(zeta::bwd_pairs_per_head(N, static_cast<int>(K)));
+    p.P = static_cast<int64_t>(zeta::bwd_pairs_per_head(N, static_cast<int>(K), o.causal));
     p.tiles = zeta::bwd_tiles_per_head(N * K);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -111,6 +190,7 @@ BwdPlan plan_bwd(const zeta_shape* sh) {
     p.r1 = take(8 * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);
+    p.counts = take(sizeof(uint32_t) * BH);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
     p.zq = take(sizeof(uint32_t) * BH * N);
     p.pq = take(sizeof(uint32_t) * BH * N);
@@ -141,26 +221,45 @@ zeta_status check_qk(const float* q, const float* k) {
     return ZETA_OK;
 }
 
-zeta_status run_select(const zeta_shape* sh, const float* q, const float* k, int32_t* idx, void* ws,
-                       hipStream_t s) {
-    const FwdPlan p = plan_fwd(sh);
+// Stage marks: 0 start, 1 after encoding, 2 after the tree, 3 after the selection (several
+// curves: 1 and 2 are recorded after the first curve's encode and tree, 3 after the merge).
+zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, const float* k,
+                       int32_t* idx, void* ws, hipStream_t s) {
+    const FwdPlan p = plan_fwd(sh, o);
     const int64_t BH = sh->B * sh->H, N = sh->N, BHN = BH * N;
-    const int L = levels_of(N);
+    const int L = p.levels;
+    const int topk = static_cast<int>(sh->topk);
     uint32_t* zq = at<uint32_t>(ws, p.zq);
     uint32_t* zk = at<uint32_t>(ws, p.zk);
     uint64_t* ta = at<uint64_t>(ws, p.tasc);
     uint64_t* td = at<uint64_t>(ws, p.tdesc);
     g_marks.record(0, s);
-    hipError_t e = zeta::launch_encode(q, BHN, zq, s);
-    if (e != hipSuccess) return fail_hip("encode launch", e);
-    e = zeta::launch_encode(k, BHN, zk, s);
-    if (e != hipSuccess) return fail_hip("encode launch", e);
-    g_marks.record(1, s);
-    e = zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
-    if (e != hipSuccess) return fail_hip("tree launch", e);
-    g_marks.record(2, s);
-    e = zeta::launch_select(BH, N, L, static_cast<int>(sh->topk), zq, ta, td, idx, s);
-    if (e != hipSuccess) return fail_hip("select launch", e);
+    const int ncurves = o.mode == ZETA_SELECT_CURVES ? o.curves : 1;
+    const int per = o.mode == ZETA_SELECT_CURVES ? topk / o.curves : topk;
+    for (int c = 0; c < ncurves; ++c) {
+        const int perm = o.mode == ZETA_SELECT_CURVES ? curve_perm(o.curves, c) : zeta::kPermIdentity;
+        hipError_t e = zeta::launch_encode_perm(q, BHN, perm, zq, s);
+        if (e == hipSuccess) e = zeta::launch_encode_perm(k, BHN, perm, zk, s);
+        if (e != hipSuccess) return fail_hip("encode launch", e);
+        if (c == 0) g_marks.record(1, s);
+        e = zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
+        if (e != hipSuccess) return fail_hip("tree launch", e);
+        if (c == 0) g_marks.record(2, s);
+        if (o.mode == ZETA_SELECT_CHUNKED) {
+            e = zeta::launch_select_chunked(BH, N, L, chunk_level(N, o.chunks), topk, zq, ta, idx, s);
+        } else if (o.mode == ZETA_SELECT_CURVES) {
+            int32_t* sel = at<int32_t>(ws, p.sel) + static_cast<int64_t>(c) * BHN * per;
+            e = zeta::launch_select(BH, N, L, per, o.causal, zq, ta, td, sel, s);
+        } else {
+            e = zeta::launch_select(BH, N, L, topk, o.causal, zq, ta, td, idx, s);
+        }
+        if (e != hipSuccess) return fail_hip("select launch", e);
+    }
+    if (o.mode == ZETA_SELECT_CURVES) {
+        hipError_t e = zeta::launch_curves_merge(BHN, o.curves, per, topk, at<int32_t>(ws, p.sel),
+                                                 idx, s);
+        if (e != hipSuccess) return fail_hip("merge launch", e);
+    }
     g_marks.record(3, s);
     return ZETA_OK;
 }
@@ -169,18 +268,25 @@ zeta_status run_select(const zeta_shape* sh, const float* q, const float* k, int
 
 extern "C" {
 
-size_t zeta_workspace_bytes(const zeta_shape* shape, int32_t kind) {
+size_t zeta_workspace_bytes_ex(const zeta_shape* shape, const zeta_select_opts* opts,
+                               int32_t kind) {
     if (check_shape(shape) != ZETA_OK) return 0;
+    Opts o;
+    if (resolve_opts(opts, shape, o) != ZETA_OK) return 0;
     switch (kind) {
         case ZETA_WS_SELECT:
         case ZETA_WS_FWD:
-            return plan_fwd(shape).total;
+            return plan_fwd(shape, o).total;
         case ZETA_WS_BWD:
-            return plan_bwd(shape).total;
+            return plan_bwd(shape, o).total;
         default:
             g_last_error = "unknown workspace kind";
             return 0;
     }
+}
+
+size_t zeta_workspace_bytes(const zeta_shape* shape, int32_t kind) {
+    return zeta_workspace_bytes_ex(shape, nullptr, kind);
 }
 
 int32_t zeta_tree_levels(int64_t N) { return N < 1 ? 0 : levels_of(N); }
@@ -214,55 +320,76 @@ zeta_status zeta_build_tree(int64_t BH, int64_t N, const uint32_t* zk, uint64_t*
     return e == hipSuccess ? ZETA_OK : fail_hip("tree launch", e);
 }
 
-zeta_status zeta_select(const zeta_shape* shape, const float* q, const float* k, int32_t* idx,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+zeta_status zeta_select_ex(const zeta_shape* shape, const zeta_select_opts* opts, const float* q,
+                           const float* k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     g_last_error.clear();
     zeta_status st = check_shape(shape);
     if (st != ZETA_OK) return st;
+    Opts o;
+    if ((st = resolve_opts(opts, shape, o)) != ZETA_OK) return st;
     if ((st = check_qk(q, k)) != ZETA_OK) return st;
     if (!idx || !aligned(idx, 4)) return fail(ZETA_ERR_INVALID_ARGUMENT, "idx NULL or misaligned");
-    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape).total)) != ZETA_OK) return st;
+    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape, o).total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
-    return run_select(shape, q, k, idx, workspace, static_cast<hipStream_t>(stream));
+    return run_select(shape, o, q, k, idx, workspace, static_cast<hipStream_t>(stream));
 }
 
-zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
-                     const float* gamma, void* out, int32_t* idx, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+zeta_status zeta_select(const zeta_shape* shape, const float* q, const float* k, int32_t* idx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return zeta_select_ex(shape, nullptr, q, k, idx, workspace, workspace_bytes, stream);
+}
+
+zeta_status zeta_fwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, const float* q,
+                        const float* k, const void* v, const float* gamma, void* out,
+                        int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     zeta_status st = check_shape(shape);
     if (st != ZETA_OK) return st;
+    Opts o;
+    if ((st = resolve_opts(opts, shape, o)) != ZETA_OK) return st;
     if ((st = check_qk(q, k)) != ZETA_OK) return st;
     if (!v || !gamma || !out || !idx) return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (!aligned(v, 16) || !aligned(out, 16))
         return fail(ZETA_ERR_INVALID_ARGUMENT, "v and out must be 16-byte aligned");
     if (!aligned(gamma, 4) || !aligned(idx, 4))
         return fail(ZETA_ERR_INVALID_ARGUMENT, "gamma and idx must be 4-byte aligned");
-    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape).total)) != ZETA_OK) return st;
+    const FwdPlan p = plan_fwd(shape, o);
+    if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_select(shape, q, k, idx, workspace, s)) != ZETA_OK) return st;
-    const FwdPlan p = plan_fwd(shape);
+    if ((st = run_select(shape, o, q, k, idx, workspace, s)) != ZETA_OK) return st;
     uint32_t* perm = at<uint32_t>(workspace, p.perm);
+    // processing order from the query codes (of the last curve when there are several: the
+    // order only schedules the gather)
     hipError_t e = zeta::launch_order(shape->B * shape->H, shape->N, at<uint32_t>(workspace, p.zq),
                                       perm, at<uint32_t>(workspace, p.ohist), s);
     if (e != hipSuccess) return fail_hip("order launch", e);
     g_marks.record(4, s);
     e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
-                            static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16, q, k, v,
-                            gamma, idx, perm, out, s);
+                            static_cast<int>(shape->topk), o.causal, shape->v_dtype == ZETA_BF16, q,
+                            k, v, gamma, idx, perm, out, s);
     if (e != hipSuccess) return fail_hip("gather launch", e);
     g_marks.record(5, s);
     return ZETA_OK;
 }
 
-zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
-                     const float* gamma, const int32_t* idx, const void* dout, float* dq,
-                     float* dk, void* dv, float* dgamma, void* workspace,
+zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
+                     const float* gamma, void* out, int32_t* idx, void* workspace,
                      size_t workspace_bytes, void* stream) {
+    return zeta_fwd_ex(shape, nullptr, q, k, v, gamma, out, idx, workspace, workspace_bytes,
+                       stream);
+}
+
+zeta_status zeta_bwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, const float* q,
+                        const float* k, const void* v, const float* gamma, const int32_t* idx,
+                        const void* dout, float* dq, float* dk, void* dv, float* dgamma,
+                        void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     zeta_status st = check_shape(shape);
     if (st != ZETA_OK) return st;
+    Opts o;
+    if ((st = resolve_opts(opts, shape, o)) != ZETA_OK) return st;
     if ((st = check_qk(q, k)) != ZETA_OK) return st;
     if (!v || !gamma || !idx || !dout || !dq || !dk || !dv || !dgamma)
         return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
@@ -271,7 +398,7 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     if (!aligned(gamma, 4) || !aligned(idx, 4) || !aligned(dq, 4) || !aligned(dk, 4) ||
         !aligned(dgamma, 4))
         return fail(ZETA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-    const BwdPlan p = plan_bwd(shape);
+    const BwdPlan p = plan_bwd(shape, o);
     if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
     zeta::BwdBuffers b{};
@@ -282,6 +409,7 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     b.rec1 = at<uint2>(workspace, p.r1);
     b.hist = at<uint32_t>(workspace, p.hist);
     b.totals = at<uint32_t>(workspace, p.totals);
+    b.counts = at<uint32_t>(workspace, p.counts);
     b.offs = at<uint32_t>(workspace, p.offs);
     b.zq = at<uint32_t>(workspace, p.zq);
     b.perm_q = at<uint32_t>(workspace, p.pq);
@@ -291,10 +419,18 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
     b.P = p.P;
     b.tiles = p.tiles;
     hipError_t e = zeta::launch_bwd(shape->B * shape->H, shape->H, shape->N, shape->dv,
-                                    static_cast<int>(shape->topk), shape->v_dtype == ZETA_BF16, q, k,
-                                    v, gamma, idx, dout, dq, dk, dv, dgamma, b, g_marks,
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<int>(shape->topk), o.causal,
+                                    shape->v_dtype == ZETA_BF16, q, k, v, gamma, idx, dout, dq, dk,
+                                    dv, dgamma, b, g_marks, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZETA_OK : fail_hip("backward launch", e);
+}
+
+zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, const void* v,
+                     const float* gamma, const int32_t* idx, const void* dout, float* dq,
+                     float* dk, void* dv, float* dgamma, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    return zeta_bwd_ex(shape, nullptr, q, k, v, gamma, idx, dout, dq, dk, dv, dgamma, workspace,
+                       workspace_bytes, stream);
 }
 
 zeta_status zeta_set_stage_events(void* const* events, int32_t count) {

@@ -47,14 +47,26 @@ struct StageEvents {
 // ----------------------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launches (hipSuccess when nothing was launched).
 hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t s);
+// Curve coordinate order: axis a of the code reads coordinate (perm >> 2a) & 3.
+constexpr int perm_code(int c0, int c1, int c2) { return c0 | (c1 << 2) | (c2 << 4); }
+constexpr int kPermIdentity = perm_code(0, 1, 2);
+hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z, hipStream_t s);
 hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
                              uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
-hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, const uint32_t* zq,
-                         const uint64_t* tree_asc, const uint64_t* tree_desc, int32_t* idx,
+hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
+                         const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
+                         int32_t* idx, hipStream_t s);
+// Chunked search over the aligned chunks of 2^lvl positions (tree level lvl).
+hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
+                                 const uint32_t* zq, const uint64_t* ta, int32_t* idx,
+                                 hipStream_t s);
+// Merge of several curves' selections sel [curves][rows][per] into idx [rows][topk].
+hipError_t launch_curves_merge(int64_t rows, int curves, int per, int topk, const int32_t* sel,
+                               int32_t* idx, hipStream_t s);
+hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal,
+                         bool bf16, const float* q, const float* k, const void* v,
+                         const float* gamma, const int32_t* idx, const uint32_t* order, void* out,
                          hipStream_t s);
-hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
-                         const float* q, const float* k, const void* v, const float* gamma,
-                         const int32_t* idx, const uint32_t* order, void* out, hipStream_t s);
 // Processing order: per (b,h), positions bucketed by the top code bits (order.hip).
 // scratch: order_scratch_words(BH, N) words.
 size_t order_scratch_words(int64_t BH, int64_t N);
@@ -69,19 +81,20 @@ struct BwdBuffers {
     uint2* rec1;
     uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
     uint32_t* totals; // [BH][256] digit totals
+    uint32_t* counts; // [BH] pairs of each (b,h)
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
     uint32_t* zq;     // [BHN] query codes
     uint32_t* perm_q; // [BHN] query processing order
     uint32_t* zk;     // [BHN] key codes
     uint32_t* perm_k; // [BHN] key processing order
     uint32_t* ohist;  // order_scratch_words(BH, N) words for the processing orders
-    int64_t P;        // valid pairs per (b,h)
+    int64_t P;        // upper bound of the pairs per (b,h)
     int64_t tiles;    // radix tiles per (b,h)
 };
-size_t bwd_pairs_per_head(int64_t N, int topk);
+size_t bwd_pairs_per_head(int64_t N, int topk, bool causal);
 int64_t bwd_tiles_per_head(int64_t P);
 int64_t dgamma_chunks(int64_t B, int64_t N);
-hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool bf16,
+hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal, bool bf16,
                       const float* q, const float* k, const void* v, const float* gamma,
                       const int32_t* idx, const void* dout, float* dq, float* dk, void* dvout,
                       float* dgamma, const BwdBuffers& ws, const StageEvents& marks,

@@ -29,6 +29,11 @@ ZETA_WS_BWD = 2
 
 ZETA_MAX_TOPK = 64
 ZETA_MAX_DV = 512
+ZETA_MAX_CHUNKS = 1024
+
+ZETA_SELECT_EXACT = 0
+ZETA_SELECT_CHUNKED = 1
+ZETA_SELECT_CURVES = 2
 
 EXPORTS = (
     "zeta_workspace_bytes",
@@ -38,6 +43,10 @@ EXPORTS = (
     "zeta_select",
     "zeta_fwd",
     "zeta_bwd",
+    "zeta_workspace_bytes_ex",
+    "zeta_select_ex",
+    "zeta_fwd_ex",
+    "zeta_bwd_ex",
     "zeta_set_stage_events",
     "zeta_status_string",
     "zeta_last_error",
@@ -54,6 +63,26 @@ class ZetaShape(ctypes.Structure):
         ("v_dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
+
+
+class ZetaSelectOpts(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("chunks", ctypes.c_int32),
+        ("curves", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def select_opts(mode: int = ZETA_SELECT_EXACT, causal: bool = True, bits: int = 10,
+                chunks: int = 0, curves: int = 0) -> ZetaSelectOpts:
+    return ZetaSelectOpts(mode, int(causal), bits, chunks, curves, 0)
+
+
+def _opts_ref(opts: ZetaSelectOpts | None):
+    return ctypes.byref(opts) if opts is not None else None
 
 
 class ZetaError(RuntimeError):
@@ -88,6 +117,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeta_build_tree.restype = i32
     lib.zeta_select.argtypes = [sp, p, p, p, p, sz, p]
     lib.zeta_select.restype = i32
+    op = ctypes.POINTER(ZetaSelectOpts)
+    lib.zeta_workspace_bytes_ex.argtypes = [sp, op, i32]
+    lib.zeta_workspace_bytes_ex.restype = sz
+    lib.zeta_select_ex.argtypes = [sp, op, p, p, p, p, sz, p]
+    lib.zeta_select_ex.restype = i32
+    lib.zeta_fwd_ex.argtypes = [sp, op, p, p, p, p, p, p, p, sz, p]
+    lib.zeta_fwd_ex.restype = i32
+    lib.zeta_bwd_ex.argtypes = [sp, op, p, p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.zeta_bwd_ex.restype = i32
     lib.zeta_fwd.argtypes = [sp, p, p, p, p, p, p, p, sz, p]
     lib.zeta_fwd.restype = i32
     lib.zeta_bwd.argtypes = [sp, p, p, p, p, p, p, p, p, p, p, p, sz, p]
@@ -151,8 +189,13 @@ def zeta_workspace_bytes(shape: ZetaShape, kind: int) -> int:
     return int(load_library().zeta_workspace_bytes(ctypes.byref(shape), kind))
 
 
-def workspace(shape: ZetaShape, kind: int, device) -> torch.Tensor:
-    n = zeta_workspace_bytes(shape, kind)
+def zeta_workspace_bytes_ex(shape: ZetaShape, opts: ZetaSelectOpts | None, kind: int) -> int:
+    return int(load_library().zeta_workspace_bytes_ex(ctypes.byref(shape), _opts_ref(opts), kind))
+
+
+def workspace(shape: ZetaShape, kind: int, device,
+              opts: ZetaSelectOpts | None = None) -> torch.Tensor:
+    n = zeta_workspace_bytes_ex(shape, opts, kind)
     if n == 0:
         _check(ZETA_ERR_INVALID_ARGUMENT)
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -191,6 +234,19 @@ def _qk_shape(q: torch.Tensor, k: torch.Tensor):
     return q.shape[:3]
 
 
+def zeta_select_ex(q: torch.Tensor, k: torch.Tensor, topk: int, opts: ZetaSelectOpts | None,
+                   ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Selection (variant `opts`, None = exact causal): idx [B, H, N, topk] int32."""
+    B, H, N = _qk_shape(q, k)
+    shape = make_shape(B, H, N, 8, topk, ZETA_F32)
+    if ws is None:
+        ws = workspace(shape, ZETA_WS_SELECT, q.device, opts)
+    idx = torch.empty((B, H, N, topk), dtype=torch.int32, device=q.device)
+    _check(load_library().zeta_select_ex(ctypes.byref(shape), _opts_ref(opts), _ptr(q), _ptr(k),
+                                         _ptr(idx), _ptr(ws), ws.numel(), _stream()))
+    return idx
+
+
 def zeta_select(q: torch.Tensor, k: torch.Tensor, topk: int,
                 ws: torch.Tensor | None = None) -> torch.Tensor:
     """Exact causal top-k selection: idx [B, H, N, topk] int32, -1 padded."""
@@ -202,6 +258,55 @@ def zeta_select(q: torch.Tensor, k: torch.Tensor, topk: int,
     _check(load_library().zeta_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws),
                                       ws.numel(), _stream()))
     return idx
+
+
+def zeta_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, topk: int,
+                opts: ZetaSelectOpts | None, ws: torch.Tensor | None = None,
+                out: torch.Tensor | None = None,
+                idx: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Forward with the selection variant `opts` (None = exact causal)."""
+    B, H, N = _qk_shape(q, k)
+    _dev(v, "v")
+    _dev(gamma, "gamma", torch.float32)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, H, N) or gamma.shape != (H,):
+        raise ValueError("v must be [B, H, N, dv] and gamma [H]")
+    shape = make_shape(B, H, N, v.shape[3], topk, _v_dtype(v))
+    if ws is None:
+        ws = workspace(shape, ZETA_WS_FWD, q.device, opts)
+    if out is None:
+        out = torch.empty_like(v)
+    if idx is None:
+        idx = torch.empty((B, H, N, topk), dtype=torch.int32, device=q.device)
+    _check(load_library().zeta_fwd_ex(ctypes.byref(shape), _opts_ref(opts), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(gamma), _ptr(out), _ptr(idx), _ptr(ws),
+                                      ws.numel(), _stream()))
+    return out, idx
+
+
+def zeta_bwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                idx: torch.Tensor, dout: torch.Tensor, opts: ZetaSelectOpts | None,
+                ws: torch.Tensor | None = None, grads: tuple | None = None):
+    """Backward for a selection made with `opts` (only its causal flag matters)."""
+    B, H, N = _qk_shape(q, k)
+    _dev(v, "v")
+    _dev(gamma, "gamma", torch.float32)
+    _dev(idx, "idx", torch.int32)
+    _dev(dout, "dout", v.dtype)
+    topk = idx.shape[-1]
+    if tuple(idx.shape[:3]) != (B, H, N) or dout.shape != v.shape:
+        raise ValueError("idx must be [B, H, N, topk] and dout shaped like v")
+    shape = make_shape(B, H, N, v.shape[3], topk, _v_dtype(v))
+    if ws is None:
+        ws = workspace(shape, ZETA_WS_BWD, q.device, opts)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty((H,), dtype=torch.float32, device=q.device))
+    dq, dk, dv, dg = grads
+    _check(load_library().zeta_bwd_ex(ctypes.byref(shape), _opts_ref(opts), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(gamma), _ptr(idx), _ptr(dout), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ws), ws.numel(),
+                                      _stream()))
+    return dq, dk, dv, dg
 
 
 def zeta_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, topk: int,

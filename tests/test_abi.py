@@ -146,3 +146,66 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert st == zeta.ZETA_ERR_HIP
     assert "device" in lib.zeta_last_error().decode()
     assert lib.zeta_encode(FAKE, 10, FAKE, None) == zeta.ZETA_ERR_HIP
+
+
+# --------------------------------------------------------------------------- variant options
+def opts(**kw):
+    base = dict(mode=zeta.ZETA_SELECT_EXACT, causal=1, bits=10, chunks=0, curves=0, reserved=0)
+    base.update(kw)
+    return zeta.ZetaSelectOpts(base["mode"], base["causal"], base["bits"], base["chunks"],
+                               base["curves"], base["reserved"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(mode=3), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(bits=11), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(bits=12), zeta.ZETA_ERR_UNSUPPORTED),
+    (dict(reserved=1), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(mode=zeta.ZETA_SELECT_CHUNKED, chunks=0), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(mode=zeta.ZETA_SELECT_CHUNKED, chunks=2000), zeta.ZETA_ERR_INVALID_ARGUMENT),
+    (dict(mode=zeta.ZETA_SELECT_CHUNKED, chunks=8, causal=0), zeta.ZETA_ERR_UNSUPPORTED),
+    (dict(mode=zeta.ZETA_SELECT_CURVES, curves=4), zeta.ZETA_ERR_INVALID_ARGUMENT),
+])
+def test_invalid_options_rejected_before_launch(lib, bad, code):
+    s = shape()
+    o = opts(**bad)
+    assert lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(o), zeta.ZETA_WS_FWD) == 0
+    st = lib.zeta_select_ex(ctypes.byref(s), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code, lib.zeta_last_error()
+    st = lib.zeta_fwd_ex(ctypes.byref(s), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         1 << 40, None)
+    assert st == code
+    st = lib.zeta_bwd_ex(ctypes.byref(s), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code
+
+
+def test_curves_need_topk_of_at_least_the_curve_count(lib):
+    s = shape(topk=2)
+    o = opts(mode=zeta.ZETA_SELECT_CURVES, curves=3)
+    assert lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(o), zeta.ZETA_WS_FWD) == 0
+
+
+def test_null_options_equal_the_plain_calls(lib):
+    s = shape()
+    for kind in (zeta.ZETA_WS_SELECT, zeta.ZETA_WS_FWD, zeta.ZETA_WS_BWD):
+        assert (lib.zeta_workspace_bytes_ex(ctypes.byref(s), None, kind) ==
+                lib.zeta_workspace_bytes(ctypes.byref(s), kind) > 0)
+    # default options describe the same selection as NULL
+    o = opts()
+    assert (lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(o), zeta.ZETA_WS_FWD) ==
+            lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_FWD))
+
+
+def test_variant_workspaces(lib):
+    s = shape(N=1000, topk=32)
+    base = lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_FWD)
+    curves = opts(mode=zeta.ZETA_SELECT_CURVES, curves=3)
+    assert lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(curves), zeta.ZETA_WS_FWD) > base
+    # one chunk of 1024 positions needs a tree level above the top one of N = 1000
+    one = opts(mode=zeta.ZETA_SELECT_CHUNKED, chunks=1)
+    assert lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(one), zeta.ZETA_WS_FWD) > base
+    nc = opts(causal=0)
+    assert (lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(nc), zeta.ZETA_WS_BWD) >
+            lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_BWD))
