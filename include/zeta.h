@@ -153,6 +153,10 @@ zeta_status zeta_bwd(const zeta_shape *shape, const float *q, const float *k, co
  *                        its exact top-(k / curves); idx lists curve 0's picks, then each
  *                        later curve's picks not listed yet; -1 in the remaining slots.
  *
+ * bits = 12: the pages' own precision ([R] answer W2/A2 "Clarification of Binary Expansion
+ * and Precision": a 4096-cell grid, three 12-bit components interleaved into 36 bits held in
+ * a 64-bit integer).  Reading taken: the same fixed range [-4, 4), cell = clamp(floor(512 x)
+ * + 2048, 0, 4095), NaN -> 0; bit b of axis a -> bit 3b + a.  Any mode; needs N < 2^28.
  * A query with no selected key outputs zero and passes no gradient.  zeta_bwd_ex uses only
  * `causal` from the options: slot r of query i is used when r < min(k, i+1) (causal) or
  * r < min(k, N) and idx >= 0; entries are clamped to the last usable key.
@@ -169,7 +173,7 @@ typedef enum zeta_select_mode {
 typedef struct zeta_select_opts {
     int32_t mode;     /* zeta_select_mode                                                   */
     int32_t causal;   /* 1: keys j <= i;  0: every key j < N (EXACT and CURVES only)        */
-    int32_t bits;     /* bits per axis of the codes: 10 (12: ZETA_ERR_UNSUPPORTED for now)   */
+    int32_t bits;     /* bits per axis of the codes: 10, or 12 (N < 2^28)                   */
     int32_t chunks;   /* CHUNKED: number of chunks C, 1 <= C <= ZETA_MAX_CHUNKS              */
     int32_t curves;   /* CURVES: 3 or 6 (and topk >= curves)                                */
     int32_t reserved; /* must be 0                                                          */

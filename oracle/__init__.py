@@ -60,7 +60,8 @@ def _load():
         lib.oracle_chunk_len.argtypes = [i64, i64]
         lib.oracle_chunk_len.restype = i64
         lib.oracle_select_chunked.argtypes = [i64, i64, i64, p, p, i64, p, p]
-        lib.oracle_select_multi.argtypes = [i64, i64, i64, i64, ctypes.c_int, p, p, i64, p, p]
+        lib.oracle_select_multi.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, p, p,
+                                            i64, p, p]
         lib.oracle_euclid_topk.argtypes = [i64, i64, ctypes.c_int, p, p, i64, p, p]
         lib.oracle_bf16_bits.argtypes = [ctypes.c_double]
         lib.oracle_bf16_bits.restype = ctypes.c_uint16
@@ -161,9 +162,10 @@ def chunk_len(N: int, chunks: int) -> int:
 
 
 def select_chunked(zq, zk, N: int, topk: int, chunks: int, rows=None) -> np.ndarray:
-    """The chunked causal search (window around the insertion position in each chunk)."""
-    zq = np.ascontiguousarray(zq, dtype=np.uint32).reshape(-1)
-    zk = np.ascontiguousarray(zk, dtype=np.uint32).reshape(-1)
+    """The chunked causal search (window around the insertion position in each chunk) on
+    10- or 12-bit codes."""
+    zq = np.ascontiguousarray(zq, dtype=np.uint64).reshape(-1)
+    zk = np.ascontiguousarray(zk, dtype=np.uint64).reshape(-1)
     r = _rows(rows, zq.size)
     idx = np.empty((r.size, topk), dtype=np.int32)
     _load().oracle_select_chunked(N, topk, chunks, _ptr(zq), _ptr(zk), r.size, _ptr(r),
@@ -171,15 +173,16 @@ def select_chunked(zq, zk, N: int, topk: int, chunks: int, rows=None) -> np.ndar
     return idx
 
 
-def select_multi(q, k, topk: int, curves: int, causal: bool = True, rows=None) -> np.ndarray:
+def select_multi(q, k, topk: int, curves: int, causal: bool = True, rows=None,
+                 bits: int = 10) -> np.ndarray:
     """Several curves (3 or 6 axis orders), each its own top-(topk // curves), merged."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     B, H, N, _ = q.shape
     r = _rows(rows, B * H * N)
     idx = np.empty((r.size, topk), dtype=np.int32)
-    _load().oracle_select_multi(B * H, N, topk, curves, int(causal), _ptr(q), _ptr(k), r.size,
-                                _ptr(r), _ptr(idx))
+    _load().oracle_select_multi(B * H, N, topk, curves, int(causal), int(bits), _ptr(q), _ptr(k),
+                                r.size, _ptr(r), _ptr(idx))
     return idx
 
 

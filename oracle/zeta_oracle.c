@@ -237,8 +237,8 @@ static int cmp_code_j(const void *a, const void *b)
  *     holds any);
  *   - the result is the first min(K, candidates) candidates by (|dz|, j), -1 padded.
  * Windows of different chunks never share a key, so no candidate repeats.                */
-void oracle_select_chunked(int64_t N, int64_t K, int64_t C, const uint32_t *zq,
-                           const uint32_t *zk, int64_t nrows, const int64_t *rows, int32_t *idx)
+void oracle_select_chunked(int64_t N, int64_t K, int64_t C, const uint64_t *zq,
+                           const uint64_t *zk, int64_t nrows, const int64_t *rows, int32_t *idx)
 {
     int64_t L = oracle_chunk_len(N, C);
 #pragma omp parallel
@@ -283,14 +283,15 @@ void oracle_select_chunked(int64_t N, int64_t K, int64_t C, const uint32_t *zq,
  * remove the asymmetry"): 3 curves with the coordinates in the orders (K1,K2,K3),
  * (K2,K3,K1), (K3,K1,K2), or 6 curves with all six orders (K1,K2,K3), (K1,K3,K2),
  * (K2,K3,K1), (K2,K1,K3), (K3,K1,K2), (K3,K2,K1); every curve collects k // P tokens.
- * Reading taken: curve p selects its own exact top-(K / P) (causal or not) on its codes;
+ * Reading taken: curve p selects its own exact top-(K / P) (causal or not) on its codes
+ * (10- or 12-bit cells);
  * the result lists curve 0's picks, then each later curve's picks that are not yet listed,
  * each curve in its own (|dz|, j) order; the rest of the K slots are -1.                  */
 static const int32_t kPerm3[3][3] = {{0, 1, 2}, {1, 2, 0}, {2, 0, 1}};
 static const int32_t kPerm6[6][3] = {{0, 1, 2}, {0, 2, 1}, {1, 2, 0},
                                      {1, 0, 2}, {2, 0, 1}, {2, 1, 0}};
 
-void oracle_select_multi(int64_t BH, int64_t N, int64_t K, int64_t P, int causal,
+void oracle_select_multi(int64_t BH, int64_t N, int64_t K, int64_t P, int causal, int bits,
                          const float *q, const float *k, int64_t nrows, const int64_t *rows,
                          int32_t *idx)
 {
@@ -302,8 +303,8 @@ void oracle_select_multi(int64_t BH, int64_t N, int64_t K, int64_t P, int causal
     int64_t *fill = (int64_t *)calloc((size_t)nrows, sizeof(int64_t));
     for (int64_t c = 0; c < P && per > 0; ++c) {
         const int32_t *perm = P == 3 ? kPerm3[c] : kPerm6[c];
-        oracle_encode_ex(q, BH * N, 10, perm, zq);
-        oracle_encode_ex(k, BH * N, 10, perm, zk);
+        oracle_encode_ex(q, BH * N, bits, perm, zq);
+        oracle_encode_ex(k, BH * N, bits, perm, zk);
         oracle_select_codes64(N, per, causal, zq, zk, nrows, rows, sel);
         for (int64_t t = 0; t < nrows; ++t) {
             for (int64_t r = 0; r < per; ++r) {

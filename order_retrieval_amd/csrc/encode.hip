@@ -81,6 +81,46 @@ hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* 
     return hipGetLastError();
 }
 
+// 12-bit cells (rebuttal page, answer W2/A2: a grid of 4096 cells per coordinate, three
+// 12-bit components interleaved into 36 bits held in a 64-bit integer).  Same fixed range
+// [-4, 4): cell = clamp(floor(512 x) + 2048, 0, 4095), NaN -> 0 (512 x is exact in fp32).
+__device__ __forceinline__ uint32_t cell12(float x) {
+    if (!(x == x)) return 0u;  // NaN
+    x = fminf(fmaxf(x, -4.0f), 4.0f);
+    int c = static_cast<int>(floorf(x * 512.0f)) + 2048;
+    return static_cast<uint32_t>(c > 4095 ? 4095 : c);
+}
+
+// Bit b of a 12-bit cell -> bit 3b (the low 10 bits as for 10-bit cells, then bits 10, 11).
+__device__ __forceinline__ uint64_t spread3_12(uint32_t v) {
+    return static_cast<uint64_t>(spread3(v & 1023u)) |
+           (static_cast<uint64_t>((v >> 10) & 1u) << 30) |
+           (static_cast<uint64_t>((v >> 11) & 1u) << 33);
+}
+
+__device__ __forceinline__ uint64_t morton3_12(float x0, float x1, float x2) {
+    return spread3_12(cell12(x0)) | (spread3_12(cell12(x1)) << 1) | (spread3_12(cell12(x2)) << 2);
+}
+
+__global__ void __launch_bounds__(256) zeta_morton36_encode_kernel(const float* __restrict__ x,
+                                                                    int64_t rows,
+                                                                    uint64_t* __restrict__ z,
+                                                                    int perm) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const float x0 = x[3 * r], x1 = x[3 * r + 1], x2 = x[3 * r + 2];
+    z[r] = morton3_12(axis_of(x0, x1, x2, perm, 0), axis_of(x0, x1, x2, perm, 1),
+                      axis_of(x0, x1, x2, perm, 2));
+}
+
+hipError_t launch_encode36_perm(const float* x, int64_t rows, int perm, uint64_t* z,
+                                hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zeta_morton36_encode_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)),
+                       dim3(256), 0, s, x, rows, z, perm);
+    return hipGetLastError();
+}
+
 hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t s) {
     return launch_encode_perm(x, rows, kPermIdentity, z, s);
 }

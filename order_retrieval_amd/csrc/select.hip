@@ -91,13 +91,13 @@ __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
 // position p + c (right walk, asc tree, key = e - target) or p - 1 - c (left walk, desc
 // tree, key = (target | 0xffffffff) - e).  Lane `lane` of the query holds list entries
 // [lane*E, lane*E + E) and pairs them with candidates K-1-t, i.e. its own block of E.
-template <int K, int L, bool RIGHT>
+template <int K, int L, bool RIGHT, int S>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
                                            int64_t roff, int64_t p, int64_t s, uint64_t target,
                                            int lane) {
     const uint64_t* run = tree + roff;
     constexpr int E = K / L;
-    const uint64_t top = target | 0xffffffffull;
+    const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
     // skip when the walk is empty or its first candidate does not beat the current K-th
     const bool empty = RIGHT ? p >= s : p <= 0;
     const uint64_t first = empty ? ~0ull : (RIGHT ? run[p] - target : top - run[p - 1]);
@@ -129,8 +129,10 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     bitonic_clean<E, L>(best, lane);
 }
 
-template <int K, int L>
-__global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __restrict__ zq,
+// CT, S: code type and position bits of the packed tree entries (uint32_t, 32 for 30-bit
+// codes; uint64_t, 28 for the 36-bit codes of 12-bit cells).
+template <int K, int L, typename CT, int S>
+__global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__ zq,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            int64_t rows, int64_t N, int levels,
@@ -143,7 +145,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
     if (row >= rows) return;  // uniform over the L lanes of a query
     const int64_t bh = row / N;
     const int64_t i = row - bh * N;
-    const uint64_t target = static_cast<uint64_t>(zq[row]) << 32;
+    constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
+    const uint64_t target = static_cast<uint64_t>(zq[row]) << S;
     const uint64_t* hA = tree_asc + bh * levels * N;
     const uint64_t* hD = tree_desc + bh * levels * N;
 
@@ -188,8 +191,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
         for (int gi = 0; gi < kSearchGroup; ++gi) {
             if (lv[gi] >= 0) {
                 const int64_t s = int64_t(1) << lv[gi];
-                merge_walk<K, L, true>(best, hA, roff[gi], pos[gi], s, target, lane);
-                merge_walk<K, L, false>(best, hD, roff[gi], pos[gi], s, target, lane);
+                merge_walk<K, L, true, S>(best, hA, roff[gi], pos[gi], s, target, lane);
+                merge_walk<K, L, false, S>(best, hD, roff[gi], pos[gi], s, target, lane);
             }
         }
     }
@@ -198,34 +201,45 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const uint32_t* __rest
 #pragma unroll
     for (int t = 0; t < E; ++t)
         if (lane * E + t < topk)
-            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(static_cast<uint32_t>(best[t]));
+            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(best[t] & kJMask);
 }
 
-template <int K, int L>
+template <int K, int L, typename CT, int S>
 static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, int causal,
-                                  const uint32_t* zq, const uint64_t* ta, const uint64_t* td,
+                                  const CT* zq, const uint64_t* ta, const uint64_t* td,
                                   int32_t* idx, hipStream_t s) {
     const int64_t blocks = (rows * L + 255) / 256;
-    hipLaunchKernelGGL((zeta_select_kernel<K, L>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       s, zq, ta, td, rows, N, levels, topk, causal, idx);
+    hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, zq, ta, td, rows, N, levels, topk, causal, idx);
     return hipGetLastError();
+}
+
+template <typename CT, int S>
+static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool causal,
+                           const CT* zq, const uint64_t* ta, const uint64_t* td, int32_t* idx,
+                           hipStream_t s) {
+    const int64_t rows = BH * N;
+    if (rows <= 0) return hipSuccess;
+    const int c = causal ? 1 : 0;
+    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 32) return launch_select_k<32, 2, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
 }
 
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
                          const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
                          int32_t* idx, hipStream_t s) {
-    const int64_t rows = BH * N;
-    if (rows <= 0) return hipSuccess;
-    const auto* ta = tree_asc;
-    const auto* td = tree_desc;
-    const int c = causal ? 1 : 0;
-    if (topk <= 1) return launch_select_k<1, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 2) return launch_select_k<2, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 4) return launch_select_k<4, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 8) return launch_select_k<8, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 32) return launch_select_k<32, 2>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    return launch_select_k<64, 4>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, idx, s);
+}
+
+hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
+                           const uint64_t* zq, const uint64_t* tree_asc,
+                           const uint64_t* tree_desc, int32_t* idx, hipStream_t s) {
+    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, idx, s);
 }
 
 // ---------------------------------------------------------------------------- chunked
@@ -271,19 +285,20 @@ __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
     }
 }
 
-template <int K, int L>
+template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
-    const uint32_t* __restrict__ zq, const uint64_t* __restrict__ tree_asc, int64_t rows,
+    const CT* __restrict__ zq, const uint64_t* __restrict__ tree_asc, int64_t rows,
     int64_t N, int levels, int lvl, int topk, int32_t* __restrict__ idx) {
     constexpr int E = K / L;
+    constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t row = g / L;
     const int lane = static_cast<int>(g % L);
     if (row >= rows) return;  // uniform over the L lanes of a query
     const int64_t bh = row / N;
     const int64_t i = row - bh * N;
-    const uint32_t z = zq[row];
-    const uint64_t target = static_cast<uint64_t>(z) << 32;
+    const uint64_t z = zq[row];
+    const uint64_t target = z << S;
     const uint64_t* run = tree_asc + bh * levels * N + static_cast<int64_t>(lvl) * N;
     const int64_t len = int64_t(1) << lvl;
 
@@ -309,10 +324,10 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
             cand[t] = ~0ull;
             if (u < w) {
                 const uint64_t e = run[lo + w0 + u];
-                const uint32_t j = static_cast<uint32_t>(e);
-                const uint32_t code = static_cast<uint32_t>(e >> 32);
+                const uint64_t j = e & kJMask;
+                const uint64_t code = e >> S;
                 const uint64_t dz = code > z ? code - z : z - code;
-                if (j <= i) cand[t] = (dz << 32) | j;  // causal mask
+                if (static_cast<int64_t>(j) <= i) cand[t] = (dz << S) | j;  // causal mask
             }
         }
         sort_blocks<E, L, 2, true>(cand, lane);
@@ -325,31 +340,43 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 #pragma unroll
     for (int t = 0; t < E; ++t)
         if (lane * E + t < topk)
-            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(static_cast<uint32_t>(best[t]));
+            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(best[t] & kJMask);
 }
 
-template <int K, int L>
+template <int K, int L, typename CT, int S>
 static hipError_t launch_chunked_k(int64_t rows, int64_t N, int levels, int lvl, int topk,
-                                   const uint32_t* zq, const uint64_t* ta, int32_t* idx,
+                                   const CT* zq, const uint64_t* ta, int32_t* idx,
                                    hipStream_t s) {
     const int64_t blocks = (rows * L + 255) / 256;
-    hipLaunchKernelGGL((zeta_select_chunked_kernel<K, L>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((zeta_select_chunked_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, s, zq, ta, rows, N, levels, lvl, topk, idx);
     return hipGetLastError();
+}
+
+template <typename CT, int S>
+static hipError_t chunked_t(int64_t BH, int64_t N, int levels, int lvl, int topk, const CT* zq,
+                            const uint64_t* ta, int32_t* idx, hipStream_t s) {
+    const int64_t rows = BH * N;
+    if (rows <= 0) return hipSuccess;
+    if (topk <= 1) return launch_chunked_k<1, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 2) return launch_chunked_k<2, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 4) return launch_chunked_k<4, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 8) return launch_chunked_k<8, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 16) return launch_chunked_k<16, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 32) return launch_chunked_k<32, 2, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    return launch_chunked_k<64, 4, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
 }
 
 hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
                                  const uint32_t* zq, const uint64_t* ta, int32_t* idx,
                                  hipStream_t s) {
-    const int64_t rows = BH * N;
-    if (rows <= 0) return hipSuccess;
-    if (topk <= 1) return launch_chunked_k<1, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 2) return launch_chunked_k<2, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 4) return launch_chunked_k<4, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 8) return launch_chunked_k<8, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 16) return launch_chunked_k<16, 1>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 32) return launch_chunked_k<32, 2>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    return launch_chunked_k<64, 4>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    return chunked_t<uint32_t, 32>(BH, N, levels, lvl, topk, zq, ta, idx, s);
+}
+
+hipError_t launch_select_chunked36(int64_t BH, int64_t N, int levels, int lvl, int topk,
+                                   const uint64_t* zq, const uint64_t* ta, int32_t* idx,
+                                   hipStream_t s) {
+    return chunked_t<uint64_t, 28>(BH, N, levels, lvl, topk, zq, ta, idx, s);
 }
 
 // ---------------------------------------------------------------------------- curves

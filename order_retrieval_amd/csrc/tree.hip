@@ -9,9 +9,10 @@
 // union of at most log2(N)+1 such blocks.
 //
 // Two trees are built from the same codes with different packed keys, both sorted as plain
-// ascending uint64:
-//   asc : (code << 32) | j          -> code ascending, j ascending
-//   desc: (code << 32) | ~j         -> code ascending, j descending
+// ascending uint64 (S = 32 for 30-bit codes; S = 28 for the 36-bit codes of 12-bit cells,
+// which holds positions below 2^28):
+//   asc : (code << S) | j           -> code ascending, j ascending
+//   desc: (code << S) | (~j mod 2^S) -> code ascending, j descending
 // The selection kernel walks the asc tree forward (codes >= the query) and the desc tree
 // backward (codes < the query), so both walks meet equal codes in ascending j order.
 //
@@ -41,22 +42,24 @@ __device__ __forceinline__ int lds_lower_bound(const uint64_t* a, int n, uint64_
     return lo;
 }
 
-__global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const uint32_t* __restrict__ zk,
+template <typename CT, int S>
+__global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const CT* __restrict__ zk,
                                                               uint64_t* __restrict__ asc,
                                                               uint64_t* __restrict__ desc,
                                                               int64_t N, int levels, int top) {
+    constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     __shared__ uint64_t buf[2][2][kTile];  // [tree][ping-pong][entry]
     const int64_t bh = blockIdx.y;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
     const int n = static_cast<int>(N - base < kTile ? N - base : kTile);
-    const uint32_t* zrow = zk + bh * N + base;
+    const CT* zrow = zk + bh * N + base;
     uint64_t* tA = asc + bh * levels * N + base;
     uint64_t* tD = desc + bh * levels * N + base;
 
     for (int e = threadIdx.x; e < n; e += blockDim.x) {
-        const uint32_t j = static_cast<uint32_t>(base + e);
-        const uint64_t c = static_cast<uint64_t>(zrow[e]) << 32;
-        const uint64_t ka = c | j, kd = c | static_cast<uint32_t>(~j);
+        const uint64_t j = static_cast<uint64_t>(base + e);
+        const uint64_t c = static_cast<uint64_t>(zrow[e]) << S;
+        const uint64_t ka = c | j, kd = c | (~j & kJMask);
         buf[0][0][e] = ka;
         buf[1][0][e] = kd;
         tA[e] = ka;
@@ -156,13 +159,14 @@ __global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restri
     }
 }
 
-hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
-                             uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
+template <typename CT, int S>
+static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, const CT* zk,
+                               uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
     if (BH <= 0 || N <= 0) return hipSuccess;
     const int top_tile = levels - 1 < kTileLog ? levels - 1 : kTileLog;
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
-    hipLaunchKernelGGL(zeta_tree_tile_kernel, grid, dim3(256), 0, s, zk, tree_asc, tree_desc,
-                       N, levels, top_tile);
+    hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(256), 0, s, zk, tree_asc,
+                       tree_desc, N, levels, top_tile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int l = top_tile; l + 1 < levels; ++l) {
@@ -174,6 +178,16 @@ hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
+                             uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
+    return build_tree_t<uint32_t, 32>(BH, N, levels, zk, tree_asc, tree_desc, s);
+}
+
+hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, const uint64_t* zk,
+                               uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
+    return build_tree_t<uint64_t, 28>(BH, N, levels, zk, tree_asc, tree_desc, s);
 }
 
 }  // namespace zeta

@@ -85,7 +85,8 @@ zeta_status resolve_opts(const zeta_select_opts* o, const zeta_shape* sh, Opts& 
     r.curves = o->curves;
     if (r.bits != 10 && r.bits != 12)
         return fail(ZETA_ERR_INVALID_ARGUMENT, "opts.bits must be 10 or 12");
-    if (r.bits == 12) return fail(ZETA_ERR_UNSUPPORTED, "12-bit codes are not available yet");
+    if (r.bits == 12 && sh->N >= (int64_t(1) << 28))
+        return fail(ZETA_ERR_UNSUPPORTED, "12-bit codes need N < 2^28");
     switch (r.mode) {
         case ZETA_SELECT_EXACT:
             break;
@@ -153,8 +154,9 @@ FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
         off += align_up(bytes);
         return at;
     };
-    p.zq = take(sizeof(uint32_t) * BHN);
-    p.zk = take(sizeof(uint32_t) * BHN);
+    const size_t code_bytes = o.bits == 12 ? sizeof(uint64_t) : sizeof(uint32_t);
+    p.zq = take(code_bytes * BHN);
+    p.zk = take(code_bytes * BHN);
     p.tasc = take(sizeof(uint64_t) * BHN * p.levels);
     p.tdesc = take(sizeof(uint64_t) * BHN * p.levels);
     p.perm = take(sizeof(uint32_t) * BHN);
@@ -236,22 +238,38 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
     g_marks.record(0, s);
     const int ncurves = o.mode == ZETA_SELECT_CURVES ? o.curves : 1;
     const int per = o.mode == ZETA_SELECT_CURVES ? topk / o.curves : topk;
+    const bool wide = o.bits == 12;  // 36-bit codes
+    uint64_t* zq64 = at<uint64_t>(ws, p.zq);
+    uint64_t* zk64 = at<uint64_t>(ws, p.zk);
     for (int c = 0; c < ncurves; ++c) {
         const int perm = o.mode == ZETA_SELECT_CURVES ? curve_perm(o.curves, c) : zeta::kPermIdentity;
-        hipError_t e = zeta::launch_encode_perm(q, BHN, perm, zq, s);
-        if (e == hipSuccess) e = zeta::launch_encode_perm(k, BHN, perm, zk, s);
+        hipError_t e;
+        if (wide) {
+            e = zeta::launch_encode36_perm(q, BHN, perm, zq64, s);
+            if (e == hipSuccess) e = zeta::launch_encode36_perm(k, BHN, perm, zk64, s);
+        } else {
+            e = zeta::launch_encode_perm(q, BHN, perm, zq, s);
+            if (e == hipSuccess) e = zeta::launch_encode_perm(k, BHN, perm, zk, s);
+        }
         if (e != hipSuccess) return fail_hip("encode launch", e);
         if (c == 0) g_marks.record(1, s);
-        e = zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
+        e = wide ? zeta::launch_build_tree36(BH, N, L, zk64, ta, td, s)
+                 : zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
         if (e != hipSuccess) return fail_hip("tree launch", e);
         if (c == 0) g_marks.record(2, s);
+        int32_t* dst = idx;
+        int kk = topk;
+        if (o.mode == ZETA_SELECT_CURVES) {
+            dst = at<int32_t>(ws, p.sel) + static_cast<int64_t>(c) * BHN * per;
+            kk = per;
+        }
         if (o.mode == ZETA_SELECT_CHUNKED) {
-            e = zeta::launch_select_chunked(BH, N, L, chunk_level(N, o.chunks), topk, zq, ta, idx, s);
-        } else if (o.mode == ZETA_SELECT_CURVES) {
-            int32_t* sel = at<int32_t>(ws, p.sel) + static_cast<int64_t>(c) * BHN * per;
-            e = zeta::launch_select(BH, N, L, per, o.causal, zq, ta, td, sel, s);
+            const int lvl = chunk_level(N, o.chunks);
+            e = wide ? zeta::launch_select_chunked36(BH, N, L, lvl, topk, zq64, ta, idx, s)
+                     : zeta::launch_select_chunked(BH, N, L, lvl, topk, zq, ta, idx, s);
         } else {
-            e = zeta::launch_select(BH, N, L, topk, o.causal, zq, ta, td, idx, s);
+            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, ta, td, dst, s)
+                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, ta, td, dst, s);
         }
         if (e != hipSuccess) return fail_hip("select launch", e);
     }
@@ -361,9 +379,14 @@ zeta_status zeta_fwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     if ((st = run_select(shape, o, q, k, idx, workspace, s)) != ZETA_OK) return st;
     uint32_t* perm = at<uint32_t>(workspace, p.perm);
     // processing order from the query codes (of the last curve when there are several: the
-    // order only schedules the gather)
-    hipError_t e = zeta::launch_order(shape->B * shape->H, shape->N, at<uint32_t>(workspace, p.zq),
-                                      perm, at<uint32_t>(workspace, p.ohist), s);
+    // order only schedules the gather); with 12-bit cells the 10-bit codes are written over
+    // the 36-bit ones first (the order buckets by the top code bits, which they share)
+    uint32_t* zo = at<uint32_t>(workspace, p.zq);
+    hipError_t e = hipSuccess;
+    if (o.bits == 12) e = zeta::launch_encode(q, shape->B * shape->H * shape->N, zo, s);
+    if (e == hipSuccess)
+        e = zeta::launch_order(shape->B * shape->H, shape->N, zo, perm,
+                               at<uint32_t>(workspace, p.ohist), s);
     if (e != hipSuccess) return fail_hip("order launch", e);
     g_marks.record(4, s);
     e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,

@@ -53,6 +53,17 @@ constexpr int kPermIdentity = perm_code(0, 1, 2);
 hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z, hipStream_t s);
 hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
                              uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
+// 12-bit cells: 36-bit codes (uint64), tree entries (code << 28) | j, N < 2^28.
+hipError_t launch_encode36_perm(const float* x, int64_t rows, int perm, uint64_t* z,
+                                hipStream_t s);
+hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, const uint64_t* zk,
+                               uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
+hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
+                           const uint64_t* zq, const uint64_t* tree_asc,
+                           const uint64_t* tree_desc, int32_t* idx, hipStream_t s);
+hipError_t launch_select_chunked36(int64_t BH, int64_t N, int levels, int lvl, int topk,
+                                   const uint64_t* zq, const uint64_t* ta, int32_t* idx,
+                                   hipStream_t s);
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
                          const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
                          int32_t* idx, hipStream_t s);

@@ -160,7 +160,6 @@ def opts(**kw):
     (dict(mode=3), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(causal=2), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(bits=11), zeta.ZETA_ERR_INVALID_ARGUMENT),
-    (dict(bits=12), zeta.ZETA_ERR_UNSUPPORTED),
     (dict(reserved=1), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(mode=zeta.ZETA_SELECT_CHUNKED, chunks=0), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(mode=zeta.ZETA_SELECT_CHUNKED, chunks=2000), zeta.ZETA_ERR_INVALID_ARGUMENT),

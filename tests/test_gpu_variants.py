@@ -263,3 +263,91 @@ def test_variant_deterministic():
         res.append([to_np(t).copy() for t in (out, idx) + tuple(g)])
     for a, b in zip(*res):
         np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- 12-bit cells
+KINDS12 = [("exact", True), ("exact", False), ("chunked", 4), ("curves", 3, True)]
+
+
+def opts12(kind):
+    o = opts_of(kind)
+    o.bits = 12
+    return o
+
+
+def oracle_select12(kind, x, topk, rows=None):
+    q, k = x["q"], x["k"]
+    N = q.shape[2]
+    if kind[0] == "exact":
+        return oracle.select_ex(q, k, topk, 12, causal=kind[1], rows=rows)
+    if kind[0] == "chunked":
+        return oracle.select_chunked(oracle.encode_ex(q, 12), oracle.encode_ex(k, 12), N, topk,
+                                     kind[1], rows=rows)
+    return oracle.select_multi(q, k, topk, kind[1], causal=kind[2], rows=rows, bits=12)
+
+
+def _select12_check(w, kind, rows=None):
+    x = inputs.make_inputs(w)
+    idx = Z.zeta_select_ex(to_dev(x["q"]), to_dev(x["k"]), w.topk, opts12(kind))
+    torch.cuda.synchronize()
+    got = to_np(idx).reshape(-1, w.topk)
+    np.testing.assert_array_equal(got if rows is None else got[rows],
+                                  oracle_select12(kind, x, w.topk, rows))
+
+
+@pytest.mark.parametrize("kind", KINDS12, ids=_name)
+@pytest.mark.parametrize("name", ["tiny", "multihead", "clustered_small"])
+def test_12bit_select_bit_exact(name, kind):
+    w = CFG[name] if name != "clustered_small" else W("c12", 2, 2, 3000, 8, 64, dist="clustered",
+                                                     seed=31)
+    log(f"12-bit select {name} {kind}")
+    _select12_check(w, kind)
+
+
+@pytest.mark.parametrize("B,H,N,topk,dist", [
+    (1, 1, 1, 1, "normal"), (2, 1, 3, 4, "discrete"), (1, 2, 777, 5, "clustered"),
+    (2, 2, 1025, 64, "discrete"), (1, 1, 2049, 16, "constant"),
+])
+@pytest.mark.parametrize("kind", KINDS12, ids=_name)
+def test_12bit_select_edge_shapes(B, H, N, topk, dist, kind):
+    if kind[0] == "curves" and topk < kind[1]:
+        pytest.skip("topk below the curve count is rejected")
+    log(f"12-bit select edge B={B} H={H} N={N} k={topk} {dist} {kind}")
+    _select12_check(W("v12", B, H, N, 8, topk, dist=dist, seed=N + topk), kind)
+
+
+def test_12bit_select_sampled_long():
+    w = CFG["long_fwd"]
+    rows = sample_rows(w, 400, seed=12)
+    log(f"12-bit select long: {rows.size} rows")
+    _select12_check(w, ("exact", True), rows)
+
+
+@pytest.mark.parametrize("kind", [("exact", True), ("chunked", 4)], ids=_name)
+def test_12bit_forward_backward_full(kind):
+    w = inputs.Workload(**{**CFG["tiny"].__dict__, "backward": True})
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    o = opts12(kind)
+    out, idx = Z.zeta_fwd_ex(d["q"], d["k"], d["v"], d["gamma"], w.topk, o)
+    dq, dk, dv, dg = Z.zeta_bwd_ex(d["q"], d["k"], d["v"], d["gamma"], idx, d["dout"], o)
+    torch.cuda.synchronize()
+    ref_idx = oracle_select12(kind, x, w.topk)
+    np.testing.assert_array_equal(to_np(idx).reshape(-1, w.topk), ref_idx)
+    ref = oracle.forward(x["q"], x["k"], x["v"], x["gamma"], ref_idx, False)
+    assert_close(to_np(out).reshape(-1, w.dv), ref, w.v_dtype, f"o 12-bit {kind}")
+    rq, rk, rv, rg = oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], ref_idx, False)
+    assert_close(to_np(dq).reshape(-1, 3), rq, w.v_dtype, f"dq 12-bit {kind}")
+    assert_close(to_np(dk), rk, w.v_dtype, f"dk 12-bit {kind}")
+    assert_close(to_np(dv), rv, w.v_dtype, f"dv 12-bit {kind}")
+    assert_close(to_np(dg), rg, w.v_dtype, f"dgamma 12-bit {kind}")
+
+
+def test_12bit_differs_from_10bit_where_cells_split():
+    """The finer grid separates points that share a 10-bit cell, so the two selections
+    differ on clustered data (and each matches its own oracle above)."""
+    w = W("split", 1, 1, 2000, 8, 16, dist="clustered", seed=33)
+    x = inputs.make_inputs(w)
+    a = to_np(Z.zeta_select_ex(to_dev(x["q"]), to_dev(x["k"]), w.topk, opts_of(("exact", True))))
+    b = to_np(Z.zeta_select_ex(to_dev(x["q"]), to_dev(x["k"]), w.topk, opts12(("exact", True))))
+    assert (a != b).any()

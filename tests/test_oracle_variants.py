@@ -119,6 +119,10 @@ def test_multi_curve_hand_examples(golden_dir):
         k = np.array(c["kp"], dtype=np.float32)[None, None]
         idx = oracle.select_multi(q, k, c["k"], c["P"])
         np.testing.assert_array_equal(idx, np.array(c["rows"]), err_msg=c["name"])
+        # 12-bit cells: coordinates 0 and 1/512 are cells 2048 and 2049, whose codes differ
+        # by the same low offsets, so the same selection follows
+        idx12 = oracle.select_multi(q / 4, k / 4, c["k"], c["P"], bits=12)
+        np.testing.assert_array_equal(idx12, np.array(c["rows"]), err_msg=c["name"] + " 12-bit")
 
 
 # --------------------------------------------------------------------------- exact, 64-bit
@@ -251,12 +255,21 @@ def test_multi_curve_equal_coordinates_is_one_curve():
     x = inputs.make_inputs(w)
     q = np.repeat(x["q"][..., :1], 3, axis=-1)
     k = np.repeat(x["k"][..., :1], 3, axis=-1)
-    for P in (3, 6):
-        per = w.topk // P
-        idx = oracle.select_multi(q, k, w.topk, P)
-        exact = oracle.select(q, k, per)
-        np.testing.assert_array_equal(idx[:, :per], exact)
-        assert np.all(idx[:, per:] == -1)
+    for bits in (10, 12):
+        for P in (3, 6):
+            per = w.topk // P
+            idx = oracle.select_multi(q, k, w.topk, P, bits=bits)
+            exact = oracle.select_ex(q, k, per, bits)
+            np.testing.assert_array_equal(idx[:, :per], exact)
+            assert np.all(idx[:, per:] == -1)
+
+
+def test_chunked_on_12_bit_codes_reduces_to_exact():
+    w = inputs.Workload("t", 1, 2, 200, 8, 16, dist="clustered", seed=23)
+    x = inputs.make_inputs(w)
+    zq, zk = oracle.encode_ex(x["q"], 12), oracle.encode_ex(x["k"], 12)
+    np.testing.assert_array_equal(oracle.select_chunked(zq, zk, w.N, w.topk, 16),
+                                  oracle.select_codes64(zq, zk, w.N, w.topk))
 
 
 @pytest.mark.parametrize("P", [3, 6])
