@@ -62,6 +62,45 @@ def select_run_bytes(w: inputs.Workload) -> float:
     return float((total + 4 + 4 * w.topk).sum())
 
 
+def variant_select_bytes(w: inputs.Workload, mode: str, causal: bool = True, chunks: int = 0,
+                         curves: int = 0, bits: int = 10) -> float:
+    """Algorithmic bytes of one selection launch (all (b,h)) of a variant, counted as for
+    the exact selection: 8 B per tree entry probed or windowed, the query code, idx out."""
+    BH, N, k = w.B * w.H, w.N, w.topk
+    zb = 8 if bits == 12 else 4
+    if mode == "exact":
+        m = np.arange(1, N + 1, dtype=np.int64) if causal else np.full(N, N, dtype=np.int64)
+        total = np.zeros(N, dtype=np.float64)
+        for l in range(int(np.log2(N)) + 1):
+            s = 1 << l
+            total += ((m >> l) & 1) * (8.0 * (l + 1) + 8.0 * min(2 * k, s))
+        return BH * float((total + zb + 4 * k).sum())
+    if mode == "chunked":
+        L = 1
+        while L * chunks < N:
+            L *= 2
+        lvl = int(np.log2(L))
+        nch = np.arange(N, dtype=np.int64) // L + 1  # chunks searched by query i
+        per = 8.0 * (lvl + 1) + 8.0 * min(k, L)
+        return BH * float((nch * per + zb + 4 * k).sum())
+    per = k // curves  # several curves: exact selections of k // P, then the merge
+    sub = inputs.Workload(**{**w.__dict__, "topk": per})
+    one = variant_select_bytes(sub, "exact", causal, bits=bits)
+    return curves * one + BH * N * (curves * per * 4 + 4 * k)
+
+
+VARIANTS = [  # name, zeta_select_opts fields
+    ("exact_noncausal", dict(mode=0, causal=False)),
+    ("exact_12bit", dict(mode=0, causal=True, bits=12)),
+    ("chunked_4", dict(mode=1, chunks=4)),
+    ("chunked_8", dict(mode=1, chunks=8)),
+    ("chunked_16", dict(mode=1, chunks=16)),
+    ("chunked_32", dict(mode=1, chunks=32)),
+    ("curves_3", dict(mode=2, curves=3)),
+    ("curves_6", dict(mode=2, curves=6)),
+]
+
+
 def kernel_bytes(w: inputs.Workload) -> dict:
     """Algorithmic bytes per launch of each kernel (every gathered row counted as read)."""
     BH = w.B * w.H
@@ -255,6 +294,95 @@ def trace_summary(d: str, workload: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+# ----------------------------------------------------------------------------- variants
+def _recall(sel, ref, torch) -> float:
+    """Mean over queries of |sel & ref| / |ref| (valid entries only)."""
+    hit = (sel.unsqueeze(-1) == ref.unsqueeze(-2)) & (ref >= 0).unsqueeze(-2)
+    found = hit.any(dim=-2).sum(dim=-1).double()
+    want = (ref >= 0).sum(dim=-1).double()
+    keep = want > 0
+    return float((found[keep] / want[keep]).mean().item())
+
+
+def _euclid_topk(q, k, rows, topk, causal, torch):
+    """Exact Euclidean top-k (by squared distance, ties to the smaller j) of sampled queries
+    of every head, brute force in fp64 on the device: [BH, S, topk] (-1 padded)."""
+    BH, N = q.shape[0] * q.shape[1], q.shape[2]
+    qf = q.reshape(BH, N, 3).double()
+    kf = k.reshape(BH, N, 3).double()
+    out = torch.full((BH, rows.numel(), topk), -1, dtype=torch.int32, device=q.device)
+    j = torch.arange(N, device=q.device)
+    for bh in range(BH):
+        d = ((qf[bh, rows].unsqueeze(1) - kf[bh].unsqueeze(0)) ** 2).sum(-1)  # [S, N]
+        if causal:
+            d = d.masked_fill(j.unsqueeze(0) > rows.unsqueeze(1), float("inf"))
+        # ties to the smaller j: a stable sort of the distances
+        order = torch.sort(d, dim=1, stable=True).indices[:, :topk]
+        valid = torch.gather(d, 1, order) < float("inf")
+        out[bh] = torch.where(valid, order, torch.full_like(order, -1)).to(torch.int32)
+    return out
+
+
+def measure_variants(w, q, k, v, gamma, dout, idx_exact, hip, lib, Z, torch, steps: int) -> dict:
+    """Each selection variant: stage times of zeta_fwd_ex (select = encode + tree + select
+    stages) and of zeta_bwd_ex, the select kernel's algorithmic bytes per second, and the
+    recall of its selection against the exact causal one and against the exact Euclidean
+    top-k (sampled queries).  Recall is computed outside the timed region."""
+    res = {}
+    BH, N, K = w.B * w.H, w.N, w.topk
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    rows = torch.randint(0, N, (256,), generator=g).to(q.device)
+    exact_rows = idx_exact.reshape(BH, N, K)[:, rows]
+    eu_causal = _euclid_topk(q, k, rows, K, True, torch)
+    eu_all = _euclid_topk(q, k, rows, K, False, torch)
+    res["exact_causal"] = {"recall_vs_euclidean": round(_recall(exact_rows, eu_causal, torch), 4)}
+    out = torch.empty_like(v)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty((w.H,), dtype=torch.float32, device=q.device))
+    shape = Z.make_shape(w.B, w.H, N, w.dv, K, Z.ZETA_BF16 if v.dtype == torch.bfloat16 else Z.ZETA_F32)
+    for name, f in VARIANTS:
+        o = Z.select_opts(f.get("mode", 0), causal=f.get("causal", True), bits=f.get("bits", 10),
+                          chunks=f.get("chunks", 0), curves=f.get("curves", 0))
+        ws_f = Z.workspace(shape, Z.ZETA_WS_FWD, q.device, o)
+        ws_b = Z.workspace(shape, Z.ZETA_WS_BWD, q.device, o)
+        idx = torch.empty((w.B, w.H, N, K), dtype=torch.int32, device=q.device)
+        for _ in range(2):
+            Z.zeta_fwd_ex(q, k, v, gamma, K, o, ws=ws_f, out=out, idx=idx)
+            Z.zeta_bwd_ex(q, k, v, gamma, idx, dout, o, ws=ws_b, grads=grads)
+        ev = [(hip.create(6), hip.create(6)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for ef, eb in ev:
+            lib.zeta_set_stage_events(ef, 6)
+            Z.zeta_fwd_ex(q, k, v, gamma, K, o, ws=ws_f, out=out, idx=idx)
+            lib.zeta_set_stage_events(eb, 6)
+            Z.zeta_bwd_ex(q, k, v, gamma, idx, dout, o, ws=ws_b, grads=grads)
+            lib.zeta_set_stage_events(None, 0)
+        torch.cuda.synchronize()
+        sel = float(np.mean([hip.elapsed_ms(ef[0], ef[3]) for ef, _ in ev]))
+        sel_k = float(np.mean([hip.elapsed_ms(ef[2], ef[3]) for ef, _ in ev]))
+        fwd = float(np.mean([hip.elapsed_ms(ef[0], ef[5]) for ef, _ in ev]))
+        bwd = float(np.mean([hip.elapsed_ms(eb[0], eb[5]) for _, eb in ev]))
+        for ef, eb in ev:
+            hip.destroy(ef)
+            hip.destroy(eb)
+        mode = ["exact", "chunked", "curves"][f.get("mode", 0)]
+        sb = variant_select_bytes(w, mode, f.get("causal", True), f.get("chunks", 0),
+                                  f.get("curves", 0), f.get("bits", 10))
+        sel_rows = idx.reshape(BH, N, K)[:, rows]
+        r = {"select_stages_ms": round(sel, 4), "select_kernel_ms": round(sel_k, 4),
+             "fwd_ms": round(fwd, 4), "fwd_bwd_ms": round(fwd + bwd, 4),
+             "select_algorithmic_GBs": round(sb / ((sel if mode == "curves" else sel_k) * 1e-3)
+                                             / 1e9, 1),
+             "recall_vs_exact_causal": round(_recall(sel_rows, exact_rows, torch), 4),
+             "recall_vs_euclidean": round(_recall(sel_rows, eu_causal if f.get("causal", True)
+                                                  else eu_all, torch), 4)}
+        if mode == "curves":  # stage 3 spans the later curves and the merge
+            r["note"] = "select_kernel_ms covers curves 2..P and the merge; GB/s over all stages"
+        res[name] = r
+        del ws_f, ws_b
+    return res
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(w: inputs.Workload, x: dict, target_s: float, seed: int = 0) -> dict:
     import oracle
@@ -294,6 +422,9 @@ def main() -> int:
     ap.add_argument("--workload", default="long_fwd_bwd", choices=sorted(inputs.CONFIGS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selection variants (chunked, several curves, unmasked, 12-bit)")
+    ap.add_argument("--variant-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (counter calibration)")
     ap.add_argument("--counters-summary", metavar="DIR",
@@ -440,6 +571,9 @@ def main() -> int:
         "pages_context": PAGES_CONTEXT,
         "input_sha256": inputs.digest(x),
     }
+    if not args.no_variants:
+        result["variants"] = measure_variants(w, q, k, v, gamma, dout, idx, hip, lib, Z, torch,
+                                              args.variant_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
