@@ -35,7 +35,7 @@ METRIC = "ms per ZETA fwd (and fwd+bwd) at N=65536,H=8; achieved HBM GB/s vs pea
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PAGES_CONTEXT = {"zeta_fwd_ms": 85.8, "zeta_fwd_bwd_ms": 608.2, "flash_fwd_ms": 805.3,
                  "flash_fwd_bwd_ms": 7044.1, "hardware": "not stated on the pages"}
-FWD_STAGES = ["encode", "tree", "select", "order", "gather"]
+FWD_STAGES = ["encode_order", "tree", "select", "order", "gather"]
 BWD_STAGES = ["bwd_order", "bwd_query", "bwd_transpose", "bwd_key", "bwd_dgamma"]
 SINGLE_KERNEL = {"select": "zeta_select_kernel", "gather": "zeta_cauchy_gather_kernel",
                  "bwd_query": "zeta_bwd_query_kernel", "bwd_key": "zeta_bwd_key_kernel"}
@@ -111,11 +111,12 @@ def kernel_bytes(w: inputs.Workload) -> dict:
     levels = int(np.log2(w.N)) + 1
     tile_levels = min(levels - 1, 10)
     b = {}
-    b["encode"] = BH * w.N * (2 * 12 + 2 * 4)
+    # encode of q and k, then the query processing order (codes counted, codes placed,
+    # order written), which the select and the gather both use
+    b["encode_order"] = BH * w.N * (2 * 12 + 2 * 4) + BH * w.N * (4 + 4 + 4)
     b["tree"] = BH * w.N * (4 + 2 * 8 * (tile_levels + 1) + 2 * 16 * (levels - 1 - tile_levels))
     b["select"] = BH * select_run_bytes(w)
-    # processing order: bucket histogram and scatter read the codes, the order is written
-    b["order"] = BH * w.N * (4 + 4 + 4)
+    b["order"] = 0  # built with the encodes on this path
     b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + 4 + row).sum())
     b["bwd_order"] = BH * w.N * (2 * 12 + 2 * 4 + 2 * 12)
     # per query: index row, q, key rows, value rows, dO row, dq and dgamma term, processing

@@ -200,8 +200,10 @@ zeta_status zeta_bwd_ex(const zeta_shape *shape, const zeta_select_opts *opts, c
  * following zeta_select / zeta_fwd / zeta_bwd call on this thread records events[0] on its
  * stream before its first launch and events[s] after stage s, for as many stages as the
  * call has and `count` allows:
- *   zeta_select, zeta_fwd: 1 encode (q and k), 2 tree build, 3 select kernel,
- *                          4 query processing order, 5 gather kernel (4, 5: zeta_fwd only);
+ *   zeta_select, zeta_fwd: 1 encode (q and k) and the query processing order (which the
+ *                          select and the gather use), 2 tree build, 3 select kernel,
+ *                          4 the processing order when stage 1 did not build it (chunked
+ *                          search, 12-bit cells), 5 gather kernel (4, 5: zeta_fwd only);
  *   zeta_bwd:              1 encode and processing orders, 2 per-query kernel,
  *                          3 selection transpose (radix passes and segment starts),
  *                          4 per-key kernel, 5 dgamma reduction.

@@ -135,14 +135,21 @@ template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__ zq,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
+                                                           const uint32_t* __restrict__ order,
                                                            int64_t rows, int64_t N, int levels,
-                                                           int topk, int causal,
+                                                           int topk, int causal, int64_t tiles,
+                                                           int64_t per_xcd,
                                                            int32_t* __restrict__ idx) {
     constexpr int E = K / L;
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t row = g / L;
+    const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
+    if (tile >= tiles) return;
+    const int64_t g = tile * blockDim.x + threadIdx.x;
+    const int64_t t = g / L;  // position in the processing order
     const int lane = static_cast<int>(g % L);
-    if (row >= rows) return;  // uniform over the L lanes of a query
+    if (t >= rows) return;  // uniform over the L lanes of a query
+    // queries close on the curve search the same parts of the tree, so taking them in the
+    // Z-order processing order keeps the probed lines in L2
+    const int64_t row = order ? (t / N) * N + order[t] : t;
     const int64_t bh = row / N;
     const int64_t i = row - bh * N;
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
@@ -207,39 +214,44 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 template <int K, int L, typename CT, int S>
 static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, int causal,
                                   const CT* zq, const uint64_t* ta, const uint64_t* td,
-                                  int32_t* idx, hipStream_t s) {
-    const int64_t blocks = (rows * L + 255) / 256;
-    hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, zq, ta, td, rows, N, levels, topk, causal, idx);
+                                  const uint32_t* order, int32_t* idx, hipStream_t s) {
+    const int64_t tiles = (rows * L + 255) / 256;
+    const int64_t per = xcd_per(tiles);
+    hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(per * kXcds)),
+                       dim3(256), 0, s, zq, ta, td, order, rows, N, levels, topk, causal, tiles,
+                       per, idx);
     return hipGetLastError();
 }
 
 template <typename CT, int S>
 static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool causal,
-                           const CT* zq, const uint64_t* ta, const uint64_t* td, int32_t* idx,
-                           hipStream_t s) {
+                           const CT* zq, const uint64_t* ta, const uint64_t* td,
+                           const uint32_t* order, int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const int c = causal ? 1 : 0;
-    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    if (topk <= 32) return launch_select_k<32, 2, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
-    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, idx, s);
+    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 32) return launch_select_k<32, 2, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
 }
 
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
                          const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
-                         int32_t* idx, hipStream_t s) {
-    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, idx, s);
+                         const uint32_t* order, int32_t* idx, hipStream_t s) {
+    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, order,
+                                  idx, s);
 }
 
 hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
                            const uint64_t* zq, const uint64_t* tree_asc,
-                           const uint64_t* tree_desc, int32_t* idx, hipStream_t s) {
-    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, idx, s);
+                           const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
+                           hipStream_t s) {
+    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, order,
+                                  idx, s);
 }
 
 // ---------------------------------------------------------------------------- chunked

@@ -252,6 +252,11 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             if (e == hipSuccess) e = zeta::launch_encode_perm(k, BHN, perm, zk, s);
         }
         if (e != hipSuccess) return fail_hip("encode launch", e);
+        // the query processing order of the select (and later of the gather)
+        if (!wide && o.mode != ZETA_SELECT_CHUNKED) {
+            e = zeta::launch_order(BH, N, zq, at<uint32_t>(ws, p.perm), at<uint32_t>(ws, p.ohist), s);
+            if (e != hipSuccess) return fail_hip("order launch", e);
+        }
         if (c == 0) g_marks.record(1, s);
         e = wide ? zeta::launch_build_tree36(BH, N, L, zk64, ta, td, s)
                  : zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
@@ -268,8 +273,9 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             e = wide ? zeta::launch_select_chunked36(BH, N, L, lvl, topk, zq64, ta, idx, s)
                      : zeta::launch_select_chunked(BH, N, L, lvl, topk, zq, ta, idx, s);
         } else {
-            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, ta, td, dst, s)
-                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, ta, td, dst, s);
+            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, ta, td, nullptr, dst, s)
+                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, ta, td,
+                                           at<uint32_t>(ws, p.perm), dst, s);
         }
         if (e != hipSuccess) return fail_hip("select launch", e);
     }
@@ -378,16 +384,19 @@ zeta_status zeta_fwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = run_select(shape, o, q, k, idx, workspace, s)) != ZETA_OK) return st;
     uint32_t* perm = at<uint32_t>(workspace, p.perm);
-    // processing order from the query codes (of the last curve when there are several: the
-    // order only schedules the gather); with 12-bit cells the 10-bit codes are written over
-    // the 36-bit ones first (the order buckets by the top code bits, which they share)
-    uint32_t* zo = at<uint32_t>(workspace, p.zq);
+    // The exact and several-curve selections with 10-bit cells built the query processing
+    // order already (from the last curve's codes: the order only schedules work).  Otherwise
+    // it is built here from 10-bit query codes, written over the 36-bit ones with 12-bit
+    // cells (the order buckets by the top code bits, which both share).
     hipError_t e = hipSuccess;
-    if (o.bits == 12) e = zeta::launch_encode(q, shape->B * shape->H * shape->N, zo, s);
-    if (e == hipSuccess)
-        e = zeta::launch_order(shape->B * shape->H, shape->N, zo, perm,
-                               at<uint32_t>(workspace, p.ohist), s);
-    if (e != hipSuccess) return fail_hip("order launch", e);
+    if (o.bits == 12 || o.mode == ZETA_SELECT_CHUNKED) {
+        uint32_t* zo = at<uint32_t>(workspace, p.zq);
+        if (o.bits == 12) e = zeta::launch_encode(q, shape->B * shape->H * shape->N, zo, s);
+        if (e == hipSuccess)
+            e = zeta::launch_order(shape->B * shape->H, shape->N, zo, perm,
+                                   at<uint32_t>(workspace, p.ohist), s);
+        if (e != hipSuccess) return fail_hip("order launch", e);
+    }
     g_marks.record(4, s);
     e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
                             static_cast<int>(shape->topk), o.causal, shape->v_dtype == ZETA_BF16, q,

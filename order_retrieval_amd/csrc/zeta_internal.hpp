@@ -60,13 +60,15 @@ hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, const uint64_t
                                uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
 hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
                            const uint64_t* zq, const uint64_t* tree_asc,
-                           const uint64_t* tree_desc, int32_t* idx, hipStream_t s);
+                           const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
+                           hipStream_t s);
 hipError_t launch_select_chunked36(int64_t BH, int64_t N, int levels, int lvl, int topk,
                                    const uint64_t* zq, const uint64_t* ta, int32_t* idx,
                                    hipStream_t s);
+// order: processing order of the queries (per (b,h) positions), or null for position order.
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
                          const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
-                         int32_t* idx, hipStream_t s);
+                         const uint32_t* order, int32_t* idx, hipStream_t s);
 // Chunked search over the aligned chunks of 2^lvl positions (tree level lvl).
 hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
                                  const uint32_t* zq, const uint64_t* ta, int32_t* idx,
