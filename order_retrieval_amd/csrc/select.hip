@@ -16,8 +16,8 @@
 // the first k of every walk gives the exact answer.
 //
 // The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
-// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = K/16 for K >= 32, so
-// every lane holds 16 entries in registers; L = 1 below).  A walk's K candidates are merged
+// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 64,
+// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below).  A walk's K candidates are merged
 // with one bitonic step: elementwise min against the reversed candidates (each lane loads
 // its own contiguous block of the walk) leaves a bitonic sequence of the K smallest, which
 // log2(K) compare-exchange stages sort; the stages whose stride spans lanes exchange values
@@ -235,7 +235,7 @@ static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool cau
     if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
     if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
     if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 32) return launch_select_k<32, 2, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
     return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
 }
 
