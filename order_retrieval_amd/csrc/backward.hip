@@ -65,7 +65,7 @@ __device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64
 // of kRowLoads slots are issued together) and a DPP butterfly over the row completes
 // g_ij = dO_i . v_j, which the owning lane keeps.
 constexpr int kRowLanes = 16;  // lanes per query or key
-constexpr int kRowLoads = 4;   // rows whose loads are issued together
+constexpr int kRowLoads = 8;   // rows whose loads are issued together
 
 template <bool BF16, int CPL, int L0>
 __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
@@ -439,6 +439,7 @@ constexpr int kKeyRow = kRowLanes;        // lanes per key
 constexpr int kKeyRecs = 2;               // records per lane per batch
 constexpr int kKeyBatch = kKeyRow * kKeyRecs;
 constexpr int kKeyLoads = kRowLoads;      // records whose dO loads are issued together
+static_assert(kKeyRow % kKeyLoads == 0 && kRowLanes % kRowLoads == 0, "whole load groups");
 
 template <bool BF16, int CPL, int U0>
 __device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* __restrict__ doh,
@@ -538,13 +539,11 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
             const float ao = own ? sv * st.x : 0.0f;
             const int left = cnt - first;  // records of this key from position `first` on
             float gmine = 0.0f;
-            key_records<BF16, CPL, 0>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
-            if (first + 4 < most)
-                key_records<BF16, CPL, 4>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
-            if (first + 8 < most)
-                key_records<BF16, CPL, 8>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
-            if (first + 12 < most)
-                key_records<BF16, CPL, 12>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            static_for<0, kKeyRow / kKeyLoads>([&](auto bc) {
+                constexpr int b = decltype(bc)::value * kKeyLoads;
+                if (first + b < most)  // uniform
+                    key_records<BF16, CPL, b>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
+            });
             if (own) {
                 const float c = ao * sv * (gmine - st.y);
                 s0 += c * dx;

@@ -29,7 +29,7 @@ namespace zeta {
 // 16-byte chunk(s) of the value row (the loads of kGatherLoads slots are issued together,
 // none waits on another load) and accumulates in fp32.
 constexpr int kGatherLanes = 16;
-constexpr int kGatherLoads = 4;
+constexpr int kGatherLoads = 8;
 
 template <bool BF16, int CPL, int L0>
 __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,

@@ -30,10 +30,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Every lane of a 16-lane row takes lane L of that row (DPP row_newbcast).
 template <int L>
 __device__ __forceinline__ float row_bcast(float x) {
+    static_assert(L >= 0 && L < 16, "a row has 16 lanes");
     return dpp_take<0x150 + L>(x);
 }
 template <int L>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+    static_assert(L >= 0 && L < 16, "a row has 16 lanes");
     return static_cast<uint32_t>(
         __builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x150 + L, 0xF, 0xF, false));
 }
