@@ -322,25 +322,32 @@ __global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restric
     if (lane == 63) totals[rowid] = incl;
 }
 
-// Stable scatter of one tile: items are ranked in (iteration, wave, lane) order, which is
-// their input order, so equal digits keep their relative order.  All of the tile's items
-// are loaded before the ranking starts, so their loads overlap.  Pass 0 also records the
-// number of pairs of each (b,h) in counts[bh] (the sum of the digit totals).
+// Stable scatter of one tile.  Wavefront w owns the tile's items [w*1024, (w+1)*1024) in
+// input order (iteration-major, then lane), ranks each item among the equal digits of its
+// iteration with 8 ballots, and keeps a running count per digit in its own LDS row, so the
+// item's rank inside its wavefront needs no barrier.  The four wavefronts' counts then give
+// every item its slot in the tile sorted by digit (equal digits in input order); the tile is
+// staged in LDS in that order and written out with consecutive lanes on consecutive slots
+// of a digit's run, so the global writes are coalesced.  Pass 0 also records the number of
+// pairs of each (b,h) in counts[bh] (the sum of the digit totals).
 template <bool FIRST>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t slots,
     uint32_t* __restrict__ counts, int64_t in_stride, int shift, int64_t tiles, PairSpec ps,
     const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int64_t P,
     uint2* __restrict__ rout) {
-    __shared__ uint32_t base[256];
+    constexpr int kWaves = kRadixThreads / 64;
+    constexpr int kWaveItems = kRadixTile / kWaves;
+    __shared__ uint2 stage[kRadixTile];
     __shared__ uint32_t scan[256];
-    __shared__ uint32_t wcnt[4][256];
-    __shared__ uint32_t wpre[4][256];
+    __shared__ uint32_t local[256];
+    __shared__ int32_t delta[256];
+    __shared__ uint32_t wcnt[kWaves][256];
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile + wave * kWaveItems;
     const int64_t items = FIRST ? slots : static_cast<int64_t>(counts[bh]);
 
     uint2 rec[kRadixItems];
@@ -349,30 +356,21 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
         const int64_t off = bh * in_stride;
 #pragma unroll
         for (int it = 0; it < kRadixItems; ++it) {
-            const int64_t e = t0 + it * kRadixThreads + tid;
+            const int64_t e = t0 + it * 64 + lane;
             rec[it] = make_uint2(0, 0);
             if (e < items && load_pair<FIRST>(idx + off, rin + off, e, ps, rec[it]))
                 okmask |= 1u << it;
         }
     }
 
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
     scan[tid] = totals[bh * 256 + tid];
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan of the totals
-        const uint32_t y = tid >= o ? scan[tid - o] : 0u;
-        __syncthreads();
-        scan[tid] += y;
-        __syncthreads();
-    }
-    base[tid] = scan[tid] - totals[bh * 256 + tid] + hist[(bh * 256 + tid) * tiles + blockIdx.x];
-    if (FIRST && blockIdx.x == 0 && tid == 255) counts[bh] = scan[255];
-    uint32_t run = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
-    __syncthreads();
 
+    // rank of every item among the equal digits before it in this wavefront
     const uint64_t lt = (1ull << lane) - 1ull;
-    uint2* out = rout + bh * P;
+    uint32_t lrank[kRadixItems];
 #pragma unroll
     for (int it = 0; it < kRadixItems; ++it) {
         const bool valid = (okmask >> it) & 1u;
@@ -384,18 +382,61 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
             const uint64_t bal = __ballot(bit);
             peers &= bit ? bal : ~bal;
         }
-        if (!valid) peers = 0;
-        const uint32_t rank = __popcll(peers & lt);
-        if (valid && (peers & lt) == 0) wcnt[wave][digit] = __popcll(peers);
-        __syncthreads();
+        // every lane reads the running count before the group's first lane advances it (LDS
+        // operations of one wavefront take effect in program order)
+        const uint32_t before = valid ? wcnt[wave][digit] : 0u;
+        if (valid && (peers & lt) == 0) wcnt[wave][digit] = before + __popcll(peers);
+        lrank[it] = before + __popcll(peers & lt);
+    }
+    __syncthreads();
+
+    // digit tid: its count in the tile, and the exclusive scans of the digit totals (global
+    // start of the digit) and of the tile's counts (start of the digit in the staged tile)
+    uint32_t tile_cnt = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            wpre[w][tid] = run;
-            run += wcnt[w][tid];
-            wcnt[w][tid] = 0;
-        }
+    for (int w = 0; w < kWaves; ++w) tile_cnt += wcnt[w][tid];
+    local[tid] = tile_cnt;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scans
+        const uint32_t y = tid >= o ? scan[tid - o] : 0u;
+        const uint32_t z = tid >= o ? local[tid - o] : 0u;
         __syncthreads();
-        if (valid) out[base[digit] + wpre[wave][digit] + rank] = rec[it];
+        scan[tid] += y;
+        local[tid] += z;
+        __syncthreads();
+    }
+    const uint32_t lstart = local[tid] - tile_cnt;
+    const uint32_t gstart =
+        scan[tid] - totals[bh * 256 + tid] + hist[(bh * 256 + tid) * tiles + blockIdx.x];
+    const uint32_t tile_items = local[255];
+    if (FIRST && blockIdx.x == 0 && tid == 255) counts[bh] = scan[255];
+    delta[tid] = static_cast<int32_t>(gstart) - static_cast<int32_t>(lstart);
+    uint32_t run = lstart;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {  // the wavefronts' shares of the digit, in order
+        const uint32_t c = wcnt[w][tid];
+        wcnt[w][tid] = run;
+        run += c;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it) {
+        if ((okmask >> it) & 1u) {
+            const uint32_t digit = (rec[it].x >> shift) & 255u;
+            stage[wcnt[wave][digit] + lrank[it]] = rec[it];
+        }
+    }
+    __syncthreads();
+
+    uint2* out = rout + bh * P;
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it) {
+        const int t = it * kRadixThreads + tid;  // slot in the staged tile
+        if (t < static_cast<int>(tile_items)) {
+            const uint2 r = stage[t];
+            out[delta[(r.x >> shift) & 255u] + t] = r;
+        }
     }
 }
 
