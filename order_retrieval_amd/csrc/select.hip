@@ -87,6 +87,38 @@ __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
     }
 }
 
+// One compare-exchange layer of a bitonic sort of the K = E*L entries (entry x = lane*E + t)
+// for block size K2 and stride J; DESC sorts descending.
+template <int E, int L, int K2, int J, bool DESC>
+__device__ __forceinline__ void sort_layer(uint64_t (&a)[E], int lane) {
+    if constexpr (J >= E) {
+        const int x = lane * E;
+        const bool up = ((x & K2) == 0) != DESC;
+        cross_stage<E, J / E>(a, up == ((x & J) == 0));
+    } else {
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            if ((t & J) == 0) {
+                const int x = lane * E + t;
+                const bool up = ((x & K2) == 0) != DESC;
+                const uint64_t p = a[t], q = a[t + J];
+                const bool sw = up ? (q < p) : (p < q);
+                a[t] = sw ? q : p;
+                a[t + J] = sw ? p : q;
+            }
+        }
+    }
+    if constexpr (J > 1) sort_layer<E, L, K2, J / 2, DESC>(a, lane);
+}
+
+template <int E, int L, int K2, bool DESC>
+__device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
+    if constexpr (K2 <= E * L) {  // a single entry (K = 1) needs no layer
+        sort_layer<E, L, K2, K2 / 2, DESC>(a, lane);
+        if constexpr (K2 < E * L) sort_blocks<E, L, K2 * 2, DESC>(a, lane);
+    }
+}
+
 // Merge one walk into the running top-K.  Candidate c (0 = first) of the walk sits at run
 // position p + c (right walk, asc tree, key = e - target) or p - 1 - c (left walk, desc
 // tree, key = (target | 0xffffffff) - e).  Lane `lane` of the query holds list entries
@@ -133,6 +165,7 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
 // codes; uint64_t, 28 for the 36-bit codes of 12-bit cells).
 template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__ zq,
+                                                           const CT* __restrict__ zk,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            const uint32_t* __restrict__ order,
@@ -163,9 +196,11 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 
     // The runs are the set bits of the number of usable keys (i+1 under the causal mask,
     // else N), largest first, taken kSearchGroup at a time: their lower_bound searches
-    // (first entry with code >= zq) advance together.
+    // (first entry with code >= zq) advance together.  Runs shorter than 2K together are the
+    // last (m mod 2K) positions, read straight from the codes below.
     const uint64_t m = causal ? static_cast<uint64_t>(i) + 1 : static_cast<uint64_t>(N);
-    uint64_t rem = m;
+    constexpr uint64_t kShort = 2 * K;
+    uint64_t rem = m & ~(kShort - 1);
     while (rem) {
         // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
         // offsets (not pointers) keep every access a global-memory access
@@ -204,6 +239,36 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         }
     }
 
+    // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K;
+    // each group is bitonic-sorted (descending) across the query's lanes and merged
+    {
+        const uint64_t z = static_cast<uint64_t>(zq[row]);
+        const int64_t sbase = static_cast<int64_t>(m & ~(kShort - 1));
+        const int scount = static_cast<int>(m & (kShort - 1));
+        const CT* zkh = zk + bh * N;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int cg = scount - g * K;  // entries of this group (uniform over the lanes)
+            if (cg <= 0) break;
+            uint64_t cand[E];
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                const int u = lane * E + t;
+                cand[t] = ~0ull;
+                if (u < cg) {
+                    const int64_t j = sbase + g * K + u;
+                    const uint64_t code = static_cast<uint64_t>(zkh[j]);
+                    const uint64_t dz = code > z ? code - z : z - code;
+                    cand[t] = (dz << S) | static_cast<uint64_t>(j);
+                }
+            }
+            sort_blocks<E, L, 2, true>(cand, lane);
+#pragma unroll
+            for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
+            bitonic_clean<E, L>(best, lane);
+        }
+    }
+
     int32_t* out = idx + row * topk + lane * E;
 #pragma unroll
     for (int t = 0; t < E; ++t)
@@ -213,45 +278,55 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 
 template <int K, int L, typename CT, int S>
 static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, int causal,
-                                  const CT* zq, const uint64_t* ta, const uint64_t* td,
-                                  const uint32_t* order, int32_t* idx, hipStream_t s) {
+                                  const CT* zq, const CT* zk, const uint64_t* ta,
+                                  const uint64_t* td, const uint32_t* order, int32_t* idx,
+                                  hipStream_t s) {
     const int64_t tiles = (rows * L + 255) / 256;
     const int64_t per = xcd_per(tiles);
     hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(per * kXcds)),
-                       dim3(256), 0, s, zq, ta, td, order, rows, N, levels, topk, causal, tiles,
-                       per, idx);
+                       dim3(256), 0, s, zq, zk, ta, td, order, rows, N, levels, topk, causal,
+                       tiles, per, idx);
     return hipGetLastError();
 }
 
 template <typename CT, int S>
 static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool causal,
-                           const CT* zq, const uint64_t* ta, const uint64_t* td,
+                           const CT* zq, const CT* zk, const uint64_t* ta, const uint64_t* td,
                            const uint32_t* order, int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const int c = causal ? 1 : 0;
-    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
-    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, ta, td, order, idx, s);
+    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
 }
 
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
-                         const uint32_t* zq, const uint64_t* tree_asc, const uint64_t* tree_desc,
-                         const uint32_t* order, int32_t* idx, hipStream_t s) {
-    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, order,
-                                  idx, s);
+                         const uint32_t* zq, const uint32_t* zk, const uint64_t* tree_asc,
+                         const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
+                         hipStream_t s) {
+    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, zk, tree_asc, tree_desc,
+                                  order, idx, s);
 }
 
 hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
-                           const uint64_t* zq, const uint64_t* tree_asc,
+                           const uint64_t* zq, const uint64_t* zk, const uint64_t* tree_asc,
                            const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
                            hipStream_t s) {
-    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, tree_asc, tree_desc, order,
-                                  idx, s);
+    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, zk, tree_asc, tree_desc,
+                                  order, idx, s);
+}
+
+int select_first_level(int topk) {
+    int k = 1;
+    while (k < topk) k <<= 1;  // K: topk padded to a power of two
+    int l = 0;
+    while ((1 << l) < 2 * k) ++l;
+    return l;  // log2(2K): shorter runs are read from the codes
 }
 
 // ---------------------------------------------------------------------------- chunked
@@ -264,38 +339,6 @@ hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool cau
 // j > i dropped.  A window is in (code, j) order, which is not (|dz|, j) order inside a
 // group of equal codes below zq, so its candidates are bitonic-sorted (descending) across
 // the query's lanes and then merged into the running top-K like a walk.
-
-// One compare-exchange layer of a bitonic sort of the K = E*L entries (entry x = lane*E + t)
-// for block size K2 and stride J; DESC sorts descending.
-template <int E, int L, int K2, int J, bool DESC>
-__device__ __forceinline__ void sort_layer(uint64_t (&a)[E], int lane) {
-    if constexpr (J >= E) {
-        const int x = lane * E;
-        const bool up = ((x & K2) == 0) != DESC;
-        cross_stage<E, J / E>(a, up == ((x & J) == 0));
-    } else {
-#pragma unroll
-        for (int t = 0; t < E; ++t) {
-            if ((t & J) == 0) {
-                const int x = lane * E + t;
-                const bool up = ((x & K2) == 0) != DESC;
-                const uint64_t p = a[t], q = a[t + J];
-                const bool sw = up ? (q < p) : (p < q);
-                a[t] = sw ? q : p;
-                a[t + J] = sw ? p : q;
-            }
-        }
-    }
-    if constexpr (J > 1) sort_layer<E, L, K2, J / 2, DESC>(a, lane);
-}
-
-template <int E, int L, int K2, bool DESC>
-__device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
-    if constexpr (K2 <= E * L) {  // a single entry (K = 1) needs no layer
-        sort_layer<E, L, K2, K2 / 2, DESC>(a, lane);
-        if constexpr (K2 < E * L) sort_blocks<E, L, K2 * 2, DESC>(a, lane);
-    }
-}
 
 template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(

@@ -16,6 +16,8 @@
 // The selection kernel walks the asc tree forward (codes >= the query) and the desc tree
 // backward (codes < the query), so both walks meet equal codes in ascending j order.
 //
+// Levels below `first` are not written (the selection reads short runs straight from the
+// codes); they are still formed in LDS on the way up.
 // Build: levels 0..10 inside one workgroup per 1024-entry tile (LDS rank merge: each entry
 // moves to its own index plus its rank in the sibling block; keys are unique, so this is
 // an exact merge), then one merge-path launch per higher level (streaming: 8 B read and
@@ -46,7 +48,8 @@ template <typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const CT* __restrict__ zk,
                                                               uint64_t* __restrict__ asc,
                                                               uint64_t* __restrict__ desc,
-                                                              int64_t N, int levels, int top) {
+                                                              int64_t N, int levels, int top,
+                                                              int first) {
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     __shared__ uint64_t buf[2][2][kTile];  // [tree][ping-pong][entry]
     const int64_t bh = blockIdx.y;
@@ -62,8 +65,10 @@ __global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const CT* __restric
         const uint64_t ka = c | j, kd = c | (~j & kJMask);
         buf[0][0][e] = ka;
         buf[1][0][e] = kd;
-        tA[e] = ka;
-        tD[e] = kd;
+        if (first == 0) {
+            tA[e] = ka;
+            tD[e] = kd;
+        }
     }
     __syncthreads();
 
@@ -86,6 +91,7 @@ __global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const CT* __restric
         }
         __syncthreads();
         cur ^= 1;
+        if (l + 1 < first) continue;  // level not read by the caller: stays in LDS only
         uint64_t* oA = tA + static_cast<int64_t>(l + 1) * N;
         uint64_t* oD = tD + static_cast<int64_t>(l + 1) * N;
         for (int e = threadIdx.x; e < n; e += blockDim.x) {
@@ -160,13 +166,15 @@ __global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restri
 }
 
 template <typename CT, int S>
-static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, const CT* zk,
+static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, const CT* zk,
                                uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
     if (BH <= 0 || N <= 0) return hipSuccess;
     const int top_tile = levels - 1 < kTileLog ? levels - 1 : kTileLog;
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
+    // the merge passes read the tile stage's top level, so it is written when they follow
+    const int first_w = (top_tile + 1 < levels && first > top_tile) ? top_tile : first;
     hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(256), 0, s, zk, tree_asc,
-                       tree_desc, N, levels, top_tile);
+                       tree_desc, N, levels, top_tile, first_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int l = top_tile; l + 1 < levels; ++l) {
@@ -180,14 +188,14 @@ static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, const CT* zk,
     return hipSuccess;
 }
 
-hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, const uint32_t* zk,
+hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, int first, const uint32_t* zk,
                              uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
-    return build_tree_t<uint32_t, 32>(BH, N, levels, zk, tree_asc, tree_desc, s);
+    return build_tree_t<uint32_t, 32>(BH, N, levels, first, zk, tree_asc, tree_desc, s);
 }
 
-hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, const uint64_t* zk,
+hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, int first, const uint64_t* zk,
                                uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
-    return build_tree_t<uint64_t, 28>(BH, N, levels, zk, tree_asc, tree_desc, s);
+    return build_tree_t<uint64_t, 28>(BH, N, levels, first, zk, tree_asc, tree_desc, s);
 }
 
 }  // namespace zeta

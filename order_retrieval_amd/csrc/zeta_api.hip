@@ -116,15 +116,19 @@ int chunk_level(int64_t N, int chunks) {
     return l;
 }
 
-// Tree levels a selection needs: every level of the exact search, and for the chunked
-// search also the chunk level (which is above the top level when 2^lvl > N).
+// Tree levels a selection needs: every level of the exact search; for the chunked search
+// only up to the chunk level (which is above the top level when 2^lvl > N).
 int tree_levels(const zeta_shape* sh, const Opts& o) {
-    const int L = levels_of(sh->N);
-    if (o.mode == ZETA_SELECT_CHUNKED) {
-        const int need = chunk_level(sh->N, o.chunks) + 1;
-        return need > L ? need : L;
-    }
-    return L;
+    if (o.mode == ZETA_SELECT_CHUNKED) return chunk_level(sh->N, o.chunks) + 1;
+    return levels_of(sh->N);
+}
+
+// Lowest tree level the selection reads (the levels below it are not written).
+int tree_first(const zeta_shape* sh, const Opts& o) {
+    if (o.mode == ZETA_SELECT_CHUNKED) return chunk_level(sh->N, o.chunks);
+    const int k = o.mode == ZETA_SELECT_CURVES ? static_cast<int>(sh->topk) / o.curves
+                                               : static_cast<int>(sh->topk);
+    return zeta::select_first_level(k);
 }
 
 // Curve coordinate orders of the several-curve variant (rebuttal page, on the asymmetry of
@@ -258,8 +262,9 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             if (e != hipSuccess) return fail_hip("order launch", e);
         }
         if (c == 0) g_marks.record(1, s);
-        e = wide ? zeta::launch_build_tree36(BH, N, L, zk64, ta, td, s)
-                 : zeta::launch_build_tree(BH, N, L, zk, ta, td, s);
+        const int first = tree_first(sh, o);
+        e = wide ? zeta::launch_build_tree36(BH, N, L, first, zk64, ta, td, s)
+                 : zeta::launch_build_tree(BH, N, L, first, zk, ta, td, s);
         if (e != hipSuccess) return fail_hip("tree launch", e);
         if (c == 0) g_marks.record(2, s);
         int32_t* dst = idx;
@@ -273,8 +278,9 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             e = wide ? zeta::launch_select_chunked36(BH, N, L, lvl, topk, zq64, ta, idx, s)
                      : zeta::launch_select_chunked(BH, N, L, lvl, topk, zq, ta, idx, s);
         } else {
-            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, ta, td, nullptr, dst, s)
-                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, ta, td,
+            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, zk64, ta, td, nullptr,
+                                             dst, s)
+                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, zk, ta, td,
                                            at<uint32_t>(ws, p.perm), dst, s);
         }
         if (e != hipSuccess) return fail_hip("select launch", e);
@@ -339,7 +345,7 @@ zeta_status zeta_build_tree(int64_t BH, int64_t N, const uint32_t* zk, uint64_t*
         return fail(ZETA_ERR_INVALID_ARGUMENT, "misaligned pointer");
     zeta_status st = preflight();
     if (st != ZETA_OK) return st;
-    hipError_t e = zeta::launch_build_tree(BH, N, levels_of(N), zk, tree_asc, tree_desc,
+    hipError_t e = zeta::launch_build_tree(BH, N, levels_of(N), 0, zk, tree_asc, tree_desc,
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ZETA_OK : fail_hip("tree launch", e);
 }
