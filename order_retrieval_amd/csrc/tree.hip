@@ -45,7 +45,7 @@ __device__ __forceinline__ int lds_lower_bound(const uint64_t* a, int n, uint64_
 }
 
 template <typename CT, int S>
-__global__ void __launch_bounds__(256) zeta_tree_tile_kernel(const CT* __restrict__ zk,
+__global__ void __launch_bounds__(kTile) zeta_tree_tile_kernel(const CT* __restrict__ zk,
                                                               uint64_t* __restrict__ asc,
                                                               uint64_t* __restrict__ desc,
                                                               int64_t N, int levels, int top,
@@ -138,7 +138,49 @@ __global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restri
     const int d0 = static_cast<int>(o0 - run0);
     const int d1 = d0 + kMergeTile < na + nb ? d0 + kMergeTile : na + nb;
 
-    if (threadIdx.x < 2) split[threadIdx.x] = diag_split(A, na, B, nb, threadIdx.x ? d1 : d0);
+    // Merge-path splits of the two diagonals d0, d1 (threads 0-127 and 128-255): the number
+    // a of A entries among the first d outputs is the first a with A[a] > B[d-1-a] (keys are
+    // unique).  Each round tests 128 evenly spaced candidates of the open interval at once,
+    // so a few rounds of independent loads replace a long chain of dependent ones.
+    {
+        __shared__ int lo_s[2], hi_s[2], lo_n[2], hi_n[2];
+        const int h = threadIdx.x >> 7;
+        const int t = threadIdx.x & 127;
+        const int d = h ? d1 : d0;
+        if (t == 0) {
+            lo_s[h] = d - nb > 0 ? d - nb : 0;
+            hi_s[h] = d < na ? d : na;
+        }
+        __syncthreads();
+        while (true) {
+            const int lo = lo_s[h], hi = hi_s[h];
+            const bool open0 = lo_s[0] < hi_s[0], open1 = lo_s[1] < hi_s[1];
+            if (!open0 && !open1) break;  // uniform over the workgroup
+            __syncthreads();
+            if (t == 0) {
+                lo_n[h] = lo;
+                hi_n[h] = hi;
+            }
+            __syncthreads();
+            if (lo < hi) {
+                const int step = (hi - lo + 127) / 128;
+                const int a = lo + t * step;
+                if (a < hi) {
+                    if (A[a] < B[d - 1 - a])
+                        atomicMax(&lo_n[h], a + 1);  // the split lies above a
+                    else
+                        atomicMin(&hi_n[h], a);      // the split is at most a
+                }
+            }
+            __syncthreads();
+            if (t == 0) {
+                lo_s[h] = lo_n[h];
+                hi_s[h] = hi_n[h];
+            }
+            __syncthreads();
+        }
+        if (t == 0) split[h] = lo_s[h];
+    }
     __syncthreads();
     const int a0 = split[0], a1 = split[1];
     const int b0 = d0 - a0, b1 = d1 - a1;
@@ -147,22 +189,28 @@ __global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restri
         seg[e] = e < ca ? A[a0 + e] : B[b0 + e - ca];
     __syncthreads();
 
+    // each thread merges 8 consecutive outputs into LDS; the tile is then written out with
+    // consecutive lanes on consecutive entries
+    __shared__ uint64_t merged[kMergeTile];
     const uint64_t* sa = seg;
     const uint64_t* sb = seg + ca;
     const int t0 = threadIdx.x * 8;
-    if (t0 >= ca + cb) return;
-    int ia = diag_split(sa, ca, sb, cb, t0);
-    int ib = t0 - ia;
-    uint64_t* out = dst + run0 + d0 + t0;
-    const int cnt = ca + cb - t0 < 8 ? ca + cb - t0 : 8;
-    for (int u = 0; u < cnt; ++u) {
-        uint64_t x;
-        if (ib >= cb || (ia < ca && sa[ia] < sb[ib]))
-            x = sa[ia++];
-        else
-            x = sb[ib++];
-        out[u] = x;
+    if (t0 < ca + cb) {
+        int ia = diag_split(sa, ca, sb, cb, t0);
+        int ib = t0 - ia;
+        const int cnt = ca + cb - t0 < 8 ? ca + cb - t0 : 8;
+        for (int u = 0; u < cnt; ++u) {
+            uint64_t x;
+            if (ib >= cb || (ia < ca && sa[ia] < sb[ib]))
+                x = sa[ia++];
+            else
+                x = sb[ib++];
+            merged[t0 + u] = x;
+        }
     }
+    __syncthreads();
+    uint64_t* out = dst + run0 + d0;
+    for (int e = threadIdx.x; e < ca + cb; e += blockDim.x) out[e] = merged[e];
 }
 
 template <typename CT, int S>
@@ -173,7 +221,7 @@ static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, con
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
     // the merge passes read the tile stage's top level, so it is written when they follow
     const int first_w = (top_tile + 1 < levels && first > top_tile) ? top_tile : first;
-    hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(256), 0, s, zk, tree_asc,
+    hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(kTile), 0, s, zk, tree_asc,
                        tree_desc, N, levels, top_tile, first_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
