@@ -75,16 +75,28 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scan_kernel(uint4* _
         tot[3] += x.w;
     }
     const uint32_t mine = tot[0] + tot[1] + tot[2] + tot[3];
-    part[tid] = mine;
-    __syncthreads();
-    for (int off = 1; off < kOrderThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-        const uint32_t y = tid >= off ? part[tid - off] : 0u;
-        __syncthreads();
-        part[tid] += y;
-        __syncthreads();
+    // exclusive scan over the threads: inside each wavefront by shuffles, then over the
+    // wavefront totals
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
     }
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t w = lane < kOrderThreads / 64 ? part[lane] : 0u;
+        uint32_t wi = w;
+        for (int off = 1; off < kOrderThreads / 64; off <<= 1) {
+            const uint32_t y = __shfl_up(wi, off, 64);
+            if (lane >= off) wi += y;
+        }
+        if (lane < kOrderThreads / 64) part[lane] = wi - w;  // exclusive wavefront offsets
+    }
+    __syncthreads();
     uint32_t run[kOrderPer];
-    run[0] = part[tid] - mine;
+    run[0] = part[wave] + incl - mine;
     run[1] = run[0] + tot[0];
     run[2] = run[1] + tot[1];
     run[3] = run[2] + tot[2];
