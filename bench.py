@@ -207,16 +207,16 @@ def counter_means(path: str, counter: str) -> dict:
 
 COUNTER_CMDS = [
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- "
-    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- "
-    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o copy_fetch -- "
     "python3 bench.py --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o copy_write -- "
     "python3 bench.py --copy-calibration",
 ]
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
-             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline")
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants")
 
 
 def counters_summary(d: str, workload: str) -> None:
@@ -536,6 +536,7 @@ def main() -> int:
     kb = kernel_bytes(w)
     dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
     achieved = kb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = stored_traffic(dom)
     fwd_bytes = sum(kb[n] for n in FWD_STAGES)
     step_bytes = sum(kb.values())
     rows = w.B * w.H * w.N
@@ -567,7 +568,12 @@ def main() -> int:
         "stage_algorithmic_bytes": {n: int(b) for n, b in kb.items()},
         "roofline": {"bound": "hbm", "kernel": SINGLE_KERNEL[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(dom)},
+                     "traffic": traffic,
+                     # measured HBM bytes over the same duration: what DRAM actually carried
+                     "dram_GBs": None if traffic is None
+                     else round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1),
+                     "dram_frac": None if traffic is None
+                     else round(traffic / (stage_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "wall_s_timed": round(wall, 3),
         "pages_context": PAGES_CONTEXT,
         "input_sha256": inputs.digest(x),
