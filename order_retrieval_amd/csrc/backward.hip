@@ -8,17 +8,16 @@
 //     dk_j =  (2/gamma^2) sum_i c_ij (q_i - k_j)        dgamma = (2/gamma^3) sum c_ij d_ij
 //
 // Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
-//   1. per-query pass: recompute s, gather v rows for g, write the query's 1/S_i and D_i,
-//      dq_i and the query's dgamma term;
+//   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij of every
+//      selection slot, dq_i and the query's dgamma term;
 //   2. selection transpose: stable LSD radix sort (8-bit digits) of the pairs of every (b,h)
-//      by j, carrying 8-byte records {j, i}; queries stay ascending inside a key's segment;
+//      by j, carrying 8-byte records {j, slot}; queries stay ascending inside a key's segment;
 //   3. segment starts offs[j] from the sorted keys;
-//   4. per-key pass (keys in Z-order): each key recomputes s_ij, g_ij = dO_i . v_j (it reads the dO_i rows for
-//      dv_j anyway), a_ij and c_ij from the query's 1/S_i and D_i, and reduces its segment
-//      in a fixed order (dv, dk);
+//   4. per-key pass (keys in Z-order): each key gathers its pairs' {a_ij, c_ij}, q_i and dO_i
+//      rows and reduces its segment in a fixed order (dv, dk);
 //   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
-// Recomputing a and c on the key side keeps the sorted records at 8 bytes (half of what
-// carrying a and c would take) and saves writing and re-reading two per-pair arrays.
+// g_ij = dO_i . v_j is formed once, on the query side, which owns dO_i; the key side only
+// scales and adds rows.
 #include "zeta_internal.hpp"
 #include "vec_io.hpp"
 #include "xlane.hpp"
@@ -66,10 +65,11 @@ __device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64
 // g_ij = dO_i . v_j, which the owning lane keeps.
 constexpr int kRowLanes = 16;  // lanes per query or key
 constexpr int kRowLoads = 8;   // rows whose loads are issued together
+constexpr int kRowsPerGroup = 256 / kRowLanes;  // queries or keys per workgroup (one (b,h))
 
-template <bool BF16, int CPL, int L0>
+template <bool BF16, bool O32, int CPL, int L0>
 __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
-                                            int dv, const int (&coff)[CPL], int32_t jo,
+                                            int dv, const int (&coff)[CPL], uint32_t jo,
                                             const float (&go)[CPL][VecIO<BF16>::kElems],
                                             int lrow, float& gmine) {
     using IO = VecIO<BF16>;
@@ -78,10 +78,9 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
     R raw[kRowLoads][CPL];
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
-        const int32_t j = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
-        const int64_t jr = j < 0 ? 0 : j;  // an empty slot reads key 0's row; its g is unused
+        const uint32_t nm = row_bcast<L0 + w>(jo);  // an empty slot names key 0's row, g unused
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + jr * dv + coff[c]);
+        for (int c = 0; c < CPL; ++c) raw[w][c] = RowRef<BF16, O32>::load(vh, nm, dv, coff[c]);
     });
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
@@ -98,25 +97,25 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
     });
 }
 
-template <bool BF16, int CPL, int U>
+template <bool BF16, bool O32, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
-    const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int causal, int64_t tiles, int64_t per_xcd,
-    float2* __restrict__ qstat, float* __restrict__ dq, float* __restrict__ dg_row) {
+    const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t N, int64_t H,
+    int dv, int topk, int causal, int64_t tph, int64_t tiles, int64_t per_xcd,
+    float2* __restrict__ coef, float* __restrict__ dq, float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;  // uniform over the workgroup
+    const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
     const int lrow = threadIdx.x & (kRowLanes - 1);
-    const int64_t t = tile * (blockDim.x / kRowLanes) + threadIdx.x / kRowLanes;
-    const bool live = t < rows;
-    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real query, stores nothing
+    const int64_t pos = (tile - bh * tph) * kRowsPerGroup + threadIdx.x / kRowLanes;
+    const bool live = pos < N;
+    const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real query, stores nothing
     const int chunks = dv / E;
-    const int64_t bh = tt / N;
-    const int64_t i = order ? static_cast<int64_t>(order[tt]) : tt - bh * N;
+    const int64_t i = order ? static_cast<int64_t>(order[bh * N + pp]) : pp;
     const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
@@ -138,18 +137,21 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         if (ch < chunks) IO::load(static_cast<const T*>(dout) + row * dv + ch * E, go[c]);
     }
 
-    int32_t jo[U];
+    uint32_t jo[U];
+    bool sel[U];
     float so[U], dx[U], dy[U], dz[U], gg[U];
     float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int r = lrow + u * kRowLanes;
-        jo[u] = -1;  // not selected: never summed
+        jo[u] = 0;  // not selected: names key 0's row, never summed
+        sel[u] = false;
         so[u] = dx[u] = dy[u] = dz[u] = gg[u] = 0.0f;
         const int32_t jr = r < m ? ir[r] : -1;
         if (jr >= 0) {
             const int32_t j = static_cast<int32_t>(clamp_index(jr, nk - 1));
-            jo[u] = j;
+            jo[u] = RowRef<BF16, O32>::name(j, dv);
+            sel[u] = true;
             nsel += 1.0f;
             dx[u] = q0 - kh[3 * j];
             dy[u] = q1 - kh[3 * j + 1];
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
             static_for<0, kRowLanes / kRowLoads>([&](auto bc) {
                 constexpr int b = decltype(bc)::value;
                 if (u * kRowLanes + b * kRowLoads < most)
-                    query_slots<BF16, CPL, b * kRowLoads>(vh, dv, coff, jo[u], go, lrow, gg[u]);
+                    query_slots<BF16, O32, CPL, b * kRowLoads>(vh, dv, coff, jo[u], go, lrow, gg[u]);
             });
         }
     });
@@ -179,16 +181,18 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     float tsum = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (jo[u] >= 0) tsum += so[u] * gg[u];
+        if (sel[u]) tsum += so[u] * gg[u];
     const float inv_S = nsel > 0.0f ? 1.0f / S : 0.0f;  // an empty selection passes no gradient
     const float D = group_sum(tsum, kRowLanes) * inv_S;
 
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
+    float2* cr = coef + row * topk;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (jo[u] >= 0) {
+        if (sel[u]) {
             const float a = so[u] * inv_S;
             const float c = a * so[u] * (gg[u] - D);
+            if (live) cr[lrow + u * kRowLanes] = make_float2(a, c);
             a0 += c * dx[u];
             a1 += c * dy[u];
             a2 += c * dz[u];
@@ -205,45 +209,57 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         dq[3 * row + 1] = f * a1;
         dq[3 * row + 2] = f * a2;
         dg_row[row] = 2.0f * inv_g2 / g * ag;
-        qstat[row] = make_float2(inv_S, D);
     }
 }
 
-template <bool BF16, int CPL>
-static hipError_t launch_query_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
+template <bool BF16, bool O32, int CPL>
+static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int topk,
                                  int causal, const float* q, const float* k, const void* v,
                                  const float* gamma, const int32_t* idx, const void* dout,
-                                 const uint32_t* order, float2* qstat, float* dq, float* dg_row,
+                                 const uint32_t* order, float2* coef, float* dq, float* dg_row,
                                  hipStream_t s) {
-    const int64_t tiles = (rows + (256 / kRowLanes) - 1) / (256 / kRowLanes);
+    const int64_t tph = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
     const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane (<= 4)
-    auto kern = u <= 1 ? zeta_bwd_query_kernel<BF16, CPL, 1>
-              : u <= 2 ? zeta_bwd_query_kernel<BF16, CPL, 2>
-                       : zeta_bwd_query_kernel<BF16, CPL, 4>;
+    auto kern = u <= 1 ? zeta_bwd_query_kernel<BF16, O32, CPL, 1>
+              : u <= 2 ? zeta_bwd_query_kernel<BF16, O32, CPL, 2>
+                       : zeta_bwd_query_kernel<BF16, O32, CPL, 4>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, dout, order, rows, N, H, dv, topk, causal, tiles, per, qstat, dq,
+                       gamma, idx, dout, order, N, H, dv, topk, causal, tph, tiles, per, coef, dq,
                        dg_row);
     return hipGetLastError();
 }
 
+template <bool BF16, int CPL>
+static hipError_t launch_query_o(int64_t BH, int64_t N, int64_t H, int dv, int topk,
+                                 int causal, const float* q, const float* k, const void* v,
+                                 const float* gamma, const int32_t* idx, const void* dout,
+                                 const uint32_t* order, float2* coef, float* dq, float* dg_row,
+                                 hipStream_t s) {
+    if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
+        return launch_query_c<BF16, true, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+    return launch_query_c<BF16, false, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+}
+
 template <bool BF16>
-static hipError_t launch_query(int64_t rows, int64_t N, int64_t H, int dv, int topk, int causal,
+static hipError_t launch_query(int64_t BH, int64_t N, int64_t H, int dv, int topk, int causal,
                                const float* q, const float* k, const void* v, const float* gamma,
                                const int32_t* idx, const void* dout, const uint32_t* order,
-                               float2* qstat, float* dq, float* dg_row, hipStream_t s) {
+                               float2* coef, float* dq, float* dg_row, hipStream_t s) {
     const int cpl = (dv / VecIO<BF16>::kElems + kRowLanes - 1) / kRowLanes;
     if (cpl <= 1)
-        return launch_query_c<BF16, 1>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_o<BF16, 1>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
     if (cpl <= 2)
-        return launch_query_c<BF16, 2>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_o<BF16, 2>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
     if (BF16 || cpl <= 4)  // bf16 rows have <= 64 chunks
-        return launch_query_c<BF16, 4>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
-    return launch_query_c<BF16, BF16 ? 4 : 8>(rows, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, qstat, dq, dg_row, s);
+        return launch_query_o<BF16, 4>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+    return launch_query_o<BF16, BF16 ? 4 : 8>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
 }
 
 // ---------------------------------------------------------------------------- 2. transpose
-// Every pair travels through the sort as one 8-byte record {j, i}.  Pass 0 reads the
+// Every pair travels through the sort as one 8-byte record {j, p}, p = i * topk + r the
+// pair's selection slot.  Pass 0 reads the
 // selection in pair order (coalesced) and builds the records; later passes move records.
 // The key kernel then reads each key's pairs as one contiguous run of records.
 template <bool FIRST>
@@ -253,7 +269,7 @@ __device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
     if (FIRST) {
         uint32_t key;
         if (!pair_item(idx, e, ps, key)) return false;
-        rec = make_uint2(key, static_cast<uint32_t>(e) / static_cast<uint32_t>(ps.topk));
+        rec = make_uint2(key, static_cast<uint32_t>(e));
         return true;
     }
     rec = rin[e];
@@ -465,132 +481,141 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* 
 }
 
 // ---------------------------------------------------------------------------- 4. keys
+// Unsigned division by a divisor fixed for the launch (the selection width): a multiply-high,
+// a subtract and two shifts, exact for every 32-bit numerator (Granlund and Montgomery,
+// "Division by Invariant Integers using Multiplication", unsigned division by a run-time
+// invariant divisor).
+struct DivU32 {
+    uint32_t m;  // low 32 bits of the 33-bit multiplier
+    int sh1, sh2;
+};
+
+static DivU32 make_div(uint32_t d) {
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
+    DivU32 r;
+    r.m = static_cast<uint32_t>((((uint64_t(1) << l) - d) << 32) / d + 1);
+    r.sh1 = l < 1 ? l : 1;
+    r.sh2 = l > 1 ? l - 1 : 0;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, const DivU32& d) {
+    const uint32_t t = __umulhi(d.m, n);
+    return (t + ((n - t) >> d.sh1)) >> d.sh2;
+}
+
 // One 16-lane row (a DPP row) per key j, four keys per wavefront, keys taken in their Z-order
 // processing order: the queries that selected a key are near it on the curve, so keys that
 // run together read overlapping dO rows and L2 serves the repeats.  A key's pairs are a
-// contiguous run of records, taken kKeyBatch at a time: lane l of the row owns records l and
-// 16 + l of the batch, loads their q_i and the query's {1/S_i, D_i} and forms s_ij, a_ij and
-// a_ij s_ij.  The row then walks the batch's records in order: i and a_ij come from the owning
-// lane by a DPP row broadcast, every lane loads its chunks of the dO_i row (the loads of
-// kKeyLoads records are issued together), adds a_ij dO_i to its chunks of dv_j and its part
-// of g_ij = dO_i . v_j, and a DPP butterfly over the row completes g_ij, which the owning lane
-// keeps for c_ij and the dk term.  No LDS traffic; the trip counts are uniform over the
+// contiguous run of records, taken 16 at a time: lane l of the row owns record l of the batch
+// (its slot is loaded one batch ahead) and loads the slot's {a_ij, c_ij} (written by the
+// per-query pass) and q_i.  The row then walks the batch's records in order: i and a_ij come from the owning lane
+// by a DPP row broadcast, every lane loads its chunks of the dO_i row (the loads of kKeyLoads
+// records are issued together) and adds a_ij dO_i to its chunks of dv_j; the owning lane adds
+// c_ij (q_i - k_j) to the dk sum.  No LDS traffic; the trip counts are uniform over the
 // wavefront (the longest of its four keys) and a key's sums run in a fixed order.
 constexpr int kKeyRow = kRowLanes;        // lanes per key
-constexpr int kKeyRecs = 2;               // records per lane per batch
-constexpr int kKeyBatch = kKeyRow * kKeyRecs;
 constexpr int kKeyLoads = kRowLoads;      // records whose dO loads are issued together
 static_assert(kKeyRow % kKeyLoads == 0 && kRowLanes % kRowLoads == 0, "whole load groups");
 
-template <bool BF16, int CPL, int U0>
+template <bool BF16, bool O32, int CPL, int U0>
 __device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* __restrict__ doh,
                                             int dv, const int (&coff)[CPL], uint32_t io,
-                                            float ao, int lrow, int left, float (&vj)[CPL][VecIO<BF16>::kElems],
-                                            float (&acc)[CPL][VecIO<BF16>::kElems], float& gmine) {
+                                            float ao, float (&acc)[CPL][VecIO<BF16>::kElems]) {
     using IO = VecIO<BF16>;
     using R = typename IO::raw_t;
     constexpr int E = IO::kElems;
     R raw[kKeyLoads][CPL];
     static_for<0, kKeyLoads>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
-        const int64_t i = row_bcast<U0 + u>(io);
+        const uint32_t nm = row_bcast<U0 + u>(io);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) raw[u][c] = IO::load_raw(doh + i * dv + coff[c]);
+        for (int c = 0; c < CPL; ++c) raw[u][c] = RowRef<BF16, O32>::load(doh, nm, dv, coff[c]);
     });
     static_for<0, kKeyLoads>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         const float a = row_bcast<U0 + u>(ao);
-        float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float x[E];
             IO::unpack(raw[u][c], x);
 #pragma unroll
-            for (int e = 0; e < E; ++e) part += x[e] * vj[c][e];
-            if (U0 + u < left) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[c][e] += a * x[e];
-            }
+            for (int e = 0; e < E; ++e) acc[c][e] += a * x[e];
         }
-        const float g = group_sum(part, kKeyRow);
-        if (lrow == U0 + u) gmine = g;
     });
 }
 
-template <bool BF16, int CPL>
+template <bool BF16, bool O32, int CPL>
 __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ gamma, const void* __restrict__ dout,
-    const float2* __restrict__ qstat, const uint2* __restrict__ recs,
-    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ order, int64_t rows,
-    int64_t N, int64_t H, int dv, int64_t P, int64_t tiles, int64_t per_xcd,
-    float* __restrict__ dk, void* __restrict__ dvout) {
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
+    const void* __restrict__ dout, const float2* __restrict__ coef,
+    const uint2* __restrict__ recs, const uint32_t* __restrict__ offs,
+    const uint32_t* __restrict__ order, int64_t N, int64_t H, int dv, int topk, DivU32 slot_div,
+    int64_t P, int64_t tph, int64_t tiles, int64_t per_xcd, float* __restrict__ dk,
+    void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;  // uniform over the workgroup
-    const int lane64 = threadIdx.x & 63;
-    const int lrow = lane64 & (kKeyRow - 1);
-    const int64_t t = tile * (blockDim.x / kKeyRow) + threadIdx.x / kKeyRow;  // processing order
-    const bool live = t < rows;
-    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real key, stores nothing
-    const int64_t row = order ? (tt / N) * N + order[tt] : tt;
+    const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
+    const int lrow = threadIdx.x & (kKeyRow - 1);
+    const int64_t pos = (tile - bh * tph) * kRowsPerGroup + threadIdx.x / kKeyRow;
+    const bool live = pos < N;
+    const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real key, stores nothing
+    const int64_t j = order ? static_cast<int64_t>(order[bh * N + pp]) : pp;
+    const int64_t row = bh * N + j;
     const int chunks = dv / E;
-    const int64_t bh = row / N;
-    const int64_t j = row - bh * N;
     const float gm = gamma[bh % H];
-    const float inv_g2 = 1.0f / (gm * gm);
     const float k0 = k[3 * row], k1 = k[3 * row + 1], k2 = k[3 * row + 2];
     const uint32_t seg0 = offs[bh * (N + 1) + j];
     const int cnt = live ? static_cast<int>(offs[bh * (N + 1) + j + 1] - seg0) : 0;
     const uint2* rh = recs + bh * P + seg0;
     const float* qh = q + bh * N * 3;
-    const float2* sh = qstat + bh * N;
+    const float2* cf = coef + bh * N * topk;
     const T* doh = static_cast<const T*>(dout) + bh * N * dv;
 
-    float vj[CPL][E], acc[CPL][E];
-    int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet vj = 0)
+    float acc[CPL][E];
+    int coff[CPL];  // element offset of the lane's chunks (clamped; never stored past the row)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int ch = lrow + c * kKeyRow;
         coff[c] = (ch < chunks ? ch : chunks - 1) * E;
 #pragma unroll
-        for (int e = 0; e < E; ++e) vj[c][e] = acc[c][e] = 0.0f;
-        if (ch < chunks) IO::load(static_cast<const T*>(v) + row * dv + ch * E, vj[c]);
+        for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
     }
     // the longest of the wavefront's four keys sets the trip counts
     int most = cnt;
     most = max(most, __shfl_xor(most, 16, 64));
     most = max(most, __shfl_xor(most, 32, 64));
 
+    // Records past the key's run repeat its last record with a = 0, so they add 0 * dO_i for
+    // a row the key sums anyway (exactly nothing unless that row is not finite, and then the
+    // key's sum already is not).  A key with no pairs stores zeros.
+    const int last = cnt > 0 ? cnt - 1 : 0;
+    auto slot_at = [&](int p) -> uint32_t { return cnt > 0 ? rh[p < last ? p : last].y : 0u; };
+    uint32_t slot_next = slot_at(lrow);
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-    for (int base = 0; base < most; base += kKeyBatch) {
-#pragma unroll
-        for (int r = 0; r < kKeyRecs; ++r) {
-            const int first = base + r * kKeyRow;  // the batch's records r*16 .. r*16+15
-            if (first >= most) break;               // uniform
-            const int p = first + lrow;
-            const bool own = p < cnt;
-            // records past the key's run name query 0 (inside the buffers) and carry a = 0
-            const uint32_t io = own ? rh[p].y : 0u;
-            const float dx = qh[3 * io] - k0, dy = qh[3 * io + 1] - k1, dz = qh[3 * io + 2] - k2;
-            const float2 st = sh[io];
-            const float sv = 1.0f / (1.0f + (dx * dx + dy * dy + dz * dz) * inv_g2);
-            const float ao = own ? sv * st.x : 0.0f;
-            const int left = cnt - first;  // records of this key from position `first` on
-            float gmine = 0.0f;
-            static_for<0, kKeyRow / kKeyLoads>([&](auto bc) {
-                constexpr int b = decltype(bc)::value * kKeyLoads;
-                if (first + b < most)  // uniform
-                    key_records<BF16, CPL, b>(doh, dv, coff, io, ao, lrow, left, vj, acc, gmine);
-            });
-            if (own) {
-                const float c = ao * sv * (gmine - st.y);
-                s0 += c * dx;
-                s1 += c * dy;
-                s2 += c * dz;
-            }
+    for (int first = 0; first < most; first += kKeyRow) {  // batches of 16 records
+        const int p = first + lrow;
+        const bool own = p < cnt;
+        const uint32_t slot = slot_next;
+        if (first + kKeyRow < most) slot_next = slot_at(p + kKeyRow);  // in flight meanwhile
+        const uint32_t io = div_u32(slot, slot_div);
+        const float2 ac = cf[slot];
+        const float dx = qh[3 * io] - k0, dy = qh[3 * io + 1] - k1, dz = qh[3 * io + 2] - k2;
+        const float ao = own ? ac.x : 0.0f;
+        const uint32_t nm = RowRef<BF16, O32>::name(io, dv);
+        static_for<0, kKeyRow / kKeyLoads>([&](auto bc) {
+            constexpr int b = decltype(bc)::value * kKeyLoads;
+            if (first + b < most)  // uniform
+                key_records<BF16, O32, CPL, b>(doh, dv, coff, nm, ao, acc);
+        });
+        if (own) {
+            s0 += ac.y * dx;
+            s1 += ac.y * dy;
+            s2 += ac.y * dz;
         }
     }
     s0 = group_sum(s0, kKeyRow);
@@ -600,11 +625,16 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int ch = lrow + c * kKeyRow;
-            if (ch < chunks) IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
+            if (ch < chunks) {
+                if (cnt == 0)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
+                IO::store(static_cast<T*>(dvout) + row * dv + ch * E, acc[c]);
+            }
         }
         if (lrow == 0) {
             // dk_j = (2/gamma^2) sum_i c_ij (q_i - k_j)
-            const float f = 2.0f * inv_g2;
+            const float f = 2.0f / (gm * gm);
             dk[3 * row] = f * s0;
             dk[3 * row + 1] = f * s1;
             dk[3 * row + 2] = f * s2;
@@ -612,24 +642,34 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     }
 }
 
-template <bool BF16>
-static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, const float* q,
-                             const float* k, const void* v, const float* gamma, const void* dout,
-                             const BwdBuffers& ws, const uint2* recs, const uint32_t* order,
-                             float* dk, void* dvout, hipStream_t s) {
-    const int64_t rows = BH * N;
+template <bool BF16, bool O32>
+static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int topk,
+                               const float* q, const float* k, const float* gamma,
+                               const void* dout, const BwdBuffers& ws, const uint2* recs,
+                               const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     const int chunks = dv / VecIO<BF16>::kElems;
     const int cpl = (chunks + kKeyRow - 1) / kKeyRow;
-    const int64_t tiles = (rows + (256 / kKeyRow) - 1) / (256 / kKeyRow);
+    const int64_t tph = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
-    auto kern = cpl <= 1 ? zeta_bwd_key_kernel<BF16, 1>
-              : cpl <= 2 ? zeta_bwd_key_kernel<BF16, 2>
-              : cpl <= 4 ? zeta_bwd_key_kernel<BF16, 4>
-                         : zeta_bwd_key_kernel<BF16, BF16 ? 4 : 8>;  // bf16 rows have <= 64 chunks
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, dout, ws.qstat, recs, ws.offs, order, rows, N, H, dv, ws.P, tiles,
-                       per, dk, dvout);
+    auto kern = cpl <= 1 ? zeta_bwd_key_kernel<BF16, O32, 1>
+              : cpl <= 2 ? zeta_bwd_key_kernel<BF16, O32, 2>
+              : cpl <= 4 ? zeta_bwd_key_kernel<BF16, O32, 4>
+                         : zeta_bwd_key_kernel<BF16, O32, BF16 ? 4 : 8>;  // bf16: <= 64 chunks
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k,
+                       gamma, dout, ws.coef, recs, ws.offs, order, N, H, dv, topk,
+                       make_div(static_cast<uint32_t>(topk)), ws.P, tph, tiles, per, dk, dvout);
     return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, int topk,
+                             const float* q, const float* k, const float* gamma,
+                             const void* dout, const BwdBuffers& ws, const uint2* recs,
+                             const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
+    if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
+        return launch_key_o<BF16, true>(BH, H, N, dv, topk, q, k, gamma, dout, ws, recs, order, dk, dvout, s);
+    return launch_key_o<BF16, false>(BH, H, N, dv, topk, q, k, gamma, dout, ws, recs, order, dk, dvout, s);
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
@@ -714,9 +754,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     if (e == hipSuccess) e = launch_order(BH, N, ws.zk, ws.perm_k, ws.ohist, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
-    e = launch_query<BF16>(rows, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,
-                           ws.perm_q, ws.qstat,
-                           dq, ws.dg_row, s);
+    e = launch_query<BF16>(BH, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,
+                           ws.perm_q, ws.coef, dq, ws.dg_row, s);
     if (e != hipSuccess) return e;
     marks.record(2, s);
 
@@ -737,7 +776,7 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
                        dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
                        dim3(256), 0, s, cur, ws.counts, ws.P, N, ws.offs);
     marks.record(3, s);
-    e = launch_key<BF16>(BH, H, N, dv, q, k, v, gamma, dout, ws, cur, ws.perm_k, dk, dvout, s);
+    e = launch_key<BF16>(BH, H, N, dv, topk, q, k, gamma, dout, ws, cur, ws.perm_k, dk, dvout, s);
     if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);

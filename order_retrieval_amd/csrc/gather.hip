@@ -19,38 +19,39 @@
 
 namespace zeta {
 
-// One 16-lane row (a DPP row) per query, four queries per wavefront.  Lane l owns slots l,
-// 16 + l, ...: it loads their indices and key rows and computes the weights, so all of the
-// row's index and key loads are in flight at once.  A slot is selected when it lies within
-// min(k, keys the query may use) and holds an index >= 0 (the exact selection fills all of
-// them; the chunked and several-curve selections can leave -1 there); a query with no
-// selected slot outputs zero.  The row then walks the slots in order:
-// index and weight come from the owning lane by a DPP row broadcast, every lane loads its
-// 16-byte chunk(s) of the value row (the loads of kGatherLoads slots are issued together,
-// none waits on another load) and accumulates in fp32.
+// One 16-lane row (a DPP row) per query, four queries per wavefront; a workgroup's 16 queries
+// belong to one (b,h), so the slice bases are uniform.  Lane l owns slots l, 16 + l, ...: it
+// loads their indices and key rows and computes the weights, so all of the row's index and key
+// loads are in flight at once.  A slot is selected when it lies within min(k, keys the query
+// may use) and holds an index >= 0 (the exact selection fills all of them; the chunked and
+// several-curve selections can leave -1 there); an unselected slot carries weight -1 and names
+// row 0, and a query with no selected slot outputs zero.  The row then walks the slots in
+// order: the value row's name and the weight come from the owning lane by a DPP row broadcast,
+// every lane loads its 16-byte chunk(s) of the value row (the loads of kGatherLoads slots are
+// issued together, none waits on another load) and accumulates in fp32.
 constexpr int kGatherLanes = 16;
 constexpr int kGatherLoads = 8;
+constexpr int kGatherRows = 256 / kGatherLanes;  // queries per workgroup
 
-template <bool BF16, int CPL, int L0>
+template <bool BF16, bool O32, int CPL, int L0>
 __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
-                                             int dv, const int (&coff)[CPL], int32_t jo, float so,
+                                             int dv, const int (&coff)[CPL], uint32_t jo, float so,
                                              float (&acc)[CPL][VecIO<BF16>::kElems]) {
     using IO = VecIO<BF16>;
+    using Ref = RowRef<BF16, O32>;
     using R = typename IO::raw_t;
     constexpr int E = IO::kElems;
     R raw[kGatherLoads][CPL];
-    int32_t jw[kGatherLoads];
     static_for<0, kGatherLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
-        jw[w] = static_cast<int32_t>(row_bcast<L0 + w>(static_cast<uint32_t>(jo)));
-        const int64_t jr = jw[w] < 0 ? 0 : jw[w];  // an empty slot reads key 0's row, adds nothing
+        const uint32_t nm = row_bcast<L0 + w>(jo);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) raw[w][c] = IO::load_raw(vh + jr * dv + coff[c]);
+        for (int c = 0; c < CPL; ++c) raw[w][c] = Ref::load(vh, nm, dv, coff[c]);
     });
     static_for<0, kGatherLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         const float s = row_bcast<L0 + w>(so);
-        if (jw[w] >= 0) {  // slot selected
+        if (!(s < 0.0f)) {  // slot selected (a NaN weight is summed and propagates)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 float x[E];
@@ -62,24 +63,25 @@ __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t*
     });
 }
 
-template <bool BF16, int CPL, int U>
+template <bool BF16, bool O32, int CPL, int U>
 __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
-    const uint32_t* __restrict__ order, void* __restrict__ out, int64_t rows, int64_t N,
-    int64_t H, int dv, int topk, int causal, int64_t tiles, int64_t per_xcd) {
+    const uint32_t* __restrict__ order, void* __restrict__ out, int64_t N, int64_t H, int dv,
+    int topk, int causal, int64_t tph, int64_t tiles, int64_t per_xcd) {
     using IO = VecIO<BF16>;
+    using Ref = RowRef<BF16, O32>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;  // uniform over the workgroup
+    const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
     const int lrow = threadIdx.x & (kGatherLanes - 1);
-    const int64_t t = tile * (blockDim.x / kGatherLanes) + threadIdx.x / kGatherLanes;
-    const bool live = t < rows;
-    const int64_t tt = live ? t : rows - 1;  // a row past the end reads a real query, stores nothing
+    const int64_t pos = (tile - bh * tph) * kGatherRows + threadIdx.x / kGatherLanes;
+    const bool live = pos < N;
+    const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real query, stores nothing
     const int chunks = dv / E;
-    const int64_t bh = tt / N;
-    const int64_t i = order ? static_cast<int64_t>(order[tt]) : tt - bh * N;
+    const int64_t i = order ? static_cast<int64_t>(order[bh * N + pp]) : pp;
     const int64_t row = bh * N + i;
     const float g = gamma[bh % H];
     const float inv_g2 = 1.0f / (g * g);
@@ -92,20 +94,20 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
-    int32_t jo[U];
+    uint32_t jo[U];
     float so[U];
     float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int r = lrow + u * kGatherLanes;
-        jo[u] = -1;
-        so[u] = 0.0f;
+        jo[u] = 0;
+        so[u] = -1.0f;
         const int32_t jr = r < m ? ir[r] : -1;
         if (jr >= 0) {
             // a selection has j <= jmax; clamping keeps every access in bounds
             const int32_t j = jr > jmax ? static_cast<int32_t>(jmax) : jr;
             const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
-            jo[u] = j;
+            jo[u] = Ref::name(j, dv);
             so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
             ssum += so[u];
             nsel += 1.0f;
@@ -133,7 +135,7 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
             static_for<0, kGatherLanes / kGatherLoads>([&](auto bc) {
                 constexpr int b = decltype(bc)::value;
                 if (u * kGatherLanes + b * kGatherLoads < most)
-                    gather_slots<BF16, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u], acc);
+                    gather_slots<BF16, O32, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u], acc);
             });
         }
     });
@@ -154,20 +156,31 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     }
 }
 
-template <bool BF16, int CPL>
-static hipError_t launch_gather_c(int64_t rows, int64_t N, int64_t H, int dv, int topk,
+template <bool BF16, bool O32, int CPL>
+static hipError_t launch_gather_c(int64_t BH, int64_t N, int64_t H, int dv, int topk,
                                   int causal, const float* q, const float* k, const void* v,
                                   const float* gamma, const int32_t* idx, const uint32_t* order,
                                   void* out, hipStream_t s) {
-    const int64_t tiles = (rows + (256 / kGatherLanes) - 1) / (256 / kGatherLanes);
+    const int64_t tph = (N + kGatherRows - 1) / kGatherRows;
+    const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
     const int u = (topk + kGatherLanes - 1) / kGatherLanes;  // slots per lane (<= 4)
-    auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, CPL, 1>
-              : u <= 2 ? zeta_cauchy_gather_kernel<BF16, CPL, 2>
-                       : zeta_cauchy_gather_kernel<BF16, CPL, 4>;
+    auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 1>
+              : u <= 2 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 2>
+                       : zeta_cauchy_gather_kernel<BF16, O32, CPL, 4>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
-                       gamma, idx, order, out, rows, N, H, dv, topk, causal, tiles, per);
+                       gamma, idx, order, out, N, H, dv, topk, causal, tph, tiles, per);
     return hipGetLastError();
+}
+
+template <bool BF16, int CPL>
+static hipError_t launch_gather_o(int64_t BH, int64_t N, int64_t H, int dv, int topk,
+                                  int causal, const float* q, const float* k, const void* v,
+                                  const float* gamma, const int32_t* idx, const uint32_t* order,
+                                  void* out, hipStream_t s) {
+    if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
+        return launch_gather_c<BF16, true, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, order, out, s);
+    return launch_gather_c<BF16, false, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, order, out, s);
 }
 
 hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal,
@@ -175,18 +188,18 @@ hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk,
                          const float* gamma, const int32_t* idx, const uint32_t* order, void* out,
                          hipStream_t s) {
     const int cz = causal ? 1 : 0;
-    const int64_t rows = BH * N;
-    if (rows <= 0) return hipSuccess;
+    if (BH * N <= 0) return hipSuccess;
     const int cpl = static_cast<int>((dv / (bf16 ? 8 : 4) + kGatherLanes - 1) / kGatherLanes);
+    const int d = static_cast<int>(dv);
     if (bf16) {  // bf16 rows have <= 64 chunks
-        if (cpl <= 1) return launch_gather_c<true, 1>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
-        if (cpl <= 2) return launch_gather_c<true, 2>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
-        return launch_gather_c<true, 4>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+        if (cpl <= 1) return launch_gather_o<true, 1>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
+        if (cpl <= 2) return launch_gather_o<true, 2>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
+        return launch_gather_o<true, 4>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
     }
-    if (cpl <= 1) return launch_gather_c<false, 1>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
-    if (cpl <= 2) return launch_gather_c<false, 2>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
-    if (cpl <= 4) return launch_gather_c<false, 4>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
-    return launch_gather_c<false, 8>(rows, N, H, (int)dv, topk, cz, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 1) return launch_gather_o<false, 1>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 2) return launch_gather_o<false, 2>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
+    if (cpl <= 4) return launch_gather_o<false, 4>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
+    return launch_gather_o<false, 8>(BH, N, H, d, topk, cz, q, k, v, gamma, idx, order, out, s);
 }
 
 }  // namespace zeta

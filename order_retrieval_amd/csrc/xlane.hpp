@@ -8,10 +8,13 @@
 namespace zeta {
 
 // x from another lane of the same 16-lane row, by a DPP pattern (a modifier of the VALU
-// instruction that reads it, no LDS round trip).  Every lane is active where these are used.
+// instruction that reads it, no LDS round trip).  Every lane is active where these are used,
+// and every pattern here reads a lane of the same row, so no lane ever takes the zero that
+// bound_ctrl supplies for a missing source; setting it lets the compiler fold the move into
+// the instruction that consumes it (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_take(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
@@ -37,7 +40,7 @@ template <int L>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
     static_assert(L >= 0 && L < 16, "a row has 16 lanes");
     return static_cast<uint32_t>(
-        __builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x150 + L, 0xF, 0xF, false));
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x150 + L, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of G lanes (G a power of two, 8 <= G <= 64).  Each step adds the

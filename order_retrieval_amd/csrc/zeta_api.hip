@@ -189,7 +189,7 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
         off += align_up(bytes);
         return at;
     };
-    p.qs = take(2 * sizeof(float) * BH * N);
+    p.qs = take(2 * sizeof(float) * BH * N * K);
     p.dg = take(sizeof(float) * BH * N);
     p.dgp = take(sizeof(float) * sh->H * zeta::dgamma_chunks(sh->B, N));
     p.r0 = take(8 * BH * p.P);
@@ -440,7 +440,7 @@ zeta_status zeta_bwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
     zeta::BwdBuffers b{};
-    b.qstat = at<float2>(workspace, p.qs);
+    b.coef = at<float2>(workspace, p.qs);
     b.dg_row = at<float>(workspace, p.dg);
     b.dg_part = at<float>(workspace, p.dgp);
     b.rec0 = at<uint2>(workspace, p.r0);

@@ -92,7 +92,7 @@ hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* 
                         uint32_t* scratch, hipStream_t s);
 
 struct BwdBuffers {
-    float2* qstat;    // [BHN] per-query {1/S_i, D_i}
+    float2* coef;     // [BH, N, topk] per selection slot {a_ij, c_ij}
     float* dg_row;    // [BHN] per-query dgamma contributions
     float* dg_part;   // [H][dgamma_chunks] partial sums
     uint2* rec0;      // [BH][P] radix-sort ping-pong records {j, i}

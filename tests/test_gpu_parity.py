@@ -315,6 +315,15 @@ def test_backward_beyond_two_byte_keys():
     _bwd_sampled_check(w, n_rows=300, tail=128)
 
 
+def test_slices_beyond_32bit_row_offsets():
+    # a (b,h) slice of value rows spanning 2^31 bytes: the gather and both backward passes
+    # address rows with 64-bit offsets there (32-bit byte offsets below that size)
+    w = W("wide", 1, 1, 1 << 20, 512, 4, inputs.F32, "normal", seed=29, backward=True)
+    log("forward+backward N=2^20 dV=512 fp32 (64-bit row offsets)")
+    _forward_check(w, sample_rows(w, 200, seed=7))
+    _bwd_sampled_check(w, n_rows=200, tail=64)
+
+
 @pytest.mark.parametrize("name", ["clustered", "long_fwd_bwd"])
 def test_backward_sampled(name):
     w = CFG[name]
