@@ -120,18 +120,18 @@ def kernel_bytes(w: inputs.Workload) -> dict:
     b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + 4 + row).sum())
     b["bwd_order"] = BH * w.N * (2 * 12 + 2 * 4 + 2 * 12)
     # per query: index row, q, key rows, value rows, dO row, dq and dgamma term, processing
-    # order entry, {1/S, D}
-    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 16 + 4 + 8).sum())
+    # order entry, and {a, c} of every selected slot
+    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 16 + 4 + 8 * m).sum())
     bits = int(np.ceil(np.log2(w.N))) if w.N > 1 else 0
     passes = 1 if bits <= 8 else -(-bits // 8)
-    # pass 0 reads the index rows twice (histogram, scatter) and writes 8-byte {j, i} records;
+    # pass 0 reads the index rows twice (histogram, scatter) and writes 8-byte {j, p} records;
     # every further pass reads the records twice (histogram, scatter) and writes them; the
     # segment starts read the sorted records and write N+1 offsets
     b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 24 * pairs +
                                8 * pairs + 4 * (w.N + 1))
-    # per key: gamma, two offsets, k, dk, its value row and its dv row; per pair: the record,
-    # q_i, {1/S_i, D_i} and the dO_i row
-    b["bwd_key"] = BH * (w.N * (4 + 8 + 12 + 12 + 2 * row) + pairs * (8 + 12 + 8 + row))
+    # per key: gamma, two offsets, k, dk and its dv row; per pair: the record, {a, c}, q_i
+    # and the dO_i row
+    b["bwd_key"] = BH * (w.N * (4 + 8 + 12 + 12 + row) + pairs * (8 + 8 + 12 + row))
     b["bwd_dgamma"] = BH * w.N * 4.0
     return b
 
