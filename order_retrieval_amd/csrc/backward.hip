@@ -10,9 +10,12 @@
 // Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
 //   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij of every
 //      selection slot, dq_i and the query's dgamma term;
-//   2. selection transpose: stable LSD radix sort (8-bit digits) of the pairs of every (b,h)
-//      by j, carrying 8-byte records {j, slot}; queries stay ascending inside a key's segment;
-//   3. segment starts offs[j] from the sorted keys;
+//   2. selection transpose, a stable radix sort of the pairs of every (b,h) by key: a global
+//      pass on the low byte of j builds 8-byte records {j, slot} grouped by that byte;
+//   3. keys below 2^16: one workgroup per low-byte group sorts it on the high byte and writes
+//      every key's segment bounds, leaving the slots in contiguous per-key segments (queries
+//      ascending inside a segment); larger keys: global passes on the further bytes, then
+//      the segment starts from the sorted keys;
 //   4. per-key pass (keys in Z-order): each key gathers its pairs' {a_ij, c_ij}, q_i and dO_i
 //      rows and reduces its segment in a fixed order (dv, dk);
 //   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
@@ -276,6 +279,24 @@ __device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
     return true;
 }
 
+// Lanes of the wavefront whose 8-bit digit equals this lane's, among the valid ones: the
+// AND over the digit's bits of the ballot of that bit (or of its complement where the lane's
+// bit is 0).  Each bit's 0 / all-ones mask is a sign-extended bit field, so a bit costs a
+// compare, a field extract and an xor per 32-bit half (gfx950 folds the AND into v_bitop3).
+__device__ __forceinline__ uint64_t digit_peers(uint32_t digit, bool valid) {
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
+    uint32_t hi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(digit << (31 - b)) >> 31);
+        const uint64_t bal = __ballot(m != 0u);
+        lo &= ~(static_cast<uint32_t>(bal) ^ m);
+        hi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
+    }
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Digit counts of one tile of items.  Pass 0 takes every selection slot (items = N * topk)
 // and keeps the pairs; later passes take the first counts[bh] records.
 template <bool FIRST>
@@ -391,13 +412,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     for (int it = 0; it < kRadixItems; ++it) {
         const bool valid = (okmask >> it) & 1u;
         const uint32_t digit = valid ? (rec[it].x >> shift) & 255u : 0u;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = (digit >> b) & 1u;
-            const uint64_t bal = __ballot(bit);
-            peers &= bit ? bal : ~bal;
-        }
+        const uint64_t peers = digit_peers(digit, valid);
         // every lane reads the running count before the group's first lane advances it (LDS
         // operations of one wavefront take effect in program order)
         const uint32_t before = valid ? wcnt[wave][digit] : 0u;
@@ -456,8 +471,156 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------- 3. offsets
-// offs[j] = first record of key j (records sorted by key), offs[N] = number of pairs.
+// ---------------------------------------------------------------------------- 3. segments
+// Keys below 2^16: the one global pass sorts the records stably by the low byte of j, so
+// bucket b holds the pairs of the keys j with j mod 256 = b (every bucket about 1/256 of the
+// pairs, whatever the key popularity) in ascending slot order.  One workgroup per bucket
+// finishes the sort on the high byte of j: it counts the bucket's digits (one per key),
+// writes every key's segment [begin, end) from their exclusive scan, and scatters the records
+// stably a tile at a time (ranked by ballots and staged in LDS like a radix tile), so the
+// slots p land in contiguous runs inside the bucket's range, ascending p inside a key.
+// A key's segment is contiguous; the segments are not in key order (the per-key pass only
+// needs each one's bounds).
+
+// Inclusive sum over the workgroup's 256 threads of one value each (wavefront shuffles, then
+// the four wavefront totals).  `part` holds 4 words; the caller syncs before reusing it.
+__device__ __forceinline__ uint32_t scan256_incl(uint32_t v, uint32_t* part) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) part[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += part[w];
+    return x;
+}
+
+__global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
+    const uint2* __restrict__ rin, const uint32_t* __restrict__ totals, int64_t N, int64_t P,
+    uint32_t* __restrict__ slots, uint32_t* __restrict__ begin, uint32_t* __restrict__ end) {
+    static_assert(kRadixThreads == 256, "one thread per digit");
+    constexpr int kWaves = kRadixThreads / 64;
+    constexpr int kWaveItems = kRadixTile / kWaves;
+    __shared__ uint2 stage[kRadixTile];
+    __shared__ uint32_t wcnt[kWaves][256];
+    __shared__ uint32_t run[256];   // bucket-relative output position of each digit's next record
+    __shared__ int32_t delta[256];
+    __shared__ uint32_t part[kWaves];
+    const int64_t bh = blockIdx.y;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+
+    // the bucket's records [s0, s1): the pass's digit totals are the bucket sizes
+    uint32_t s0, s1;
+    {
+        const uint32_t incl = scan256_incl(totals[bh * 256 + tid], part);
+        if (tid == b) run[0] = incl;
+        __syncthreads();
+        s1 = run[0];
+        s0 = s1 - totals[bh * 256 + b];
+        __syncthreads();
+    }
+    const uint32_t n = s1 - s0;
+    const uint2* rb = rin + bh * P + s0;
+
+    // digit counts over the bucket; the first tile stays in registers for the scatter
+    run[tid] = 0;
+    __syncthreads();
+    uint2 rec[kRadixItems];
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it) {
+        const uint32_t e = wave * kWaveItems + it * 64 + lane;
+        rec[it] = make_uint2(0, 0);
+        if (e < n) {
+            rec[it] = rb[e];
+            atomicAdd(&run[rec[it].x >> 8], 1u);
+        }
+    }
+    for (uint32_t c0 = kRadixTile; c0 < n; c0 += kRadixTile) {
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) {
+            const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
+            if (e < n) atomicAdd(&run[rb[e].x >> 8], 1u);
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t c = run[tid];
+        const uint32_t ex = scan256_incl(c, part) - c;
+        const int64_t j = static_cast<int64_t>(tid) * 256 + b;  // the key of digit tid
+        if (j < N) {
+            begin[bh * (N + 1) + j] = s0 + ex;
+            end[bh * (N + 1) + j] = s0 + ex + c;
+        }
+        __syncthreads();
+        run[tid] = ex;
+    }
+
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t* out = slots + bh * P + s0;
+    for (uint32_t c0 = 0; c0 < n; c0 += kRadixTile) {
+        if (c0 > 0) {
+#pragma unroll
+            for (int it = 0; it < kRadixItems; ++it) {
+                const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
+                rec[it] = e < n ? rb[e] : make_uint2(0, 0);
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
+        __syncthreads();
+        // rank of every record among the equal digits before it in this wavefront's share
+        uint32_t lrank[kRadixItems];
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) {
+            const bool valid = c0 + wave * kWaveItems + it * 64 + lane < n;
+            const uint32_t digit = rec[it].x >> 8;
+            const uint64_t peers = digit_peers(digit, valid);
+            const uint32_t before = valid ? wcnt[wave][digit] : 0u;
+            if (valid && (peers & lt) == 0) wcnt[wave][digit] = before + __popcll(peers);
+            lrank[it] = before + __popcll(peers & lt);
+        }
+        __syncthreads();
+        uint32_t tile_cnt = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tile_cnt += wcnt[w][tid];
+        const uint32_t lstart = scan256_incl(tile_cnt, part) - tile_cnt;
+        delta[tid] = static_cast<int32_t>(run[tid]) - static_cast<int32_t>(lstart);
+        uint32_t r = lstart;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = wcnt[w][tid];
+            wcnt[w][tid] = r;
+            r += c;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) {
+            if (c0 + wave * kWaveItems + it * 64 + lane < n)
+                stage[wcnt[wave][rec[it].x >> 8] + lrank[it]] = rec[it];
+        }
+        __syncthreads();
+        const uint32_t items = n - c0 < kRadixTile ? n - c0 : kRadixTile;
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) {
+            const uint32_t t = it * kRadixThreads + tid;
+            if (t < items) {
+                const uint2 rr = stage[t];
+                out[delta[rr.x >> 8] + static_cast<int32_t>(t)] = rr.y;
+            }
+        }
+        run[tid] += tile_cnt;
+        __syncthreads();
+    }
+}
+
+// Keys of more than 16 bits: the global passes sort the records fully by j, and
+// offs[j] = first record of key j, offs[N] = number of pairs (key j's segment is
+// [offs[j], offs[j+1])).
 __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* __restrict__ recs,
                                                                     const uint32_t* __restrict__ counts,
                                                                     int64_t P, int64_t N,
@@ -550,8 +713,9 @@ template <bool BF16, bool O32, int CPL>
 __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
     const void* __restrict__ dout, const float2* __restrict__ coef,
-    const uint2* __restrict__ recs, const uint32_t* __restrict__ offs,
-    const uint32_t* __restrict__ order, int64_t N, int64_t H, int dv, int topk, DivU32 slot_div,
+    const uint32_t* __restrict__ slots, int slot_stride, const uint32_t* __restrict__ seg_lo,
+    const uint32_t* __restrict__ seg_hi, const uint32_t* __restrict__ order, int64_t N,
+    int64_t H, int dv, int topk, DivU32 slot_div,
     int64_t P, int64_t tph, int64_t tiles, int64_t per_xcd, float* __restrict__ dk,
     void* __restrict__ dvout) {
     using IO = VecIO<BF16>;
@@ -569,9 +733,9 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     const int chunks = dv / E;
     const float gm = gamma[bh % H];
     const float k0 = k[3 * row], k1 = k[3 * row + 1], k2 = k[3 * row + 2];
-    const uint32_t seg0 = offs[bh * (N + 1) + j];
-    const int cnt = live ? static_cast<int>(offs[bh * (N + 1) + j + 1] - seg0) : 0;
-    const uint2* rh = recs + bh * P + seg0;
+    const uint32_t seg0 = seg_lo[bh * (N + 1) + j];
+    const int cnt = live ? static_cast<int>(seg_hi[bh * (N + 1) + j] - seg0) : 0;
+    const uint32_t* rh = slots + (bh * P + seg0) * slot_stride;
     const float* qh = q + bh * N * 3;
     const float2* cf = coef + bh * N * topk;
     const T* doh = static_cast<const T*>(dout) + bh * N * dv;
@@ -594,7 +758,9 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     // a row the key sums anyway (exactly nothing unless that row is not finite, and then the
     // key's sum already is not).  A key with no pairs stores zeros.
     const int last = cnt > 0 ? cnt - 1 : 0;
-    auto slot_at = [&](int p) -> uint32_t { return cnt > 0 ? rh[p < last ? p : last].y : 0u; };
+    auto slot_at = [&](int p) -> uint32_t {
+        return cnt > 0 ? rh[(p < last ? p : last) * slot_stride] : 0u;
+    };
     uint32_t slot_next = slot_at(lrow);
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
     for (int first = 0; first < most; first += kKeyRow) {  // batches of 16 records
@@ -642,10 +808,18 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     }
 }
 
+// A key's pairs: slots[(segment start + r) * slot_stride], r < seg_hi[j] - seg_lo[j].
+struct KeySegments {
+    const uint32_t* slots;
+    int stride;
+    const uint32_t* lo;
+    const uint32_t* hi;
+};
+
 template <bool BF16, bool O32>
 static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int topk,
                                const float* q, const float* k, const float* gamma,
-                               const void* dout, const BwdBuffers& ws, const uint2* recs,
+                               const void* dout, const BwdBuffers& ws, const KeySegments& sg,
                                const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     const int chunks = dv / VecIO<BF16>::kElems;
     const int cpl = (chunks + kKeyRow - 1) / kKeyRow;
@@ -657,7 +831,8 @@ static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int top
               : cpl <= 4 ? zeta_bwd_key_kernel<BF16, O32, 4>
                          : zeta_bwd_key_kernel<BF16, O32, BF16 ? 4 : 8>;  // bf16: <= 64 chunks
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k,
-                       gamma, dout, ws.coef, recs, ws.offs, order, N, H, dv, topk,
+                       gamma, dout, ws.coef, sg.slots, sg.stride, sg.lo, sg.hi, order, N, H, dv,
+                       topk,
                        make_div(static_cast<uint32_t>(topk)), ws.P, tph, tiles, per, dk, dvout);
     return hipGetLastError();
 }
@@ -665,11 +840,11 @@ static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int top
 template <bool BF16>
 static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, int topk,
                              const float* q, const float* k, const float* gamma,
-                             const void* dout, const BwdBuffers& ws, const uint2* recs,
+                             const void* dout, const BwdBuffers& ws, const KeySegments& sg,
                              const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
-        return launch_key_o<BF16, true>(BH, H, N, dv, topk, q, k, gamma, dout, ws, recs, order, dk, dvout, s);
-    return launch_key_o<BF16, false>(BH, H, N, dv, topk, q, k, gamma, dout, ws, recs, order, dk, dvout, s);
+        return launch_key_o<BF16, true>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, order, dk, dvout, s);
+    return launch_key_o<BF16, false>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, order, dk, dvout, s);
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
@@ -724,6 +899,7 @@ size_t bwd_pairs_per_head(int64_t N, int topk, bool causal) {
 
 int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
 
+
 // items: slots of pass 0 (N * topk), else the upper bound P of the pairs per (b,h) (the
 // grid size; the kernels stop at the device-side count).
 template <bool FIRST>
@@ -761,22 +937,34 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
 
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
-    const int passes = bits <= 8 ? 1 : (bits + 7) / 8;
     const PairSpec ps{topk, causal ? 1 : 0, N};
+    KeySegments sg{};
     radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
-    uint2* cur = ws.rec0;
-    for (int p = 1; p < passes; ++p) {
-        uint2* nxt = (p & 1) ? ws.rec1 : ws.rec0;
-        radix_pass<false>(BH, nullptr, cur, ws.P, ws.P, 8 * p, ps, ws, nxt, s);
-        cur = nxt;
+    if (bits <= 16) {
+        // one global pass on the low byte of j, then one workgroup per low-byte bucket
+        uint32_t* sl = reinterpret_cast<uint32_t*>(ws.rec1);
+        hipLaunchKernelGGL(zeta_bucket_sort_kernel,
+                           dim3(static_cast<unsigned>(N < 256 ? N : 256), static_cast<unsigned>(BH)),
+                           dim3(kRadixThreads), 0, s, ws.rec0, ws.totals, N, ws.P, sl, ws.offs,
+                           ws.ends);
+        sg = KeySegments{sl, 1, ws.offs, ws.ends};
+    } else {
+        // LSD passes over every byte of j, then the segment starts from the sorted keys
+        uint2* cur = ws.rec0;
+        for (int shift = 8; shift < bits; shift += 8) {
+            uint2* nxt = cur == ws.rec0 ? ws.rec1 : ws.rec0;
+            radix_pass<false>(BH, nullptr, cur, ws.P, ws.P, shift, ps, ws, nxt, s);
+            cur = nxt;
+        }
+        hipLaunchKernelGGL(zeta_segment_offsets_kernel,
+                           dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
+                           dim3(256), 0, s, cur, ws.counts, ws.P, N, ws.offs);
+        sg = KeySegments{reinterpret_cast<const uint32_t*>(cur) + 1, 2, ws.offs, ws.offs + 1};
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(zeta_segment_offsets_kernel,
-                       dim3(static_cast<unsigned>((ws.P + 255) / 256), static_cast<unsigned>(BH)),
-                       dim3(256), 0, s, cur, ws.counts, ws.P, N, ws.offs);
     marks.record(3, s);
-    e = launch_key<BF16>(BH, H, N, dv, topk, q, k, gamma, dout, ws, cur, ws.perm_k, dk, dvout, s);
+    e = launch_key<BF16>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, ws.perm_k, dk, dvout, s);
     if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);

@@ -174,7 +174,7 @@ FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
 }
 
 struct BwdPlan {
-    size_t qs, dg, dgp, r0, r1, hist, totals, counts, offs, zq, pq, zk, pk, ohist, total;
+    size_t qs, dg, dgp, r0, r1, hist, totals, counts, offs, ends, zq, pq, zk, pk, ohist, total;
     int64_t P, tiles;
 };
 
@@ -198,6 +198,7 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
     p.totals = take(sizeof(uint32_t) * BH * 256);
     p.counts = take(sizeof(uint32_t) * BH);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
+    p.ends = take(sizeof(uint32_t) * BH * (N + 1));
     p.zq = take(sizeof(uint32_t) * BH * N);
     p.pq = take(sizeof(uint32_t) * BH * N);
     p.zk = take(sizeof(uint32_t) * BH * N);
@@ -449,6 +450,7 @@ zeta_status zeta_bwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     b.totals = at<uint32_t>(workspace, p.totals);
     b.counts = at<uint32_t>(workspace, p.counts);
     b.offs = at<uint32_t>(workspace, p.offs);
+    b.ends = at<uint32_t>(workspace, p.ends);
     b.zq = at<uint32_t>(workspace, p.zq);
     b.perm_q = at<uint32_t>(workspace, p.pq);
     b.zk = at<uint32_t>(workspace, p.zk);

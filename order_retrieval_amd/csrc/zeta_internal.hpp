@@ -95,12 +95,13 @@ struct BwdBuffers {
     float2* coef;     // [BH, N, topk] per selection slot {a_ij, c_ij}
     float* dg_row;    // [BHN] per-query dgamma contributions
     float* dg_part;   // [H][dgamma_chunks] partial sums
-    uint2* rec0;      // [BH][P] radix-sort ping-pong records {j, i}
-    uint2* rec1;
+    uint2* rec0;      // [BH][P] radix-sort ping-pong records {j, p}; with keys below 2^16
+    uint2* rec1;      // rec1 takes the final slot list (u32 p per pair, in key segments)
     uint32_t* hist;   // [BH][256][tiles] per-tile digit counts, scanned in place
     uint32_t* totals; // [BH][256] digit totals
     uint32_t* counts; // [BH] pairs of each (b,h)
     uint32_t* offs;   // [BH][N+1] segment starts of the key-sorted pair list
+    uint32_t* ends;   // [BH][N+1] segment ends (keys below 2^16: segments not in key order)
     uint32_t* zq;     // [BHN] query codes
     uint32_t* perm_q; // [BHN] query processing order
     uint32_t* zk;     // [BHN] key codes
