@@ -123,12 +123,17 @@ def kernel_bytes(w: inputs.Workload) -> dict:
     # order entry, and {a, c} of every selected slot
     b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 16 + 4 + 8 * m).sum())
     bits = int(np.ceil(np.log2(w.N))) if w.N > 1 else 0
-    passes = 1 if bits <= 8 else -(-bits // 8)
     # pass 0 reads the index rows twice (histogram, scatter) and writes 8-byte {j, p} records;
-    # every further pass reads the records twice (histogram, scatter) and writes them; the
-    # segment starts read the sorted records and write N+1 offsets
-    b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 24 * pairs +
-                               8 * pairs + 4 * (w.N + 1))
+    # keys below 2^16: the per-group sort reads the records twice (count, scatter) and writes
+    # 4-byte slots and two segment bounds per key; wider keys: every further pass reads the
+    # records twice and writes them, and the segment starts read the sorted records
+    if bits <= 16:
+        b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + 16 * pairs + 4 * pairs +
+                                   8 * w.N)
+    else:
+        passes = -(-bits // 8)
+        b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 24 * pairs +
+                                   8 * pairs + 4 * (w.N + 1))
     # per key: gamma, two offsets, k, dk and its dv row; per pair: the record, {a, c}, q_i
     # and the dO_i row
     b["bwd_key"] = BH * (w.N * (4 + 8 + 12 + 12 + row) + pairs * (8 + 8 + 12 + row))
