@@ -131,8 +131,12 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     constexpr int E = K / L;
     const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
     // skip when the walk is empty or its first candidate does not beat the current K-th
+    // (every load below reads a clamped, in-run position and the value is selected after, so
+    // no load sits behind a branch and they all issue before the first wait)
     const bool empty = RIGHT ? p >= s : p <= 0;
-    const uint64_t first = empty ? ~0ull : (RIGHT ? run[p] - target : top - run[p - 1]);
+    const int64_t p0 = RIGHT ? (empty ? s - 1 : p) : (empty ? 0 : p - 1);
+    const uint64_t e0 = run[p0];
+    const uint64_t first = empty ? ~0ull : (RIGHT ? e0 - target : top - e0);
     const uint64_t kth = from_last_lane<L>(best[E - 1]);
     if (first >= kth) return;
     constexpr int CH = kChunk < E ? kChunk : E;
@@ -149,10 +153,11 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
 #pragma unroll
         for (int v = 0; v < CH; ++v) {
             const int u = u0 + v;
-            if (RIGHT)
-                c[v] = u > lim ? wp[-u] - target : ~0ull;
-            else
-                c[v] = u >= lim ? top - wp[u] : ~0ull;
+            const bool ok = RIGHT ? u > lim : u >= lim;
+            // an invalid entry reads the walk's first position instead (inside the run)
+            const int64_t at = ok ? b + (RIGHT ? -u : u) : p0;
+            const uint64_t e = run[at];
+            c[v] = ok ? (RIGHT ? e - target : top - e) : ~0ull;
         }
 #pragma unroll
         for (int v = 0; v < CH; ++v) best[u0 + v] = c[v] < best[u0 + v] ? c[v] : best[u0 + v];
@@ -219,16 +224,36 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 roff[gi] = static_cast<int64_t>(l) * N + static_cast<int64_t>((m >> (l + 1)) << (l + 1));
             }
         }
+        // the probes of the group's runs are unconditional loads (a run that has no probe at
+        // this step reads its own first entry), so they are in flight together
+        int64_t len[kSearchGroup];
+#pragma unroll
+        for (int gi = 0; gi < kSearchGroup; ++gi) len[gi] = lv[gi] >= 0 ? int64_t(1) << lv[gi] : 1;
         for (int64_t step = (int64_t(1) << lv[0]) >> 1; step > 0; step >>= 1) {
+            uint64_t e[kSearchGroup];
+#pragma unroll
+            for (int gi = 0; gi < kSearchGroup; ++gi) {
+                const int64_t at = pos[gi] + step - 1;
+                e[gi] = hA[roff[gi] + (at < len[gi] ? at : len[gi] - 1)];
+            }
+            // an empty asm that takes every probe keeps the loads unconditional (the compiler
+            // would otherwise move each behind its run's step test and wait on it alone)
+#pragma unroll
+            for (int gi = 0; gi < kSearchGroup; ++gi) asm volatile("" : "+v"(e[gi]));
 #pragma unroll
             for (int gi = 0; gi < kSearchGroup; ++gi)
-                if (lv[gi] >= 0 && step < (int64_t(1) << lv[gi]) &&
-                    hA[roff[gi] + pos[gi] + step - 1] < target)
-                    pos[gi] += step;
+                if (pos[gi] + step < len[gi] && e[gi] < target) pos[gi] += step;
         }
+        {
+            uint64_t e[kSearchGroup];
 #pragma unroll
-        for (int gi = 0; gi < kSearchGroup; ++gi)
-            if (lv[gi] >= 0 && hA[roff[gi] + pos[gi]] < target) pos[gi] += 1;
+            for (int gi = 0; gi < kSearchGroup; ++gi) e[gi] = hA[roff[gi] + pos[gi]];
+#pragma unroll
+            for (int gi = 0; gi < kSearchGroup; ++gi) asm volatile("" : "+v"(e[gi]));
+#pragma unroll
+            for (int gi = 0; gi < kSearchGroup; ++gi)
+                if (lv[gi] >= 0 && e[gi] < target) pos[gi] += 1;
+        }
 #pragma unroll
         for (int gi = 0; gi < kSearchGroup; ++gi) {
             if (lv[gi] >= 0) {
