@@ -45,13 +45,13 @@ struct PairSpec {
     int64_t N;
 };
 
-__device__ __forceinline__ bool pair_item(const int32_t* __restrict__ idx, int64_t e,
-                                          const PairSpec& ps, uint32_t& key) {
+// j: the index stored in slot e.
+__device__ __forceinline__ bool pair_item(int32_t j, int64_t e, const PairSpec& ps,
+                                          uint32_t& key) {
     const uint32_t i = static_cast<uint32_t>(e) / static_cast<uint32_t>(ps.topk);
     const uint32_t r = static_cast<uint32_t>(e) - i * static_cast<uint32_t>(ps.topk);
     const int64_t nk = ps.causal ? static_cast<int64_t>(i) + 1 : ps.N;
     if (r >= nk) return false;  // slot beyond min(topk, nk)
-    const int32_t j = idx[e];
     if (j < 0) return false;    // no selection in this slot
     key = static_cast<uint32_t>(clamp_index(j, nk - 1));
     return true;
@@ -129,36 +129,62 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
+    // every setup load reads a clamped position and is held live before any test, so the
+    // loads of a kind are in flight together
     float go[CPL][E];
     int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet go = 0)
+    typename IO::raw_t graw[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int ch = lrow + c * kRowLanes;
         coff[c] = (ch < chunks ? ch : chunks - 1) * E;
+        graw[c] = IO::load_raw(static_cast<const T*>(dout) + row * dv + coff[c]);
+    }
+    int32_t jr[U];
 #pragma unroll
-        for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
-        if (ch < chunks) IO::load(static_cast<const T*>(dout) + row * dv + ch * E, go[c]);
+    for (int u = 0; u < U; ++u) {
+        const int r = lrow + u * kRowLanes;
+        jr[u] = ir[r < topk ? r : topk - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) keep(jr[u]);
+    bool sel[U];
+    float kx[U], ky[U], kz[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        sel[u] = lrow + u * kRowLanes < m && jr[u] >= 0;
+        jr[u] = sel[u] ? static_cast<int32_t>(clamp_index(jr[u], nk - 1)) : 0;
+        kx[u] = kh[3 * jr[u]];
+        ky[u] = kh[3 * jr[u] + 1];
+        kz[u] = kh[3 * jr[u] + 2];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        keep(kx[u]);
+        keep(ky[u]);
+        keep(kz[u]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        IO::unpack(graw[c], go[c]);
+        if (lrow + c * kRowLanes >= chunks)
+#pragma unroll
+            for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
     }
 
     uint32_t jo[U];
-    bool sel[U];
     float so[U], dx[U], dy[U], dz[U], gg[U];
     float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lrow + u * kRowLanes;
         jo[u] = 0;  // not selected: names key 0's row, never summed
-        sel[u] = false;
         so[u] = dx[u] = dy[u] = dz[u] = gg[u] = 0.0f;
-        const int32_t jr = r < m ? ir[r] : -1;
-        if (jr >= 0) {
-            const int32_t j = static_cast<int32_t>(clamp_index(jr, nk - 1));
-            jo[u] = RowRef<BF16, O32>::name(j, dv);
-            sel[u] = true;
+        if (sel[u]) {
+            jo[u] = RowRef<BF16, O32>::name(jr[u], dv);
             nsel += 1.0f;
-            dx[u] = q0 - kh[3 * j];
-            dy[u] = q1 - kh[3 * j + 1];
-            dz[u] = q2 - kh[3 * j + 2];
+            dx[u] = q0 - kx[u];
+            dy[u] = q1 - ky[u];
+            dz[u] = q2 - kz[u];
             so[u] = 1.0f / (1.0f + (dx[u] * dx[u] + dy[u] * dy[u] + dz[u] * dz[u]) * inv_g2);
             ssum += so[u];
         }
@@ -265,17 +291,28 @@ static hipError_t launch_query(int64_t BH, int64_t N, int64_t H, int dv, int top
 // pair's selection slot.  Pass 0 reads the
 // selection in pair order (coalesced) and builds the records; later passes move records.
 // The key kernel then reads each key's pairs as one contiguous run of records.
+// A tile's items are loaded from clamped positions (item min(e, items - 1); with no items at
+// all, position 0, inside the buffers) and all held live before any is tested, so the loads
+// are in flight together.  Pass 0 loads the slot's index into rec.x and turns it into the
+// record {j, e} (or an invalid item) afterwards.
 template <bool FIRST>
-__device__ __forceinline__ bool load_pair(const int32_t* __restrict__ idx,
-                                          const uint2* __restrict__ rin, int64_t e,
-                                          const PairSpec& ps, uint2& rec) {
+__device__ __forceinline__ uint2 load_item(const int32_t* __restrict__ idx,
+                                           const uint2* __restrict__ rin, int64_t e,
+                                           int64_t items) {
+    const int64_t ec = e < items ? e : (items > 0 ? items - 1 : 0);
+    if (FIRST) return make_uint2(static_cast<uint32_t>(idx[ec]), 0u);
+    return rin[ec];
+}
+
+template <bool FIRST>
+__device__ __forceinline__ bool make_item(uint2& rec, int64_t e, int64_t items,
+                                          const PairSpec& ps) {
+    if (e >= items) return false;
     if (FIRST) {
         uint32_t key;
-        if (!pair_item(idx, e, ps, key)) return false;
+        if (!pair_item(static_cast<int32_t>(rec.x), e, ps, key)) return false;
         rec = make_uint2(key, static_cast<uint32_t>(e));
-        return true;
     }
-    rec = rin[e];
     return true;
 }
 
@@ -310,25 +347,17 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_hist_kernel(
     cnt[threadIdx.x] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRadixTile;
-    uint32_t keys[kRadixItems];
-    bool valid[kRadixItems];
-#pragma unroll
-    for (int it = 0; it < kRadixItems; ++it) {
-        const int64_t e = t0 + it * kRadixThreads + threadIdx.x;
-        valid[it] = false;
-        keys[it] = 0;
-        if (e < items) {
-            if (FIRST)
-                valid[it] = pair_item(idx + bh * in_stride, e, ps, keys[it]);
-            else {
-                valid[it] = true;
-                keys[it] = rin[bh * in_stride + e].x;
-            }
-        }
-    }
+    uint2 rec[kRadixItems];
 #pragma unroll
     for (int it = 0; it < kRadixItems; ++it)
-        if (valid[it]) atomicAdd(&cnt[(keys[it] >> shift) & 255u], 1u);
+        rec[it] = load_item<FIRST>(idx + bh * in_stride, rin + bh * in_stride,
+                                   t0 + it * kRadixThreads + threadIdx.x, items);
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it) keep(rec[it].x);
+#pragma unroll
+    for (int it = 0; it < kRadixItems; ++it)
+        if (make_item<FIRST>(rec[it], t0 + it * kRadixThreads + threadIdx.x, items, ps))
+            atomicAdd(&cnt[(rec[it].x >> shift) & 255u], 1u);
     __syncthreads();
     hist[(bh * 256 + threadIdx.x) * tiles + blockIdx.x] = cnt[threadIdx.x];
 }
@@ -392,12 +421,13 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     {
         const int64_t off = bh * in_stride;
 #pragma unroll
-        for (int it = 0; it < kRadixItems; ++it) {
-            const int64_t e = t0 + it * 64 + lane;
-            rec[it] = make_uint2(0, 0);
-            if (e < items && load_pair<FIRST>(idx + off, rin + off, e, ps, rec[it]))
-                okmask |= 1u << it;
-        }
+        for (int it = 0; it < kRadixItems; ++it)
+            rec[it] = load_item<FIRST>(idx + off, rin + off, t0 + it * 64 + lane, items);
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) keep(rec[it]);
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it)
+            if (make_item<FIRST>(rec[it], t0 + it * 64 + lane, items, ps)) okmask |= 1u << it;
     }
 
 #pragma unroll
@@ -530,21 +560,36 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
     // digit counts over the bucket; the first tile stays in registers for the scatter
     run[tid] = 0;
     __syncthreads();
+    // (loads from clamped positions, all in flight before any is used; an empty bucket
+    // loads nothing)
     uint2 rec[kRadixItems];
-#pragma unroll
-    for (int it = 0; it < kRadixItems; ++it) {
-        const uint32_t e = wave * kWaveItems + it * 64 + lane;
-        rec[it] = make_uint2(0, 0);
-        if (e < n) {
-            rec[it] = rb[e];
-            atomicAdd(&run[rec[it].x >> 8], 1u);
-        }
-    }
-    for (uint32_t c0 = kRadixTile; c0 < n; c0 += kRadixTile) {
+    auto load_tile = [&](uint32_t c0) {
 #pragma unroll
         for (int it = 0; it < kRadixItems; ++it) {
             const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
-            if (e < n) atomicAdd(&run[rb[e].x >> 8], 1u);
+            rec[it] = rb[e < n ? e : n - 1];
+        }
+#pragma unroll
+        for (int it = 0; it < kRadixItems; ++it) keep(rec[it]);
+    };
+    for (uint32_t c0 = 0; c0 < n; c0 += kRadixTile) {
+        if (c0 == 0) {
+            load_tile(0);  // stays in registers for the scatter
+#pragma unroll
+            for (int it = 0; it < kRadixItems; ++it)
+                if (wave * kWaveItems + it * 64 + lane < n) atomicAdd(&run[rec[it].x >> 8], 1u);
+        } else {
+            uint32_t dg[kRadixItems];
+#pragma unroll
+            for (int it = 0; it < kRadixItems; ++it) {
+                const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
+                dg[it] = rb[e < n ? e : n - 1].x;
+            }
+#pragma unroll
+            for (int it = 0; it < kRadixItems; ++it) keep(dg[it]);
+#pragma unroll
+            for (int it = 0; it < kRadixItems; ++it)
+                if (c0 + wave * kWaveItems + it * 64 + lane < n) atomicAdd(&run[dg[it] >> 8], 1u);
         }
     }
     __syncthreads();
@@ -563,13 +608,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
     const uint64_t lt = (1ull << lane) - 1ull;
     uint32_t* out = slots + bh * P + s0;
     for (uint32_t c0 = 0; c0 < n; c0 += kRadixTile) {
-        if (c0 > 0) {
-#pragma unroll
-            for (int it = 0; it < kRadixItems; ++it) {
-                const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
-                rec[it] = e < n ? rb[e] : make_uint2(0, 0);
-            }
-        }
+        if (c0 > 0) load_tile(c0);
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) wcnt[w][tid] = 0;
         __syncthreads();
@@ -860,15 +899,20 @@ __global__ void __launch_bounds__(256) zeta_dgamma_partial_kernel(const float* _
     const int64_t h = blockIdx.y;
     const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kDgChunk;
     const int64_t total = B * N;
+    float x[kDgChunk / 256];
+#pragma unroll
+    for (int u = 0; u < kDgChunk / 256; ++u) {  // clamped positions: the loads issue together
+        int64_t f = f0 + u * 256 + threadIdx.x;
+        f = f < total ? f : total - 1;
+        const int64_t b = f / N, i = f - b * N;
+        x[u] = dg_row[(b * H + h) * N + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kDgChunk / 256; ++u) keep(x[u]);
     float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kDgChunk / 256; ++u) {
-        const int64_t f = f0 + u * 256 + threadIdx.x;
-        if (f < total) {
-            const int64_t b = f / N, i = f - b * N;
-            acc += dg_row[(b * H + h) * N + i];
-        }
-    }
+    for (int u = 0; u < kDgChunk / 256; ++u)
+        if (f0 + u * 256 + threadIdx.x < total) acc += x[u];
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {

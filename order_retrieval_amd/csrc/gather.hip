@@ -51,6 +51,8 @@ __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t*
     static_for<0, kGatherLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         const float s = row_bcast<L0 + w>(so);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) keep(raw[w][c]);  // the load stays ahead of the test
         if (!(s < 0.0f)) {  // slot selected (a NaN weight is summed and propagates)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
@@ -94,20 +96,43 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
 
+    // the index and key-row loads read clamped positions and are held live before any test,
+    // so the loads of a kind are in flight together
+    int32_t jr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int r = lrow + u * kGatherLanes;
+        jr[u] = ir[r < topk ? r : topk - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) keep(jr[u]);
+    bool sel[U];
+    float kx[U], ky[U], kz[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        sel[u] = lrow + u * kGatherLanes < m && jr[u] >= 0;
+        // a selection has j <= jmax; clamping keeps every access in bounds
+        jr[u] = sel[u] ? (jr[u] > jmax ? static_cast<int32_t>(jmax) : jr[u]) : 0;
+        kx[u] = kh[3 * jr[u]];
+        ky[u] = kh[3 * jr[u] + 1];
+        kz[u] = kh[3 * jr[u] + 2];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        keep(kx[u]);
+        keep(ky[u]);
+        keep(kz[u]);
+    }
     uint32_t jo[U];
     float so[U];
     float ssum = 0.0f, nsel = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lrow + u * kGatherLanes;
         jo[u] = 0;
         so[u] = -1.0f;
-        const int32_t jr = r < m ? ir[r] : -1;
-        if (jr >= 0) {
-            // a selection has j <= jmax; clamping keeps every access in bounds
-            const int32_t j = jr > jmax ? static_cast<int32_t>(jmax) : jr;
-            const float d0 = q0 - kh[3 * j], d1 = q1 - kh[3 * j + 1], d2 = q2 - kh[3 * j + 2];
-            jo[u] = Ref::name(j, dv);
+        if (sel[u]) {
+            const float d0 = q0 - kx[u], d1 = q1 - ky[u], d2 = q2 - kz[u];
+            jo[u] = Ref::name(jr[u], dv);
             so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
             ssum += so[u];
             nsel += 1.0f;

@@ -48,7 +48,14 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_hist_kernel(
 #pragma unroll
     for (int it = 0; it < kOrderItems; ++it) {
         const int64_t e = t0 + it * kOrderThreads + tid;
-        bk[it] = e < N ? order_bucket(c[e]) : kOrderBuckets;
+        bk[it] = c[e < N ? e : N - 1];  // clamped: the tile's loads issue together
+    }
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it) keep(bk[it]);
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it) {
+        const int64_t e = t0 + it * kOrderThreads + tid;
+        bk[it] = e < N ? order_bucket(bk[it]) : kOrderBuckets;
     }
 #pragma unroll
     for (int it = 0; it < kOrderItems; ++it)
@@ -131,7 +138,14 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
 #pragma unroll
     for (int it = 0; it < kOrderItems; ++it) {
         const int64_t e = t0 + it * kOrderThreads + tid;
-        bk[it] = e < N ? order_bucket(c[e]) : kOrderBuckets;
+        bk[it] = c[e < N ? e : N - 1];  // clamped: the tile's loads issue together
+    }
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it) keep(bk[it]);
+#pragma unroll
+    for (int it = 0; it < kOrderItems; ++it) {
+        const int64_t e = t0 + it * kOrderThreads + tid;
+        bk[it] = e < N ? order_bucket(bk[it]) : kOrderBuckets;
     }
 #pragma unroll
     for (int it = 0; it < kOrderItems; ++it) {

@@ -30,6 +30,7 @@ namespace zeta {
 
 constexpr int kSearchGroup = 2;  // runs whose binary searches advance in lock-step
 constexpr int kChunk = 8;        // candidates of a walk loaded per step (register budget)
+constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (chunked search)
 
 // Value of the lane `lane ^ D` of the same quad (D = 1 or 2).
 template <int D>
@@ -275,6 +276,15 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         for (int g = 0; g < 2; ++g) {
             const int cg = scount - g * K;  // entries of this group (uniform over the lanes)
             if (cg <= 0) break;
+            // codes from clamped positions, all loaded before any is used
+            CT code[E];
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                const int u = lane * E + t;
+                code[t] = zkh[sbase + g * K + (u < cg ? u : cg - 1)];
+            }
+#pragma unroll
+            for (int t = 0; t < E; ++t) keep(code[t]);
             uint64_t cand[E];
 #pragma unroll
             for (int t = 0; t < E; ++t) {
@@ -282,8 +292,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 cand[t] = ~0ull;
                 if (u < cg) {
                     const int64_t j = sbase + g * K + u;
-                    const uint64_t code = static_cast<uint64_t>(zkh[j]);
-                    const uint64_t dz = code > z ? code - z : z - code;
+                    const uint64_t c = static_cast<uint64_t>(code[t]);
+                    const uint64_t dz = c > z ? c - z : z - c;
                     cand[t] = (dz << S) | static_cast<uint64_t>(j);
                 }
             }
@@ -386,34 +396,75 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 #pragma unroll
     for (int t = 0; t < E; ++t) best[t] = ~0ull;
 
-    for (int64_t c = 0; c <= i >> lvl; ++c) {
-        const int64_t lo = c * len;
-        const int64_t n = N - lo < len ? N - lo : len;
-        int64_t p = 0;  // lower_bound of zq in run[lo .. lo + n)
-        for (int64_t step = len >> 1; step > 0; step >>= 1)
-            if (p + step <= n && run[lo + p + step - 1] < target) p += step;
-        if (p < n && run[lo + p] < target) p += 1;
-        const int64_t w = topk < n ? topk : n;  // window of k entries (K pads k to a power of 2)
-        int64_t w0 = p - topk / 2;
-        if (w0 > n - w) w0 = n - w;
-        if (w0 < 0) w0 = 0;
-        uint64_t cand[E];
+    // chunks 0 .. i >> lvl, kChunkGroup at a time: their lower_bound searches advance in
+    // lock-step (probes from clamped positions, in flight together), then each chunk's window
+    // is loaded in one batch and merged
+    const int64_t nch = (i >> lvl) + 1;
+    for (int64_t c0 = 0; c0 < nch; c0 += kChunkGroup) {
+        int64_t lo[kChunkGroup], n[kChunkGroup], p[kChunkGroup];
 #pragma unroll
-        for (int t = 0; t < E; ++t) {
-            const int64_t u = lane * E + t;
-            cand[t] = ~0ull;
-            if (u < w) {
-                const uint64_t e = run[lo + w0 + u];
-                const uint64_t j = e & kJMask;
-                const uint64_t code = e >> S;
-                const uint64_t dz = code > z ? code - z : z - code;
-                if (static_cast<int64_t>(j) <= i) cand[t] = (dz << S) | j;  // causal mask
-            }
+        for (int gi = 0; gi < kChunkGroup; ++gi) {
+            const int64_t c = c0 + gi < nch ? c0 + gi : nch - 1;
+            lo[gi] = c * len;
+            n[gi] = N - lo[gi] < len ? N - lo[gi] : len;
+            p[gi] = 0;
         }
-        sort_blocks<E, L, 2, true>(cand, lane);
+        for (int64_t step = len >> 1; step > 0; step >>= 1) {
+            uint64_t e[kChunkGroup];
 #pragma unroll
-        for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
-        bitonic_clean<E, L>(best, lane);
+            for (int gi = 0; gi < kChunkGroup; ++gi) {
+                const int64_t at = p[gi] + step - 1;
+                e[gi] = run[lo[gi] + (at < n[gi] ? at : n[gi] - 1)];
+            }
+#pragma unroll
+            for (int gi = 0; gi < kChunkGroup; ++gi) keep(e[gi]);
+#pragma unroll
+            for (int gi = 0; gi < kChunkGroup; ++gi)
+                if (p[gi] + step <= n[gi] && e[gi] < target) p[gi] += step;
+        }
+        {
+            uint64_t e[kChunkGroup];
+#pragma unroll
+            for (int gi = 0; gi < kChunkGroup; ++gi)
+                e[gi] = run[lo[gi] + (p[gi] < n[gi] ? p[gi] : n[gi] - 1)];
+#pragma unroll
+            for (int gi = 0; gi < kChunkGroup; ++gi) keep(e[gi]);
+#pragma unroll
+            for (int gi = 0; gi < kChunkGroup; ++gi)
+                if (p[gi] < n[gi] && e[gi] < target) p[gi] += 1;
+        }
+#pragma unroll
+        for (int gi = 0; gi < kChunkGroup; ++gi) {
+            if (c0 + gi >= nch) break;  // uniform over the query's lanes
+            const int64_t w = topk < n[gi] ? topk : n[gi];  // window of k entries (K pads k)
+            int64_t w0 = p[gi] - topk / 2;
+            if (w0 > n[gi] - w) w0 = n[gi] - w;
+            if (w0 < 0) w0 = 0;
+            uint64_t ev[E];
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                const int64_t u = lane * E + t;
+                ev[t] = run[lo[gi] + w0 + (u < w ? u : w - 1)];
+            }
+#pragma unroll
+            for (int t = 0; t < E; ++t) keep(ev[t]);
+            uint64_t cand[E];
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                const int64_t u = lane * E + t;
+                cand[t] = ~0ull;
+                if (u < w) {
+                    const uint64_t j = ev[t] & kJMask;
+                    const uint64_t code = ev[t] >> S;
+                    const uint64_t dz = code > z ? code - z : z - code;
+                    if (static_cast<int64_t>(j) <= i) cand[t] = (dz << S) | j;  // causal mask
+                }
+            }
+            sort_blocks<E, L, 2, true>(cand, lane);
+#pragma unroll
+            for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
+            bitonic_clean<E, L>(best, lane);
+        }
     }
 
     int32_t* out = idx + row * topk + lane * E;

@@ -35,6 +35,22 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t block, int64_t per_xcd) {
 }
 inline int64_t xcd_per(int64_t tiles) { return (tiles + kXcds - 1) / kXcds; }
 
+// Marks a loaded value as used here.  Placed after a batch of loads from clamped (always
+// valid) positions, it keeps each load unconditional: without it the compiler may move a load
+// behind the later test that decides whether its value matters, and then wait on that load
+// alone, so the batch no longer has its loads in flight together.
+__device__ __forceinline__ void keep(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(int32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(uint64_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(uint2& x) { asm volatile("" : "+v"(x.x), "+v"(x.y)); }
+__device__ __forceinline__ void keep(uint4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+__device__ __forceinline__ void keep(float4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+
 // Optional events recorded between the stages of one call (measurement hook).
 struct StageEvents {
     void* const* ev = nullptr;
