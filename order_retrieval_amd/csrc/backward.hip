@@ -764,7 +764,32 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     if (tile >= tiles) return;  // uniform over the workgroup
     const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
     const int lrow = threadIdx.x & (kKeyRow - 1);
-    const int64_t pos = (tile - bh * tph) * kRowsPerGroup + threadIdx.x / kKeyRow;
+    const int64_t pos0 = (tile - bh * tph) * kRowsPerGroup;  // the workgroup's 16 keys
+    // The workgroup's keys go to its rows by decreasing pair count, so each wavefront's four
+    // keys have similar counts and few of its row slots idle (a wavefront runs as long as its
+    // longest key).  Which row sums a key does not change the key's sums.
+    __shared__ uint32_t wcount[kRowsPerGroup];
+    __shared__ int wkey[kRowsPerGroup];
+    if (threadIdx.x < kRowsPerGroup) {
+        const int64_t p = pos0 + threadIdx.x;
+        const int64_t pc = p < N ? p : N - 1;
+        const int64_t jj = order ? static_cast<int64_t>(order[bh * N + pc]) : pc;
+        wcount[threadIdx.x] =
+            p < N ? seg_hi[bh * (N + 1) + jj] - seg_lo[bh * (N + 1) + jj] : 0u;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRowsPerGroup) {
+        const uint32_t c = wcount[threadIdx.x];
+        int rank = 0;
+#pragma unroll
+        for (int u = 0; u < kRowsPerGroup; ++u) {
+            const uint32_t cu = wcount[u];
+            rank += (cu > c || (cu == c && u < static_cast<int>(threadIdx.x))) ? 1 : 0;
+        }
+        wkey[rank] = static_cast<int>(threadIdx.x);
+    }
+    __syncthreads();
+    const int64_t pos = pos0 + wkey[threadIdx.x / kKeyRow];
     const bool live = pos < N;
     const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real key, stores nothing
     const int64_t j = order ? static_cast<int64_t>(order[bh * N + pp]) : pp;
