@@ -22,9 +22,12 @@
 // its own contiguous block of the walk) leaves a bitonic sequence of the K smallest, which
 // log2(K) compare-exchange stages sort; the stages whose stride spans lanes exchange values
 // with DPP quad permutes.  A walk whose first candidate is not better than the current K-th
-// is skipped.  The binary searches of up to kSearchGroup runs advance in lock-step, so their
-// probes are independent loads in flight together.
+// is skipped.  The runs are taken in groups: with several lanes per query each lane
+// binary-searches its own run of the group (with one lane, kSearchGroup runs advance in
+// lock-step), so the probes are independent loads in flight together, and the insertion
+// positions reach the query's lanes by a DPP quad broadcast.
 #include "zeta_internal.hpp"
+#include "xlane.hpp"
 
 namespace zeta {
 
@@ -55,6 +58,19 @@ __device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
         const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)),
                                                 ctrl, 0xF, 0xF, false);
         return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    }
+}
+
+// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad); x < 2^32.
+template <int L, int SRC>
+__device__ __forceinline__ int64_t from_lane(int64_t x) {
+    if constexpr (L == 1) {
+        return x;
+    } else {
+        // quad_perm [SRC, SRC, SRC, SRC] for a quad; [SRC, SRC, 2+SRC, 2+SRC] for lane pairs
+        constexpr int ctrl = L == 4 ? SRC * 0x55 : (SRC * 0x5) | ((2 + SRC) * 0x50);
+        return static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
+            static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF, 0xF, false)));
     }
 }
 
@@ -207,16 +223,19 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
     const uint64_t m = causal ? static_cast<uint64_t>(i) + 1 : static_cast<uint64_t>(N);
     constexpr uint64_t kShort = 2 * K;
     uint64_t rem = m & ~(kShort - 1);
+    // A group takes the next kRuns runs (largest first).  With several lanes per query each
+    // lane binary-searches its own run(s) of the group (kPer per lane, in lock-step), and the
+    // insertion positions then reach every lane of the query by a DPP quad broadcast.
+    constexpr int kPer = L == 1 ? kSearchGroup : 1;
+    constexpr int kRuns = kPer * L;
     while (rem) {
         // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
         // offsets (not pointers) keep every access a global-memory access
-        int lv[kSearchGroup];
-        int64_t pos[kSearchGroup];
-        int64_t roff[kSearchGroup];
+        int lv[kRuns];
+        int64_t roff[kRuns];
 #pragma unroll
-        for (int gi = 0; gi < kSearchGroup; ++gi) {
+        for (int gi = 0; gi < kRuns; ++gi) {
             lv[gi] = -1;
-            pos[gi] = 0;
             roff[gi] = 0;
             if (rem) {
                 const int l = 63 - __clzll(rem);
@@ -225,44 +244,58 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 roff[gi] = static_cast<int64_t>(l) * N + static_cast<int64_t>((m >> (l + 1)) << (l + 1));
             }
         }
-        // the probes of the group's runs are unconditional loads (a run that has no probe at
-        // this step reads its own first entry), so they are in flight together
-        int64_t len[kSearchGroup];
+        // this lane's runs: gi = lane * kPer + t
+        int64_t mro[kPer], mlen[kPer], pos[kPer];
+        bool mon[kPer];
 #pragma unroll
-        for (int gi = 0; gi < kSearchGroup; ++gi) len[gi] = lv[gi] >= 0 ? int64_t(1) << lv[gi] : 1;
+        for (int t = 0; t < kPer; ++t) {
+            int ml = lv[t];
+            int64_t mr = roff[t];
+#pragma unroll
+            for (int u = 1; u < L; ++u)
+                if (lane == u) {
+                    ml = lv[u * kPer + t];
+                    mr = roff[u * kPer + t];
+                }
+            mon[t] = ml >= 0;
+            mro[t] = mr;
+            mlen[t] = ml >= 0 ? int64_t(1) << ml : 1;
+            pos[t] = 0;
+        }
+        // probes from clamped positions, held live together (see keep()), so the searches'
+        // loads are in flight together
         for (int64_t step = (int64_t(1) << lv[0]) >> 1; step > 0; step >>= 1) {
-            uint64_t e[kSearchGroup];
+            uint64_t e[kPer];
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi) {
-                const int64_t at = pos[gi] + step - 1;
-                e[gi] = hA[roff[gi] + (at < len[gi] ? at : len[gi] - 1)];
+            for (int t = 0; t < kPer; ++t) {
+                const int64_t at = pos[t] + step - 1;
+                e[t] = hA[mro[t] + (at < mlen[t] ? at : mlen[t] - 1)];
             }
-            // an empty asm that takes every probe keeps the loads unconditional (the compiler
-            // would otherwise move each behind its run's step test and wait on it alone)
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi) asm volatile("" : "+v"(e[gi]));
+            for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi)
-                if (pos[gi] + step < len[gi] && e[gi] < target) pos[gi] += step;
+            for (int t = 0; t < kPer; ++t)
+                if (pos[t] + step < mlen[t] && e[t] < target) pos[t] += step;
         }
         {
-            uint64_t e[kSearchGroup];
+            uint64_t e[kPer];
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi) e[gi] = hA[roff[gi] + pos[gi]];
+            for (int t = 0; t < kPer; ++t) e[t] = hA[mro[t] + pos[t]];
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi) asm volatile("" : "+v"(e[gi]));
+            for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
-            for (int gi = 0; gi < kSearchGroup; ++gi)
-                if (lv[gi] >= 0 && e[gi] < target) pos[gi] += 1;
+            for (int t = 0; t < kPer; ++t)
+                if (mon[t] && e[t] < target) pos[t] += 1;
         }
-#pragma unroll
-        for (int gi = 0; gi < kSearchGroup; ++gi) {
+        static_for<0, kRuns>([&](auto gc) {
+            constexpr int gi = decltype(gc)::value;
+            const int64_t pg = from_lane<L, gi / kPer>(pos[gi % kPer]);
             if (lv[gi] >= 0) {
                 const int64_t s = int64_t(1) << lv[gi];
-                merge_walk<K, L, true, S>(best, hA, roff[gi], pos[gi], s, target, lane);
-                merge_walk<K, L, false, S>(best, hD, roff[gi], pos[gi], s, target, lane);
+                merge_walk<K, L, true, S>(best, hA, roff[gi], pg, s, target, lane);
+                merge_walk<K, L, false, S>(best, hD, roff[gi], pg, s, target, lane);
             }
-        }
+        });
     }
 
     // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K;
