@@ -299,7 +299,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
     }
 
     // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K;
-    // each group is bitonic-sorted (descending) across the query's lanes and merged
+    // each group is bitonic-sorted (descending) across the query's lanes and merged, unless
+    // none of the wavefront's candidates would enter a list
     {
         const uint64_t z = static_cast<uint64_t>(zq[row]);
         const int64_t sbase = static_cast<int64_t>(m & ~(kShort - 1));
@@ -330,6 +331,13 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                     cand[t] = (dz << S) | static_cast<uint64_t>(j);
                 }
             }
+            // nothing to do when no candidate beats its query's current K-th anywhere in the
+            // wavefront (once the prefix is long the recent keys rarely do)
+            const uint64_t kth = from_last_lane<L>(best[E - 1]);
+            bool beats = false;
+#pragma unroll
+            for (int t = 0; t < E; ++t) beats |= cand[t] < kth;
+            if (__ballot(beats) == 0) continue;  // uniform over the active lanes
             sort_blocks<E, L, 2, true>(cand, lane);
 #pragma unroll
             for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
