@@ -149,21 +149,15 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) keep(jr[u]);
     bool sel[U];
-    float kx[U], ky[U], kz[U];
+    Point3 kp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         sel[u] = lrow + u * kRowLanes < m && jr[u] >= 0;
         jr[u] = sel[u] ? static_cast<int32_t>(clamp_index(jr[u], nk - 1)) : 0;
-        kx[u] = kh[3 * jr[u]];
-        ky[u] = kh[3 * jr[u] + 1];
-        kz[u] = kh[3 * jr[u] + 2];
+        kp[u] = load_point(kh, jr[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        keep(kx[u]);
-        keep(ky[u]);
-        keep(kz[u]);
-    }
+    for (int u = 0; u < U; ++u) keep(kp[u]);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         IO::unpack(graw[c], go[c]);
@@ -182,9 +176,9 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
         if (sel[u]) {
             jo[u] = RowRef<BF16, O32>::name(jr[u], dv);
             nsel += 1.0f;
-            dx[u] = q0 - kx[u];
-            dy[u] = q1 - ky[u];
-            dz[u] = q2 - kz[u];
+            dx[u] = q0 - kp[u].x;
+            dy[u] = q1 - kp[u].y;
+            dz[u] = q2 - kp[u].z;
             so[u] = 1.0f / (1.0f + (dx[u] * dx[u] + dy[u] * dy[u] + dz[u] * dz[u]) * inv_g2);
             ssum += so[u];
         }
@@ -834,7 +828,8 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
         if (first + kKeyRow < most) slot_next = slot_at(p + kKeyRow);  // in flight meanwhile
         const uint32_t io = div_u32(slot, slot_div);
         const float2 ac = cf[slot];
-        const float dx = qh[3 * io] - k0, dy = qh[3 * io + 1] - k1, dz = qh[3 * io + 2] - k2;
+        const Point3 qi = load_point(qh, io);
+        const float dx = qi.x - k0, dy = qi.y - k1, dz = qi.z - k2;
         const float ao = own ? ac.x : 0.0f;
         const uint32_t nm = RowRef<BF16, O32>::name(io, dv);
         static_for<0, kKeyRow / kKeyLoads>([&](auto bc) {

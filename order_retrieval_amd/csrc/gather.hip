@@ -107,22 +107,16 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) keep(jr[u]);
     bool sel[U];
-    float kx[U], ky[U], kz[U];
+    Point3 kp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         sel[u] = lrow + u * kGatherLanes < m && jr[u] >= 0;
         // a selection has j <= jmax; clamping keeps every access in bounds
         jr[u] = sel[u] ? (jr[u] > jmax ? static_cast<int32_t>(jmax) : jr[u]) : 0;
-        kx[u] = kh[3 * jr[u]];
-        ky[u] = kh[3 * jr[u] + 1];
-        kz[u] = kh[3 * jr[u] + 2];
+        kp[u] = load_point(kh, jr[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        keep(kx[u]);
-        keep(ky[u]);
-        keep(kz[u]);
-    }
+    for (int u = 0; u < U; ++u) keep(kp[u]);
     uint32_t jo[U];
     float so[U];
     float ssum = 0.0f, nsel = 0.0f;
@@ -131,7 +125,7 @@ __global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
         jo[u] = 0;
         so[u] = -1.0f;
         if (sel[u]) {
-            const float d0 = q0 - kx[u], d1 = q1 - ky[u], d2 = q2 - kz[u];
+            const float d0 = q0 - kp[u].x, d1 = q1 - kp[u].y, d2 = q2 - kp[u].z;
             jo[u] = Ref::name(jr[u], dv);
             so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
             ssum += so[u];

@@ -35,6 +35,18 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t block, int64_t per_xcd) {
 }
 inline int64_t xcd_per(int64_t tiles) { return (tiles + kXcds - 1) / kXcds; }
 
+// One 12-byte point (x, y, z) of a q or k row, read with a single 12-byte load (the rows
+// are 4-byte aligned).
+struct __attribute__((packed, aligned(4))) Point3 {
+    float x, y, z;
+};
+__device__ __forceinline__ Point3 load_point(const float* rows, int64_t r) {
+    return *reinterpret_cast<const Point3*>(rows + 3 * r);
+}
+__device__ __forceinline__ void keep(Point3& p) {
+    asm volatile("" : "+v"(p.x), "+v"(p.y), "+v"(p.z));
+}
+
 // Marks a loaded value as used here.  Placed after a batch of loads from clamped (always
 // valid) positions, it keeps each load unconditional: without it the compiler may move a load
 // behind the later test that decides whether its value matters, and then wait on that load
