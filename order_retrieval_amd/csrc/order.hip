@@ -23,6 +23,7 @@ constexpr int kOrderPer = kOrderBuckets / kOrderThreads;  // buckets per thread 
 constexpr int kOrderItems = 4;
 constexpr int kOrderTile = kOrderThreads * kOrderItems;
 static_assert(kOrderPer == 4, "counts move as uint4");
+constexpr int kScanChunk = 16;  // tiles whose counts the scan reads at once
 
 int64_t order_tiles(int64_t N) { return (N + kOrderTile - 1) / kOrderTile; }
 size_t order_scratch_words(int64_t BH, int64_t N) {
@@ -72,14 +73,27 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scan_kernel(uint4* _
     __shared__ uint32_t part[kOrderThreads];
     const int tid = threadIdx.x;
     uint4* h = hist + static_cast<int64_t>(blockIdx.x) * tiles * kOrderThreads + tid;
+    // the tiles' counts are read kScanChunk at a time from clamped positions, all in flight
+    // together; with at most kScanChunk tiles they stay in registers for the second pass
     uint32_t tot[kOrderPer] = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int64_t t = 0; t < tiles; ++t) {
-        const uint4 x = h[t * kOrderThreads];
-        tot[0] += x.x;
-        tot[1] += x.y;
-        tot[2] += x.z;
-        tot[3] += x.w;
+    uint4 x[kScanChunk];
+    for (int64_t t0 = 0; t0 < tiles; t0 += kScanChunk) {
+#pragma unroll
+        for (int u = 0; u < kScanChunk; ++u) {
+            const int64_t t = t0 + u < tiles ? t0 + u : tiles - 1;
+            x[u] = h[t * kOrderThreads];
+        }
+#pragma unroll
+        for (int u = 0; u < kScanChunk; ++u) keep(x[u]);
+#pragma unroll
+        for (int u = 0; u < kScanChunk; ++u) {
+            if (t0 + u < tiles) {
+                tot[0] += x[u].x;
+                tot[1] += x[u].y;
+                tot[2] += x[u].z;
+                tot[3] += x[u].w;
+            }
+        }
     }
     const uint32_t mine = tot[0] + tot[1] + tot[2] + tot[3];
     // exclusive scan over the threads: inside each wavefront by shuffles, then over the
@@ -107,14 +121,26 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scan_kernel(uint4* _
     run[1] = run[0] + tot[0];
     run[2] = run[1] + tot[1];
     run[3] = run[2] + tot[2];
-#pragma unroll 4
-    for (int64_t t = 0; t < tiles; ++t) {
-        const uint4 x = h[t * kOrderThreads];
-        h[t * kOrderThreads] = make_uint4(run[0], run[1], run[2], run[3]);
-        run[0] += x.x;
-        run[1] += x.y;
-        run[2] += x.z;
-        run[3] += x.w;
+    for (int64_t t0 = 0; t0 < tiles; t0 += kScanChunk) {
+        if (tiles > kScanChunk) {
+#pragma unroll
+            for (int u = 0; u < kScanChunk; ++u) {
+                const int64_t t = t0 + u < tiles ? t0 + u : tiles - 1;
+                x[u] = h[t * kOrderThreads];
+            }
+#pragma unroll
+            for (int u = 0; u < kScanChunk; ++u) keep(x[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kScanChunk; ++u) {
+            if (t0 + u < tiles) {
+                h[(t0 + u) * kOrderThreads] = make_uint4(run[0], run[1], run[2], run[3]);
+                run[0] += x[u].x;
+                run[1] += x[u].y;
+                run[2] += x[u].z;
+                run[3] += x[u].w;
+            }
+        }
     }
 }
 
