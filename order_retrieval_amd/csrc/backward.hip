@@ -68,7 +68,13 @@ __device__ __forceinline__ bool pair_item(int32_t j, int64_t e, const PairSpec& 
 // g_ij = dO_i . v_j, which the owning lane keeps.
 constexpr int kRowLanes = 16;  // lanes per query or key
 constexpr int kRowLoads = 8;   // rows whose loads are issued together
-constexpr int kRowsPerGroup = 256 / kRowLanes;  // queries or keys per workgroup (one (b,h))
+// Workgroup sizes (measured): more curve neighbours per workgroup share a CU's L1 in the
+// per-query pass; the per-key pass keeps 256 (its rows are ordered by pair count within a
+// workgroup, and more VGPRs per lane limit larger workgroups to fewer waves per SIMD).
+constexpr int kQueryThreads = 512;  // workgroup of the per-query pass
+constexpr int kKeyThreads = 256;    // workgroup of the per-key pass
+constexpr int kQueryRows = kQueryThreads / kRowLanes;  // queries per workgroup (one (b,h))
+constexpr int kKeyRows = kKeyThreads / kRowLanes;      // keys per workgroup (one (b,h))
 
 template <bool BF16, bool O32, int CPL, int L0>
 __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
@@ -101,7 +107,7 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
 }
 
 template <bool BF16, bool O32, int CPL, int U>
-__global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
+__global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t N, int64_t H,
@@ -114,7 +120,7 @@ __global__ void __launch_bounds__(256) zeta_bwd_query_kernel(
     if (tile >= tiles) return;  // uniform over the workgroup
     const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
     const int lrow = threadIdx.x & (kRowLanes - 1);
-    const int64_t pos = (tile - bh * tph) * kRowsPerGroup + threadIdx.x / kRowLanes;
+    const int64_t pos = (tile - bh * tph) * kQueryRows + threadIdx.x / kRowLanes;
     const bool live = pos < N;
     const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real query, stores nothing
     const int chunks = dv / E;
@@ -241,14 +247,15 @@ static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int t
                                  const float* gamma, const int32_t* idx, const void* dout,
                                  const uint32_t* order, float2* coef, float* dq, float* dg_row,
                                  hipStream_t s) {
-    const int64_t tph = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t tph = (N + kQueryRows - 1) / kQueryRows;
     const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
     const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane (<= 4)
     auto kern = u <= 1 ? zeta_bwd_query_kernel<BF16, O32, CPL, 1>
               : u <= 2 ? zeta_bwd_query_kernel<BF16, O32, CPL, 2>
                        : zeta_bwd_query_kernel<BF16, O32, CPL, 4>;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kQueryThreads), 0, s,
+                       q, k, v,
                        gamma, idx, dout, order, N, H, dv, topk, causal, tph, tiles, per, coef, dq,
                        dg_row);
     return hipGetLastError();
@@ -743,7 +750,7 @@ __device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* 
 }
 
 template <bool BF16, bool O32, int CPL>
-__global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
+__global__ void __launch_bounds__(kKeyThreads) zeta_bwd_key_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
     const void* __restrict__ dout, const float2* __restrict__ coef,
     const uint32_t* __restrict__ slots, int slot_stride, const uint32_t* __restrict__ seg_lo,
@@ -758,13 +765,13 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
     if (tile >= tiles) return;  // uniform over the workgroup
     const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
     const int lrow = threadIdx.x & (kKeyRow - 1);
-    const int64_t pos0 = (tile - bh * tph) * kRowsPerGroup;  // the workgroup's 16 keys
+    const int64_t pos0 = (tile - bh * tph) * kKeyRows;  // the workgroup's keys
     // The workgroup's keys go to its rows by decreasing pair count, so each wavefront's four
     // keys have similar counts and few of its row slots idle (a wavefront runs as long as its
     // longest key).  Which row sums a key does not change the key's sums.
-    __shared__ uint32_t wcount[kRowsPerGroup];
-    __shared__ int wkey[kRowsPerGroup];
-    if (threadIdx.x < kRowsPerGroup) {
+    __shared__ uint32_t wcount[kKeyRows];
+    __shared__ int wkey[kKeyRows];
+    if (threadIdx.x < kKeyRows) {
         const int64_t p = pos0 + threadIdx.x;
         const int64_t pc = p < N ? p : N - 1;
         const int64_t jj = order ? static_cast<int64_t>(order[bh * N + pc]) : pc;
@@ -772,11 +779,11 @@ __global__ void __launch_bounds__(256) zeta_bwd_key_kernel(
             p < N ? seg_hi[bh * (N + 1) + jj] - seg_lo[bh * (N + 1) + jj] : 0u;
     }
     __syncthreads();
-    if (threadIdx.x < kRowsPerGroup) {
+    if (threadIdx.x < kKeyRows) {
         const uint32_t c = wcount[threadIdx.x];
         int rank = 0;
 #pragma unroll
-        for (int u = 0; u < kRowsPerGroup; ++u) {
+        for (int u = 0; u < kKeyRows; ++u) {
             const uint32_t cu = wcount[u];
             rank += (cu > c || (cu == c && u < static_cast<int>(threadIdx.x))) ? 1 : 0;
         }
@@ -882,14 +889,14 @@ static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int top
                                const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     const int chunks = dv / VecIO<BF16>::kElems;
     const int cpl = (chunks + kKeyRow - 1) / kKeyRow;
-    const int64_t tph = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t tph = (N + kKeyRows - 1) / kKeyRows;
     const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
     auto kern = cpl <= 1 ? zeta_bwd_key_kernel<BF16, O32, 1>
               : cpl <= 2 ? zeta_bwd_key_kernel<BF16, O32, 2>
               : cpl <= 4 ? zeta_bwd_key_kernel<BF16, O32, 4>
                          : zeta_bwd_key_kernel<BF16, O32, BF16 ? 4 : 8>;  // bf16: <= 64 chunks
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kKeyThreads), 0, s, q, k,
                        gamma, dout, ws.coef, sg.slots, sg.stride, sg.lo, sg.hi, order, N, H, dv,
                        topk,
                        make_div(static_cast<uint32_t>(topk)), ws.P, tph, tiles, per, dk, dvout);

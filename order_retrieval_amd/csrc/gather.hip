@@ -31,7 +31,10 @@ namespace zeta {
 // issued together, none waits on another load) and accumulates in fp32.
 constexpr int kGatherLanes = 16;
 constexpr int kGatherLoads = 8;
-constexpr int kGatherRows = 256 / kGatherLanes;  // queries per workgroup
+// Large workgroups: the 64 queries of one workgroup are neighbours on the curve and share
+// one CU's L1, which then serves more of their selected rows.
+constexpr int kGatherThreads = 1024;
+constexpr int kGatherRows = kGatherThreads / kGatherLanes;  // queries per workgroup
 
 template <bool BF16, bool O32, int CPL, int L0>
 __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
@@ -66,7 +69,7 @@ __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t*
 }
 
 template <bool BF16, bool O32, int CPL, int U>
-__global__ void __launch_bounds__(256) zeta_cauchy_gather_kernel(
+__global__ void __launch_bounds__(kGatherThreads) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ order, void* __restrict__ out, int64_t N, int64_t H, int dv,
@@ -187,7 +190,7 @@ static hipError_t launch_gather_c(int64_t BH, int64_t N, int64_t H, int dv, int 
     auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 1>
               : u <= 2 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 2>
                        : zeta_cauchy_gather_kernel<BF16, O32, CPL, 4>;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(256), 0, s, q, k, v,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kGatherThreads), 0, s, q, k, v,
                        gamma, idx, order, out, N, H, dv, topk, causal, tph, tiles, per);
     return hipGetLastError();
 }
