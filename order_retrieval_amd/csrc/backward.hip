@@ -39,16 +39,41 @@ __device__ __forceinline__ int64_t clamp_index(int32_t j, int64_t jmax) {
     return j < 0 ? 0 : (j > jmax ? jmax : j);
 }
 
+// Unsigned division by a divisor fixed for the launch (the selection width): a multiply-high,
+// a subtract and two shifts, exact for every 32-bit numerator (Granlund and Montgomery,
+// "Division by Invariant Integers using Multiplication", unsigned division by a run-time
+// invariant divisor).
+struct DivU32 {
+    uint32_t m;  // low 32 bits of the 33-bit multiplier
+    int sh1, sh2;
+};
+
+static DivU32 make_div(uint32_t d) {
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
+    DivU32 r;
+    r.m = static_cast<uint32_t>((((uint64_t(1) << l) - d) << 32) / d + 1);
+    r.sh1 = l < 1 ? l : 1;
+    r.sh2 = l > 1 ? l - 1 : 0;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, const DivU32& d) {
+    const uint32_t t = __umulhi(d.m, n);
+    return (t + ((n - t) >> d.sh1)) >> d.sh2;
+}
+
 struct PairSpec {
     int topk;
     int causal;
     int64_t N;
+    DivU32 by_topk;  // division by topk
 };
 
 // j: the index stored in slot e.
 __device__ __forceinline__ bool pair_item(int32_t j, int64_t e, const PairSpec& ps,
                                           uint32_t& key) {
-    const uint32_t i = static_cast<uint32_t>(e) / static_cast<uint32_t>(ps.topk);
+    const uint32_t i = div_u32(static_cast<uint32_t>(e), ps.by_topk);
     const uint32_t r = static_cast<uint32_t>(e) - i * static_cast<uint32_t>(ps.topk);
     const int64_t nk = ps.causal ? static_cast<int64_t>(i) + 1 : ps.N;
     if (r >= nk) return false;  // slot beyond min(topk, nk)
@@ -684,30 +709,6 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* 
 }
 
 // ---------------------------------------------------------------------------- 4. keys
-// Unsigned division by a divisor fixed for the launch (the selection width): a multiply-high,
-// a subtract and two shifts, exact for every 32-bit numerator (Granlund and Montgomery,
-// "Division by Invariant Integers using Multiplication", unsigned division by a run-time
-// invariant divisor).
-struct DivU32 {
-    uint32_t m;  // low 32 bits of the 33-bit multiplier
-    int sh1, sh2;
-};
-
-static DivU32 make_div(uint32_t d) {
-    int l = 0;
-    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
-    DivU32 r;
-    r.m = static_cast<uint32_t>((((uint64_t(1) << l) - d) << 32) / d + 1);
-    r.sh1 = l < 1 ? l : 1;
-    r.sh2 = l > 1 ? l - 1 : 0;
-    return r;
-}
-
-__device__ __forceinline__ uint32_t div_u32(uint32_t n, const DivU32& d) {
-    const uint32_t t = __umulhi(d.m, n);
-    return (t + ((n - t) >> d.sh1)) >> d.sh2;
-}
-
 // One 16-lane row (a DPP row) per key j, four keys per wavefront, keys taken in their Z-order
 // processing order: the queries that selected a key are near it on the curve, so keys that
 // run together read overlapping dO rows and L2 serves the repeats.  A key's pairs are a
@@ -995,10 +996,11 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
                                const StageEvents& marks, hipStream_t s) {
     const int64_t rows = BH * N;
     marks.record(0, s);
+    // the key codes and order follow the query ones in memory (zk = zq + BH N, perm_k =
+    // perm_q + BH N): one order build takes both as 2 BH slices
     hipError_t e = launch_encode(q, rows, ws.zq, s);
-    if (e == hipSuccess) e = launch_order(BH, N, ws.zq, ws.perm_q, ws.ohist, s);
     if (e == hipSuccess) e = launch_encode(k, rows, ws.zk, s);
-    if (e == hipSuccess) e = launch_order(BH, N, ws.zk, ws.perm_k, ws.ohist, s);
+    if (e == hipSuccess) e = launch_order(2 * BH, N, ws.zq, ws.perm_q, ws.ohist, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
     e = launch_query<BF16>(BH, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,
@@ -1008,7 +1010,7 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
 
     int bits = 0;
     while ((int64_t(1) << bits) < N) ++bits;
-    const PairSpec ps{topk, causal ? 1 : 0, N};
+    const PairSpec ps{topk, causal ? 1 : 0, N, make_div(static_cast<uint32_t>(topk))};
     KeySegments sg{};
     radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
     if (bits <= 16) {

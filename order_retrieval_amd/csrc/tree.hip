@@ -28,7 +28,10 @@ namespace zeta {
 
 constexpr int kTileLog = 10;
 constexpr int kTile = 1 << kTileLog;
-constexpr int kMergeTile = 2048;  // merged outputs per workgroup, 8 per thread
+constexpr int kMergeThreads = 256;
+constexpr int kMergeTile = 2048;  // merged outputs per workgroup
+constexpr int kMergePer = kMergeTile / kMergeThreads;
+static_assert(kMergeThreads == 256, "the split search runs two diagonals on 128 threads each");
 
 __device__ __forceinline__ int lds_lower_bound(const uint64_t* a, int n, uint64_t x) {
     int lo = 0;
@@ -117,7 +120,7 @@ __device__ __forceinline__ int diag_split(const uint64_t* A, int na, const uint6
 }
 
 // Level l -> l+1 for l >= kTileLog: merge sibling blocks of 2^l entries (merge path).
-__global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restrict__ asc,
+__global__ void __launch_bounds__(kMergeThreads) zeta_tree_merge_kernel(uint64_t* __restrict__ asc,
                                                                uint64_t* __restrict__ desc,
                                                                int64_t N, int levels, int l) {
     __shared__ uint64_t seg[kMergeTile];
@@ -189,16 +192,16 @@ __global__ void __launch_bounds__(256) zeta_tree_merge_kernel(uint64_t* __restri
         seg[e] = e < ca ? A[a0 + e] : B[b0 + e - ca];
     __syncthreads();
 
-    // each thread merges 8 consecutive outputs into LDS; the tile is then written out with
-    // consecutive lanes on consecutive entries
+    // each thread merges kMergePer consecutive outputs into LDS; the tile is then written out
+    // with consecutive lanes on consecutive entries
     __shared__ uint64_t merged[kMergeTile];
     const uint64_t* sa = seg;
     const uint64_t* sb = seg + ca;
-    const int t0 = threadIdx.x * 8;
+    const int t0 = threadIdx.x * kMergePer;
     if (t0 < ca + cb) {
         int ia = diag_split(sa, ca, sb, cb, t0);
         int ib = t0 - ia;
-        const int cnt = ca + cb - t0 < 8 ? ca + cb - t0 : 8;
+        const int cnt = ca + cb - t0 < kMergePer ? ca + cb - t0 : kMergePer;
         for (int u = 0; u < cnt; ++u) {
             uint64_t x;
             if (ib >= cb || (ia < ca && sa[ia] < sb[ib]))
@@ -228,7 +231,7 @@ static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, con
     for (int l = top_tile; l + 1 < levels; ++l) {
         dim3 g(static_cast<unsigned>((N + kMergeTile - 1) / kMergeTile),
                static_cast<unsigned>(BH), 2);
-        hipLaunchKernelGGL(zeta_tree_merge_kernel, g, dim3(256), 0, s, tree_asc, tree_desc, N,
+        hipLaunchKernelGGL(zeta_tree_merge_kernel, g, dim3(kMergeThreads), 0, s, tree_asc, tree_desc, N,
                            levels, l);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -199,11 +199,13 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
     p.counts = take(sizeof(uint32_t) * BH);
     p.offs = take(sizeof(uint32_t) * BH * (N + 1));
     p.ends = take(sizeof(uint32_t) * BH * (N + 1));
-    p.zq = take(sizeof(uint32_t) * BH * N);
-    p.pq = take(sizeof(uint32_t) * BH * N);
-    p.zk = take(sizeof(uint32_t) * BH * N);
-    p.pk = take(sizeof(uint32_t) * BH * N);
-    p.ohist = take(sizeof(uint32_t) * zeta::order_scratch_words(BH, N));
+    // query and key codes (and their processing orders) adjacent, so one order build covers
+    // both as 2 BH slices
+    p.zq = take(sizeof(uint32_t) * 2 * BH * N);
+    p.zk = p.zq + sizeof(uint32_t) * BH * N;
+    p.pq = take(sizeof(uint32_t) * 2 * BH * N);
+    p.pk = p.pq + sizeof(uint32_t) * BH * N;
+    p.ohist = take(sizeof(uint32_t) * zeta::order_scratch_words(2 * BH, N));
     p.total = off;
     return p;
 }

@@ -134,7 +134,7 @@ struct BwdBuffers {
     uint32_t* perm_q; // [BHN] query processing order
     uint32_t* zk;     // [BHN] key codes
     uint32_t* perm_k; // [BHN] key processing order
-    uint32_t* ohist;  // order_scratch_words(BH, N) words for the processing orders
+    uint32_t* ohist;  // order_scratch_words(2 BH, N) words for the processing orders
     int64_t P;        // upper bound of the pairs per (b,h)
     int64_t tiles;    // radix tiles per (b,h)
 };
