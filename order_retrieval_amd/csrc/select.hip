@@ -136,23 +136,44 @@ __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
     }
 }
 
+// Entries of one (b,h)'s tree levels are addressed from the slice base.  When the slice holds
+// fewer than 2^28 entries per tree (O32) offsets are 32-bit and a load is a uniform base plus
+// a 32-bit byte offset; otherwise 64-bit indices.
+template <bool O32>
+struct TreeIx;
+template <>
+struct TreeIx<true> {
+    using T = int32_t;
+    __device__ __forceinline__ static uint64_t load(const uint64_t* base, int32_t i) {
+        return *reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(base) +
+                                                  static_cast<uint32_t>(i) * 8u);
+    }
+};
+template <>
+struct TreeIx<false> {
+    using T = int64_t;
+    __device__ __forceinline__ static uint64_t load(const uint64_t* base, int64_t i) {
+        return base[i];
+    }
+};
+
 // Merge one walk into the running top-K.  Candidate c (0 = first) of the walk sits at run
 // position p + c (right walk, asc tree, key = e - target) or p - 1 - c (left walk, desc
 // tree, key = (target | 0xffffffff) - e).  Lane `lane` of the query holds list entries
 // [lane*E, lane*E + E) and pairs them with candidates K-1-t, i.e. its own block of E.
-template <int K, int L, bool RIGHT, int S>
+template <int K, int L, bool RIGHT, int S, bool O32>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
-                                           int64_t roff, int64_t p, int64_t s, uint64_t target,
-                                           int lane) {
-    const uint64_t* run = tree + roff;
+                                           typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
+                                           typename TreeIx<O32>::T s, uint64_t target, int lane) {
+    using IX = typename TreeIx<O32>::T;
     constexpr int E = K / L;
     const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
     // skip when the walk is empty or its first candidate does not beat the current K-th
     // (every load below reads a clamped, in-run position and the value is selected after, so
     // no load sits behind a branch and they all issue before the first wait)
     const bool empty = RIGHT ? p >= s : p <= 0;
-    const int64_t p0 = RIGHT ? (empty ? s - 1 : p) : (empty ? 0 : p - 1);
-    const uint64_t e0 = run[p0];
+    const IX p0 = RIGHT ? (empty ? s - 1 : p) : (empty ? 0 : p - 1);
+    const uint64_t e0 = TreeIx<O32>::load(tree, roff + p0);
     const uint64_t first = empty ? ~0ull : (RIGHT ? e0 - target : top - e0);
     const uint64_t kth = from_last_lane<L>(best[E - 1]);
     if (first >= kth) return;
@@ -161,9 +182,8 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     // (immediate offsets of the loads, so no per-candidate address is kept in registers).
     // Right walk: entry u of this lane is run[b - u], valid while b - u < s.
     // Left walk:  entry u of this lane is run[b + u], valid while b + u >= 0.
-    const int64_t b = RIGHT ? p + (K - 1 - lane * E) : p - K + lane * E;
-    const uint64_t* wp = run + b;
-    const int64_t lim = RIGHT ? b - s : -b;  // right: valid iff u > lim; left: valid iff u >= lim
+    const IX b = RIGHT ? p + (K - 1 - lane * E) : p - K + lane * E;
+    const IX lim = RIGHT ? b - s : -b;  // right: valid iff u > lim; left: valid iff u >= lim
 #pragma unroll
     for (int u0 = 0; u0 < E; u0 += CH) {
         uint64_t c[CH];
@@ -172,8 +192,8 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
             const int u = u0 + v;
             const bool ok = RIGHT ? u > lim : u >= lim;
             // an invalid entry reads the walk's first position instead (inside the run)
-            const int64_t at = ok ? b + (RIGHT ? -u : u) : p0;
-            const uint64_t e = run[at];
+            const IX at = ok ? b + (RIGHT ? -u : u) : p0;
+            const uint64_t e = TreeIx<O32>::load(tree, roff + at);
             c[v] = ok ? (RIGHT ? e - target : top - e) : ~0ull;
         }
 #pragma unroll
@@ -185,28 +205,28 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
 
 // CT, S: code type and position bits of the packed tree entries (uint32_t, 32 for 30-bit
 // codes; uint64_t, 28 for the 36-bit codes of 12-bit cells).
-template <int K, int L, typename CT, int S>
+template <int K, int L, typename CT, int S, bool O32>
 __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__ zq,
                                                            const CT* __restrict__ zk,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            const uint32_t* __restrict__ order,
-                                                           int64_t rows, int64_t N, int levels,
-                                                           int topk, int causal, int64_t tiles,
+                                                           int64_t N, int levels, int topk,
+                                                           int causal, int64_t tph, int64_t tiles,
                                                            int64_t per_xcd,
                                                            int32_t* __restrict__ idx) {
+    using IX = typename TreeIx<O32>::T;
     constexpr int E = K / L;
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;
-    const int64_t g = tile * blockDim.x + threadIdx.x;
-    const int64_t t = g / L;  // position in the processing order
-    const int lane = static_cast<int>(g % L);
-    if (t >= rows) return;  // uniform over the L lanes of a query
+    const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
+    const int64_t t = (tile - bh * tph) * (256 / L) + threadIdx.x / L;  // processing position
+    const int lane = static_cast<int>(threadIdx.x % L);
+    if (t >= N) return;  // uniform over the L lanes of a query
     // queries close on the curve search the same parts of the tree, so taking them in the
     // Z-order processing order keeps the probed lines in L2
-    const int64_t row = order ? (t / N) * N + order[t] : t;
-    const int64_t bh = row / N;
-    const int64_t i = row - bh * N;
+    const int64_t i = order ? static_cast<int64_t>(order[bh * N + t]) : t;
+    const int64_t row = bh * N + i;
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     const uint64_t target = static_cast<uint64_t>(zq[row]) << S;
     const uint64_t* hA = tree_asc + bh * levels * N;
@@ -232,7 +252,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
         // offsets (not pointers) keep every access a global-memory access
         int lv[kRuns];
-        int64_t roff[kRuns];
+        IX roff[kRuns];
 #pragma unroll
         for (int gi = 0; gi < kRuns; ++gi) {
             lv[gi] = -1;
@@ -241,16 +261,17 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 const int l = 63 - __clzll(rem);
                 rem ^= uint64_t(1) << l;
                 lv[gi] = l;
-                roff[gi] = static_cast<int64_t>(l) * N + static_cast<int64_t>((m >> (l + 1)) << (l + 1));
+                roff[gi] = static_cast<IX>(static_cast<int64_t>(l) * N +
+                                           static_cast<int64_t>((m >> (l + 1)) << (l + 1)));
             }
         }
         // this lane's runs: gi = lane * kPer + t
-        int64_t mro[kPer], mlen[kPer], pos[kPer];
+        IX mro[kPer], mlen[kPer], pos[kPer];
         bool mon[kPer];
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
             int ml = lv[t];
-            int64_t mr = roff[t];
+            IX mr = roff[t];
 #pragma unroll
             for (int u = 1; u < L; ++u)
                 if (lane == u) {
@@ -259,17 +280,17 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 }
             mon[t] = ml >= 0;
             mro[t] = mr;
-            mlen[t] = ml >= 0 ? int64_t(1) << ml : 1;
+            mlen[t] = ml >= 0 ? IX(1) << ml : 1;
             pos[t] = 0;
         }
         // probes from clamped positions, held live together (see keep()), so the searches'
         // loads are in flight together
-        for (int64_t step = (int64_t(1) << lv[0]) >> 1; step > 0; step >>= 1) {
+        for (IX step = (IX(1) << lv[0]) >> 1; step > 0; step >>= 1) {
             uint64_t e[kPer];
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
-                const int64_t at = pos[t] + step - 1;
-                e[t] = hA[mro[t] + (at < mlen[t] ? at : mlen[t] - 1)];
+                const IX at = pos[t] + step - 1;
+                e[t] = TreeIx<O32>::load(hA, mro[t] + (at < mlen[t] ? at : mlen[t] - 1));
             }
 #pragma unroll
             for (int t = 0; t < kPer; ++t) keep(e[t]);
@@ -280,7 +301,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         {
             uint64_t e[kPer];
 #pragma unroll
-            for (int t = 0; t < kPer; ++t) e[t] = hA[mro[t] + pos[t]];
+            for (int t = 0; t < kPer; ++t) e[t] = TreeIx<O32>::load(hA, mro[t] + pos[t]);
 #pragma unroll
             for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
@@ -289,11 +310,11 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         }
         static_for<0, kRuns>([&](auto gc) {
             constexpr int gi = decltype(gc)::value;
-            const int64_t pg = from_lane<L, gi / kPer>(pos[gi % kPer]);
+            const IX pg = static_cast<IX>(from_lane<L, gi / kPer>(pos[gi % kPer]));
             if (lv[gi] >= 0) {
-                const int64_t s = int64_t(1) << lv[gi];
-                merge_walk<K, L, true, S>(best, hA, roff[gi], pg, s, target, lane);
-                merge_walk<K, L, false, S>(best, hD, roff[gi], pg, s, target, lane);
+                const IX s = IX(1) << lv[gi];
+                merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane);
+                merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane);
             }
         });
     }
@@ -357,11 +378,17 @@ static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk,
                                   const CT* zq, const CT* zk, const uint64_t* ta,
                                   const uint64_t* td, const uint32_t* order, int32_t* idx,
                                   hipStream_t s) {
-    const int64_t tiles = (rows * L + 255) / 256;
+    // tiles of 256 / L queries, never straddling two (b,h)
+    const int64_t tph = (N + (256 / L) - 1) / (256 / L);
+    const int64_t tiles = (rows / N) * tph;
     const int64_t per = xcd_per(tiles);
-    hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(per * kXcds)),
-                       dim3(256), 0, s, zq, zk, ta, td, order, rows, N, levels, topk, causal,
-                       tiles, per, idx);
+    const dim3 grid(static_cast<unsigned>(per * kXcds));
+    if (static_cast<int64_t>(levels) * N < (int64_t(1) << 28))
+        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, true>), grid, dim3(256), 0, s, zq, zk,
+                           ta, td, order, N, levels, topk, causal, tph, tiles, per, idx);
+    else
+        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, false>), grid, dim3(256), 0, s, zq,
+                           zk, ta, td, order, N, levels, topk, causal, tph, tiles, per, idx);
     return hipGetLastError();
 }
 
