@@ -150,6 +150,15 @@ def test_select_edge_shapes(B, H, N, topk, dist):
     _select_and_compare(W("e", B, H, N, 8, topk, dist=dist, seed=N + topk))
 
 
+def test_select_beyond_32bit_tree_offsets():
+    # a (b,h) slice whose tree levels hold 2^28 entries or more: the selection addresses the
+    # tree with 64-bit offsets there (32-bit below that size)
+    w = W("wt", 1, 1, 10_000_000, 8, 4, seed=31)
+    rows = sample_rows(w, 150, seed=9)
+    log(f"select N=10^7 (64-bit tree offsets): {rows.size} rows")
+    _select_and_compare(w, rows)
+
+
 def test_select_nonfinite_inputs():
     w = W("e", 1, 2, 600, 8, 12, seed=9)
     x = inputs.make_inputs(w)
