@@ -219,7 +219,38 @@ COUNTER_CMDS = [
     "python3 bench.py --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o copy_write -- "
     "python3 bench.py --copy-calibration",
+    "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES "
+    "SQ_BUSY_CYCLES --output-format csv -d {d}/lds -o lds -- "
+    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
 ]
+# sort and select stages, whose LDS use and occupancy the counters report
+SORT_SELECT = ("zeta_order_", "zeta_tree_", "zeta_radix_", "zeta_bucket_sort", "zeta_select_")
+CU_COUNT, SIMDS_PER_CU, CLOCK_GHZ, LDS_BYTES_PER_CU = 256, 4, 2.4, 160 * 1024
+
+
+def trace_kernels(d: str) -> dict:
+    """Per kernel (base name): average duration (us) and resources from a kernel trace dir."""
+    out: dict = {}
+    for f in glob.glob(os.path.join(d, "*kernel_trace.csv")):
+        for r in csv.DictReader(open(f)):
+            k = kernel_base(r["Kernel_Name"])
+            e = out.setdefault(k, {"n": 0, "ns": 0.0})
+            e["n"] += 1
+            e["ns"] += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            e.update(vgpr=int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]),
+                     lds=int(r["LDS_Block_Size"]), wg=int(r["Workgroup_Size_X"]) *
+                     int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+    for e in out.values():
+        e["us"] = e["ns"] / e["n"] / 1e3
+    return out
+
+
+def waves_by_lds(lds: int, wg: int) -> int:
+    """Resident wavefronts per SIMD that a workgroup's LDS allows (160 KiB per CU, 4 SIMDs,
+    at most 8 wavefronts per SIMD)."""
+    waves_wg = -(-wg // 64)
+    wgs = LDS_BYTES_PER_CU // lds if lds > 0 else 64
+    return min(8, (wgs * waves_wg) // SIMDS_PER_CU)
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants")
 
@@ -266,6 +297,47 @@ def counters_summary(d: str, workload: str) -> None:
                "commands": cmds}
         with open(os.path.join(prof, f"{stage}_{workload}_counters.json"), "w") as f:
             json.dump(rec, f, indent=1)
+    tr = os.path.join(os.path.dirname(os.path.abspath(d)), "trace")
+    kt = trace_kernels(tr) if os.path.isdir(tr) else {}
+    if kt:
+        lines += ["", f"Achieved HBM rate: the bytes above over the average kernel duration of the "
+                  f"kernel trace in {tr} (the same bench command, its own run):", "",
+                  "| kernel | HBM MB per launch | average us | HBM GB/s | of 8 TB/s |", "|---|---|---|---|---|"]
+        for kname in sorted(fetch, key=lambda n: -fetch[n]):
+            if not kname.startswith("zeta_") or kname not in kt:
+                continue
+            hb = fetch[kname] * 1024 * fscale + write.get(kname, 0.0) * 1024 * wscale
+            gbs = hb / (kt[kname]["us"] * 1e-6) / 1e9
+            lines.append(f"| {kname} | {hb / 1e6:.1f} | {kt[kname]['us']:.1f} | {gbs:.0f} | "
+                         f"{gbs / HBM_PEAK_GBS:.1%} |")
+    ldsdir = os.path.join(d, "lds")
+    if os.path.isdir(ldsdir) and kt:
+        m = {c: counter_means(ldsdir, c) for c in ("SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+                                                   "SQ_INSTS_LDS", "SQ_WAVES", "SQ_WAVE_CYCLES")}
+        lines += ["", "Sort and select stages: LDS bank conflicts and occupancy (one counter pass "
+                  "with SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_LDS, SQ_INSTS_LDS, SQ_WAVES, "
+                  "SQ_WAVE_CYCLES, SQ_BUSY_CYCLES; workgroup size, LDS bytes and the VGPR_Count "
+                  "field as the kernel trace records them).  \"conflict cycles per LDS "
+                  "instruction\" is SQ_LDS_BANK_CONFLICT over SQ_INSTS_LDS (wavefront "
+                  "instructions); \"waves/SIMD (LDS)\" is the residency the workgroup's LDS allows "
+                  "(160 KiB per CU, at most 8); \"waves/SIMD mean\" is SQ_WAVE_CYCLES (counted in "
+                  "4-cycle units) over the SIMDs' cycles of the average duration.", "",
+                  "| kernel | LDS instructions | bank-conflict cycles | conflict cycles per LDS "
+                  "instruction | VGPR_Count (trace) | LDS bytes | workgroup | waves/SIMD (LDS) | "
+                  "waves/SIMD mean |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for kname in sorted(kt, key=lambda n: -kt[n]["us"]):
+            if not kname.startswith(SORT_SELECT) or kname not in m["SQ_WAVES"]:
+                continue
+            e = kt[kname]
+            ninst = m["SQ_INSTS_LDS"].get(kname, 0.0)
+            conf = m["SQ_LDS_BANK_CONFLICT"].get(kname, 0.0)
+            share = f"{conf / ninst:.2f}" if ninst > 0 else "-"
+            mean = 4 * m["SQ_WAVE_CYCLES"][kname] / (CU_COUNT * SIMDS_PER_CU * e["us"] * 1e3 *
+                                                      CLOCK_GHZ)
+            lines.append(f"| {kname} | {m['SQ_INSTS_LDS'].get(kname, 0.0):.0f} | {conf:.0f} | "
+                         f"{share} | {e['vgpr']} | {e['lds']} | {e['wg']} | "
+                         f"{waves_by_lds(e['lds'], e['wg'])} | {mean:.1f} |")
     with open(os.path.join(prof, f"counters_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
