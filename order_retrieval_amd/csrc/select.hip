@@ -203,6 +203,25 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     bitonic_clean<E, L>(best, lane);
 }
 
+// The first walk of a query (the right walk of its largest run) into the empty list: its
+// candidates are already in (|dz|, j) order, so lane `lane` takes candidates
+// [lane*E, lane*E + E) in place -- no merge network.
+template <int K, int L, int S, bool O32>
+__device__ __forceinline__ void fill_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
+                                          typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
+                                          typename TreeIx<O32>::T s, uint64_t target, int lane) {
+    using IX = typename TreeIx<O32>::T;
+    constexpr int E = K / L;
+    const IX b = p + lane * E;  // entry t of this lane: run[b + t], valid while b + t < s
+    uint64_t c[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) c[t] = TreeIx<O32>::load(tree, roff + (b + t < s ? b + t : s - 1));
+#pragma unroll
+    for (int t = 0; t < E; ++t) keep(c[t]);
+#pragma unroll
+    for (int t = 0; t < E; ++t) best[t] = b + t < s ? c[t] - target : ~0ull;
+}
+
 // CT, S: code type and position bits of the packed tree entries (uint32_t, 32 for 30-bit
 // codes; uint64_t, 28 for the 36-bit codes of 12-bit cells).
 template <int K, int L, typename CT, int S, bool O32>
@@ -248,6 +267,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
     // insertion positions then reach every lane of the query by a DPP quad broadcast.
     constexpr int kPer = L == 1 ? kSearchGroup : 1;
     constexpr int kRuns = kPer * L;
+    bool fresh = true;  // the list is still empty
     while (rem) {
         // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
         // offsets (not pointers) keep every access a global-memory access
@@ -313,10 +333,14 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
             const IX pg = static_cast<IX>(from_lane<L, gi / kPer>(pos[gi % kPer]));
             if (lv[gi] >= 0) {
                 const IX s = IX(1) << lv[gi];
-                merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane);
+                if (gi == 0 && fresh)  // uniform: every query's first group
+                    fill_walk<K, L, S, O32>(best, hA, roff[gi], pg, s, target, lane);
+                else
+                    merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane);
                 merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane);
             }
         });
+        fresh = false;
     }
 
     // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K;
