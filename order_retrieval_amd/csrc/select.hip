@@ -74,31 +74,67 @@ __device__ __forceinline__ int64_t from_lane(int64_t x) {
     }
 }
 
+// Packed keys (|dz| << S) | j.  With 30-bit codes (S = 32) a key is below 2^62, so its bit
+// pattern read as an IEEE double is non-negative and finite (subnormal while |dz| < 2^20),
+// and for such patterns the double order is the integer order.  A compare-exchange is then
+// one v_min_f64 and one v_max_f64 instead of 64-bit compares and two selects per output; the
+// kernels keep f64 subnormals (the default FP mode), so no pattern is flushed, and neither
+// instruction changes a non-NaN input.  The empty slot is 2^62 - 1, above every key (j <
+// 2^31).  With 36-bit codes (S = 28) keys use all 64 bits: integer compares, empty = ~0.
+template <int S>
+constexpr uint64_t kNone = S == 32 ? 0x3fffffffffffffffull : ~0ull;
+
+template <int S>
+__device__ __forceinline__ uint64_t kmin(uint64_t a, uint64_t b) {
+    if constexpr (S == 32) {
+        uint64_t r;
+        asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    } else {
+        return b < a ? b : a;
+    }
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) {
+    if constexpr (S == 32) {
+        uint64_t r;
+        asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    } else {
+        return b < a ? a : b;
+    }
+}
+
 // Cross-lane compare-exchange stage with partner lane ^ D: the lower lane keeps minima.
-template <int E, int D>
+template <int E, int D, int S>
 __device__ __forceinline__ void cross_stage(uint64_t (&a)[E], bool keep_min) {
 #pragma unroll
     for (int u = 0; u < E; ++u) {
         const uint64_t y = quad_xor<D>(a[u]);
-        const bool lt = y < a[u];
-        a[u] = (lt == keep_min) ? y : a[u];
+        if constexpr (S == 32) {
+            const uint64_t lo = kmin<S>(a[u], y), hi = kmax<S>(a[u], y);
+            a[u] = keep_min ? lo : hi;
+        } else {
+            const bool lt = y < a[u];
+            a[u] = (lt == keep_min) ? y : a[u];
+        }
     }
 }
 
 // Sort the bitonic sequence held as L lanes x E registers (lane-major) ascending.
-template <int E, int L>
+template <int E, int L, int S>
 __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
-    if constexpr (L == 4) cross_stage<E, 2>(a, (lane & 2) == 0);
-    if constexpr (L >= 2) cross_stage<E, 1>(a, (lane & 1) == 0);
+    if constexpr (L == 4) cross_stage<E, 2, S>(a, (lane & 2) == 0);
+    if constexpr (L >= 2) cross_stage<E, 1, S>(a, (lane & 1) == 0);
 #pragma unroll
     for (int stride = E / 2; stride > 0; stride >>= 1) {
 #pragma unroll
         for (int t = 0; t < E; ++t) {
             if ((t & stride) == 0) {
                 const uint64_t x = a[t], y = a[t + stride];
-                const bool sw = y < x;
-                a[t] = sw ? y : x;
-                a[t + stride] = sw ? x : y;
+                a[t] = kmin<S>(x, y);
+                a[t + stride] = kmax<S>(x, y);
             }
         }
     }
@@ -106,12 +142,12 @@ __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
 
 // One compare-exchange layer of a bitonic sort of the K = E*L entries (entry x = lane*E + t)
 // for block size K2 and stride J; DESC sorts descending.
-template <int E, int L, int K2, int J, bool DESC>
+template <int E, int L, int K2, int J, bool DESC, int S>
 __device__ __forceinline__ void sort_layer(uint64_t (&a)[E], int lane) {
     if constexpr (J >= E) {
         const int x = lane * E;
         const bool up = ((x & K2) == 0) != DESC;
-        cross_stage<E, J / E>(a, up == ((x & J) == 0));
+        cross_stage<E, J / E, S>(a, up == ((x & J) == 0));
     } else {
 #pragma unroll
         for (int t = 0; t < E; ++t) {
@@ -119,20 +155,20 @@ __device__ __forceinline__ void sort_layer(uint64_t (&a)[E], int lane) {
                 const int x = lane * E + t;
                 const bool up = ((x & K2) == 0) != DESC;
                 const uint64_t p = a[t], q = a[t + J];
-                const bool sw = up ? (q < p) : (p < q);
-                a[t] = sw ? q : p;
-                a[t + J] = sw ? p : q;
+                const uint64_t lo = kmin<S>(p, q), hi = kmax<S>(p, q);
+                a[t] = up ? lo : hi;
+                a[t + J] = up ? hi : lo;
             }
         }
     }
-    if constexpr (J > 1) sort_layer<E, L, K2, J / 2, DESC>(a, lane);
+    if constexpr (J > 1) sort_layer<E, L, K2, J / 2, DESC, S>(a, lane);
 }
 
-template <int E, int L, int K2, bool DESC>
+template <int E, int L, int K2, bool DESC, int S>
 __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
     if constexpr (K2 <= E * L) {  // a single entry (K = 1) needs no layer
-        sort_layer<E, L, K2, K2 / 2, DESC>(a, lane);
-        if constexpr (K2 < E * L) sort_blocks<E, L, K2 * 2, DESC>(a, lane);
+        sort_layer<E, L, K2, K2 / 2, DESC, S>(a, lane);
+        if constexpr (K2 < E * L) sort_blocks<E, L, K2 * 2, DESC, S>(a, lane);
     }
 }
 
@@ -174,7 +210,7 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     const bool empty = RIGHT ? p >= s : p <= 0;
     const IX p0 = RIGHT ? (empty ? s - 1 : p) : (empty ? 0 : p - 1);
     const uint64_t e0 = TreeIx<O32>::load(tree, roff + p0);
-    const uint64_t first = empty ? ~0ull : (RIGHT ? e0 - target : top - e0);
+    const uint64_t first = empty ? kNone<S> : (RIGHT ? e0 - target : top - e0);
     const uint64_t kth = from_last_lane<L>(best[E - 1]);
     if (first >= kth) return;
     constexpr int CH = kChunk < E ? kChunk : E;
@@ -194,13 +230,13 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
             // an invalid entry reads the walk's first position instead (inside the run)
             const IX at = ok ? b + (RIGHT ? -u : u) : p0;
             const uint64_t e = TreeIx<O32>::load(tree, roff + at);
-            c[v] = ok ? (RIGHT ? e - target : top - e) : ~0ull;
+            c[v] = ok ? (RIGHT ? e - target : top - e) : kNone<S>;
         }
 #pragma unroll
-        for (int v = 0; v < CH; ++v) best[u0 + v] = c[v] < best[u0 + v] ? c[v] : best[u0 + v];
+        for (int v = 0; v < CH; ++v) best[u0 + v] = kmin<S>(c[v], best[u0 + v]);
         if (CH < E) __builtin_amdgcn_sched_barrier(0);
     }
-    bitonic_clean<E, L>(best, lane);
+    bitonic_clean<E, L, S>(best, lane);
 }
 
 // The first walk of a query (the right walk of its largest run) into the empty list: its
@@ -219,7 +255,7 @@ __device__ __forceinline__ void fill_walk(uint64_t (&best)[K / L], const uint64_
 #pragma unroll
     for (int t = 0; t < E; ++t) keep(c[t]);
 #pragma unroll
-    for (int t = 0; t < E; ++t) best[t] = b + t < s ? c[t] - target : ~0ull;
+    for (int t = 0; t < E; ++t) best[t] = b + t < s ? c[t] - target : kNone<S>;
 }
 
 // CT, S: code type and position bits of the packed tree entries (uint32_t, 32 for 30-bit
@@ -253,7 +289,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 
     uint64_t best[E];
 #pragma unroll
-    for (int t = 0; t < E; ++t) best[t] = ~0ull;
+    for (int t = 0; t < E; ++t) best[t] = kNone<S>;
 
     // The runs are the set bits of the number of usable keys (i+1 under the causal mask,
     // else N), largest first, taken kSearchGroup at a time: their lower_bound searches
@@ -368,7 +404,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 #pragma unroll
             for (int t = 0; t < E; ++t) {
                 const int u = lane * E + t;
-                cand[t] = ~0ull;
+                cand[t] = kNone<S>;
                 if (u < cg) {
                     const int64_t j = sbase + g * K + u;
                     const uint64_t c = static_cast<uint64_t>(code[t]);
@@ -383,10 +419,10 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 #pragma unroll
             for (int t = 0; t < E; ++t) beats |= cand[t] < kth;
             if (__ballot(beats) == 0) continue;  // uniform over the active lanes
-            sort_blocks<E, L, 2, true>(cand, lane);
+            sort_blocks<E, L, 2, true, S>(cand, lane);
 #pragma unroll
-            for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
-            bitonic_clean<E, L>(best, lane);
+            for (int t = 0; t < E; ++t) best[t] = kmin<S>(cand[t], best[t]);
+            bitonic_clean<E, L, S>(best, lane);
         }
     }
 
@@ -394,7 +430,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 #pragma unroll
     for (int t = 0; t < E; ++t)
         if (lane * E + t < topk)
-            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(best[t] & kJMask);
+            out[t] = best[t] == kNone<S> ? -1 : static_cast<int32_t>(best[t] & kJMask);
 }
 
 template <int K, int L, typename CT, int S>
@@ -486,7 +522,7 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 
     uint64_t best[E];
 #pragma unroll
-    for (int t = 0; t < E; ++t) best[t] = ~0ull;
+    for (int t = 0; t < E; ++t) best[t] = kNone<S>;
 
     // chunks 0 .. i >> lvl, kChunkGroup at a time: their lower_bound searches advance in
     // lock-step (probes from clamped positions, in flight together), then each chunk's window
@@ -544,7 +580,7 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 #pragma unroll
             for (int t = 0; t < E; ++t) {
                 const int64_t u = lane * E + t;
-                cand[t] = ~0ull;
+                cand[t] = kNone<S>;
                 if (u < w) {
                     const uint64_t j = ev[t] & kJMask;
                     const uint64_t code = ev[t] >> S;
@@ -552,10 +588,10 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
                     if (static_cast<int64_t>(j) <= i) cand[t] = (dz << S) | j;  // causal mask
                 }
             }
-            sort_blocks<E, L, 2, true>(cand, lane);
+            sort_blocks<E, L, 2, true, S>(cand, lane);
 #pragma unroll
-            for (int t = 0; t < E; ++t) best[t] = cand[t] < best[t] ? cand[t] : best[t];
-            bitonic_clean<E, L>(best, lane);
+            for (int t = 0; t < E; ++t) best[t] = kmin<S>(cand[t], best[t]);
+            bitonic_clean<E, L, S>(best, lane);
         }
     }
 
@@ -563,7 +599,7 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 #pragma unroll
     for (int t = 0; t < E; ++t)
         if (lane * E + t < topk)
-            out[t] = best[t] == ~0ull ? -1 : static_cast<int32_t>(best[t] & kJMask);
+            out[t] = best[t] == kNone<S> ? -1 : static_cast<int32_t>(best[t] & kJMask);
 }
 
 template <int K, int L, typename CT, int S>
