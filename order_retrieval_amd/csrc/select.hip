@@ -21,8 +21,8 @@
 // with one bitonic step: elementwise min against the reversed candidates (each lane loads
 // its own contiguous block of the walk) leaves a bitonic sequence of the K smallest, which
 // log2(K) compare-exchange stages sort; the stages whose stride spans lanes exchange values
-// with DPP quad permutes.  A walk whose first candidate is not better than the current K-th
-// is skipped.  The runs are taken in groups: with several lanes per query each lane
+// with DPP quad permutes.  A walk whose first candidate cannot beat the current K-th is
+// skipped, decided from values the search already holds.  The runs are taken in groups: with several lanes per query each lane
 // binary-searches its own run of the group (with one lane, kSearchGroup runs advance in
 // lock-step), so the probes are independent loads in flight together, and the insertion
 // positions reach the query's lanes by a DPP quad broadcast.
@@ -53,6 +53,21 @@ __device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
         return x;
     } else {
         constexpr int ctrl = L == 2 ? 0xF5 : 0xFF;  // quad_perm [1,1,3,3] / [3,3,3,3]
+        const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl,
+                                                0xF, 0xF, false);
+        const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)),
+                                                ctrl, 0xF, 0xF, false);
+        return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    }
+}
+
+// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad), 64 bits.
+template <int L, int SRC>
+__device__ __forceinline__ uint64_t from_lane64(uint64_t x) {
+    if constexpr (L == 1) {
+        return x;
+    } else {
+        constexpr int ctrl = L == 4 ? SRC * 0x55 : (SRC * 0x5) | ((2 + SRC) * 0x50);
         const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl,
                                                 0xF, 0xF, false);
         const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)),
@@ -193,67 +208,84 @@ struct TreeIx<false> {
     }
 };
 
-// Merge one walk into the running top-K.  Candidate c (0 = first) of the walk sits at run
-// position p + c (right walk, asc tree, key = e - target) or p - 1 - c (left walk, desc
-// tree, key = (target | 0xffffffff) - e).  Lane `lane` of the query holds list entries
-// [lane*E, lane*E + E) and pairs them with candidates K-1-t, i.e. its own block of E.
+// Walks.  Candidate c (0 = first) of the right walk sits at run position p + c (asc tree,
+// key = e - target), of the left walk at p - 1 - c (desc tree, key = (target | jmask) - e).
+// For a merge, lane `lane` of the query pairs its list entries [lane*E, lane*E + E) with
+// candidates K-1-t, i.e. entry u of its share is candidate K-1-lane*E-u: the elementwise
+// minimum of the ascending list and the reversed candidates leaves a bitonic sequence of the
+// K smallest.  A position outside the run reads the walk's first position (always inside the
+// run when the walk is not empty) and becomes the empty key, so no load sits behind a branch.
+template <int K, int L, bool RIGHT, bool O32>
+struct WalkShare {
+    using IX = typename TreeIx<O32>::T;
+    static constexpr int E = K / L;
+    IX b, lim, p0;
+    // right: entry u is run[b - u], valid iff u > lim; left: run[b + u], valid iff u >= lim
+    __device__ __forceinline__ WalkShare(IX p, IX s, int lane)
+        : b(RIGHT ? p + (K - 1 - lane * E) : p - K + lane * E),
+          lim(RIGHT ? b - s : -b),
+          p0(RIGHT ? (p < s ? p : s - 1) : (p > 0 ? p - 1 : 0)) {}
+    __device__ __forceinline__ bool ok(int u) const { return RIGHT ? u > lim : u >= lim; }
+    __device__ __forceinline__ IX at(int u) const { return ok(u) ? b + (RIGHT ? -u : u) : p0; }
+};
+
+template <int K, int L, bool RIGHT, int S, bool O32, int U0, int CH>
+__device__ __forceinline__ void walk_load(uint64_t (&c)[CH], const uint64_t* __restrict__ tree,
+                                          typename TreeIx<O32>::T roff,
+                                          const WalkShare<K, L, RIGHT, O32>& w) {
+#pragma unroll
+    for (int v = 0; v < CH; ++v) c[v] = TreeIx<O32>::load(tree, roff + w.at(U0 + v));
+}
+
+template <int K, int L, bool RIGHT, int S, bool O32, int U0, int CH>
+__device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, L, RIGHT, O32>& w,
+                                          uint64_t target) {
+    const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
+#pragma unroll
+    for (int v = 0; v < CH; ++v)
+        c[v] = w.ok(U0 + v) ? (RIGHT ? c[v] - target : top - c[v]) : kNone<S>;
+}
+
+// Merge one walk into the running top-K, its candidates loaded kChunk at a time (register
+// budget for K = 64); the caller has checked that its first candidate may enter the list.
 template <int K, int L, bool RIGHT, int S, bool O32>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
                                            typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
                                            typename TreeIx<O32>::T s, uint64_t target, int lane) {
-    using IX = typename TreeIx<O32>::T;
     constexpr int E = K / L;
-    const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
-    // skip when the walk is empty or its first candidate does not beat the current K-th
-    // (every load below reads a clamped, in-run position and the value is selected after, so
-    // no load sits behind a branch and they all issue before the first wait)
-    const bool empty = RIGHT ? p >= s : p <= 0;
-    const IX p0 = RIGHT ? (empty ? s - 1 : p) : (empty ? 0 : p - 1);
-    const uint64_t e0 = TreeIx<O32>::load(tree, roff + p0);
-    const uint64_t first = empty ? kNone<S> : (RIGHT ? e0 - target : top - e0);
-    const uint64_t kth = from_last_lane<L>(best[E - 1]);
-    if (first >= kth) return;
     constexpr int CH = kChunk < E ? kChunk : E;
-    // One base pointer per walk and lane; the E candidates sit at constant offsets from it
-    // (immediate offsets of the loads, so no per-candidate address is kept in registers).
-    // Right walk: entry u of this lane is run[b - u], valid while b - u < s.
-    // Left walk:  entry u of this lane is run[b + u], valid while b + u >= 0.
-    const IX b = RIGHT ? p + (K - 1 - lane * E) : p - K + lane * E;
-    const IX lim = RIGHT ? b - s : -b;  // right: valid iff u > lim; left: valid iff u >= lim
-#pragma unroll
-    for (int u0 = 0; u0 < E; u0 += CH) {
+    const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
+    static_for<0, E / CH>([&](auto ic) {
+        constexpr int u0 = decltype(ic)::value * CH;
         uint64_t c[CH];
-#pragma unroll
-        for (int v = 0; v < CH; ++v) {
-            const int u = u0 + v;
-            const bool ok = RIGHT ? u > lim : u >= lim;
-            // an invalid entry reads the walk's first position instead (inside the run)
-            const IX at = ok ? b + (RIGHT ? -u : u) : p0;
-            const uint64_t e = TreeIx<O32>::load(tree, roff + at);
-            c[v] = ok ? (RIGHT ? e - target : top - e) : kNone<S>;
-        }
+        walk_load<K, L, RIGHT, S, O32, u0, CH>(c, tree, roff, w);
+        walk_keys<K, L, RIGHT, S, O32, u0, CH>(c, w, target);
 #pragma unroll
         for (int v = 0; v < CH; ++v) best[u0 + v] = kmin<S>(c[v], best[u0 + v]);
         if (CH < E) __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     bitonic_clean<E, L, S>(best, lane);
 }
 
-// The first walk of a query (the right walk of its largest run) into the empty list: its
-// candidates are already in (|dz|, j) order, so lane `lane` takes candidates
+// The first walk of a query (the right walk of its largest run) goes into the empty list:
+// its candidates are already in (|dz|, j) order, so lane `lane` takes candidates
 // [lane*E, lane*E + E) in place -- no merge network.
-template <int K, int L, int S, bool O32>
-__device__ __forceinline__ void fill_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
+template <int K, int L, bool O32>
+__device__ __forceinline__ void fill_load(uint64_t (&c)[K / L], const uint64_t* __restrict__ tree,
                                           typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
-                                          typename TreeIx<O32>::T s, uint64_t target, int lane) {
-    using IX = typename TreeIx<O32>::T;
+                                          typename TreeIx<O32>::T s, int lane) {
     constexpr int E = K / L;
-    const IX b = p + lane * E;  // entry t of this lane: run[b + t], valid while b + t < s
-    uint64_t c[E];
+    const typename TreeIx<O32>::T b = p + lane * E;  // entry t: run[b + t], valid while b + t < s
 #pragma unroll
     for (int t = 0; t < E; ++t) c[t] = TreeIx<O32>::load(tree, roff + (b + t < s ? b + t : s - 1));
-#pragma unroll
-    for (int t = 0; t < E; ++t) keep(c[t]);
+}
+
+template <int K, int L, int S, bool O32>
+__device__ __forceinline__ void fill_keys(uint64_t (&best)[K / L], const uint64_t (&c)[K / L],
+                                          typename TreeIx<O32>::T p, typename TreeIx<O32>::T s,
+                                          uint64_t target, int lane) {
+    constexpr int E = K / L;
+    const typename TreeIx<O32>::T b = p + lane * E;
 #pragma unroll
     for (int t = 0; t < E; ++t) best[t] = b + t < s ? c[t] - target : kNone<S>;
 }
@@ -340,7 +372,14 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
             pos[t] = 0;
         }
         // probes from clamped positions, held live together (see keep()), so the searches'
-        // loads are in flight together
+        // loads are in flight together.  A lower_bound search by halving steps probes both
+        // neighbours of the insertion position p: the probe of the last step that moved is
+        // entry p - 1 and the final probe, when it does not move, is entry p.  They give the
+        // right walk's first key exactly and a lower bound of the left walk's first key
+        // (same code as entry p - 1), so a walk is skipped without loading anything.
+        uint64_t below[kPer], rfirst[kPer], lbound[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) below[t] = 0;
         for (IX step = (IX(1) << lv[0]) >> 1; step > 0; step >>= 1) {
             uint64_t e[kPer];
 #pragma unroll
@@ -351,8 +390,12 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 #pragma unroll
             for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
-            for (int t = 0; t < kPer; ++t)
-                if (pos[t] + step < mlen[t] && e[t] < target) pos[t] += step;
+            for (int t = 0; t < kPer; ++t) {
+                if (pos[t] + step < mlen[t] && e[t] < target) {
+                    pos[t] += step;
+                    below[t] = e[t];
+                }
+            }
         }
         {
             uint64_t e[kPer];
@@ -361,19 +404,37 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 #pragma unroll
             for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
-            for (int t = 0; t < kPer; ++t)
-                if (mon[t] && e[t] < target) pos[t] += 1;
+            for (int t = 0; t < kPer; ++t) {
+                // a move here means every entry of the run is below the target
+                const bool mv = mon[t] && e[t] < target;
+                if (mv) {
+                    pos[t] += 1;
+                    below[t] = e[t];
+                }
+                rfirst[t] = mv || !mon[t] ? kNone<S> : e[t] - target;
+                lbound[t] = pos[t] == 0 ? kNone<S> : target - (below[t] & ~kJMask);
+            }
         }
         static_for<0, kRuns>([&](auto gc) {
             constexpr int gi = decltype(gc)::value;
-            const IX pg = static_cast<IX>(from_lane<L, gi / kPer>(pos[gi % kPer]));
+            constexpr int src = gi / kPer, slot = gi % kPer;
+            const IX pg = static_cast<IX>(from_lane<L, src>(pos[slot]));
+            const uint64_t rf = from_lane64<L, src>(rfirst[slot]);
+            const uint64_t lb = from_lane64<L, src>(lbound[slot]);
             if (lv[gi] >= 0) {
                 const IX s = IX(1) << lv[gi];
-                if (gi == 0 && fresh)  // uniform: every query's first group
-                    fill_walk<K, L, S, O32>(best, hA, roff[gi], pg, s, target, lane);
-                else
+                const bool fill = gi == 0 && fresh;  // uniform: every query's first group
+                if (fill) {
+                    uint64_t c[E];
+                    fill_load<K, L, O32>(c, hA, roff[gi], pg, s, lane);
+#pragma unroll
+                    for (int t = 0; t < E; ++t) keep(c[t]);
+                    fill_keys<K, L, S, O32>(best, c, pg, s, target, lane);
+                } else if (rf < from_last_lane<L>(best[E - 1])) {
                     merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane);
-                merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane);
+                }
+                if (lb < from_last_lane<L>(best[E - 1]))
+                    merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane);
             }
         });
         fresh = false;
