@@ -121,27 +121,74 @@ __device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) {
     }
 }
 
+// One word of lane `lane ^ D` of the same quad, by a DPP quad permute that the compiler can
+// fold into the instruction consuming it (every lane of the quad is active where it is used).
+template <int D>
+__device__ __forceinline__ uint32_t quad_take(uint32_t x) {
+    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), ctrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ uint64_t pack64(uint32_t lo, uint32_t hi) {
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Cross-lane compare-exchange stage with partner lane ^ D: the lower lane keeps minima.
+// 30-bit-code keys: a lane that keeps maxima negates both operands (flips the sign bit of the
+// high word; the partner's arrives flipped from the DPP instruction that fetches it), takes
+// the one v_min_f64 -- the negated maximum -- and flips the result back.
 template <int E, int D, int S>
 __device__ __forceinline__ void cross_stage(uint64_t (&a)[E], bool keep_min) {
+    if constexpr (S == 32) {
+        const uint32_t m = keep_min ? 0u : 0x80000000u;
 #pragma unroll
-    for (int u = 0; u < E; ++u) {
-        const uint64_t y = quad_xor<D>(a[u]);
-        if constexpr (S == 32) {
-            const uint64_t lo = kmin<S>(a[u], y), hi = kmax<S>(a[u], y);
-            a[u] = keep_min ? lo : hi;
-        } else {
+        for (int u = 0; u < E; ++u) {
+            const uint32_t lo = static_cast<uint32_t>(a[u]), hi = static_cast<uint32_t>(a[u] >> 32);
+            const uint64_t y = pack64(quad_take<D>(lo), quad_take<D>(hi) ^ m);
+            const uint64_t r = kmin<S>(pack64(lo, hi ^ m), y);
+            a[u] = pack64(static_cast<uint32_t>(r), static_cast<uint32_t>(r >> 32) ^ m);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+            const uint64_t y = quad_xor<D>(a[u]);
             const bool lt = y < a[u];
             a[u] = (lt == keep_min) ? y : a[u];
         }
     }
 }
 
+// The two cross-lane stages of a clean over a quad (partners lane ^ 2, then lane ^ 1) on
+// 30-bit-code keys, chained in signed form: after the first stage a value stays negated by
+// its lane's first mask, and the second stage re-signs both operands by the xor of the two
+// masks (a lane and its ^ 1 partner share the first mask), so one flip per stage remains.
+template <int E>
+__device__ __forceinline__ void cross_stages_quad(uint64_t (&a)[E], int lane) {
+    const uint32_t m2 = (lane & 2) ? 0x80000000u : 0u;
+    const uint32_t m1 = (lane & 1) ? 0x80000000u : 0u;
+    const uint32_t m12 = m1 ^ m2;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        uint32_t lo = static_cast<uint32_t>(a[u]), hi = static_cast<uint32_t>(a[u] >> 32);
+        const uint64_t r2 = kmin<32>(pack64(lo, hi ^ m2),
+                                     pack64(quad_take<2>(lo), quad_take<2>(hi) ^ m2));
+        lo = static_cast<uint32_t>(r2);
+        hi = static_cast<uint32_t>(r2 >> 32);  // negated by m2
+        const uint64_t r1 = kmin<32>(pack64(lo, hi ^ m12),
+                                     pack64(quad_take<1>(lo), quad_take<1>(hi) ^ m12));
+        a[u] = pack64(static_cast<uint32_t>(r1), static_cast<uint32_t>(r1 >> 32) ^ m1);
+    }
+}
+
 // Sort the bitonic sequence held as L lanes x E registers (lane-major) ascending.
 template <int E, int L, int S>
 __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
-    if constexpr (L == 4) cross_stage<E, 2, S>(a, (lane & 2) == 0);
-    if constexpr (L >= 2) cross_stage<E, 1, S>(a, (lane & 1) == 0);
+    if constexpr (L == 4 && S == 32) {
+        cross_stages_quad<E>(a, lane);
+    } else {
+        if constexpr (L == 4) cross_stage<E, 2, S>(a, (lane & 2) == 0);
+        if constexpr (L >= 2) cross_stage<E, 1, S>(a, (lane & 1) == 0);
+    }
 #pragma unroll
     for (int stride = E / 2; stride > 0; stride >>= 1) {
 #pragma unroll
