@@ -17,12 +17,13 @@
 //
 // The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
 // (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 64,
-// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below).  A walk's K candidates are merged
-// with one bitonic step: elementwise min against the reversed candidates (each lane loads
-// its own contiguous block of the walk) leaves a bitonic sequence of the K smallest, which
-// log2(K) compare-exchange stages sort; the stages whose stride spans lanes exchange values
-// with DPP quad permutes.  A walk whose first candidate cannot beat the current K-th is
-// skipped, decided from values the search already holds.  The runs are taken in groups: with several lanes per query each lane
+// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below).  A
+// walk's K candidates are merged with one bitonic step: elementwise min against the
+// reversed candidates (each lane loads its own contiguous block of the walk) leaves a
+// bitonic sequence of the K smallest, which log2(K) compare-exchange stages sort; the stages
+// whose stride spans lanes exchange values with DPP quad permutes.  A walk whose first
+// candidate cannot beat the current K-th is skipped, decided from values the search already
+// holds.  The runs are taken in groups: with several lanes per query each lane
 // binary-searches its own run of the group (with one lane, kSearchGroup runs advance in
 // lock-step), so the probes are independent loads in flight together, and the insertion
 // positions reach the query's lanes by a DPP quad broadcast.
