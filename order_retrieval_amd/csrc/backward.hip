@@ -85,14 +85,22 @@ __device__ __forceinline__ bool pair_item(int32_t j, int64_t e, const PairSpec& 
 
 // ---------------------------------------------------------------------------- 1. queries
 // One 16-lane row (a DPP row) per query i, four queries per wavefront, taken in the Z-order
-// processing order.  Lane l owns slots l, 16 + l, ...: it loads their indices and key rows
-// and forms s, the distance terms and later a, c and the dq / dgamma terms.  The row keeps
-// its chunks of dO_i in registers and walks the slots in order: the index comes from the
-// owning lane by a DPP row broadcast, every lane loads its chunks of the v_j row (the loads
-// of kRowLoads slots are issued together) and a DPP butterfly over the row completes
-// g_ij = dO_i . v_j, which the owning lane keeps.
+// processing order.  Each lane owns one slot of every group of 16 (query_slot_of_lane): it
+// loads their indices and key rows and forms s, the distance terms and later a, c and the
+// dq / dgamma terms.  The row keeps its chunks of dO_i in registers and walks the slots in
+// batches of eight: the index comes from the owning lane by a DPP row broadcast, every lane
+// loads its chunks of the v_j row (the batch's loads are issued together) and forms its
+// parts of g_ij = dO_i . v_j, and one row reduce-scatter completes the batch's eight dot
+// products in their owners.
 constexpr int kRowLanes = 16;  // lanes per query or key
 constexpr int kRowLoads = 8;   // rows whose loads are issued together
+static_assert(kRowLoads == 8 && kRowLanes == 16, "two 8-slot reduce-scatters per 16-slot group");
+
+// Slot ownership in the per-query pass: inside each group of 16 slots, lane l of the row owns
+// slot (l & 1) * 8 + l / 2 (even lanes the first eight, odd lanes the last eight), which is
+// where an 8-slot row reduce-scatter leaves each slot's total.
+__device__ __forceinline__ int query_slot_of_lane(int l) { return (l & 1) * 8 + (l >> 1); }
+constexpr int query_lane_of_slot(int s) { return (s & 7) * 2 + (s >> 3); }
 // Workgroup sizes (measured): more curve neighbours per workgroup share a CU's L1 in the
 // per-query pass; the per-key pass keeps 256 (its rows are ordered by pair count within a
 // workgroup, and more VGPRs per lane limit larger workgroups to fewer waves per SIMD).
@@ -101,6 +109,10 @@ constexpr int kKeyThreads = 256;    // workgroup of the per-key pass
 constexpr int kQueryRows = kQueryThreads / kRowLanes;  // queries per workgroup (one (b,h))
 constexpr int kKeyRows = kKeyThreads / kRowLanes;      // keys per workgroup (one (b,h))
 
+// g for slots L0 .. L0 + 7 of a 16-slot group: every lane forms its part of each dot product
+// (its dO_i chunks with its chunks of the slot's value row; the row name comes from the
+// slot's owner, and the batch's loads are issued together), then one row reduce-scatter
+// leaves each slot's total in its owner.
 template <bool BF16, bool O32, int CPL, int L0>
 __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* __restrict__ vh,
                                             int dv, const int (&coff)[CPL], uint32_t jo,
@@ -112,10 +124,12 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
     R raw[kRowLoads][CPL];
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
-        const uint32_t nm = row_bcast<L0 + w>(jo);  // an empty slot names key 0's row, g unused
+        // an empty slot names key 0's row, g unused
+        const uint32_t nm = row_bcast<query_lane_of_slot(L0 + w)>(jo);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) raw[w][c] = RowRef<BF16, O32>::load(vh, nm, dv, coff[c]);
     });
+    float parts[kRowLoads];
     static_for<0, kRowLoads>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         float part = 0.0f;
@@ -126,9 +140,10 @@ __device__ __forceinline__ void query_slots(const typename VecIO<BF16>::elem_t* 
 #pragma unroll
             for (int e = 0; e < E; ++e) part += go[c][e] * x[e];
         }
-        const float g = group_sum(part, kRowLanes);
-        if (lrow == L0 + w) gmine = g;
+        parts[w] = part;
     });
+    const float g = row_reduce_scatter8(parts, lrow);  // slot L0 + lrow / 2
+    if ((lrow & 1) == L0 / kRowLoads) gmine = g;
 }
 
 template <bool BF16, bool O32, int CPL, int U>
@@ -174,7 +189,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     int32_t jr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int r = lrow + u * kRowLanes;
+        const int r = query_slot_of_lane(lrow) + u * kRowLanes;
         jr[u] = ir[r < topk ? r : topk - 1];
     }
 #pragma unroll
@@ -183,7 +198,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     Point3 kp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        sel[u] = lrow + u * kRowLanes < m && jr[u] >= 0;
+        sel[u] = query_slot_of_lane(lrow) + u * kRowLanes < m && jr[u] >= 0;
         jr[u] = sel[u] ? static_cast<int32_t>(clamp_index(jr[u], nk - 1)) : 0;
         kp[u] = load_point(kh, jr[u]);
     }
@@ -246,7 +261,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
         if (sel[u]) {
             const float a = so[u] * inv_S;
             const float c = a * so[u] * (gg[u] - D);
-            if (live) cr[lrow + u * kRowLanes] = make_float2(a, c);
+            if (live) cr[query_slot_of_lane(lrow) + u * kRowLanes] = make_float2(a, c);
             a0 += c * dx[u];
             a1 += c * dy[u];
             a2 += c * dz[u];

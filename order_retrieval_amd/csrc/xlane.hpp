@@ -43,6 +43,27 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
         __builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x150 + L, 0xF, 0xF, true));
 }
 
+// Reduce-scatter of 8 slots over a 16-lane row: v[s] is this lane's part of slot s's sum;
+// lanes 2s and 2s + 1 of the row return the row's total of slot s.  Three exchange steps,
+// with the partners 15 - l, then 7 - l inside the half-row, then l ^ 2 (their lowest
+// differing lane bits are 3, 2, 1), each halve the slots a lane holds: it keeps the half whose
+// slot bit equals its lane bit and adds the partner's part of it; a last add with lane l ^ 1
+// joins the two halves of the row.  The summation order is fixed, so the result is
+// reproducible.  22 VALU instructions for 8 slots (a group_sum per slot takes 32, in longer
+// dependent chains).
+__device__ __forceinline__ float row_reduce_scatter8(const float (&v)[8], int lrow) {
+    float a[4], b[2];
+    const bool b3 = (lrow & 8) != 0, b2 = (lrow & 4) != 0, b1 = (lrow & 2) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        a[k] = (b3 ? v[4 + k] : v[k]) + dpp_take<kDppMirror>(b3 ? v[k] : v[4 + k]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        b[k] = (b2 ? a[2 + k] : a[k]) + dpp_take<kDppHalfMirror>(b2 ? a[k] : a[2 + k]);
+    const float c = (b1 ? b[1] : b[0]) + dpp_take<kDppXor2>(b1 ? b[0] : b[1]);
+    return c + dpp_take<kDppXor1>(c);
+}
+
 // Sum over aligned groups of G lanes (G a power of two, 8 <= G <= 64).  Each step adds the
 // partner block's partial sum: partners xor 1 and xor 2 inside a quad, then the mirrored
 // quad of the half-row and the mirrored half of the row, then xor 16 and xor 32 across rows.
