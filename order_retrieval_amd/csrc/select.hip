@@ -35,6 +35,7 @@ namespace zeta {
 constexpr int kSearchGroup = 2;  // runs whose binary searches advance in lock-step
 constexpr int kChunk = 8;        // candidates of a walk loaded per step (register budget)
 constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (chunked search)
+constexpr int kInsert = 2;       // walk candidates merged by insertion when no more can enter
 
 // Value of the lane `lane ^ D` of the same quad (D = 1 or 2).
 template <int D>
@@ -235,6 +236,68 @@ __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
     }
 }
 
+// Value of the previous lane of this query's lane group (L = 2 or 4 lanes in a quad); the
+// group's first lane reads its own value.
+template <int L>
+__device__ __forceinline__ uint64_t from_prev_lane(uint64_t x) {
+    constexpr int ctrl = L == 4 ? 0x90 : 0xA0;  // quad_perm [0,0,1,2] / [0,0,2,2]
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF,
+                                            0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)), ctrl,
+                                            0xF, 0xF, false);
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Merge R ascending candidates c_0 <= ... <= c_{R-1}, the same on every lane of the query,
+// into the ascending list (L lanes x E registers, lane-major).  Entry t of the merged list is
+// the t-th smallest of the union of two sorted lists: the least of b_t and of
+// max(b_{t-1-r}, c_r) for r < R, where entries before the list's first count as the smallest
+// key, 0.  That is 2R min/max per entry and one lane shift per r, against log2(K)
+// compare-exchange stages for a bitonic merge.
+template <int E, int L, int R, int S>
+__device__ __forceinline__ void insert_few(uint64_t (&best)[E], const uint64_t (&c)[R], int lane) {
+    static_assert(R <= E, "the shifted entries come from the previous lane only");
+    uint64_t prev[R];  // prev[r]: list entry lane*E - 1 - r
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if constexpr (L == 1) {
+            prev[r] = 0;
+        } else {
+            const uint64_t y = from_prev_lane<L>(best[E - 1 - r]);
+            prev[r] = lane == 0 ? 0 : y;
+        }
+    }
+    uint64_t out[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+        uint64_t v = best[t];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int u = t - 1 - r;
+            v = kmin<S>(v, kmax<S>(u >= 0 ? best[u] : prev[-1 - u], c[r]));
+        }
+        out[t] = v;
+    }
+#pragma unroll
+    for (int t = 0; t < E; ++t) best[t] = out[t];
+}
+
+// True when no lane group of L lanes (aligned in the wavefront) has two bits set in m.
+template <int L>
+__device__ __forceinline__ bool one_per_group(uint64_t m) {
+    if constexpr (L == 1) {
+        return true;
+    } else {
+        const uint64_t pair_both = m & (m >> 1) & 0x5555555555555555ull;
+        if constexpr (L == 2) {
+            return pair_both == 0;
+        } else {
+            const uint64_t pair_any = (m | (m >> 1)) & 0x5555555555555555ull;
+            return pair_both == 0 && (pair_any & (pair_any >> 2) & 0x1111111111111111ull) == 0;
+        }
+    }
+}
+
 // Entries of one (b,h)'s tree levels are addressed from the slice base.  When the slice holds
 // fewer than 2^28 entries per tree (O32) offsets are 32-bit and a load is a uniform base plus
 // a 32-bit byte offset; otherwise 64-bit indices.
@@ -285,17 +348,26 @@ __device__ __forceinline__ void walk_load(uint64_t (&c)[CH], const uint64_t* __r
     for (int v = 0; v < CH; ++v) c[v] = TreeIx<O32>::load(tree, roff + w.at(U0 + v));
 }
 
+// Key of the tree entry e loaded for entry u of the lane's share.
+template <int K, int L, bool RIGHT, int S, bool O32>
+__device__ __forceinline__ uint64_t walk_key(uint64_t e, const WalkShare<K, L, RIGHT, O32>& w,
+                                             int u, uint64_t target) {
+    const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
+    return w.ok(u) ? (RIGHT ? e - target : top - e) : kNone<S>;
+}
+
 template <int K, int L, bool RIGHT, int S, bool O32, int U0, int CH>
 __device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, L, RIGHT, O32>& w,
                                           uint64_t target) {
-    const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
 #pragma unroll
-    for (int v = 0; v < CH; ++v)
-        c[v] = w.ok(U0 + v) ? (RIGHT ? c[v] - target : top - c[v]) : kNone<S>;
+    for (int v = 0; v < CH; ++v) c[v] = walk_key<K, L, RIGHT, S, O32>(c[v], w, U0 + v, target);
 }
 
 // Merge one walk into the running top-K, its candidates loaded kChunk at a time (register
 // budget for K = 64); the caller has checked that its first candidate may enter the list.
+// Deep in the prefix a walk admits a key or two at most: when candidate kInsert cannot beat
+// its query's K-th for any query of the wavefront, the first kInsert candidates are merged
+// by insertion and the bitonic merge is skipped (the choice is uniform over the wavefront).
 template <int K, int L, bool RIGHT, int S, bool O32>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
                                            typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
@@ -303,6 +375,28 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     constexpr int E = K / L;
     constexpr int CH = kChunk < E ? kChunk : E;
     const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
+    if constexpr (CH == E && kInsert > 0 && kInsert < E) {
+        uint64_t c[E];
+        walk_load<K, L, RIGHT, S, O32, 0, E>(c, tree, roff, w);
+        // candidate r (r < E) is entry E-1-r of the query's last lane
+        uint64_t f[kInsert + 1];
+#pragma unroll
+        for (int r = 0; r <= kInsert; ++r)
+            f[r] = walk_key<K, L, RIGHT, S, O32>(c[E - 1 - r], w, E - 1 - r, target);
+        const bool more = lane == L - 1 && f[kInsert] < best[E - 1];
+        if (__ballot(more) == 0) {
+            uint64_t g[kInsert];
+#pragma unroll
+            for (int r = 0; r < kInsert; ++r) g[r] = from_last_lane<L>(f[r]);
+            insert_few<E, L, kInsert, S>(best, g, lane);
+            return;
+        }
+        walk_keys<K, L, RIGHT, S, O32, 0, E>(c, w, target);
+#pragma unroll
+        for (int v = 0; v < E; ++v) best[v] = kmin<S>(c[v], best[v]);
+        bitonic_clean<E, L, S>(best, lane);
+        return;
+    }
     static_for<0, E / CH>([&](auto ic) {
         constexpr int u0 = decltype(ic)::value * CH;
         uint64_t c[CH];
@@ -524,10 +618,22 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
             // nothing to do when no candidate beats its query's current K-th anywhere in the
             // wavefront (once the prefix is long the recent keys rarely do)
             const uint64_t kth = from_last_lane<L>(best[E - 1]);
-            bool beats = false;
+            int below = 0;
 #pragma unroll
-            for (int t = 0; t < E; ++t) beats |= cand[t] < kth;
-            if (__ballot(beats) == 0) continue;  // uniform over the active lanes
+            for (int t = 0; t < E; ++t) below += cand[t] < kth ? 1 : 0;
+            const uint64_t any = __ballot(below > 0);
+            if (any == 0) continue;  // uniform over the active lanes
+            // when no query has two candidates below its K-th, the one that can enter is the
+            // query's smallest: insert it instead of sorting the group (also uniform)
+            if (__ballot(below > 1) == 0 && one_per_group<L>(any)) {
+                uint64_t mn[1] = {cand[0]};
+#pragma unroll
+                for (int t = 1; t < E; ++t) mn[0] = kmin<S>(mn[0], cand[t]);
+                if constexpr (L >= 2) mn[0] = kmin<S>(mn[0], quad_xor<1>(mn[0]));
+                if constexpr (L == 4) mn[0] = kmin<S>(mn[0], quad_xor<2>(mn[0]));
+                insert_few<E, L, 1, S>(best, mn, lane);
+                continue;
+            }
             sort_blocks<E, L, 2, true, S>(cand, lane);
 #pragma unroll
             for (int t = 0; t < E; ++t) best[t] = kmin<S>(cand[t], best[t]);
