@@ -375,7 +375,26 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     constexpr int E = K / L;
     constexpr int CH = kChunk < E ? kChunk : E;
     const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
-    if constexpr (CH == E && kInsert > 0 && kInsert < E) {
+    if constexpr (L == 4 && kInsert > 0 && kInsert < L) {
+        // lane r of the query loads candidate r first (run position p + r, or p - 1 - r on
+        // the left); the whole walk is loaded only when candidate kInsert may enter
+        using IX = typename TreeIx<O32>::T;
+        const IX q = RIGHT ? p + lane : p - 1 - lane;
+        const bool in = RIGHT ? q < s : q >= 0;
+        const uint64_t e = TreeIx<O32>::load(tree, roff + (in ? q : w.p0));
+        const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
+        const uint64_t key = in ? (RIGHT ? e - target : top - e) : kNone<S>;
+        const uint64_t kth = from_last_lane<L>(best[E - 1]);
+        if (__ballot(lane == kInsert && key < kth) == 0) {
+            uint64_t g[kInsert];
+            static_for<0, kInsert>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                g[r] = from_lane64<L, r>(key);
+            });
+            insert_few<E, L, kInsert, S>(best, g, lane);
+            return;
+        }
+    } else if constexpr (CH == E && kInsert > 0 && kInsert < E) {
         uint64_t c[E];
         walk_load<K, L, RIGHT, S, O32, 0, E>(c, tree, roff, w);
         // candidate r (r < E) is entry E-1-r of the query's last lane
