@@ -298,6 +298,34 @@ __device__ __forceinline__ bool one_per_group(uint64_t m) {
     }
 }
 
+// Merge E*L unsorted candidates (lane-major, empty = kNone) into the running top-K.  Nothing
+// is done when no candidate beats its query's K-th anywhere in the wavefront (once the prefix
+// is long the recent keys rarely do); when no query has two that do, the one that can enter
+// is the query's smallest and is inserted; otherwise the candidates are bitonic-sorted
+// (descending) and merged.  Each choice is uniform over the active lanes.
+template <int E, int L, int S>
+__device__ __forceinline__ void merge_unsorted(uint64_t (&best)[E], uint64_t (&cand)[E], int lane) {
+    const uint64_t kth = from_last_lane<L>(best[E - 1]);
+    int below = 0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) below += cand[t] < kth ? 1 : 0;
+    const uint64_t any = __ballot(below > 0);
+    if (any == 0) return;
+    if (__ballot(below > 1) == 0 && one_per_group<L>(any)) {
+        uint64_t mn[1] = {cand[0]};
+#pragma unroll
+        for (int t = 1; t < E; ++t) mn[0] = kmin<S>(mn[0], cand[t]);
+        if constexpr (L >= 2) mn[0] = kmin<S>(mn[0], quad_xor<1>(mn[0]));
+        if constexpr (L == 4) mn[0] = kmin<S>(mn[0], quad_xor<2>(mn[0]));
+        insert_few<E, L, 1, S>(best, mn, lane);
+        return;
+    }
+    sort_blocks<E, L, 2, true, S>(cand, lane);
+#pragma unroll
+    for (int t = 0; t < E; ++t) best[t] = kmin<S>(cand[t], best[t]);
+    bitonic_clean<E, L, S>(best, lane);
+}
+
 // Entries of one (b,h)'s tree levels are addressed from the slice base.  When the slice holds
 // fewer than 2^28 entries per tree (O32) offsets are 32-bit and a load is a uniform base plus
 // a 32-bit byte offset; otherwise 64-bit indices.
@@ -601,9 +629,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         fresh = false;
     }
 
-    // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K;
-    // each group is bitonic-sorted (descending) across the query's lanes and merged, unless
-    // none of the wavefront's candidates would enter a list
+    // the short runs: positions [m - (m mod 2K), m), at most 2K - 1 keys in two groups of K,
+    // each merged as unsorted candidates
     {
         const uint64_t z = static_cast<uint64_t>(zq[row]);
         const int64_t sbase = static_cast<int64_t>(m & ~(kShort - 1));
@@ -634,29 +661,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                     cand[t] = (dz << S) | static_cast<uint64_t>(j);
                 }
             }
-            // nothing to do when no candidate beats its query's current K-th anywhere in the
-            // wavefront (once the prefix is long the recent keys rarely do)
-            const uint64_t kth = from_last_lane<L>(best[E - 1]);
-            int below = 0;
-#pragma unroll
-            for (int t = 0; t < E; ++t) below += cand[t] < kth ? 1 : 0;
-            const uint64_t any = __ballot(below > 0);
-            if (any == 0) continue;  // uniform over the active lanes
-            // when no query has two candidates below its K-th, the one that can enter is the
-            // query's smallest: insert it instead of sorting the group (also uniform)
-            if (__ballot(below > 1) == 0 && one_per_group<L>(any)) {
-                uint64_t mn[1] = {cand[0]};
-#pragma unroll
-                for (int t = 1; t < E; ++t) mn[0] = kmin<S>(mn[0], cand[t]);
-                if constexpr (L >= 2) mn[0] = kmin<S>(mn[0], quad_xor<1>(mn[0]));
-                if constexpr (L == 4) mn[0] = kmin<S>(mn[0], quad_xor<2>(mn[0]));
-                insert_few<E, L, 1, S>(best, mn, lane);
-                continue;
-            }
-            sort_blocks<E, L, 2, true, S>(cand, lane);
-#pragma unroll
-            for (int t = 0; t < E; ++t) best[t] = kmin<S>(cand[t], best[t]);
-            bitonic_clean<E, L, S>(best, lane);
+            merge_unsorted<E, L, S>(best, cand, lane);
         }
     }
 
@@ -735,7 +740,9 @@ int select_first_level(int topk) {
 // window of min(k, n) sorted entries from p - floor(k/2) shifted inside the chunk, keys
 // j > i dropped.  A window is in (code, j) order, which is not (|dz|, j) order inside a
 // group of equal codes below zq, so its candidates are bitonic-sorted (descending) across
-// the query's lanes and then merged into the running top-K like a walk.
+// the query's lanes and then merged into the running top-K like a walk (the windows of
+// most chunks admit keys, so the skip and insertion checks of the exact search only cost
+// here).
 
 template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
