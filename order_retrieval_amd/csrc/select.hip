@@ -338,12 +338,53 @@ struct TreeIx<true> {
         return *reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(base) +
                                                   static_cast<uint32_t>(i) * 8u);
     }
+    // the high word of entry i (little-endian: bytes 8 i + 4 .. 8 i + 7)
+    __device__ __forceinline__ static uint32_t load_hi(const uint64_t* base, int32_t i) {
+        return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) +
+                                                  (static_cast<uint32_t>(i) * 8u + 4u));
+    }
 };
 template <>
 struct TreeIx<false> {
     using T = int64_t;
     __device__ __forceinline__ static uint64_t load(const uint64_t* base, int64_t i) {
         return base[i];
+    }
+    __device__ __forceinline__ static uint32_t load_hi(const uint64_t* base, int64_t i) {
+        return reinterpret_cast<const uint32_t*>(base + i)[1];
+    }
+};
+
+// What a lower_bound probe reads of a tree entry.  With 30-bit codes (S = 32) the code is the
+// entry's high word, and comparing it with the query's code decides the step exactly as the
+// full entry against target = zq << 32 does (a 32-bit load and compare); with 36-bit codes
+// the code spans both words and the probe reads the entry.  gap() is target minus the packed
+// code of entry p - 1 with its position bits cleared: a lower bound of the left walk's first
+// key.
+template <int S>
+struct Probe {
+    using T = uint64_t;
+    __device__ __forceinline__ static T target(uint64_t t) { return t; }
+    template <bool O32>
+    __device__ __forceinline__ static T load(const uint64_t* base, typename TreeIx<O32>::T i) {
+        return TreeIx<O32>::load(base, i);
+    }
+    __device__ __forceinline__ static T of(uint64_t e) { return e; }
+    __device__ __forceinline__ static uint64_t gap(uint64_t t, T below) {
+        return t - (below & ~((uint64_t(1) << S) - 1));
+    }
+};
+template <>
+struct Probe<32> {
+    using T = uint32_t;
+    __device__ __forceinline__ static T target(uint64_t t) { return static_cast<uint32_t>(t >> 32); }
+    template <bool O32>
+    __device__ __forceinline__ static T load(const uint64_t* base, typename TreeIx<O32>::T i) {
+        return TreeIx<O32>::load_hi(base, i);
+    }
+    __device__ __forceinline__ static T of(uint64_t e) { return static_cast<uint32_t>(e >> 32); }
+    __device__ __forceinline__ static uint64_t gap(uint64_t t, T below) {
+        return t - (static_cast<uint64_t>(below) << 32);
     }
 };
 
@@ -566,21 +607,25 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
         // entry p - 1 and the final probe, when it does not move, is entry p.  They give the
         // right walk's first key exactly and a lower bound of the left walk's first key
         // (same code as entry p - 1), so a walk is skipped without loading anything.
-        uint64_t below[kPer], rfirst[kPer], lbound[kPer];
+        // With 30-bit codes a probe compares codes only, so it reads the entry's high word.
+        using PV = typename Probe<S>::T;
+        const PV ptarget = Probe<S>::target(target);
+        PV below[kPer];
+        uint64_t rfirst[kPer], lbound[kPer];
 #pragma unroll
         for (int t = 0; t < kPer; ++t) below[t] = 0;
         for (IX step = (IX(1) << lv[0]) >> 1; step > 0; step >>= 1) {
-            uint64_t e[kPer];
+            PV e[kPer];
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
                 const IX at = pos[t] + step - 1;
-                e[t] = TreeIx<O32>::load(hA, mro[t] + (at < mlen[t] ? at : mlen[t] - 1));
+                e[t] = Probe<S>::template load<O32>(hA, mro[t] + (at < mlen[t] ? at : mlen[t] - 1));
             }
 #pragma unroll
             for (int t = 0; t < kPer; ++t) keep(e[t]);
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
-                if (pos[t] + step < mlen[t] && e[t] < target) {
+                if (pos[t] + step < mlen[t] && e[t] < ptarget) {
                     pos[t] += step;
                     below[t] = e[t];
                 }
@@ -598,10 +643,10 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 const bool mv = mon[t] && e[t] < target;
                 if (mv) {
                     pos[t] += 1;
-                    below[t] = e[t];
+                    below[t] = Probe<S>::of(e[t]);
                 }
                 rfirst[t] = mv || !mon[t] ? kNone<S> : e[t] - target;
-                lbound[t] = pos[t] == 0 ? kNone<S> : target - (below[t] & ~kJMask);
+                lbound[t] = pos[t] == 0 ? kNone<S> : Probe<S>::gap(target, below[t]);
             }
         }
         static_for<0, kRuns>([&](auto gc) {
