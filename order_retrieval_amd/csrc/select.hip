@@ -463,6 +463,18 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
             insert_few<E, L, kInsert, S>(best, g, lane);
             return;
         }
+        // one more candidate from the same loads when candidate L - 1 cannot enter
+        if constexpr (kInsert + 1 < L) {
+            if (__ballot(lane == L - 1 && key < kth) == 0) {
+                uint64_t g[L - 1];
+                static_for<0, L - 1>([&](auto rc) {
+                    constexpr int r = decltype(rc)::value;
+                    g[r] = from_lane64<L, r>(key);
+                });
+                insert_few<E, L, L - 1, S>(best, g, lane);
+                return;
+            }
+        }
     } else if constexpr (CH == E && kInsert > 0 && kInsert < E) {
         uint64_t c[E];
         walk_load<K, L, RIGHT, S, O32, 0, E>(c, tree, roff, w);
