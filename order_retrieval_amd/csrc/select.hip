@@ -434,9 +434,10 @@ __device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, 
 
 // Merge one walk into the running top-K, its candidates loaded kChunk at a time (register
 // budget for K = 64); the caller has checked that its first candidate may enter the list.
-// Deep in the prefix a walk admits a key or two at most: when candidate kInsert cannot beat
+// Deep in the prefix a walk admits a few keys at most: when candidate kInsert cannot beat
 // its query's K-th for any query of the wavefront, the first kInsert candidates are merged
-// by insertion and the bitonic merge is skipped (the choice is uniform over the wavefront).
+// by insertion and the bitonic merge is skipped; with four lanes per query, failing that,
+// the first three when candidate 3 cannot enter (each choice uniform over the wavefront).
 template <int K, int L, bool RIGHT, int S, bool O32>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
                                            typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
