@@ -438,42 +438,47 @@ __device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, 
 // its query's K-th for any query of the wavefront, the first kInsert candidates are merged
 // by insertion and the bitonic merge is skipped; with four lanes per query, failing that,
 // the first three when candidate 3 cannot enter (each choice uniform over the wavefront).
+// `few` = false skips those checks for walks that nearly always admit more (the walks of a
+// query's two largest runs).
 template <int K, int L, bool RIGHT, int S, bool O32>
 __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64_t* __restrict__ tree,
                                            typename TreeIx<O32>::T roff, typename TreeIx<O32>::T p,
-                                           typename TreeIx<O32>::T s, uint64_t target, int lane) {
+                                           typename TreeIx<O32>::T s, uint64_t target, int lane,
+                                           bool few = true) {
     constexpr int E = K / L;
     constexpr int CH = kChunk < E ? kChunk : E;
     const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
     if constexpr (L == 4 && kInsert > 0 && kInsert < L) {
-        // lane r of the query loads candidate r first (run position p + r, or p - 1 - r on
-        // the left); the whole walk is loaded only when candidate kInsert may enter
-        using IX = typename TreeIx<O32>::T;
-        const IX q = RIGHT ? p + lane : p - 1 - lane;
-        const bool in = RIGHT ? q < s : q >= 0;
-        const uint64_t e = TreeIx<O32>::load(tree, roff + (in ? q : w.p0));
-        const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
-        const uint64_t key = in ? (RIGHT ? e - target : top - e) : kNone<S>;
-        const uint64_t kth = from_last_lane<L>(best[E - 1]);
-        if (__ballot(lane == kInsert && key < kth) == 0) {
-            uint64_t g[kInsert];
-            static_for<0, kInsert>([&](auto rc) {
-                constexpr int r = decltype(rc)::value;
-                g[r] = from_lane64<L, r>(key);
-            });
-            insert_few<E, L, kInsert, S>(best, g, lane);
-            return;
-        }
-        // one more candidate from the same loads when candidate L - 1 cannot enter
-        if constexpr (kInsert + 1 < L) {
-            if (__ballot(lane == L - 1 && key < kth) == 0) {
-                uint64_t g[L - 1];
-                static_for<0, L - 1>([&](auto rc) {
+        if (few) {
+            // lane r of the query loads candidate r first (run position p + r, or p - 1 - r on
+            // the left); the whole walk is loaded only when candidate kInsert may enter
+            using IX = typename TreeIx<O32>::T;
+            const IX q = RIGHT ? p + lane : p - 1 - lane;
+            const bool in = RIGHT ? q < s : q >= 0;
+            const uint64_t e = TreeIx<O32>::load(tree, roff + (in ? q : w.p0));
+            const uint64_t top = target | ((S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1));
+            const uint64_t key = in ? (RIGHT ? e - target : top - e) : kNone<S>;
+            const uint64_t kth = from_last_lane<L>(best[E - 1]);
+            if (__ballot(lane == kInsert && key < kth) == 0) {
+                uint64_t g[kInsert];
+                static_for<0, kInsert>([&](auto rc) {
                     constexpr int r = decltype(rc)::value;
                     g[r] = from_lane64<L, r>(key);
                 });
-                insert_few<E, L, L - 1, S>(best, g, lane);
+                insert_few<E, L, kInsert, S>(best, g, lane);
                 return;
+            }
+            // one more candidate from the same loads when candidate L - 1 cannot enter
+            if constexpr (kInsert + 1 < L) {
+                if (__ballot(lane == L - 1 && key < kth) == 0) {
+                    uint64_t g[L - 1];
+                    static_for<0, L - 1>([&](auto rc) {
+                        constexpr int r = decltype(rc)::value;
+                        g[r] = from_lane64<L, r>(key);
+                    });
+                    insert_few<E, L, L - 1, S>(best, g, lane);
+                    return;
+                }
             }
         }
     } else if constexpr (CH == E && kInsert > 0 && kInsert < E) {
@@ -678,10 +683,12 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                     for (int t = 0; t < E; ++t) keep(c[t]);
                     fill_keys<K, L, S, O32>(best, c, pg, s, target, lane);
                 } else if (rf < from_last_lane<L>(best[E - 1])) {
-                    merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane);
+                    merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane,
+                                                   !(fresh && gi < 2));
                 }
                 if (lb < from_last_lane<L>(best[E - 1]))
-                    merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane);
+                    merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane,
+                                                    !(fresh && gi < 2));
             }
         });
         fresh = false;
