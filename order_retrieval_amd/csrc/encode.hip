@@ -47,10 +47,16 @@ __device__ __forceinline__ uint32_t morton3p(float x0, float x1, float x2, int p
 // perm packs the curve's coordinate order (several-curve variant, rebuttal page on the
 // asymmetry of interleaving: the coordinates are fed to the curve in a permuted order);
 // kPermIdentity = axis a reads coordinate a.
-__global__ void __launch_bounds__(256) zeta_morton_encode_kernel(const float* __restrict__ x,
+// blockIdx.y selects the point set: (x, z), or (x1, z1) for the second of two encoded in
+// one launch (queries and keys).
+__global__ void __launch_bounds__(256) zeta_morton_encode_kernel(const float* __restrict__ x0,
                                                                   int64_t rows,
-                                                                  uint32_t* __restrict__ z,
-                                                                  int vec_ok, int perm) {
+                                                                  uint32_t* __restrict__ z0,
+                                                                  int vec_ok, int perm,
+                                                                  const float* __restrict__ x1,
+                                                                  uint32_t* __restrict__ z1) {
+    const float* __restrict__ x = blockIdx.y ? x1 : x0;
+    uint32_t* __restrict__ z = blockIdx.y ? z1 : z0;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t r0 = t * 4;
     if (r0 >= rows) return;
@@ -69,16 +75,27 @@ __global__ void __launch_bounds__(256) zeta_morton_encode_kernel(const float* __
     }
 }
 
-hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z,
-                              hipStream_t s) {
+static hipError_t encode_sets(const float* x0, uint32_t* z0, const float* x1, uint32_t* z1,
+                              int64_t rows, int perm, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    const int vec_ok = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
-                        (reinterpret_cast<uintptr_t>(z) & 15u) == 0);
+    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const int vec_ok = a16(x0) && a16(z0) && (!x1 || (a16(x1) && a16(z1)));
     const int64_t threads = (rows + 3) / 4;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL(zeta_morton_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                       0, s, x, rows, z, vec_ok, perm);
+    hipLaunchKernelGGL(zeta_morton_encode_kernel,
+                       dim3(static_cast<unsigned>(blocks), x1 ? 2u : 1u), dim3(256), 0, s, x0,
+                       rows, z0, vec_ok, perm, x1, z1);
     return hipGetLastError();
+}
+
+hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z,
+                              hipStream_t s) {
+    return encode_sets(x, z, nullptr, nullptr, rows, perm, s);
+}
+
+hipError_t launch_encode2_perm(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
+                               int64_t rows, int perm, hipStream_t s) {
+    return encode_sets(q, zq, k, zk, rows, perm, s);
 }
 
 // 12-bit cells (rebuttal page, answer W2/A2: a grid of 4096 cells per coordinate, three

@@ -255,8 +255,7 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             e = zeta::launch_encode36_perm(q, BHN, perm, zq64, s);
             if (e == hipSuccess) e = zeta::launch_encode36_perm(k, BHN, perm, zk64, s);
         } else {
-            e = zeta::launch_encode_perm(q, BHN, perm, zq, s);
-            if (e == hipSuccess) e = zeta::launch_encode_perm(k, BHN, perm, zk, s);
+            e = zeta::launch_encode2_perm(q, zq, k, zk, BHN, perm, s);
         }
         if (e != hipSuccess) return fail_hip("encode launch", e);
         // the query processing order of the select (and later of the gather)

@@ -79,6 +79,9 @@ hipError_t launch_encode(const float* x, int64_t rows, uint32_t* z, hipStream_t 
 constexpr int perm_code(int c0, int c1, int c2) { return c0 | (c1 << 2) | (c2 << 4); }
 constexpr int kPermIdentity = perm_code(0, 1, 2);
 hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* z, hipStream_t s);
+// Both point sets (queries and keys, rows points each) in one launch.
+hipError_t launch_encode2_perm(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
+                               int64_t rows, int perm, hipStream_t s);
 // Levels 0 .. first-1 are not written.
 hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, int first, const uint32_t* zk,
                              uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
