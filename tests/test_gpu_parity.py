@@ -317,6 +317,64 @@ def _bwd_sampled_check(w, n_rows=600, tail=256):
     assert np.abs(colsum - colsum_ref).max() <= tol, np.abs(colsum - colsum_ref).max()
 
 
+def _bwd_hub_check(w, heads, n_hub=30, n_rand=100):
+    """Element-wise dk / dv of the most-selected keys (and of random keys) at full size.
+
+    Per checked (b,h): the n_hub keys that the GPU selection names most often, plus n_rand
+    random keys.  Every query row whose GPU index row names one of them is compared bit for
+    bit with the oracle's selection, and the oracle's backward over exactly those rows gives
+    those keys' complete gradients, compared element by element.  These are the long
+    segments of the per-key reduction (hundreds of pairs, ties broken toward small j on
+    clustered inputs), where bf16 dv rounding is tightest."""
+    x = inputs.make_inputs(w)
+    d = device_inputs(w, x)
+    bf = w.v_dtype == inputs.BF16
+    out, idx = Z.zeta_fwd(d["q"], d["k"], d["v"], d["gamma"], w.topk)
+    _, dk, dv, _ = Z.zeta_bwd(d["q"], d["k"], d["v"], d["gamma"], idx, d["dout"])
+    torch.cuda.synchronize()
+    BH, N, K = w.B * w.H, w.N, w.topk
+    idx = to_np(idx).reshape(BH, N, K)
+    dk = to_np(dk).reshape(BH, N, 3)
+    dv = to_np(dv).reshape(BH, N, w.dv)
+    rng = np.random.default_rng(17)
+    rows, keys = [], []
+    for bh in heads:
+        sel = idx[bh]
+        cnt = np.bincount(sel[sel >= 0], minlength=N)
+        hub = np.argsort(-cnt, kind="stable")[:n_hub]
+        rnd = rng.choice(N, size=n_rand, replace=False)
+        ks = np.union1d(hub, rnd)
+        qs = np.nonzero(np.isin(sel, ks).any(axis=1))[0]
+        log(f"  (b,h) {bh}: {ks.size} keys, pairs per hub key {cnt[hub].min()}..{cnt[hub].max()}, "
+            f"{qs.size} query rows select them")
+        rows.append(bh * N + qs)
+        keys.append((bh, ks))
+    rows = np.concatenate(rows).astype(np.int64)
+    ridx = oracle.select(x["q"], x["k"], K, rows=rows)
+    np.testing.assert_array_equal(idx.reshape(-1, K)[rows], ridx)
+    _, rk, rv, _ = oracle.backward(x["q"], x["k"], x["v"], x["gamma"], x["dout"], ridx, bf,
+                                   rows=rows)
+    rk, rv = rk.reshape(BH, N, 3), rv.reshape(BH, N, w.dv)
+    gk = np.concatenate([dk[bh, ks] for bh, ks in keys])
+    gv = np.concatenate([dv[bh, ks] for bh, ks in keys])
+    ek = np.concatenate([rk[bh, ks] for bh, ks in keys])
+    ev = np.concatenate([rv[bh, ks] for bh, ks in keys])
+    assert_close(gk, ek, w.v_dtype, f"dk {w.name} hub and random keys")
+    assert_close(gv, ev, w.v_dtype, f"dv {w.name} hub and random keys", bf16_output=bf)
+    if bf:
+        err = np.abs(gv.astype(np.float64) - ev)
+        used = int(((err > 2e-2) & (np.abs(ev) >= 8.0)).sum())
+        log(f"  dv values inside one bf16 ulp but beyond 2e-2: {used} of {ev.size}")
+
+
+@pytest.mark.parametrize("name,heads", [("clustered", (0, 5, 9, 14, 18, 23, 27, 31)),
+                                        ("long_fwd_bwd", tuple(range(8)))])
+def test_backward_hub_keys(name, heads):
+    w = CFG[name]
+    log(f"backward hub keys {name}")
+    _bwd_hub_check(inputs.Workload(**{**w.__dict__, "backward": True}), heads)
+
+
 def test_backward_beyond_two_byte_keys():
     # N > 65536: the selection transpose takes the all-bytes radix path
     w = W("lsd", 1, 1, 70000, 8, 8, inputs.BF16, "normal", seed=17, backward=True)
