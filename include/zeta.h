@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define ZETA_MAX_TOPK 64
+#define ZETA_MAX_TOPK 256
 #define ZETA_MAX_DV 512
 
 typedef enum zeta_status {

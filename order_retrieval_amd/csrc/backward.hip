@@ -281,6 +281,165 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     }
 }
 
+// The per-query pass for selections wider than 64 slots: the slots are taken in batches of
+// 64 (four per lane) in two passes over the row's selection.  The first pass forms s_ij and
+// g_ij batch by batch (as above), keeps their running sums S_i and sum_j s_ij g_ij, and parks
+// {s_ij, g_ij} in the slot's coefficient entry; the second pass, with D_i known, reads them
+// back (the lane that wrote an entry reads it), forms a_ij and c_ij, overwrites the entry with
+// {a_ij, c_ij} and adds the dq and dgamma terms.
+constexpr int kWideU = 4;
+constexpr int kWideBatch = kWideU * kRowLanes;
+
+template <bool BF16, bool O32, int CPL>
+__global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_wide_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ gamma, const int32_t* __restrict__ idx,
+    const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t N, int64_t H,
+    int dv, int topk, int causal, int64_t tph, int64_t tiles, int64_t per_xcd,
+    float2* __restrict__ coef, float* __restrict__ dq, float* __restrict__ dg_row) {
+    using IO = VecIO<BF16>;
+    using T = typename IO::elem_t;
+    constexpr int E = IO::kElems;
+    constexpr int U = kWideU;
+    const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
+    if (tile >= tiles) return;  // uniform over the workgroup
+    const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
+    const int lrow = threadIdx.x & (kRowLanes - 1);
+    const int64_t pos = (tile - bh * tph) * kQueryRows + threadIdx.x / kRowLanes;
+    const bool live = pos < N;
+    const int64_t pp = live ? pos : N - 1;  // a row past the end reads a real query, stores nothing
+    const int chunks = dv / E;
+    const int64_t i = order ? static_cast<int64_t>(order[bh * N + pp]) : pp;
+    const int64_t row = bh * N + i;
+    const float g = gamma[bh % H];
+    const float inv_g2 = 1.0f / (g * g);
+    const float q0 = q[3 * row], q1 = q[3 * row + 1], q2 = q[3 * row + 2];
+    const int64_t nk = causal ? i + 1 : N;  // keys the query may use
+    const int m = live ? static_cast<int>(nk < topk ? nk : topk) : 0;
+    const int32_t* ir = idx + row * topk;
+    const float* kh = k + bh * N * 3;
+    const T* vh = static_cast<const T*>(v) + bh * N * dv;
+    float2* cr = coef + row * topk;
+
+    float go[CPL][E];
+    int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet go = 0)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lrow + c * kRowLanes;
+        coff[c] = (ch < chunks ? ch : chunks - 1) * E;
+        IO::unpack(IO::load_raw(static_cast<const T*>(dout) + row * dv + coff[c]), go[c]);
+        if (ch >= chunks)
+#pragma unroll
+            for (int e = 0; e < E; ++e) go[c][e] = 0.0f;
+    }
+    int most = m;
+    most = max(most, __shfl_xor(most, 16, 64));
+    most = max(most, __shfl_xor(most, 32, 64));
+    const int batches = (most + kWideBatch - 1) / kWideBatch;
+
+    // slot u of the lane in batch sb: selected?, its key (clamped) and point
+    auto slot_setup = [&](int sb, int32_t (&jr)[U], bool (&sel)[U], Point3 (&kp)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = sb + query_slot_of_lane(lrow) + u * kRowLanes;
+            jr[u] = ir[r < topk ? r : topk - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) keep(jr[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            sel[u] = sb + query_slot_of_lane(lrow) + u * kRowLanes < m && jr[u] >= 0;
+            jr[u] = sel[u] ? static_cast<int32_t>(clamp_index(jr[u], nk - 1)) : 0;
+            kp[u] = load_point(kh, jr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) keep(kp[u]);
+    };
+
+    // pass 1: s, g, their sums; {s, g} parked in the slot's entry
+    float ssum = 0.0f, nsel = 0.0f, tsum = 0.0f;
+    for (int bt = 0; bt < batches; ++bt) {
+        const int sb = bt * kWideBatch;
+        int32_t jr[U];
+        bool sel[U];
+        Point3 kp[U];
+        slot_setup(sb, jr, sel, kp);
+        uint32_t jo[U];
+        float so[U], gg[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            jo[u] = 0;  // not selected: names key 0's row, never summed
+            so[u] = gg[u] = 0.0f;
+            if (sel[u]) {
+                jo[u] = RowRef<BF16, O32>::name(jr[u], dv);
+                const float dx = q0 - kp[u].x, dy = q1 - kp[u].y, dz = q2 - kp[u].z;
+                so[u] = 1.0f / (1.0f + (dx * dx + dy * dy + dz * dz) * inv_g2);
+            }
+        }
+        const int left = most - sb;
+        static_for<0, U>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            if (u * kRowLanes < left) {
+                static_for<0, kRowLanes / kRowLoads>([&](auto bc) {
+                    constexpr int b = decltype(bc)::value;
+                    if (u * kRowLanes + b * kRowLoads < left)
+                        query_slots<BF16, O32, CPL, b * kRowLoads>(vh, dv, coff, jo[u], go, lrow,
+                                                                   gg[u]);
+                });
+            }
+        });
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sel[u]) {
+                ssum += so[u];
+                nsel += 1.0f;
+                tsum += so[u] * gg[u];
+                if (live) cr[sb + query_slot_of_lane(lrow) + u * kRowLanes] = make_float2(so[u], gg[u]);
+            }
+        }
+    }
+    const float S = group_sum(ssum, kRowLanes);
+    nsel = group_sum(nsel, kRowLanes);
+    const float inv_S = nsel > 0.0f ? 1.0f / S : 0.0f;  // an empty selection passes no gradient
+    const float D = group_sum(tsum, kRowLanes) * inv_S;
+
+    // pass 2: a, c from the parked {s, g}; the dq and dgamma terms
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
+    for (int bt = 0; bt < batches; ++bt) {
+        const int sb = bt * kWideBatch;
+        int32_t jr[U];
+        bool sel[U];
+        Point3 kp[U];
+        slot_setup(sb, jr, sel, kp);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sel[u] && live) {
+                const int r = sb + query_slot_of_lane(lrow) + u * kRowLanes;
+                const float2 sg = cr[r];
+                const float dx = q0 - kp[u].x, dy = q1 - kp[u].y, dz = q2 - kp[u].z;
+                const float a = sg.x * inv_S;
+                const float c = a * sg.x * (sg.y - D);
+                cr[r] = make_float2(a, c);
+                a0 += c * dx;
+                a1 += c * dy;
+                a2 += c * dz;
+                ag += c * (dx * dx + dy * dy + dz * dz);
+            }
+        }
+    }
+    a0 = group_sum(a0, kRowLanes);
+    a1 = group_sum(a1, kRowLanes);
+    a2 = group_sum(a2, kRowLanes);
+    ag = group_sum(ag, kRowLanes);
+    if (live && lrow == 0) {
+        const float f = -2.0f * inv_g2;
+        dq[3 * row] = f * a0;
+        dq[3 * row + 1] = f * a1;
+        dq[3 * row + 2] = f * a2;
+        dg_row[row] = 2.0f * inv_g2 / g * ag;
+    }
+}
+
 template <bool BF16, bool O32, int CPL>
 static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int topk,
                                  int causal, const float* q, const float* k, const void* v,
@@ -290,10 +449,11 @@ static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int t
     const int64_t tph = (N + kQueryRows - 1) / kQueryRows;
     const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
-    const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane (<= 4)
+    const int u = (topk + kRowLanes - 1) / kRowLanes;  // slots per lane
     auto kern = u <= 1 ? zeta_bwd_query_kernel<BF16, O32, CPL, 1>
               : u <= 2 ? zeta_bwd_query_kernel<BF16, O32, CPL, 2>
-                       : zeta_bwd_query_kernel<BF16, O32, CPL, 4>;
+              : u <= 4 ? zeta_bwd_query_kernel<BF16, O32, CPL, 4>
+                       : zeta_bwd_query_wide_kernel<BF16, O32, CPL>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kQueryThreads), 0, s,
                        q, k, v,
                        gamma, idx, dout, order, N, H, dv, topk, causal, tph, tiles, per, coef, dq,

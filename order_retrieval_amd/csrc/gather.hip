@@ -68,7 +68,7 @@ __device__ __forceinline__ void gather_slots(const typename VecIO<BF16>::elem_t*
     });
 }
 
-template <bool BF16, bool O32, int CPL, int U>
+template <bool BF16, bool O32, int CPL, int U, bool MULTI>
 __global__ void __launch_bounds__(kGatherThreads) zeta_cauchy_gather_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
@@ -78,6 +78,7 @@ __global__ void __launch_bounds__(kGatherThreads) zeta_cauchy_gather_kernel(
     using Ref = RowRef<BF16, O32>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
+    constexpr int kBatch = U * kGatherLanes;  // slots per batch
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;  // uniform over the workgroup
     const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
@@ -98,45 +99,6 @@ __global__ void __launch_bounds__(kGatherThreads) zeta_cauchy_gather_kernel(
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
-
-    // the index and key-row loads read clamped positions and are held live before any test,
-    // so the loads of a kind are in flight together
-    int32_t jr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int r = lrow + u * kGatherLanes;
-        jr[u] = ir[r < topk ? r : topk - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) keep(jr[u]);
-    bool sel[U];
-    Point3 kp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        sel[u] = lrow + u * kGatherLanes < m && jr[u] >= 0;
-        // a selection has j <= jmax; clamping keeps every access in bounds
-        jr[u] = sel[u] ? (jr[u] > jmax ? static_cast<int32_t>(jmax) : jr[u]) : 0;
-        kp[u] = load_point(kh, jr[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) keep(kp[u]);
-    uint32_t jo[U];
-    float so[U];
-    float ssum = 0.0f, nsel = 0.0f;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        jo[u] = 0;
-        so[u] = -1.0f;
-        if (sel[u]) {
-            const float d0 = q0 - kp[u].x, d1 = q1 - kp[u].y, d2 = q2 - kp[u].z;
-            jo[u] = Ref::name(jr[u], dv);
-            so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
-            ssum += so[u];
-            nsel += 1.0f;
-        }
-    }
-    ssum = group_sum(ssum, kGatherLanes);
-    nsel = group_sum(nsel, kGatherLanes);
     // the longest selection among the wavefront's four queries sets the trip count
     int most = m;
     most = max(most, __shfl_xor(most, 16, 64));
@@ -151,16 +113,62 @@ __global__ void __launch_bounds__(kGatherThreads) zeta_cauchy_gather_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[c][e] = 0.0f;
     }
-    static_for<0, U>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if (u * kGatherLanes < most) {
-            static_for<0, kGatherLanes / kGatherLoads>([&](auto bc) {
-                constexpr int b = decltype(bc)::value;
-                if (u * kGatherLanes + b * kGatherLoads < most)
-                    gather_slots<BF16, O32, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u], acc);
-            });
+    float ssum = 0.0f, nsel = 0.0f;
+    // Slots are taken kBatch at a time (one batch unless k > 64): the weights are summed
+    // unnormalised and the output is scaled by 1 / S once at the end.
+    const int batches = MULTI ? (most + kBatch - 1) / kBatch : 1;
+    for (int bt = 0; bt < batches; ++bt) {
+        const int sb = bt * kBatch;  // first slot of the batch
+        // the index and key-row loads read clamped positions and are held live before any
+        // test, so the loads of a kind are in flight together
+        int32_t jr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = sb + lrow + u * kGatherLanes;
+            jr[u] = ir[r < topk ? r : topk - 1];
         }
-    });
+#pragma unroll
+        for (int u = 0; u < U; ++u) keep(jr[u]);
+        bool sel[U];
+        Point3 kp[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            sel[u] = sb + lrow + u * kGatherLanes < m && jr[u] >= 0;
+            // a selection has j <= jmax; clamping keeps every access in bounds
+            jr[u] = sel[u] ? (jr[u] > jmax ? static_cast<int32_t>(jmax) : jr[u]) : 0;
+            kp[u] = load_point(kh, jr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) keep(kp[u]);
+        uint32_t jo[U];
+        float so[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            jo[u] = 0;
+            so[u] = -1.0f;
+            if (sel[u]) {
+                const float d0 = q0 - kp[u].x, d1 = q1 - kp[u].y, d2 = q2 - kp[u].z;
+                jo[u] = Ref::name(jr[u], dv);
+                so[u] = 1.0f / (1.0f + (d0 * d0 + d1 * d1 + d2 * d2) * inv_g2);
+                ssum += so[u];
+                nsel += 1.0f;
+            }
+        }
+        const int left = most - sb;  // slots of this batch any query of the wavefront uses
+        static_for<0, U>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            if (u * kGatherLanes < left) {
+                static_for<0, kGatherLanes / kGatherLoads>([&](auto bc) {
+                    constexpr int b = decltype(bc)::value;
+                    if (u * kGatherLanes + b * kGatherLoads < left)
+                        gather_slots<BF16, O32, CPL, b * kGatherLoads>(vh, dv, coff, jo[u], so[u],
+                                                                       acc);
+                });
+            }
+        });
+    }
+    ssum = group_sum(ssum, kGatherLanes);
+    nsel = group_sum(nsel, kGatherLanes);
 
     if (live) {
         const float inv_S = nsel > 0.0f ? 1.0f / ssum : 0.0f;  // an empty selection outputs 0
@@ -186,10 +194,12 @@ static hipError_t launch_gather_c(int64_t BH, int64_t N, int64_t H, int dv, int 
     const int64_t tph = (N + kGatherRows - 1) / kGatherRows;
     const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
-    const int u = (topk + kGatherLanes - 1) / kGatherLanes;  // slots per lane (<= 4)
-    auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 1>
-              : u <= 2 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 2>
-                       : zeta_cauchy_gather_kernel<BF16, O32, CPL, 4>;
+    // slots per lane: 1, 2 or 4 in one batch; above 64 slots, batches of 4 per lane
+    const int u = (topk + kGatherLanes - 1) / kGatherLanes;
+    auto kern = u <= 1 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 1, false>
+              : u <= 2 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 2, false>
+              : u <= 4 ? zeta_cauchy_gather_kernel<BF16, O32, CPL, 4, false>
+                       : zeta_cauchy_gather_kernel<BF16, O32, CPL, 4, true>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kGatherThreads), 0, s, q, k, v,
                        gamma, idx, order, out, N, H, dv, topk, causal, tph, tiles, per);
     return hipGetLastError();

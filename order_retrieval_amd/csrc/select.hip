@@ -17,11 +17,13 @@
 //
 // The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
 // (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 64,
-// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below).  A
+// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below; a whole
+// 16-lane row for K = 128 and 256, 8 or 16 entries per lane).  A
 // walk's K candidates are merged with one bitonic step: elementwise min against the
 // reversed candidates (each lane loads its own contiguous block of the walk) leaves a
 // bitonic sequence of the K smallest, which log2(K) compare-exchange stages sort; the stages
-// whose stride spans lanes exchange values with DPP quad permutes.  A walk whose first
+// whose stride spans lanes exchange values with DPP quad permutes (lanes 4 or 8 apart: a
+// ds_swizzle, which moves data between lanes without touching LDS memory).  A walk whose first
 // candidate cannot beat the current K-th is skipped, decided from values the search already
 // holds.  The runs are taken in groups: with several lanes per query each lane
 // binary-searches its own run of the group (with one lane, kSearchGroup runs advance in
@@ -36,23 +38,55 @@ constexpr int kSearchGroup = 2;  // runs whose binary searches advance in lock-s
 constexpr int kChunk = 8;        // candidates of a walk loaded per step (register budget)
 constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (chunked search)
 constexpr int kInsert = 2;       // walk candidates merged by insertion when no more can enter
+constexpr int kInsert2 = 3;      // the second insertion tier (lane groups of 4 or more lanes)
 
-// Value of the lane `lane ^ D` of the same quad (D = 1 or 2).
+// One word of lane `lane ^ D` (D = 1, 2: a DPP quad permute that the compiler can fold into
+// the instruction consuming it; D = 4, 8: a ds_swizzle in bitmask mode, and-mask 31 with
+// xor-mask D, inside the 32-lane half of the wavefront).  Every lane of the query's group is
+// active where these are used, and its partner is in the same group.
 template <int D>
-__device__ __forceinline__ uint64_t quad_xor(uint64_t x) {
-    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF,
-                                            0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)), ctrl,
-                                            0xF, 0xF, false);
-    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+    if constexpr (D == 1 || D == 2) {
+        constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+        return static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(x), ctrl, 0xF, 0xF, true));
+    } else {
+        static_assert(D == 4 || D == 8, "partners within a 16-lane row");
+        return static_cast<uint32_t>(
+            __builtin_amdgcn_ds_swizzle(static_cast<int>(x), 0x1F | (D << 10)));
+    }
 }
 
-// Value of the last lane of this query's lane group (L = 1, 2 or 4 lanes in a quad).
+// Value of the lane `lane ^ D` of the same lane group, 64 bits.
+template <int D>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x) {
+    const uint32_t lo = lane_xor32<D>(static_cast<uint32_t>(x));
+    const uint32_t hi = lane_xor32<D>(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t pack64(uint32_t lo, uint32_t hi) {
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One word of lane SRC of this 16-lane row (DPP row_newbcast).
+template <int SRC>
+__device__ __forceinline__ uint32_t row_lane32(uint32_t x) {
+    static_assert(SRC >= 0 && SRC < 16, "a row has 16 lanes");
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x150 + SRC, 0xF, 0xF, true));
+}
+
+// Value of the last lane of this query's lane group (L = 1, 2 or 4 lanes in a quad, or a
+// 16-lane row).
 template <int L>
 __device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
+    static_assert(L == 1 || L == 2 || L == 4 || L == 16, "lane groups of 1, 2, 4 or 16");
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 16) {
+        return pack64(row_lane32<15>(static_cast<uint32_t>(x)),
+                      row_lane32<15>(static_cast<uint32_t>(x >> 32)));
     } else {
         constexpr int ctrl = L == 2 ? 0xF5 : 0xFF;  // quad_perm [1,1,3,3] / [3,3,3,3]
         const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl,
@@ -63,11 +97,15 @@ __device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
     }
 }
 
-// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad), 64 bits.
+// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad, or a 16-lane
+// row), 64 bits.
 template <int L, int SRC>
 __device__ __forceinline__ uint64_t from_lane64(uint64_t x) {
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 16) {
+        return pack64(row_lane32<SRC>(static_cast<uint32_t>(x)),
+                      row_lane32<SRC>(static_cast<uint32_t>(x >> 32)));
     } else {
         constexpr int ctrl = L == 4 ? SRC * 0x55 : (SRC * 0x5) | ((2 + SRC) * 0x50);
         const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl,
@@ -78,11 +116,14 @@ __device__ __forceinline__ uint64_t from_lane64(uint64_t x) {
     }
 }
 
-// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad); x < 2^32.
+// Value of lane SRC of this query's lane group (L = 1, 2 or 4 lanes in a quad, or a 16-lane
+// row); x < 2^32.
 template <int L, int SRC>
 __device__ __forceinline__ int64_t from_lane(int64_t x) {
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 16) {
+        return static_cast<int64_t>(row_lane32<SRC>(static_cast<uint32_t>(x)));
     } else {
         // quad_perm [SRC, SRC, SRC, SRC] for a quad; [SRC, SRC, 2+SRC, 2+SRC] for lane pairs
         constexpr int ctrl = L == 4 ? SRC * 0x55 : (SRC * 0x5) | ((2 + SRC) * 0x50);
@@ -123,18 +164,6 @@ __device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) {
     }
 }
 
-// One word of lane `lane ^ D` of the same quad, by a DPP quad permute that the compiler can
-// fold into the instruction consuming it (every lane of the quad is active where it is used).
-template <int D>
-__device__ __forceinline__ uint32_t quad_take(uint32_t x) {
-    constexpr int ctrl = D == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), ctrl, 0xF, 0xF, true));
-}
-__device__ __forceinline__ uint64_t pack64(uint32_t lo, uint32_t hi) {
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 // Cross-lane compare-exchange stage with partner lane ^ D: the lower lane keeps minima.
 // 30-bit-code keys: a lane that keeps maxima negates both operands (flips the sign bit of the
 // high word; the partner's arrives flipped from the DPP instruction that fetches it), takes
@@ -146,14 +175,14 @@ __device__ __forceinline__ void cross_stage(uint64_t (&a)[E], bool keep_min) {
 #pragma unroll
         for (int u = 0; u < E; ++u) {
             const uint32_t lo = static_cast<uint32_t>(a[u]), hi = static_cast<uint32_t>(a[u] >> 32);
-            const uint64_t y = pack64(quad_take<D>(lo), quad_take<D>(hi) ^ m);
+            const uint64_t y = pack64(lane_xor32<D>(lo), lane_xor32<D>(hi) ^ m);
             const uint64_t r = kmin<S>(pack64(lo, hi ^ m), y);
             a[u] = pack64(static_cast<uint32_t>(r), static_cast<uint32_t>(r >> 32) ^ m);
         }
     } else {
 #pragma unroll
         for (int u = 0; u < E; ++u) {
-            const uint64_t y = quad_xor<D>(a[u]);
+            const uint64_t y = lane_xor64<D>(a[u]);
             const bool lt = y < a[u];
             a[u] = (lt == keep_min) ? y : a[u];
         }
@@ -173,11 +202,11 @@ __device__ __forceinline__ void cross_stages_quad(uint64_t (&a)[E], int lane) {
     for (int u = 0; u < E; ++u) {
         uint32_t lo = static_cast<uint32_t>(a[u]), hi = static_cast<uint32_t>(a[u] >> 32);
         const uint64_t r2 = kmin<32>(pack64(lo, hi ^ m2),
-                                     pack64(quad_take<2>(lo), quad_take<2>(hi) ^ m2));
+                                     pack64(lane_xor32<2>(lo), lane_xor32<2>(hi) ^ m2));
         lo = static_cast<uint32_t>(r2);
         hi = static_cast<uint32_t>(r2 >> 32);  // negated by m2
         const uint64_t r1 = kmin<32>(pack64(lo, hi ^ m12),
-                                     pack64(quad_take<1>(lo), quad_take<1>(hi) ^ m12));
+                                     pack64(lane_xor32<1>(lo), lane_xor32<1>(hi) ^ m12));
         a[u] = pack64(static_cast<uint32_t>(r1), static_cast<uint32_t>(r1 >> 32) ^ m1);
     }
 }
@@ -185,10 +214,12 @@ __device__ __forceinline__ void cross_stages_quad(uint64_t (&a)[E], int lane) {
 // Sort the bitonic sequence held as L lanes x E registers (lane-major) ascending.
 template <int E, int L, int S>
 __device__ __forceinline__ void bitonic_clean(uint64_t (&a)[E], int lane) {
-    if constexpr (L == 4 && S == 32) {
+    if constexpr (L >= 16) cross_stage<E, 8, S>(a, (lane & 8) == 0);
+    if constexpr (L >= 8) cross_stage<E, 4, S>(a, (lane & 4) == 0);
+    if constexpr (L >= 4 && S == 32) {
         cross_stages_quad<E>(a, lane);
     } else {
-        if constexpr (L == 4) cross_stage<E, 2, S>(a, (lane & 2) == 0);
+        if constexpr (L >= 4) cross_stage<E, 2, S>(a, (lane & 2) == 0);
         if constexpr (L >= 2) cross_stage<E, 1, S>(a, (lane & 1) == 0);
     }
 #pragma unroll
@@ -236,11 +267,12 @@ __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
     }
 }
 
-// Value of the previous lane of this query's lane group (L = 2 or 4 lanes in a quad); the
-// group's first lane reads its own value.
+// Value of the previous lane of this query's lane group (L = 2 or 4 lanes in a quad, or a
+// 16-lane row); the group's first lane reads its own (quads) or an undefined value (rows).
 template <int L>
 __device__ __forceinline__ uint64_t from_prev_lane(uint64_t x) {
-    constexpr int ctrl = L == 4 ? 0x90 : 0xA0;  // quad_perm [0,0,1,2] / [0,0,2,2]
+    // quad_perm [0,0,1,2] / [0,0,2,2]; row_shr:1 for a row
+    constexpr int ctrl = L == 16 ? 0x111 : (L == 4 ? 0x90 : 0xA0);
     const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF,
                                             0xF, false);
     const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)), ctrl,
@@ -291,6 +323,14 @@ __device__ __forceinline__ bool one_per_group(uint64_t m) {
         const uint64_t pair_both = m & (m >> 1) & 0x5555555555555555ull;
         if constexpr (L == 2) {
             return pair_both == 0;
+        } else if constexpr (L == 16) {
+            bool ok = true;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t c = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
+                ok = ok && (c & (c - 1u)) == 0u;
+            }
+            return ok;
         } else {
             const uint64_t pair_any = (m | (m >> 1)) & 0x5555555555555555ull;
             return pair_both == 0 && (pair_any & (pair_any >> 2) & 0x1111111111111111ull) == 0;
@@ -315,8 +355,10 @@ __device__ __forceinline__ void merge_unsorted(uint64_t (&best)[E], uint64_t (&c
         uint64_t mn[1] = {cand[0]};
 #pragma unroll
         for (int t = 1; t < E; ++t) mn[0] = kmin<S>(mn[0], cand[t]);
-        if constexpr (L >= 2) mn[0] = kmin<S>(mn[0], quad_xor<1>(mn[0]));
-        if constexpr (L == 4) mn[0] = kmin<S>(mn[0], quad_xor<2>(mn[0]));
+        if constexpr (L >= 2) mn[0] = kmin<S>(mn[0], lane_xor64<1>(mn[0]));
+        if constexpr (L >= 4) mn[0] = kmin<S>(mn[0], lane_xor64<2>(mn[0]));
+        if constexpr (L >= 8) mn[0] = kmin<S>(mn[0], lane_xor64<4>(mn[0]));
+        if constexpr (L >= 16) mn[0] = kmin<S>(mn[0], lane_xor64<8>(mn[0]));
         insert_few<E, L, 1, S>(best, mn, lane);
         return;
     }
@@ -436,8 +478,8 @@ __device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, 
 // budget for K = 64); the caller has checked that its first candidate may enter the list.
 // Deep in the prefix a walk admits a few keys at most: when candidate kInsert cannot beat
 // its query's K-th for any query of the wavefront, the first kInsert candidates are merged
-// by insertion and the bitonic merge is skipped; with four lanes per query, failing that,
-// the first three when candidate 3 cannot enter (each choice uniform over the wavefront).
+// by insertion and the bitonic merge is skipped; with four or more lanes per query, failing
+// that, the first three when candidate 3 cannot enter (each choice uniform over the wavefront).
 // `few` = false skips those checks for walks that nearly always admit more (the walks of a
 // query's two largest runs).
 template <int K, int L, bool RIGHT, int S, bool O32>
@@ -448,10 +490,10 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
     constexpr int E = K / L;
     constexpr int CH = kChunk < E ? kChunk : E;
     const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
-    if constexpr (L == 4 && kInsert > 0 && kInsert < L) {
+    if constexpr (L >= 4 && kInsert > 0 && kInsert < kInsert2 && kInsert2 < L) {
         if (few) {
             // lane r of the query loads candidate r first (run position p + r, or p - 1 - r on
-            // the left); the whole walk is loaded only when candidate kInsert may enter
+            // the left); the whole walk is loaded only when candidate kInsert2 may enter
             using IX = typename TreeIx<O32>::T;
             const IX q = RIGHT ? p + lane : p - 1 - lane;
             const bool in = RIGHT ? q < s : q >= 0;
@@ -468,17 +510,15 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
                 insert_few<E, L, kInsert, S>(best, g, lane);
                 return;
             }
-            // one more candidate from the same loads when candidate L - 1 cannot enter
-            if constexpr (kInsert + 1 < L) {
-                if (__ballot(lane == L - 1 && key < kth) == 0) {
-                    uint64_t g[L - 1];
-                    static_for<0, L - 1>([&](auto rc) {
-                        constexpr int r = decltype(rc)::value;
-                        g[r] = from_lane64<L, r>(key);
-                    });
-                    insert_few<E, L, L - 1, S>(best, g, lane);
-                    return;
-                }
+            // one more candidate from the same loads when candidate kInsert2 cannot enter
+            if (__ballot(lane == kInsert2 && key < kth) == 0) {
+                uint64_t g[kInsert2];
+                static_for<0, kInsert2>([&](auto rc) {
+                    constexpr int r = decltype(rc)::value;
+                    g[r] = from_lane64<L, r>(key);
+                });
+                insert_few<E, L, kInsert2, S>(best, g, lane);
+                return;
             }
         }
     } else if constexpr (CH == E && kInsert > 0 && kInsert < E) {
@@ -769,7 +809,9 @@ static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool cau
     if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 64) return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 128) return launch_select_k<128, 16, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    return launch_select_k<256, 16, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
 }
 
 hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
@@ -929,7 +971,9 @@ static hipError_t chunked_t(int64_t BH, int64_t N, int levels, int lvl, int topk
     if (topk <= 8) return launch_chunked_k<8, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
     if (topk <= 16) return launch_chunked_k<16, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
     if (topk <= 32) return launch_chunked_k<32, 2, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    return launch_chunked_k<64, 4, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 64) return launch_chunked_k<64, 4, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 128) return launch_chunked_k<128, 16, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    return launch_chunked_k<256, 16, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
 }
 
 hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,

@@ -7,7 +7,7 @@
 
 namespace zeta {
 
-constexpr int kMaxTopK = 64;
+constexpr int kMaxTopK = 256;
 constexpr int kMaxDv = 512;
 constexpr size_t kAlign = 256;
 

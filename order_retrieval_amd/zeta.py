@@ -27,7 +27,7 @@ ZETA_WS_SELECT = 0
 ZETA_WS_FWD = 1
 ZETA_WS_BWD = 2
 
-ZETA_MAX_TOPK = 64
+ZETA_MAX_TOPK = 256
 ZETA_MAX_DV = 512
 ZETA_MAX_CHUNKS = 1024
 
@@ -235,13 +235,15 @@ def _qk_shape(q: torch.Tensor, k: torch.Tensor):
 
 
 def zeta_select_ex(q: torch.Tensor, k: torch.Tensor, topk: int, opts: ZetaSelectOpts | None,
-                   ws: torch.Tensor | None = None) -> torch.Tensor:
+                   ws: torch.Tensor | None = None,
+                   idx: torch.Tensor | None = None) -> torch.Tensor:
     """Selection (variant `opts`, None = exact causal): idx [B, H, N, topk] int32."""
     B, H, N = _qk_shape(q, k)
     shape = make_shape(B, H, N, 8, topk, ZETA_F32)
     if ws is None:
         ws = workspace(shape, ZETA_WS_SELECT, q.device, opts)
-    idx = torch.empty((B, H, N, topk), dtype=torch.int32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, H, N, topk), dtype=torch.int32, device=q.device)
     _check(load_library().zeta_select_ex(ctypes.byref(shape), _opts_ref(opts), _ptr(q), _ptr(k),
                                          _ptr(idx), _ptr(ws), ws.numel(), _stream()))
     return idx

@@ -69,7 +69,7 @@ def test_status_strings(lib):
     (dict(H=0), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(N=0), zeta.ZETA_ERR_INVALID_ARGUMENT),
     (dict(topk=0), zeta.ZETA_ERR_INVALID_ARGUMENT),
-    (dict(topk=65), zeta.ZETA_ERR_UNSUPPORTED),
+    (dict(topk=257), zeta.ZETA_ERR_UNSUPPORTED),
     (dict(dv=12), zeta.ZETA_ERR_UNSUPPORTED),
     (dict(dv=0), zeta.ZETA_ERR_UNSUPPORTED),
     (dict(dv=520), zeta.ZETA_ERR_UNSUPPORTED),

@@ -144,10 +144,23 @@ def test_select_bit_exact_sampled(name):
     (2, 3, 3000, 32, "discrete"), (1, 2, 3000, 64, "constant"), (1, 2, 2500, 1, "normal"),
     (1, 1, 1500, 5, "discrete"), (3, 1, 777, 7, "clustered"), (1, 1, 5000, 3, "normal"),
     (1, 1, 1100, 33, "discrete"), (1, 1, 2000, 2, "constant"), (1, 1, 1030, 16, "discrete"),
+    # selections wider than 64 (a 16-lane row per query)
+    (1, 1, 1, 256, "normal"), (1, 2, 65, 65, "normal"), (1, 1, 300, 128, "normal"),
+    (1, 2, 3000, 65, "clustered"), (2, 1, 2100, 96, "discrete"), (1, 1, 5000, 256, "normal"),
+    (1, 1, 200, 256, "clustered"), (1, 1, 1025, 256, "constant"), (1, 3, 4500, 128, "discrete"),
+    (1, 1, 2000, 200, "clustered"),
 ])
 def test_select_edge_shapes(B, H, N, topk, dist):
     log(f"select edge B={B} H={H} N={N} k={topk} {dist}")
     _select_and_compare(W("e", B, H, N, 8, topk, dist=dist, seed=N + topk))
+
+
+@pytest.mark.parametrize("topk", [65, 96, 128, 256])
+def test_select_wide_topk_clustered_batch(topk):
+    # the clustered mixture (heavy code ties) with four batch entries, selections wider than 64
+    w = W("cw", 4, 2, 4096, 8, topk, dist="clustered", seed=41 + topk)
+    log(f"select clustered B4 k={topk}")
+    _select_and_compare(w)
 
 
 def test_select_beyond_32bit_tree_offsets():
@@ -220,6 +233,9 @@ def test_forward_sampled(name):
     (300, 512, 16, inputs.BF16, "normal"), (700, 136, 5, inputs.BF16, "discrete"),
     (1025, 8, 32, inputs.BF16, "constant"), (2000, 64, 48, inputs.F32, "discrete"),
     (999, 256, 32, inputs.BF16, "clustered"), (64, 40, 64, inputs.F32, "normal"),
+    (600, 64, 128, inputs.F32, "normal"), (300, 24, 256, inputs.BF16, "clustered"),
+    (2000, 128, 96, inputs.BF16, "discrete"), (70, 8, 65, inputs.F32, "normal"),
+    (257, 512, 256, inputs.F32, "normal"),
 ])
 def test_forward_edge_shapes(N, dv, topk, vt, dist):
     log(f"forward edge N={N} dv={dv} k={topk} {vt} {dist}")
@@ -263,6 +279,10 @@ def test_backward_full(name):
     (1, 2, 300, 512, 16, inputs.F32, "discrete"), (2, 1, 1025, 136, 5, inputs.BF16, "normal"),
     (1, 1, 2000, 32, 64, inputs.F32, "constant"), (3, 2, 700, 8, 1, inputs.F32, "clustered"),
     (1, 1, 4500, 64, 33, inputs.F32, "normal"),
+    # selections wider than 64: the two-pass per-query kernel
+    (1, 2, 600, 64, 128, inputs.F32, "clustered"), (4, 1, 1100, 32, 256, inputs.BF16, "normal"),
+    (1, 1, 2000, 16, 65, inputs.F32, "discrete"), (2, 1, 300, 8, 96, inputs.F32, "constant"),
+    (1, 1, 70, 512, 256, inputs.F32, "normal"), (4, 2, 2048, 64, 128, inputs.BF16, "clustered"),
 ])
 def test_backward_edge_shapes(B, H, N, dv, topk, vt, dist):
     log(f"backward edge B={B} H={H} N={N} dv={dv} k={topk} {vt} {dist}")

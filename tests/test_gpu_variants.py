@@ -58,6 +58,18 @@ def _name(kind):
 
 
 # ----------------------------------------------------------------------------- selection
+def _assert_rejected(w, opts):
+    """topk below the curve count: the call is refused before any launch, idx untouched."""
+    x = inputs.make_inputs(w)
+    idx = torch.full((w.B, w.H, w.N, w.topk), 7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Z.ZetaError) as e:
+        Z.zeta_select_ex(to_dev(x["q"]), to_dev(x["k"]), w.topk, opts, ws=ws, idx=idx)
+    assert e.value.status == Z.ZETA_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+    assert torch.all(idx == 7)
+
+
 def _select_check(w, kind, rows=None):
     x = inputs.make_inputs(w)
     idx = Z.zeta_select_ex(to_dev(x["q"]), to_dev(x["k"]), w.topk, opts_of(kind))
@@ -71,8 +83,6 @@ def _select_check(w, kind, rows=None):
 @pytest.mark.parametrize("kind", KINDS, ids=_name)
 @pytest.mark.parametrize("name", ["tiny", "multihead"])
 def test_variant_select_bit_exact_full(name, kind):
-    if kind[0] == "curves" and name == "multihead" and kind[1] == 6:
-        pytest.skip("six curves covered on tiny and on the edge shapes")
     log(f"variant select {name} {kind}")
     _select_check(CFG[name], kind)
 
@@ -94,9 +104,10 @@ def test_variant_select_sampled_long(kind):
 @pytest.mark.parametrize("kind", KINDS + [("chunked", 1024), ("chunked", 3), ("curves", 6, False)],
                          ids=_name)
 def test_variant_select_edge_shapes(B, H, N, topk, dist, kind):
-    if kind[0] == "curves" and topk < kind[1]:
-        pytest.skip("topk below the curve count is rejected")
     log(f"variant select edge B={B} H={H} N={N} k={topk} {dist} {kind}")
+    if kind[0] == "curves" and topk < kind[1]:
+        _assert_rejected(W("ve", B, H, N, 8, topk, dist=dist, seed=N + topk), opts_of(kind))
+        return
     _select_check(W("ve", B, H, N, 8, topk, dist=dist, seed=N + topk), kind)
 
 
@@ -135,6 +146,17 @@ def test_variant_forward_full(name, kind):
 def test_variant_forward_edge_shapes(N, dv, vt, kind):
     log(f"variant forward edge N={N} dv={dv} {vt} {kind}")
     _forward_check(W("vf", 2, 2, N, dv, 16, vt, "clustered", seed=N + dv), kind)
+
+
+@pytest.mark.parametrize("kind", [("chunked", 4), ("chunked", 16), ("curves", 3, True),
+                                  ("curves", 6, False), ("exact", False)], ids=_name)
+@pytest.mark.parametrize("B,H,N,topk,dist", [(1, 2, 3000, 128, "clustered"),
+                                             (2, 1, 1500, 256, "normal"),
+                                             (1, 1, 700, 96, "discrete")])
+def test_variant_wide_topk(B, H, N, topk, dist, kind):
+    log(f"variant wide k={topk} B={B} H={H} N={N} {dist} {kind}")
+    w = W("vw", B, H, N, 32, topk, inputs.BF16, dist, seed=N + topk, backward=True)
+    _backward_check(w, kind)
 
 
 def test_variant_forward_sampled_long():
@@ -310,9 +332,10 @@ def test_12bit_select_bit_exact(name, kind):
 ])
 @pytest.mark.parametrize("kind", KINDS12, ids=_name)
 def test_12bit_select_edge_shapes(B, H, N, topk, dist, kind):
-    if kind[0] == "curves" and topk < kind[1]:
-        pytest.skip("topk below the curve count is rejected")
     log(f"12-bit select edge B={B} H={H} N={N} k={topk} {dist} {kind}")
+    if kind[0] == "curves" and topk < kind[1]:
+        _assert_rejected(W("v12", B, H, N, 8, topk, dist=dist, seed=N + topk), opts12(kind))
+        return
     _select12_check(W("v12", B, H, N, 8, topk, dist=dist, seed=N + topk), kind)
 
 
