@@ -586,8 +586,9 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
                                                            const uint32_t* __restrict__ order,
-                                                           int64_t N, int levels, int topk,
-                                                           int causal, int64_t tph, int64_t tiles,
+                                                           int64_t N, int stored, int base,
+                                                           int topk, int causal, int64_t tph,
+                                                           int64_t tiles,
                                                            int64_t per_xcd,
                                                            int32_t* __restrict__ idx) {
     using IX = typename TreeIx<O32>::T;
@@ -604,8 +605,9 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
     const int64_t row = bh * N + i;
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     const uint64_t target = static_cast<uint64_t>(zq[row]) << S;
-    const uint64_t* hA = tree_asc + bh * levels * N;
-    const uint64_t* hD = tree_desc + bh * levels * N;
+    // the trees hold levels base .. base + stored - 1 of every (b,h), level l at (l - base) N
+    const uint64_t* hA = tree_asc + bh * stored * N;
+    const uint64_t* hD = tree_desc + bh * stored * N;
 
     uint64_t best[E];
 #pragma unroll
@@ -637,7 +639,7 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
                 const int l = 63 - __clzll(rem);
                 rem ^= uint64_t(1) << l;
                 lv[gi] = l;
-                roff[gi] = static_cast<IX>(static_cast<int64_t>(l) * N +
+                roff[gi] = static_cast<IX>(static_cast<int64_t>(l - base) * N +
                                            static_cast<int64_t>((m >> (l + 1)) << (l + 1)));
             }
         }
@@ -778,7 +780,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
 }
 
 template <int K, int L, typename CT, int S>
-static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk, int causal,
+static hipError_t launch_select_k(int64_t rows, int64_t N, int stored, int base, int topk,
+                                  int causal,
                                   const CT* zq, const CT* zk, const uint64_t* ta,
                                   const uint64_t* td, const uint32_t* order, int32_t* idx,
                                   hipStream_t s) {
@@ -787,46 +790,46 @@ static hipError_t launch_select_k(int64_t rows, int64_t N, int levels, int topk,
     const int64_t tiles = (rows / N) * tph;
     const int64_t per = xcd_per(tiles);
     const dim3 grid(static_cast<unsigned>(per * kXcds));
-    if (static_cast<int64_t>(levels) * N < (int64_t(1) << 28))
+    if (static_cast<int64_t>(stored) * N < (int64_t(1) << 28))
         hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, true>), grid, dim3(256), 0, s, zq, zk,
-                           ta, td, order, N, levels, topk, causal, tph, tiles, per, idx);
+                           ta, td, order, N, stored, base, topk, causal, tph, tiles, per, idx);
     else
         hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, false>), grid, dim3(256), 0, s, zq,
-                           zk, ta, td, order, N, levels, topk, causal, tph, tiles, per, idx);
+                           zk, ta, td, order, N, stored, base, topk, causal, tph, tiles, per, idx);
     return hipGetLastError();
 }
 
 template <typename CT, int S>
-static hipError_t select_t(int64_t BH, int64_t N, int levels, int topk, bool causal,
+static hipError_t select_t(int64_t BH, int64_t N, int stored, int base, int topk, bool causal,
                            const CT* zq, const CT* zk, const uint64_t* ta, const uint64_t* td,
                            const uint32_t* order, int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
     const int c = causal ? 1 : 0;
-    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 64) return launch_select_k<64, 4, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 128) return launch_select_k<128, 16, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
-    return launch_select_k<256, 16, CT, S>(rows, N, levels, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 64) return launch_select_k<64, 4, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 128) return launch_select_k<128, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    return launch_select_k<256, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
 }
 
-hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
+hipError_t launch_select(int64_t BH, int64_t N, int stored, int base, int topk, bool causal,
                          const uint32_t* zq, const uint32_t* zk, const uint64_t* tree_asc,
                          const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
                          hipStream_t s) {
-    return select_t<uint32_t, 32>(BH, N, levels, topk, causal, zq, zk, tree_asc, tree_desc,
+    return select_t<uint32_t, 32>(BH, N, stored, base, topk, causal, zq, zk, tree_asc, tree_desc,
                                   order, idx, s);
 }
 
-hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
+hipError_t launch_select36(int64_t BH, int64_t N, int stored, int base, int topk, bool causal,
                            const uint64_t* zq, const uint64_t* zk, const uint64_t* tree_asc,
                            const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
                            hipStream_t s) {
-    return select_t<uint64_t, 28>(BH, N, levels, topk, causal, zq, zk, tree_asc, tree_desc,
+    return select_t<uint64_t, 28>(BH, N, stored, base, topk, causal, zq, zk, tree_asc, tree_desc,
                                   order, idx, s);
 }
 
@@ -854,7 +857,7 @@ int select_first_level(int topk) {
 template <int K, int L, typename CT, int S>
 __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
     const CT* __restrict__ zq, const uint64_t* __restrict__ tree_asc, int64_t rows,
-    int64_t N, int levels, int lvl, int topk, int32_t* __restrict__ idx) {
+    int64_t N, int stored, int base, int lvl, int topk, int32_t* __restrict__ idx) {
     constexpr int E = K / L;
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -865,7 +868,7 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
     const int64_t i = row - bh * N;
     const uint64_t z = zq[row];
     const uint64_t target = z << S;
-    const uint64_t* run = tree_asc + bh * levels * N + static_cast<int64_t>(lvl) * N;
+    const uint64_t* run = tree_asc + bh * stored * N + static_cast<int64_t>(lvl - base) * N;
     const int64_t len = int64_t(1) << lvl;
 
     uint64_t best[E];
@@ -951,41 +954,44 @@ __global__ void __launch_bounds__(256) zeta_select_chunked_kernel(
 }
 
 template <int K, int L, typename CT, int S>
-static hipError_t launch_chunked_k(int64_t rows, int64_t N, int levels, int lvl, int topk,
+static hipError_t launch_chunked_k(int64_t rows, int64_t N, int stored, int base, int lvl,
+                                   int topk,
                                    const CT* zq, const uint64_t* ta, int32_t* idx,
                                    hipStream_t s) {
     const int64_t blocks = (rows * L + 255) / 256;
     hipLaunchKernelGGL((zeta_select_chunked_kernel<K, L, CT, S>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, zq, ta, rows, N, levels, lvl, topk, idx);
+                       dim3(256), 0, s, zq, ta, rows, N, stored, base, lvl, topk, idx);
     return hipGetLastError();
 }
 
 template <typename CT, int S>
-static hipError_t chunked_t(int64_t BH, int64_t N, int levels, int lvl, int topk, const CT* zq,
+static hipError_t chunked_t(int64_t BH, int64_t N, int stored, int base, int lvl, int topk,
+                            const CT* zq,
                             const uint64_t* ta, int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
-    if (topk <= 1) return launch_chunked_k<1, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 2) return launch_chunked_k<2, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 4) return launch_chunked_k<4, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 8) return launch_chunked_k<8, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 16) return launch_chunked_k<16, 1, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 32) return launch_chunked_k<32, 2, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 64) return launch_chunked_k<64, 4, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    if (topk <= 128) return launch_chunked_k<128, 16, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
-    return launch_chunked_k<256, 16, CT, S>(rows, N, levels, lvl, topk, zq, ta, idx, s);
+    if (topk <= 1) return launch_chunked_k<1, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 2) return launch_chunked_k<2, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 4) return launch_chunked_k<4, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 8) return launch_chunked_k<8, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 16) return launch_chunked_k<16, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 32) return launch_chunked_k<32, 2, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 64) return launch_chunked_k<64, 4, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 128) return launch_chunked_k<128, 16, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    return launch_chunked_k<256, 16, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
 }
 
-hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
+hipError_t launch_select_chunked(int64_t BH, int64_t N, int stored, int base, int lvl, int topk,
                                  const uint32_t* zq, const uint64_t* ta, int32_t* idx,
                                  hipStream_t s) {
-    return chunked_t<uint32_t, 32>(BH, N, levels, lvl, topk, zq, ta, idx, s);
+    return chunked_t<uint32_t, 32>(BH, N, stored, base, lvl, topk, zq, ta, idx, s);
 }
 
-hipError_t launch_select_chunked36(int64_t BH, int64_t N, int levels, int lvl, int topk,
+hipError_t launch_select_chunked36(int64_t BH, int64_t N, int stored, int base, int lvl,
+                                   int topk,
                                    const uint64_t* zq, const uint64_t* ta, int32_t* idx,
                                    hipStream_t s) {
-    return chunked_t<uint64_t, 28>(BH, N, levels, lvl, topk, zq, ta, idx, s);
+    return chunked_t<uint64_t, 28>(BH, N, stored, base, lvl, topk, zq, ta, idx, s);
 }
 
 // ---------------------------------------------------------------------------- curves

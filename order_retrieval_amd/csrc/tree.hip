@@ -17,7 +17,9 @@
 // backward (codes < the query), so both walks meet equal codes in ascending j order.
 //
 // Levels below `first` are not written (the selection reads short runs straight from the
-// codes); they are still formed in LDS on the way up.
+// codes); they are still formed in LDS on the way up.  Only the levels from
+// tree_store_base(levels, first) up are stored: level l of (b,h) sits at
+// tree + (bh * stored + l - base) * N, stored = levels - base.
 // Build: levels 0..10 inside one workgroup per 1024-entry tile (LDS rank merge: each entry
 // moves to its own index plus its rank in the sibling block; keys are unique, so this is
 // an exact merge), then one merge-path launch per higher level (streaming: 8 B read and
@@ -51,7 +53,7 @@ template <typename CT, int S>
 __global__ void __launch_bounds__(kTile) zeta_tree_tile_kernel(const CT* __restrict__ zk,
                                                               uint64_t* __restrict__ asc,
                                                               uint64_t* __restrict__ desc,
-                                                              int64_t N, int levels, int top,
+                                                              int64_t N, int stored, int top,
                                                               int first) {
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     __shared__ uint64_t buf[2][2][kTile];  // [tree][ping-pong][entry]
@@ -59,8 +61,9 @@ __global__ void __launch_bounds__(kTile) zeta_tree_tile_kernel(const CT* __restr
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
     const int n = static_cast<int>(N - base < kTile ? N - base : kTile);
     const CT* zrow = zk + bh * N + base;
-    uint64_t* tA = asc + bh * levels * N + base;
-    uint64_t* tD = desc + bh * levels * N + base;
+    // level l at (l - first) N: `first` is also the lowest stored level
+    uint64_t* tA = asc + bh * stored * N + base;
+    uint64_t* tD = desc + bh * stored * N + base;
 
     for (int e = threadIdx.x; e < n; e += blockDim.x) {
         const uint64_t j = static_cast<uint64_t>(base + e);
@@ -95,8 +98,8 @@ __global__ void __launch_bounds__(kTile) zeta_tree_tile_kernel(const CT* __restr
         __syncthreads();
         cur ^= 1;
         if (l + 1 < first) continue;  // level not read by the caller: stays in LDS only
-        uint64_t* oA = tA + static_cast<int64_t>(l + 1) * N;
-        uint64_t* oD = tD + static_cast<int64_t>(l + 1) * N;
+        uint64_t* oA = tA + static_cast<int64_t>(l + 1 - first) * N;
+        uint64_t* oD = tD + static_cast<int64_t>(l + 1 - first) * N;
         for (int e = threadIdx.x; e < n; e += blockDim.x) {
             oA[e] = buf[0][cur][e];
             oD[e] = buf[1][cur][e];
@@ -122,13 +125,14 @@ __device__ __forceinline__ int diag_split(const uint64_t* A, int na, const uint6
 // Level l -> l+1 for l >= kTileLog: merge sibling blocks of 2^l entries (merge path).
 __global__ void __launch_bounds__(kMergeThreads) zeta_tree_merge_kernel(uint64_t* __restrict__ asc,
                                                                uint64_t* __restrict__ desc,
-                                                               int64_t N, int levels, int l) {
+                                                               int64_t N, int stored, int base,
+                                                               int l) {
     __shared__ uint64_t seg[kMergeTile];
     __shared__ int split[2];
     const int64_t bh = blockIdx.y;
-    uint64_t* T = (blockIdx.z ? desc : asc) + bh * levels * N;
-    const uint64_t* src = T + static_cast<int64_t>(l) * N;
-    uint64_t* dst = T + static_cast<int64_t>(l + 1) * N;
+    uint64_t* T = (blockIdx.z ? desc : asc) + bh * stored * N;
+    const uint64_t* src = T + static_cast<int64_t>(l - base) * N;
+    uint64_t* dst = T + static_cast<int64_t>(l + 1 - base) * N;
     const int64_t s = int64_t(1) << l;
     const int64_t o0 = static_cast<int64_t>(blockIdx.x) * kMergeTile;
     if (o0 >= N) return;
@@ -216,23 +220,30 @@ __global__ void __launch_bounds__(kMergeThreads) zeta_tree_merge_kernel(uint64_t
     for (int e = threadIdx.x; e < ca + cb; e += blockDim.x) out[e] = merged[e];
 }
 
+// Lowest stored level: `first`, or the tile stage's top level when merge passes follow and
+// read it.
+int tree_store_base(int levels, int first) {
+    const int top_tile = levels - 1 < kTileLog ? levels - 1 : kTileLog;
+    return (top_tile + 1 < levels && first > top_tile) ? top_tile : first;
+}
+
 template <typename CT, int S>
 static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, const CT* zk,
                                uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s) {
     if (BH <= 0 || N <= 0) return hipSuccess;
     const int top_tile = levels - 1 < kTileLog ? levels - 1 : kTileLog;
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
-    // the merge passes read the tile stage's top level, so it is written when they follow
-    const int first_w = (top_tile + 1 < levels && first > top_tile) ? top_tile : first;
+    const int base = tree_store_base(levels, first);
+    const int stored = levels > base ? levels - base : 0;
     hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(kTile), 0, s, zk, tree_asc,
-                       tree_desc, N, levels, top_tile, first_w);
+                       tree_desc, N, stored, top_tile, base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int l = top_tile; l + 1 < levels; ++l) {
         dim3 g(static_cast<unsigned>((N + kMergeTile - 1) / kMergeTile),
                static_cast<unsigned>(BH), 2);
         hipLaunchKernelGGL(zeta_tree_merge_kernel, g, dim3(kMergeThreads), 0, s, tree_asc, tree_desc, N,
-                           levels, l);
+                           stored, base, l);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

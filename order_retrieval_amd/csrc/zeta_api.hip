@@ -145,13 +145,19 @@ int curve_perm(int curves, int c) {
 
 struct FwdPlan {
     size_t zq, zk, tasc, tdesc, perm, ohist, sel, total;
-    int levels;
+    int levels;  // tree levels of the selection
+    int first;   // lowest level it reads
+    int base;    // lowest level stored (levels below are never stored)
+    int stored;  // levels stored per (b,h) and tree
 };
 
 FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
     const int64_t BHN = sh->B * sh->H * sh->N;
     FwdPlan p{};
     p.levels = tree_levels(sh, o);
+    p.first = tree_first(sh, o);
+    p.base = zeta::tree_store_base(p.levels, p.first);
+    p.stored = p.levels > p.base ? p.levels - p.base : 0;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -161,8 +167,8 @@ FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
     const size_t code_bytes = o.bits == 12 ? sizeof(uint64_t) : sizeof(uint32_t);
     p.zq = take(code_bytes * BHN);
     p.zk = take(code_bytes * BHN);
-    p.tasc = take(sizeof(uint64_t) * BHN * p.levels);
-    p.tdesc = take(sizeof(uint64_t) * BHN * p.levels);
+    p.tasc = take(sizeof(uint64_t) * BHN * p.stored);
+    p.tdesc = take(sizeof(uint64_t) * BHN * p.stored);
     p.perm = take(sizeof(uint32_t) * BHN);
     p.ohist = take(sizeof(uint32_t) * zeta::order_scratch_words(sh->B * sh->H, sh->N));
     // several curves: each curve's picks, [curves][BHN][topk / curves]
@@ -192,8 +198,12 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
     p.qs = take(2 * sizeof(float) * BH * N * K);
     p.dg = take(sizeof(float) * BH * N);
     p.dgp = take(sizeof(float) * sh->H * zeta::dgamma_chunks(sh->B, N));
+    // rec1: the second radix ping-pong buffer of 8-byte records when keys need more than 16
+    // bits; otherwise it takes only the final 4-byte slot list
+    int key_bits = 0;
+    while ((int64_t(1) << key_bits) < N) ++key_bits;
     p.r0 = take(8 * BH * p.P);
-    p.r1 = take(8 * BH * p.P);
+    p.r1 = take((key_bits <= 16 ? 4 : 8) * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);
     p.counts = take(sizeof(uint32_t) * BH);
@@ -264,9 +274,8 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
             if (e != hipSuccess) return fail_hip("order launch", e);
         }
         if (c == 0) g_marks.record(1, s);
-        const int first = tree_first(sh, o);
-        e = wide ? zeta::launch_build_tree36(BH, N, L, first, zk64, ta, td, s)
-                 : zeta::launch_build_tree(BH, N, L, first, zk, ta, td, s);
+        e = wide ? zeta::launch_build_tree36(BH, N, L, p.first, zk64, ta, td, s)
+                 : zeta::launch_build_tree(BH, N, L, p.first, zk, ta, td, s);
         if (e != hipSuccess) return fail_hip("tree launch", e);
         if (c == 0) g_marks.record(2, s);
         int32_t* dst = idx;
@@ -277,12 +286,14 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
         }
         if (o.mode == ZETA_SELECT_CHUNKED) {
             const int lvl = chunk_level(N, o.chunks);
-            e = wide ? zeta::launch_select_chunked36(BH, N, L, lvl, topk, zq64, ta, idx, s)
-                     : zeta::launch_select_chunked(BH, N, L, lvl, topk, zq, ta, idx, s);
+            e = wide ? zeta::launch_select_chunked36(BH, N, p.stored, p.base, lvl, topk, zq64, ta,
+                                                     idx, s)
+                     : zeta::launch_select_chunked(BH, N, p.stored, p.base, lvl, topk, zq, ta, idx,
+                                                   s);
         } else {
-            e = wide ? zeta::launch_select36(BH, N, L, kk, o.causal, zq64, zk64, ta, td, nullptr,
-                                             dst, s)
-                     : zeta::launch_select(BH, N, L, kk, o.causal, zq, zk, ta, td,
+            e = wide ? zeta::launch_select36(BH, N, p.stored, p.base, kk, o.causal, zq64, zk64, ta,
+                                             td, nullptr, dst, s)
+                     : zeta::launch_select(BH, N, p.stored, p.base, kk, o.causal, zq, zk, ta, td,
                                            at<uint32_t>(ws, p.perm), dst, s);
         }
         if (e != hipSuccess) return fail_hip("select launch", e);

@@ -83,6 +83,9 @@ hipError_t launch_encode_perm(const float* x, int64_t rows, int perm, uint32_t* 
 hipError_t launch_encode2_perm(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
                                int64_t rows, int perm, hipStream_t s);
 // Levels 0 .. first-1 are not written.
+// The trees store levels tree_store_base(levels, first) .. levels - 1 of every (b,h), as
+// [BH][levels - base][N].
+int tree_store_base(int levels, int first);
 hipError_t launch_build_tree(int64_t BH, int64_t N, int levels, int first, const uint32_t* zk,
                              uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
 // 12-bit cells: 36-bit codes (uint64), tree entries (code << 28) | j, N < 2^28.
@@ -90,23 +93,24 @@ hipError_t launch_encode36_perm(const float* x, int64_t rows, int perm, uint64_t
                                 hipStream_t s);
 hipError_t launch_build_tree36(int64_t BH, int64_t N, int levels, int first, const uint64_t* zk,
                                uint64_t* tree_asc, uint64_t* tree_desc, hipStream_t s);
-hipError_t launch_select36(int64_t BH, int64_t N, int levels, int topk, bool causal,
+hipError_t launch_select36(int64_t BH, int64_t N, int stored, int base, int topk, bool causal,
                            const uint64_t* zq, const uint64_t* zk, const uint64_t* tree_asc,
                            const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
                            hipStream_t s);
-hipError_t launch_select_chunked36(int64_t BH, int64_t N, int levels, int lvl, int topk,
+hipError_t launch_select_chunked36(int64_t BH, int64_t N, int stored, int base, int lvl,
+                                   int topk,
                                    const uint64_t* zq, const uint64_t* ta, int32_t* idx,
                                    hipStream_t s);
 // order: processing order of the queries (per (b,h) positions), or null for position order.
 // zk: the key codes (runs shorter than 2K are read from them, not from the tree).
-hipError_t launch_select(int64_t BH, int64_t N, int levels, int topk, bool causal,
+hipError_t launch_select(int64_t BH, int64_t N, int stored, int base, int topk, bool causal,
                          const uint32_t* zq, const uint32_t* zk, const uint64_t* tree_asc,
                          const uint64_t* tree_desc, const uint32_t* order, int32_t* idx,
                          hipStream_t s);
 // Lowest tree level the exact selection reads for this topk.
 int select_first_level(int topk);
 // Chunked search over the aligned chunks of 2^lvl positions (tree level lvl).
-hipError_t launch_select_chunked(int64_t BH, int64_t N, int levels, int lvl, int topk,
+hipError_t launch_select_chunked(int64_t BH, int64_t N, int stored, int base, int lvl, int topk,
                                  const uint32_t* zq, const uint64_t* ta, int32_t* idx,
                                  hipStream_t s);
 // Merge of several curves' selections sel [curves][rows][per] into idx [rows][topk].
