@@ -126,6 +126,23 @@ zeta_status zeta_bwd(const zeta_shape *shape, const float *q, const float *k, co
                      float *dk, void *dv, float *dgamma, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): zeta_fwd without a workspace argument.  Its
+ * scratch is a device array of ZETA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends; the first zeta_fwd_noalloc call on a GPU looks up its
+ * address (hipGetSymbolAddress) and keeps it.  The call allocates nothing.  Shapes whose
+ * forward workspace (zeta_workspace_bytes(shape, ZETA_WS_FWD)) exceeds the scratch return
+ * ZETA_ERR_WORKSPACE_TOO_SMALL, outputs untouched (B1 H8 N65536 dv128 k32 needs about
+ * 101 MB and fits).  The scratch is that of the calling thread's current device, and
+ * `stream` must belong to that device.  Every call on one GPU shares its scratch: no part
+ * of it needs to start at zero (a call reads only what it wrote itself), and calls that
+ * overlap on one GPU (other streams or threads) race, so serialise them.  Otherwise exactly
+ * zeta_fwd: exact causal selection, same kernels, same results.                          */
+#define ZETA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+zeta_status zeta_fwd_noalloc(const zeta_shape *shape, const float *q, const float *k,
+                             const void *v, const float *gamma, void *out, int32_t *idx,
+                             void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * Selection variants (the _ex calls).  NULL options = the exact causal selection with
  * 10-bit cells, i.e. the calls above.

@@ -4,10 +4,16 @@
 // nothing (scratch lives in the caller's workspace) and never synchronises the stream.
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "zeta.h"
 #include "zeta_internal.hpp"
+
+// Device scratch of zeta_fwd_noalloc: one array per GPU, held from the library's first use on
+// that GPU until the process ends.  In host code its name is only a handle for
+// hipGetSymbolAddress; the device address is looked up once per device and used everywhere.
+static __device__ __align__(256) unsigned char scratch[ZETA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -307,6 +313,72 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
     return ZETA_OK;
 }
 
+zeta_status check_fwd_args(const float* q, const float* k, const void* v, const float* gamma,
+                           const void* out, const int32_t* idx) {
+    zeta_status st = check_qk(q, k);
+    if (st != ZETA_OK) return st;
+    if (!v || !gamma || !out || !idx) return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned(v, 16) || !aligned(out, 16))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "v and out must be 16-byte aligned");
+    if (!aligned(gamma, 4) || !aligned(idx, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "gamma and idx must be 4-byte aligned");
+    return ZETA_OK;
+}
+
+// The forward's launches on a validated call: selection, processing order, gather.
+zeta_status run_fwd(const zeta_shape* shape, const Opts& o, const float* q, const float* k,
+                    const void* v, const float* gamma, void* out, int32_t* idx, void* workspace,
+                    hipStream_t s) {
+    const FwdPlan p = plan_fwd(shape, o);
+    zeta_status st = run_select(shape, o, q, k, idx, workspace, s);
+    if (st != ZETA_OK) return st;
+    uint32_t* perm = at<uint32_t>(workspace, p.perm);
+    // The exact and several-curve selections with 10-bit cells built the query processing
+    // order already (from the last curve's codes: the order only schedules work).  Otherwise
+    // it is built here from 10-bit query codes, written over the 36-bit ones with 12-bit
+    // cells (the order buckets by the top code bits, which both share).
+    hipError_t e = hipSuccess;
+    if (o.bits == 12 || o.mode == ZETA_SELECT_CHUNKED) {
+        uint32_t* zo = at<uint32_t>(workspace, p.zq);
+        if (o.bits == 12) e = zeta::launch_encode(q, shape->B * shape->H * shape->N, zo, s);
+        if (e == hipSuccess)
+            e = zeta::launch_order(shape->B * shape->H, shape->N, zo, perm,
+                                   at<uint32_t>(workspace, p.ohist), s);
+        if (e != hipSuccess) return fail_hip("order launch", e);
+    }
+    g_marks.record(4, s);
+    e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
+                            static_cast<int>(shape->topk), o.causal, shape->v_dtype == ZETA_BF16, q,
+                            k, v, gamma, idx, perm, out, s);
+    if (e != hipSuccess) return fail_hip("gather launch", e);
+    g_marks.record(5, s);
+    return ZETA_OK;
+}
+
+// Device address of the no-allocation scratch on the calling thread's current device, looked
+// up on the first call on that device (with it current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+zeta_status scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip("no usable HIP device", e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ZETA_ERR_UNSUPPORTED, "zeta_fwd_noalloc supports device ordinals below 64");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip("hipGetSymbolAddress(scratch)", e);
+        if (!p) return fail(ZETA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ZETA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,38 +463,34 @@ zeta_status zeta_fwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     if (st != ZETA_OK) return st;
     Opts o;
     if ((st = resolve_opts(opts, shape, o)) != ZETA_OK) return st;
-    if ((st = check_qk(q, k)) != ZETA_OK) return st;
-    if (!v || !gamma || !out || !idx) return fail(ZETA_ERR_INVALID_ARGUMENT, "NULL pointer");
-    if (!aligned(v, 16) || !aligned(out, 16))
-        return fail(ZETA_ERR_INVALID_ARGUMENT, "v and out must be 16-byte aligned");
-    if (!aligned(gamma, 4) || !aligned(idx, 4))
-        return fail(ZETA_ERR_INVALID_ARGUMENT, "gamma and idx must be 4-byte aligned");
-    const FwdPlan p = plan_fwd(shape, o);
-    if ((st = check_ws(workspace, workspace_bytes, p.total)) != ZETA_OK) return st;
+    if ((st = check_fwd_args(q, k, v, gamma, out, idx)) != ZETA_OK) return st;
+    if ((st = check_ws(workspace, workspace_bytes, plan_fwd(shape, o).total)) != ZETA_OK) return st;
     if ((st = preflight()) != ZETA_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_select(shape, o, q, k, idx, workspace, s)) != ZETA_OK) return st;
-    uint32_t* perm = at<uint32_t>(workspace, p.perm);
-    // The exact and several-curve selections with 10-bit cells built the query processing
-    // order already (from the last curve's codes: the order only schedules work).  Otherwise
-    // it is built here from 10-bit query codes, written over the 36-bit ones with 12-bit
-    // cells (the order buckets by the top code bits, which both share).
-    hipError_t e = hipSuccess;
-    if (o.bits == 12 || o.mode == ZETA_SELECT_CHUNKED) {
-        uint32_t* zo = at<uint32_t>(workspace, p.zq);
-        if (o.bits == 12) e = zeta::launch_encode(q, shape->B * shape->H * shape->N, zo, s);
-        if (e == hipSuccess)
-            e = zeta::launch_order(shape->B * shape->H, shape->N, zo, perm,
-                                   at<uint32_t>(workspace, p.ohist), s);
-        if (e != hipSuccess) return fail_hip("order launch", e);
+    return run_fwd(shape, o, q, k, v, gamma, out, idx, workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
+zeta_status zeta_fwd_noalloc(const zeta_shape* shape, const float* q, const float* k,
+                             const void* v, const float* gamma, void* out, int32_t* idx,
+                             void* stream) {
+    g_last_error.clear();
+    zeta_status st = check_shape(shape);
+    if (st != ZETA_OK) return st;
+    const Opts o;  // the exact causal selection with 10-bit cells
+    if ((st = check_fwd_args(q, k, v, gamma, out, idx)) != ZETA_OK) return st;
+    const size_t need = plan_fwd(shape, o).total;
+    if (need > ZETA_NOALLOC_SCRATCH_BYTES) {
+        char buf[192];
+        snprintf(buf, sizeof buf,
+                 "this shape's forward needs %zu bytes of scratch; zeta_fwd_noalloc holds %zu "
+                 "(ZETA_NOALLOC_SCRATCH_BYTES)",
+                 need, static_cast<size_t>(ZETA_NOALLOC_SCRATCH_BYTES));
+        return fail(ZETA_ERR_WORKSPACE_TOO_SMALL, buf);
     }
-    g_marks.record(4, s);
-    e = zeta::launch_gather(shape->B * shape->H, shape->H, shape->N, shape->dv,
-                            static_cast<int>(shape->topk), o.causal, shape->v_dtype == ZETA_BF16, q,
-                            k, v, gamma, idx, perm, out, s);
-    if (e != hipSuccess) return fail_hip("gather launch", e);
-    g_marks.record(5, s);
-    return ZETA_OK;
+    if ((st = preflight()) != ZETA_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != ZETA_OK) return st;
+    return run_fwd(shape, o, q, k, v, gamma, out, idx, ws, static_cast<hipStream_t>(stream));
 }
 
 zeta_status zeta_fwd(const zeta_shape* shape, const float* q, const float* k, const void* v,

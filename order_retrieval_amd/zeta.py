@@ -37,6 +37,7 @@ ZETA_SELECT_CURVES = 2
 
 EXPORTS = (
     "zeta_workspace_bytes",
+    "zeta_fwd_noalloc",
     "zeta_encode",
     "zeta_tree_levels",
     "zeta_build_tree",
@@ -128,6 +129,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeta_bwd_ex.restype = i32
     lib.zeta_fwd.argtypes = [sp, p, p, p, p, p, p, p, sz, p]
     lib.zeta_fwd.restype = i32
+    lib.zeta_fwd_noalloc.argtypes = [sp, p, p, p, p, p, p, p]
+    lib.zeta_fwd_noalloc.restype = i32
     lib.zeta_bwd.argtypes = [sp, p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.zeta_bwd.restype = i32
     lib.zeta_set_stage_events.argtypes = [p, i32]
@@ -329,6 +332,25 @@ def zeta_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Ten
         idx = torch.empty((B, H, N, topk), dtype=torch.int32, device=q.device)
     _check(load_library().zeta_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                    _ptr(out), _ptr(idx), _ptr(ws), ws.numel(), _stream()))
+    return out, idx
+
+
+def zeta_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                     topk: int, out: torch.Tensor, idx: torch.Tensor):
+    """Forward into caller-provided out / idx with the library's device scratch (no workspace,
+    nothing allocated by the call)."""
+    B, H, N = _qk_shape(q, k)
+    _dev(v, "v")
+    _dev(gamma, "gamma", torch.float32)
+    _dev(out, "out", v.dtype)
+    _dev(idx, "idx", torch.int32)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, H, N) or gamma.shape != (H,):
+        raise ValueError("v must be [B, H, N, dv] and gamma [H]")
+    if out.shape != v.shape or tuple(idx.shape) != (B, H, N, topk):
+        raise ValueError("out must be shaped like v and idx [B, H, N, topk]")
+    shape = make_shape(B, H, N, v.shape[3], topk, _v_dtype(v))
+    _check(load_library().zeta_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(gamma), _ptr(out), _ptr(idx), _stream()))
     return out, idx
 
 

@@ -131,6 +131,20 @@ def test_workspace_too_small(lib):
     assert st == zeta.ZETA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_noalloc_validates_before_any_launch(lib):
+    # invalid shapes and NULL pointers as for zeta_fwd; a shape whose forward scratch exceeds
+    # ZETA_NOALLOC_SCRATCH_BYTES is refused with the sizes in the message
+    assert lib.zeta_fwd_noalloc(ctypes.byref(shape(topk=0)), *([FAKE] * 6), None) == 1
+    assert lib.zeta_fwd_noalloc(ctypes.byref(shape()), None, *([FAKE] * 5), None) == 1
+    big = shape(B=1, H=16, N=65536, dv=128, topk=32, dt=zeta.ZETA_BF16)
+    assert lib.zeta_workspace_bytes(ctypes.byref(big), zeta.ZETA_WS_FWD) > 128 << 20
+    st = lib.zeta_fwd_noalloc(ctypes.byref(big), *([FAKE] * 6), None)
+    assert st == zeta.ZETA_ERR_WORKSPACE_TOO_SMALL
+    assert "ZETA_NOALLOC_SCRATCH_BYTES" in lib.zeta_last_error().decode()
+    fits = shape(B=1, H=8, N=65536, dv=128, topk=32, dt=zeta.ZETA_BF16)
+    assert lib.zeta_workspace_bytes(ctypes.byref(fits), zeta.ZETA_WS_FWD) <= 128 << 20
+
+
 def test_workspace_grows_with_shape(lib):
     a = lib.zeta_workspace_bytes(ctypes.byref(shape(N=1000)), zeta.ZETA_WS_FWD)
     b = lib.zeta_workspace_bytes(ctypes.byref(shape(N=4000)), zeta.ZETA_WS_FWD)
