@@ -4,7 +4,9 @@
 A step is one zeta_fwd (encode, tree build, select, Cauchy gather) plus one zeta_bwd
 (per-query pass, selection transpose, per-key pass, dgamma) on the 65536-token workload
 B=1, H=8, N=65536, d_K=3, d_V=128, k=32 with bf16 v and dO (seeded synthetic inputs,
-already resident in HBM when the timed region starts).  Prints one JSON line.
+already resident in HBM when the timed region starts).  Prints one JSON line: that step,
+the same measurement for every other synthetic configuration, the memory footprint, the
+measured row-gather ceiling that bounds the row kernels, and the oracle's CPU time.
 
 Kernel durations come from HIP events that the library records on its launch stream
 between stages (zeta_set_stage_events), inside the timed steps.  The CPU baseline is the
@@ -39,6 +41,12 @@ FWD_STAGES = ["encode_order", "tree", "select", "order", "gather"]
 BWD_STAGES = ["bwd_order", "bwd_query", "bwd_transpose", "bwd_key", "bwd_dgamma"]
 SINGLE_KERNEL = {"select": "zeta_select_kernel", "gather": "zeta_cauchy_gather_kernel",
                  "bwd_query": "zeta_bwd_query_kernel", "bwd_key": "zeta_bwd_key_kernel"}
+# kernels whose time goes to gathering whole rows named by the selection (mostly L2 hits):
+# bounded by the rate of such gathers (zeta_probe_row_gather), not by HBM bandwidth
+ROW_KERNELS = ("gather", "bwd_query", "bwd_key")
+# the row-gather ceiling: tables of 256-byte rows (one bf16 row of dV = 128)
+CEILING_TABLES = [("l2_2MiB", 2 << 20), ("mall_16MiB", 16 << 20), ("hbm_1GiB", 1 << 30)]
+CEILING_ROW_BYTES, CEILING_GROUPS, CEILING_ROWS = 256, 1 << 19, 32
 KERNEL_SOURCE = {"select": "select.hip", "gather": "gather.hip", "bwd_query": "backward.hip",
                  "bwd_key": "backward.hip"}
 
@@ -50,9 +58,10 @@ def valid_slots(w: inputs.Workload) -> np.ndarray:
 
 
 def select_run_bytes(w: inputs.Workload) -> float:
-    """Per (b,h): for every query, the sorted runs of its causal prefix (set bits of i+1):
-    a binary search (floor(log2 s)+1 probes of 8 B) and two k-wide windows (<= s entries of
-    8 B) per run, plus the query code (4 B) and the written index row (4k B)."""
+    """Per (b,h), as the kernel reads them: for every query, the sorted runs of its causal
+    prefix (set bits of i+1): a binary search (floor(log2 s)+1 probes of 8 B) and two k-wide
+    windows (<= s entries of 8 B) per run, plus the query code (4 B) and the written index
+    row (4k B)."""
     i1 = np.arange(1, w.N + 1, dtype=np.int64)
     total = np.zeros(w.N, dtype=np.float64)
     for l in range(int(np.log2(w.N)) + 1):
@@ -64,8 +73,8 @@ def select_run_bytes(w: inputs.Workload) -> float:
 
 def variant_select_bytes(w: inputs.Workload, mode: str, causal: bool = True, chunks: int = 0,
                          curves: int = 0, bits: int = 10) -> float:
-    """Algorithmic bytes of one selection launch (all (b,h)) of a variant, counted as for
-    the exact selection: 8 B per tree entry probed or windowed, the query code, idx out."""
+    """Bytes of one selection launch (all (b,h)) of a variant, counted as the kernels read
+    them: 8 B per tree entry probed or windowed, the query code, idx out."""
     BH, N, k = w.B * w.H, w.N, w.topk
     zb = 8 if bits == 12 else 4
     if mode == "exact":
@@ -101,43 +110,68 @@ VARIANTS = [  # name, zeta_select_opts fields
 ]
 
 
-def kernel_bytes(w: inputs.Workload) -> dict:
-    """Algorithmic bytes per launch of each kernel (every gathered row counted as read)."""
-    BH = w.B * w.H
+def materialised_levels(w: inputs.Workload) -> int:
+    """L_m = ceil(log2 N) - floor(log2 2k): tree levels the selection reads."""
+    return max(0, int(np.ceil(np.log2(w.N))) - int(np.floor(np.log2(2 * w.topk))))
+
+
+def algorithmic_bytes(w: inputs.Workload) -> dict:
+    """Algorithmic bytes per launch of each stage, per query-head as the method's byte model
+    fixes them (every gathered row counted as read; m = min(k, i+1) selected keys):
+        encode   32 (q and k rows in, codes out)
+        sort     4 + 8 L_m (codes in, one 8-byte entry per materialised level)
+        select   4 + 4k + per run of size s: 2k * 8 + 4 log2(s) if s > 2k, else 4 s
+        gather   4m + 12 + 12m + m dV|v| + dV|v|
+        pass 1   m (16 + dV|v| + 8) + 12 + dV|v| + 12
+        transp.  12k + 8
+        pass 3   m (24 + dV|v|) + dV|v| + 24
+    The processing-order builds and the dgamma reduction are not in that model; they are
+    counted as the kernels move them (codes in, order out; one float per query)."""
+    BH, N, k = w.B * w.H, w.N, w.topk
     vb = 2 if w.v_dtype == inputs.BF16 else 4
     row = w.dv * vb
     m = valid_slots(w).astype(np.float64)
-    pairs = float(m.sum())  # per (b,h)
-    levels = int(np.log2(w.N)) + 1
-    tile_levels = min(levels - 1, 10)
+    i1 = np.arange(1, N + 1, dtype=np.int64)
+    runs = np.zeros(N, dtype=np.float64)
+    for l in range(int(np.log2(N)) + 1):
+        s = 1 << l
+        has = ((i1 >> l) & 1).astype(np.float64)
+        runs += has * ((2 * k * 8 + 4 * l) if s > 2 * k else 4 * s)
     b = {}
-    # encode of q and k, then the query processing order (codes counted, codes placed,
-    # order written), which the select and the gather both use
-    b["encode_order"] = BH * w.N * (2 * 12 + 2 * 4) + BH * w.N * (4 + 4 + 4)
-    b["tree"] = BH * w.N * (4 + 2 * 8 * (tile_levels + 1) + 2 * 16 * (levels - 1 - tile_levels))
-    b["select"] = BH * select_run_bytes(w)
+    b["encode_order"] = BH * N * (32 + 12)  # encode, then the query order (codes, placed, out)
+    b["tree"] = BH * N * (4 + 8 * materialised_levels(w))
+    b["select"] = BH * float((4 + 4 * k + runs).sum())
     b["order"] = 0  # built with the encodes on this path
-    b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + 4 + row).sum())
-    b["bwd_order"] = BH * w.N * (2 * 12 + 2 * 4 + 2 * 12)
-    # per query: index row, q, key rows, value rows, dO row, dq and dgamma term, processing
-    # order entry, and {a, c} of every selected slot
-    b["bwd_query"] = BH * float((4 * m + 12 + 12 * m + m * row + row + 16 + 4 + 8 * m).sum())
-    bits = int(np.ceil(np.log2(w.N))) if w.N > 1 else 0
-    # pass 0 reads the index rows twice (histogram, scatter) and writes 8-byte {j, p} records;
-    # keys below 2^16: the per-group sort reads the records twice (count, scatter) and writes
-    # 4-byte slots and two segment bounds per key; wider keys: every further pass reads the
-    # records twice and writes them, and the segment starts read the sorted records
-    if bits <= 16:
-        b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + 16 * pairs + 4 * pairs +
-                                   8 * w.N)
-    else:
-        passes = -(-bits // 8)
-        b["bwd_transpose"] = BH * (2 * 4 * w.N * w.topk + 8 * pairs + (passes - 1) * 24 * pairs +
-                                   8 * pairs + 4 * (w.N + 1))
-    # per key: gamma, two offsets, k, dk and its dv row; per pair: the record, {a, c}, q_i
-    # and the dO_i row
-    b["bwd_key"] = BH * (w.N * (4 + 8 + 12 + 12 + row) + pairs * (8 + 8 + 12 + row))
-    b["bwd_dgamma"] = BH * w.N * 4.0
+    b["gather"] = BH * float((4 * m + 12 + 12 * m + m * row + row).sum())
+    b["bwd_order"] = BH * N * (32 + 2 * 12)
+    b["bwd_query"] = BH * float((m * (16 + row + 8) + 12 + row + 12).sum())
+    b["bwd_transpose"] = BH * N * (12 * k + 8)
+    b["bwd_key"] = BH * float((m * (24 + row) + row + 24).sum())
+    b["bwd_dgamma"] = BH * N * 4.0
+    return b
+
+
+def compulsory_bytes(w: inputs.Workload, stored_levels: int) -> dict:
+    """Bytes each stage must move through HBM at least: every distinct input byte it reads
+    once and every output byte once (rows that many queries gather count once).  The trees
+    are counted once written (tree) and once read (select); the transpose writes and reads
+    its 8-byte records once and writes the 4-byte slot list and the segment bounds."""
+    BH, N, k = w.B * w.H, w.N, w.topk
+    vb = 2 if w.v_dtype == inputs.BF16 else 4
+    row = w.dv * vb
+    P = float(valid_slots(w).sum())  # pairs per (b,h)
+    tree = 2 * 8 * stored_levels
+    b = {}
+    b["encode_order"] = BH * N * (24 + 8 + 4 + 4)
+    b["tree"] = BH * N * (4 + tree)
+    b["select"] = BH * (N * (4 + 4 + tree + 4 * k + 4))
+    b["order"] = 0
+    b["gather"] = BH * (N * (4 * k + 12 + 12 + row + row + 4))
+    b["bwd_order"] = BH * N * (24 + 8 + 8 + 8)
+    b["bwd_query"] = BH * (N * (4 * k + 12 + 12 + row + row + 8 * k + 12 + 4 + 4))
+    b["bwd_transpose"] = BH * (N * 4 * k + P * (8 + 8 + 4) + N * 8)
+    b["bwd_key"] = BH * (P * (4 + 8) + N * (12 + 12 + row + row + 12 + 8 + 4))
+    b["bwd_dgamma"] = BH * N * 4.0
     return b
 
 
@@ -210,18 +244,21 @@ def counter_means(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
+PROFILED = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants --no-configs"
+COPY = "python3 bench.py --copy-calibration"
+# one counter group per run (rocprofv3 collects one pass per run)
 COUNTER_CMDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- "
-    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- "
-    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o copy_fetch -- "
-    "python3 bench.py --copy-calibration",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o copy_write -- "
-    "python3 bench.py --copy-calibration",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- " + PROFILED,
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- " + PROFILED,
+    "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d {d}/l2 -o l2 -- " + PROFILED,
+    "rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum --output-format csv "
+    "-d {d}/ea -o ea -- " + PROFILED,
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o copy_fetch -- " + COPY,
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o copy_write -- " + COPY,
+    "rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum --output-format csv "
+    "-d {d}/copy_ea -o copy_ea -- " + COPY,
     "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES "
-    "SQ_BUSY_CYCLES --output-format csv -d {d}/lds -o lds -- "
-    "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-variants",
+    "SQ_BUSY_CYCLES --output-format csv -d {d}/lds -o lds -- " + PROFILED,
 ]
 # sort and select stages, whose LDS use and occupancy the counters report
 SORT_SELECT = ("zeta_order_", "zeta_tree_", "zeta_radix_", "zeta_bucket_sort", "zeta_select_")
@@ -252,14 +289,20 @@ def waves_by_lds(lds: int, wg: int) -> int:
     wgs = LDS_BYTES_PER_CU // lds if lds > 0 else 64
     return min(8, (wgs * waves_wg) // SIMDS_PER_CU)
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
-             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants")
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants --no-configs")
+CEILING_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
+               "python3 bench.py --gather-ceiling")
+
+
+def _maybe_means(path: str, counter: str) -> dict:
+    return counter_means(path, counter) if os.path.isdir(path) else {}
 
 
 def counters_summary(d: str, workload: str) -> None:
-    """HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE passes, each scaled
-    by what the same counter reads for a plain 1 GiB device copy; writes
-    profiles/<stage>_<workload>_counters.json (keyed to the kernel source's sha256) and a
-    markdown table of every kernel."""
+    """Bytes each kernel moves beyond L2 (FETCH_SIZE, WRITE_SIZE; each scaled by what the same
+    counter reads for a plain 1 GiB device copy), the raw read requests beyond L2 by size,
+    and the L2 hit rate (TCC_HIT, TCC_MISS); writes profiles/<stage>_<workload>_counters.json
+    (keyed to the kernel source's sha256) and profiles/counters_<workload>.md."""
     copy_bytes = float(1 << 30)
     cf = counter_means(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
     cw = counter_means(os.path.join(d, "copy_write"), "WRITE_SIZE")
@@ -268,21 +311,51 @@ def counters_summary(d: str, workload: str) -> None:
     wscale = copy_bytes / (cw[copy_name] * 1024.0)
     fetch = counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
     write = counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    hit = _maybe_means(os.path.join(d, "l2"), "TCC_HIT_sum")
+    miss = _maybe_means(os.path.join(d, "l2"), "TCC_MISS_sum")
+    ea = {c: _maybe_means(os.path.join(d, "ea"), c)
+          for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum")}
+    cea = {c: _maybe_means(os.path.join(d, "copy_ea"), c)
+           for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum")}
     cmds = [c.format(d=d) for c in COUNTER_CMDS]
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
-    lines = [f"# HBM traffic per launch, {workload} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
-             "Commands (each pass its own run, from the repository root):", ""]
+    lines = [f"# Memory traffic per launch, {workload} (rocprofv3 counters)", "",
+             "Commands (each counter group its own run, from the repository root):", ""]
     lines += [f"    {c}" for c in cmds] + [f"    python3 bench.py --counters-summary {d}", ""]
     lines += [f"Copy calibration: a 1 GiB device copy reads {cf[copy_name]:.0f} KiB (FETCH_SIZE) and "
-              f"writes {cw[copy_name]:.0f} KiB (WRITE_SIZE): scale {fscale:.3f} and {wscale:.3f}.", "",
-              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB per launch (scaled) |",
-              "|---|---|---|---|"]
+              f"writes {cw[copy_name]:.0f} KiB (WRITE_SIZE): scale {fscale:.3f} and {wscale:.3f}."]
+    if cea["TCC_EA0_RDREQ_sum"].get(copy_name):
+        creq = cea["TCC_EA0_RDREQ_sum"][copy_name]
+        lines += [f"The copy makes {creq:.0f} read requests beyond L2 ({copy_bytes / creq:.1f} bytes "
+                  f"each; {cea['TCC_EA0_RDREQ_32B_sum'].get(copy_name, 0):.0f} of 32 bytes, "
+                  f"TCC_BUBBLE {cea['TCC_BUBBLE_sum'].get(copy_name, 0):.0f}).  The kernels' "
+                  "request sizes are in the table: where their 32-byte share is as small as the "
+                  "copy's, every request moves a whole 128-byte line and the copy's scale holds "
+                  "for them too."]
+    lines += ["", "FETCH_SIZE and WRITE_SIZE count traffic between L2 and the data fabric, which "
+              "includes hits in the 256 MB Infinity Cache: an upper bound of the HBM bytes.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | beyond-L2 MB per launch (scaled) | "
+              "read requests | of them 32 B | L2 hit rate |",
+              "|---|---|---|---|---|---|---|"]
+
+    def hbm(k):
+        return fetch[k] * 1024 * fscale + write.get(k, 0.0) * 1024 * wscale
+
+    def l2rate(k):
+        h, mm = hit.get(k), miss.get(k)
+        return h / (h + mm) if h is not None and mm is not None and h + mm > 0 else None
+
     for kname in sorted(fetch, key=lambda n: -fetch[n]):
         if not kname.startswith("zeta_"):
             continue
-        hb = fetch[kname] * 1024 * fscale + write.get(kname, 0.0) * 1024 * wscale
-        lines.append(f"| {kname} | {fetch[kname]:.0f} | {write.get(kname, 0.0):.0f} | {hb / 1e6:.1f} |")
+        req = ea["TCC_EA0_RDREQ_sum"].get(kname)
+        r32 = ea["TCC_EA0_RDREQ_32B_sum"].get(kname)
+        rate = l2rate(kname)
+        lines.append(f"| {kname} | {fetch[kname]:.0f} | {write.get(kname, 0.0):.0f} | "
+                     f"{hbm(kname) / 1e6:.1f} | {'-' if req is None else f'{req:.0f}'} | "
+                     f"{'-' if r32 is None else f'{r32:.0f}'} | "
+                     f"{'-' if rate is None else f'{rate:.1%}'} |")
     for stage, kname in SINGLE_KERNEL.items():
         if kname not in fetch:
             continue
@@ -290,8 +363,8 @@ def counters_summary(d: str, workload: str) -> None:
         rec = {"kernel": kname, "workload": workload,
                "fetch_kib": fetch[kname], "write_kib": write.get(kname, 0.0),
                "fetch_scale": fscale, "write_scale": wscale,
-               "hbm_bytes_per_launch": int(fetch[kname] * 1024 * fscale +
-                                           write.get(kname, 0.0) * 1024 * wscale),
+               "hbm_bytes_per_launch": int(hbm(kname)),
+               "l2_hit_rate": l2rate(kname),
                "source": KERNEL_SOURCE[stage],
                "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
                "commands": cmds}
@@ -300,15 +373,15 @@ def counters_summary(d: str, workload: str) -> None:
     tr = os.path.join(os.path.dirname(os.path.abspath(d)), "trace")
     kt = trace_kernels(tr) if os.path.isdir(tr) else {}
     if kt:
-        lines += ["", f"Achieved HBM rate: the bytes above over the average kernel duration of the "
-                  f"kernel trace in {tr} (the same bench command, its own run):", "",
-                  "| kernel | HBM MB per launch | average us | HBM GB/s | of 8 TB/s |", "|---|---|---|---|---|"]
+        lines += ["", f"Achieved rate beyond L2: the bytes above over the average kernel duration "
+                  f"of the kernel trace in {tr} (the same bench command, its own run):", "",
+                  "| kernel | beyond-L2 MB per launch | average us | GB/s | of 8 TB/s |",
+                  "|---|---|---|---|---|"]
         for kname in sorted(fetch, key=lambda n: -fetch[n]):
             if not kname.startswith("zeta_") or kname not in kt:
                 continue
-            hb = fetch[kname] * 1024 * fscale + write.get(kname, 0.0) * 1024 * wscale
-            gbs = hb / (kt[kname]["us"] * 1e-6) / 1e9
-            lines.append(f"| {kname} | {hb / 1e6:.1f} | {kt[kname]['us']:.1f} | {gbs:.0f} | "
+            gbs = hbm(kname) / (kt[kname]["us"] * 1e-6) / 1e9
+            lines.append(f"| {kname} | {hbm(kname) / 1e6:.1f} | {kt[kname]['us']:.1f} | {gbs:.0f} | "
                          f"{gbs / HBM_PEAK_GBS:.1%} |")
     ldsdir = os.path.join(d, "lds")
     if os.path.isdir(ldsdir) and kt:
@@ -339,6 +412,42 @@ def counters_summary(d: str, workload: str) -> None:
                          f"{share} | {e['vgpr']} | {e['lds']} | {e['wg']} | "
                          f"{waves_by_lds(e['lds'], e['wg'])} | {mean:.1f} |")
     with open(os.path.join(prof, f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def ceiling_summary(d: str) -> None:
+    """profiles/gather_ceiling.md: the row-gather ceiling that bench.py --gather-ceiling
+    printed (HIP events) next to the kernel trace of the same run."""
+    stats = glob.glob(os.path.join(d, "*kernel_stats.csv"))
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    line = None
+    log = os.path.join(d, "run.log")
+    if os.path.exists(log):
+        for ln in open(log):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    kt = trace_kernels(d)
+    probe = kt.get("zeta_probe_row_gather_kernel")
+    lines = ["# Row-gather ceiling (zeta_probe_row_gather)", "",
+             "What bounds the gather and both backward passes: groups of 16 lanes each read 32 "
+             "rows of 256 bytes drawn uniformly from a table, 16 bytes per lane, eight rows' "
+             "loads in flight together (the access shape of those kernels, without their other "
+             f"work); {CEILING_GROUPS} groups per launch, "
+             f"{CEILING_GROUPS * CEILING_ROWS * CEILING_ROW_BYTES / 1e9:.2f} GB read per launch.  "
+             "A 2 MiB table sits in every XCD's 4 MB L2; 16 MiB (one head's bf16 values at "
+             "N = 65536, dV = 128) in the Infinity Cache; 1 GiB comes from HBM.", "",
+             "Command (from the repository root; stdout to run.log in the same folder):", "",
+             f"    {CEILING_CMD.format(d=d)}", f"    python3 bench.py --ceiling-summary {d}", ""]
+    if line is not None:
+        lines += ["| table | launches timed | GB/s (HIP events) | us per launch |", "|---|---|---|---|"]
+        for name, r in line["gather_ceiling"].items():
+            lines.append(f"| {name} | {r['launches']} | {r['GBs']:.0f} | {r['us']:.1f} |")
+    if probe is not None:
+        lines += ["", f"Kernel trace of the same run: zeta_probe_row_gather_kernel, {probe['n']} "
+                  f"dispatches, average {probe['us']:.1f} us (all table sizes together; the table "
+                  "above splits them by size).", ""]
+    with open(os.path.join(ROOT, "profiles", "gather_ceiling.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -462,6 +571,16 @@ def measure_variants(w, q, k, v, gamma, dout, idx_exact, hip, lib, Z, torch, ste
 
 
 # ----------------------------------------------------------------------------- CPU baseline
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w: inputs.Workload, x: dict, target_s: float, seed: int = 0) -> dict:
     import oracle
 
@@ -485,10 +604,244 @@ def cpu_baseline(w: inputs.Workload, x: dict, target_s: float, seed: int = 0) ->
     count = int(min(total, max(p2, (target_s - t1) / per_row)))
     t = run(count)
     return {"value": round(t / count * total * 1e3, 1), "unit": "ms", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": (f"{count} uniformly drawn query rows of the same workload (select + forward "
                        f"+ backward contributions, {t:.1f} s), scaled by {total}/{count}; "
                        f"selection and forward use all threads, backward runs on one")}
+
+
+# ----------------------------------------------------------------------------- GPU runs
+def measure_ceiling(Z, torch, launches: int = 10) -> dict:
+    """Rate of scattered 16-lane 256-byte row gathers (zeta_probe_row_gather) per table size,
+    timed with events on the launch stream."""
+    res = {}
+    sink = torch.empty(CEILING_GROUPS, dtype=torch.int32, device="cuda")
+    nbytes = CEILING_GROUPS * CEILING_ROWS * CEILING_ROW_BYTES
+    for name, size in CEILING_TABLES:
+        table = torch.randint(0, 255, (size,), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            Z.zeta_probe_row_gather(table, CEILING_ROW_BYTES, CEILING_GROUPS, CEILING_ROWS, 1, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for t in range(launches):
+            Z.zeta_probe_row_gather(table, CEILING_ROW_BYTES, CEILING_GROUPS, CEILING_ROWS, 2 + t,
+                                    sink)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / launches
+        res[name] = {"GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "us": round(us, 2),
+                     "launches": launches, "bytes": nbytes}
+        del table
+    return res
+
+
+class Run:
+    """One workload resident on the device, with its workspaces and outputs."""
+
+    def __init__(self, w: inputs.Workload, Z, torch):
+        self.w, self.Z, self.torch = w, Z, torch
+        x = inputs.make_inputs(w)
+        self.sha = inputs.digest(x)
+        dev = torch.device("cuda", 0)
+        bf = w.v_dtype == inputs.BF16
+
+        def to_dev(a, as_bf16=False):
+            if as_bf16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        self.q, self.k, self.gamma = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["gamma"])
+        self.v, self.dout = to_dev(x["v"], bf), to_dev(x["dout"], bf)
+        self.shape = Z.make_shape(w.B, w.H, w.N, w.dv, w.topk, Z.ZETA_BF16 if bf else Z.ZETA_F32)
+        self.ws_f = Z.workspace(self.shape, Z.ZETA_WS_FWD, dev)
+        self.ws_b = Z.workspace(self.shape, Z.ZETA_WS_BWD, dev)
+        self.out = torch.empty_like(self.v)
+        self.idx = torch.empty((w.B, w.H, w.N, w.topk), dtype=torch.int32, device=dev)
+        self.grads = (torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v),
+                      torch.empty((w.H,), dtype=torch.float32, device=dev))
+        self.x = x
+
+    def fwd(self):
+        self.Z.zeta_fwd(self.q, self.k, self.v, self.gamma, self.w.topk, ws=self.ws_f,
+                        out=self.out, idx=self.idx)
+
+    def bwd(self):
+        self.Z.zeta_bwd(self.q, self.k, self.v, self.gamma, self.idx, self.dout, ws=self.ws_b,
+                        grads=self.grads)
+
+    def tensor_bytes(self) -> int:
+        ts = (self.q, self.k, self.v, self.gamma, self.dout, self.out, self.idx) + self.grads
+        return int(sum(t.numel() * t.element_size() for t in ts))
+
+
+def time_run(r: Run, lib, hip, steps: int, warmup: int) -> dict:
+    """Stage times (HIP events the library records between its stages), the fwd+bwd step
+    and the forward alone (events around `steps` back-to-back calls)."""
+    torch = r.torch
+    for _ in range(warmup):
+        r.fwd()
+        r.bwd()
+    ev = [(hip.create(len(FWD_STAGES) + 1), hip.create(len(BWD_STAGES) + 1))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for evf, evb in ev:
+        lib.zeta_set_stage_events(evf, len(evf))
+        r.fwd()
+        lib.zeta_set_stage_events(evb, len(evb))
+        r.bwd()
+        lib.zeta_set_stage_events(None, 0)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    stages = {n: [] for n in FWD_STAGES + BWD_STAGES}
+    for evf, evb in ev:
+        for s_, n in enumerate(FWD_STAGES):
+            stages[n].append(hip.elapsed_ms(evf[s_], evf[s_ + 1]))
+        for s_, n in enumerate(BWD_STAGES):
+            stages[n].append(hip.elapsed_ms(evb[s_], evb[s_ + 1]))
+        hip.destroy(evf)
+        hip.destroy(evb)
+    stage_ms = {n: float(np.mean(t)) for n, t in stages.items()}
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record()
+    for _ in range(steps):
+        r.fwd()
+    f1.record()
+    torch.cuda.synchronize()
+    return {"step_ms": step_ms, "fwd_only_ms": f0.elapsed_time(f1) / steps, "stage_ms": stage_ms,
+            "wall_s": wall}
+
+
+def stored_levels(w: inputs.Workload) -> int:
+    """Tree levels the forward workspace stores: from log2(2K) (K = k padded to a power of two;
+    shorter runs are read from the codes) to the top level floor(log2 N), and from the tile
+    stage's top level (10) when that is lower and merge passes build the rest from it."""
+    L = int(np.floor(np.log2(w.N))) + 1
+    K = 1
+    while K < w.topk:
+        K *= 2
+    first = int(np.log2(2 * K))
+    top_tile = min(L - 1, 10)
+    base = top_tile if (top_tile + 1 < L and first > top_tile) else first
+    return max(0, L - base)
+
+
+def summarise(r: Run, t: dict, Z) -> dict:
+    """Per-workload figures: times, queries/s, bytes and fractions."""
+    w = r.w
+    alg = algorithmic_bytes(w)
+    comp = compulsory_bytes(w, stored_levels(w))
+    sm = t["stage_ms"]
+    fwd_stage_ms = sum(sm[n] for n in FWD_STAGES)
+    fwd_alg = sum(alg[n] for n in FWD_STAGES)
+    fwd_comp = sum(comp[n] for n in FWD_STAGES)
+    step_alg = sum(alg.values())
+    step_comp = sum(comp.values())
+    rows = w.B * w.H * w.N
+    kern = {}
+    for n in FWD_STAGES + BWD_STAGES:
+        if sm[n] <= 0 or alg[n] == 0:
+            continue
+        kern[n] = {"ms": round(sm[n], 4), "algorithmic_bytes": int(alg[n]),
+                   "compulsory_bytes": int(comp[n]),
+                   "effective_GBs": round(alg[n] / (sm[n] * 1e-3) / 1e9, 1),
+                   "hbm_frac_compulsory": round(comp[n] / (sm[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {
+        "shape": f"B{w.B} H{w.H} N{w.N} dK3 dV{w.dv} k{w.topk} v/dO {w.v_dtype} {w.dist}",
+        "fwd_ms": round(t["fwd_only_ms"], 4),
+        "fwd_bwd_ms": round(t["step_ms"], 4),
+        "queries_per_s_fwd": round(rows / (t["fwd_only_ms"] * 1e-3), 1),
+        "queries_per_s_fwd_bwd": round(rows / (t["step_ms"] * 1e-3), 1),
+        "fwd_algorithmic_bytes": int(fwd_alg),
+        "fwd_effective_GBs": round(fwd_alg / (fwd_stage_ms * 1e-3) / 1e9, 1),
+        "fwd_compulsory_bytes": int(fwd_comp),
+        "fwd_hbm_frac": round(fwd_comp / (fwd_stage_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_effective_GBs": round(step_alg / (t["step_ms"] * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_comp / (t["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage_ms": {n: round(v, 4) for n, v in sm.items()},
+        "kernels": kern,
+        "input_sha256": r.sha,
+    }
+
+
+def roofline(summary: dict, w: inputs.Workload, ceiling: dict) -> dict:
+    """The dominant single-kernel stage against what bounds it.  The row kernels gather rows
+    that are mostly L2 hits, so their ceiling is the measured rate of such gathers (an
+    L2-resident table); the selection is bounded by VALU issue and reported against HBM."""
+    stages = {n: summary["kernels"][n] for n in SINGLE_KERNEL if n in summary["kernels"]}
+    dom = max(stages, key=lambda n: stages[n]["ms"])
+    st = stages[dom]
+    ms = st["ms"]
+    traffic = stored_traffic(dom)
+    peak = ceiling["l2_2MiB"]["GBs"]
+    hbm = {"compulsory_bytes": st["compulsory_bytes"],
+           "achieved": round(st["compulsory_bytes"] / (ms * 1e-3) / 1e9, 1),
+           "peak": HBM_PEAK_GBS, "frac": st["hbm_frac_compulsory"]}
+    dram = None if traffic is None else {
+        "bytes": traffic, "GBs": round(traffic / (ms * 1e-3) / 1e9, 1),
+        "frac": round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"bound": "vmem" if dom in ROW_KERNELS else "hbm", "kernel": SINGLE_KERNEL[dom],
+            "stage": dom, "ms": ms, "achieved": st["effective_GBs"],
+            "peak": peak if dom in ROW_KERNELS else HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(st["effective_GBs"] / (peak if dom in ROW_KERNELS else HBM_PEAK_GBS), 4),
+            "traffic": traffic,
+            "peak_kind": ("measured in this run: scattered 16-lane 256-byte row gathers from an "
+                          "L2-resident table (zeta_probe_row_gather), the access these kernels make"
+                          if dom in ROW_KERNELS else "MI355X HBM3E, published"),
+            "achieved_kind": "the stage's algorithmic bytes (every gathered row counted as read) "
+                             "over its HIP-event duration",
+            "hbm": hbm, "dram": dram}
+
+
+def memory_footprint(w: inputs.Workload, Z, torch) -> dict:
+    """Device memory of one forward and one forward+backward through the autograd wrapper
+    (inputs, outputs, index tensor, gradients and the per-call workspaces), from a clean
+    allocator state."""
+    bf = w.v_dtype == inputs.BF16
+    x = inputs.make_inputs(w)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def to_dev(a, as_bf16=False):
+        if as_bf16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(a).to("cuda")
+
+    q, k, g = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["gamma"])
+    v, dout = to_dev(x["v"], bf), to_dev(x["dout"], bf)
+    with torch.no_grad():
+        out, idx = Z.zeta_fwd(q, k, v, g, w.topk)
+    torch.cuda.synchronize()
+    peak_fwd = torch.cuda.max_memory_allocated() - base
+    del out, idx
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    qr, kr, vr, gr = (t.clone().requires_grad_() for t in (q, k, v, g))
+    out, idx = Z.zeta_attention(qr, kr, vr, gr, w.topk)
+    out.backward(dout)
+    torch.cuda.synchronize()
+    peak_step = torch.cuda.max_memory_allocated() - base
+    shape = Z.make_shape(w.B, w.H, w.N, w.dv, w.topk, Z.ZETA_BF16 if bf else Z.ZETA_F32)
+    res = {"fwd_workspace_MB": round(Z.zeta_workspace_bytes(shape, Z.ZETA_WS_FWD) / 1e6, 1),
+           "bwd_workspace_MB": round(Z.zeta_workspace_bytes(shape, Z.ZETA_WS_BWD) / 1e6, 1),
+           "peak_allocated_MB_fwd": round(peak_fwd / 1e6, 1),
+           "peak_allocated_MB_fwd_bwd": round(peak_step / 1e6, 1),
+           "note": ("torch.cuda.max_memory_allocated over one zeta_fwd, and over one forward + "
+                    "backward through zeta_attention (the fwd+bwd figure also holds a copy of "
+                    "q, k, v, gamma made to request gradients); pages' context: 17348.2 MB for "
+                    "ZETA and 10516.1 MB for FlashAttention at 65536 tokens, shapes unstated")}
+    del qr, kr, vr, gr, out, idx, q, k, g, v, dout
+    torch.cuda.empty_cache()
+    return res
 
 
 # ----------------------------------------------------------------------------- main
@@ -502,19 +855,28 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the selection variants (chunked, several curves, unmasked, 12-bit)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other synthetic configurations and the memory footprint")
     ap.add_argument("--variant-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (counter calibration)")
+    ap.add_argument("--gather-ceiling", action="store_true",
+                    help="only measure the row-gather ceiling (zeta_probe_row_gather)")
     ap.add_argument("--counters-summary", metavar="DIR",
                     help="write profiles/*_counters.json from rocprofv3 --pmc outputs under DIR")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write profiles/kernels_<workload>.md from a rocprofv3 kernel-trace run")
+    ap.add_argument("--ceiling-summary", metavar="DIR",
+                    help="write profiles/gather_ceiling.md from a traced --gather-ceiling run")
     args = ap.parse_args()
     if args.counters_summary:
         counters_summary(args.counters_summary, args.workload)
         return 0
     if args.trace_summary:
         trace_summary(args.trace_summary, args.workload)
+        return 0
+    if args.ceiling_summary:
+        ceiling_summary(args.ceiling_summary)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -539,92 +901,28 @@ def main() -> int:
 
     from order_retrieval_amd import zeta as Z
 
+    if args.gather_ceiling:
+        print(json.dumps({"gather_ceiling": measure_ceiling(Z, torch)}), flush=True)
+        return 0
+
+    lib = Z.load_library()
+    hip = HipEvents(Z.hip_runtimes_mapped()[0])
     w = inputs.CONFIGS[args.workload]
     w = inputs.Workload(**{**w.__dict__, "backward": True})
-    x = inputs.make_inputs(w)
-    dev = torch.device("cuda", 0)
-    bf = w.v_dtype == inputs.BF16
-
-    def to_dev(a, as_bf16=False):
-        if as_bf16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    q, k, gamma = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["gamma"])
-    v, dout = to_dev(x["v"], bf), to_dev(x["dout"], bf)
-    shape = Z.make_shape(w.B, w.H, w.N, w.dv, w.topk, Z.ZETA_BF16 if bf else Z.ZETA_F32)
-    ws_f = Z.workspace(shape, Z.ZETA_WS_FWD, dev)
-    ws_b = Z.workspace(shape, Z.ZETA_WS_BWD, dev)
-    out = torch.empty_like(v)
-    idx = torch.empty((w.B, w.H, w.N, w.topk), dtype=torch.int32, device=dev)
-    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-             torch.empty((w.H,), dtype=torch.float32, device=dev))
-    lib = Z.load_library()
+    r = Run(w, Z, torch)
     torch.cuda.synchronize()
-    hip = HipEvents(Z.hip_runtimes_mapped()[0])
-
-    def step(ev_f=None, ev_b=None):
-        if ev_f is not None:
-            lib.zeta_set_stage_events(ev_f, len(ev_f))
-        Z.zeta_fwd(q, k, v, gamma, w.topk, ws=ws_f, out=out, idx=idx)
-        if ev_b is not None:
-            lib.zeta_set_stage_events(ev_b, len(ev_b))
-        Z.zeta_bwd(q, k, v, gamma, idx, dout, ws=ws_b, grads=grads)
-        lib.zeta_set_stage_events(None, 0)
-
-    for _ in range(args.warmup):
-        step()
-    ev = [(hip.create(len(FWD_STAGES) + 1), hip.create(len(BWD_STAGES) + 1))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for s in range(args.steps):
-        step(*ev[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t_start.elapsed_time(t_end) / args.steps
-
-    stages = {n: [] for n in FWD_STAGES + BWD_STAGES}
-    for evf, evb in ev:
-        for s, n in enumerate(FWD_STAGES):
-            stages[n].append(hip.elapsed_ms(evf[s], evf[s + 1]))
-        for s, n in enumerate(BWD_STAGES):
-            stages[n].append(hip.elapsed_ms(evb[s], evb[s + 1]))
-    stage_ms = {n: float(np.mean(t)) for n, t in stages.items()}
-    fwd_ms = sum(stage_ms[n] for n in FWD_STAGES)
-    bwd_ms = sum(stage_ms[n] for n in BWD_STAGES)
-    for evf, evb in ev:
-        hip.destroy(evf)
-        hip.destroy(evb)
-
-    # forward alone, for the forward-only figure
-    fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    fs.record()
-    for _ in range(args.steps):
-        Z.zeta_fwd(q, k, v, gamma, w.topk, ws=ws_f, out=out, idx=idx)
-    fe.record()
-    torch.cuda.synchronize()
-    fwd_only_ms = fs.elapsed_time(fe) / args.steps
-
-    kb = kernel_bytes(w)
-    dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
-    achieved = kb[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    traffic = stored_traffic(dom)
-    fwd_bytes = sum(kb[n] for n in FWD_STAGES)
-    step_bytes = sum(kb.values())
-    rows = w.B * w.H * w.N
+    t = time_run(r, lib, hip, args.steps, args.warmup)
+    main_sum = summarise(r, t, Z)
+    ceiling = measure_ceiling(Z, torch)
+    roof = roofline(main_sum, w, ceiling)
     result = {
         "metric": METRIC,
-        "value": round(step_ms, 4),
+        "value": round(t["step_ms"], 4),
         "unit": "ms",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": round(t["step_ms"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -634,32 +932,43 @@ def main() -> int:
                                f"v/dO {w.v_dtype}, forward+backward",
                    "B": w.B, "H": w.H, "N": w.N, "d_K": 3, "d_V": w.dv, "topk": w.topk,
                    "v_dtype": w.v_dtype, "seed": w.seed},
-        "fwd_ms": round(fwd_only_ms, 4),
-        "fwd_bwd_ms": round(step_ms, 4),
-        "queries_per_s_fwd": round(rows / (fwd_only_ms * 1e-3), 1),
-        "queries_per_s_fwd_bwd": round(rows / (step_ms * 1e-3), 1),
-        "fwd_algorithmic_GBs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
-        "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_algorithmic_GBs": round(step_bytes / ((fwd_ms + bwd_ms) * 1e-3) / 1e9, 1),
-        "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()},
-        "stage_algorithmic_bytes": {n: int(b) for n, b in kb.items()},
-        "roofline": {"bound": "hbm", "kernel": SINGLE_KERNEL[dom], "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     # measured HBM bytes over the same duration: what DRAM actually carried
-                     "dram_GBs": None if traffic is None
-                     else round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1),
-                     "dram_frac": None if traffic is None
-                     else round(traffic / (stage_ms[dom] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "wall_s_timed": round(wall, 3),
+        **{k_: main_sum[k_] for k_ in ("fwd_ms", "fwd_bwd_ms", "queries_per_s_fwd",
+                                       "queries_per_s_fwd_bwd", "fwd_algorithmic_bytes",
+                                       "fwd_effective_GBs", "fwd_compulsory_bytes", "fwd_hbm_frac",
+                                       "step_effective_GBs", "step_hbm_frac", "stage_ms",
+                                       "kernels")},
+        "roofline": roof,
+        "gather_ceiling": ceiling,
+        "wall_s_timed": round(t["wall_s"], 3),
         "pages_context": PAGES_CONTEXT,
-        "input_sha256": inputs.digest(x),
+        "input_sha256": r.sha,
     }
+    idx_main = r.idx
     if not args.no_variants:
-        result["variants"] = measure_variants(w, q, k, v, gamma, dout, idx, hip, lib, Z, torch,
-                                              args.variant_steps)
+        result["variants"] = measure_variants(w, r.q, r.k, r.v, r.gamma, r.dout, idx_main, hip, lib,
+                                              Z, torch, args.variant_steps)
+    x_main = r.x
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        configs = {}
+        for name, cw in inputs.CONFIGS.items():
+            if name in ("long_fwd", "long_fwd_bwd") and w.name in ("long_fwd", "long_fwd_bwd"):
+                s_ = {k_: v_ for k_, v_ in main_sum.items() if k_ != "kernels"}
+            else:
+                rr = Run(inputs.Workload(**{**cw.__dict__, "backward": True}), Z, torch)
+                s_ = summarise(rr, time_run(rr, lib, hip, args.steps, args.warmup), Z)
+                s_.pop("kernels")
+                del rr
+                torch.cuda.empty_cache()
+            if name == "long_fwd":  # the forward of the 65536-token workload (same inputs)
+                s_ = {k_: v_ for k_, v_ in s_.items() if not k_.startswith(("fwd_bwd", "step_"))
+                      and k_ != "queries_per_s_fwd_bwd"}
+            configs[name] = s_
+        result["configs"] = configs
+        result["memory"] = memory_footprint(w, Z, torch)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, x_main, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -228,6 +228,19 @@ zeta_status zeta_bwd_ex(const zeta_shape *shape, const zeta_select_opts *opts, c
  * must outlive the calls that record them.                                               */
 zeta_status zeta_set_stage_events(void *const *events, int32_t count);
 
+/* Measurement hook: the rate of the scattered row gathers that the gather and backward
+ * kernels make (whose rows are mostly L2 hits, so that rate, not HBM bandwidth, bounds them).
+ * `groups` groups of 16 lanes each read `rows_per_group` rows of `row_bytes` bytes from
+ * table [table_rows][row_bytes], 16 bytes per lane, the loads of eight rows in flight
+ * together, rows drawn uniformly by a counter-based hash of (seed, group, row number); each
+ * group writes one word folded from what it loaded to sink[group].  Bytes read per call:
+ * groups * rows_per_group * row_bytes.  table: device, 16-byte aligned; table_rows a power of
+ * two <= 2^32; row_bytes a multiple of 16 in [16, 256]; rows_per_group a multiple of 8 in
+ * [8, 2^20]; 1 <= groups <= 2^34; sink: device uint32 [groups].  Validated on the host.  */
+zeta_status zeta_probe_row_gather(const void *table, int64_t table_rows, int32_t row_bytes,
+                                  int64_t groups, int32_t rows_per_group, uint32_t seed,
+                                  uint32_t *sink, void *stream);
+
 /* Static description of a status code.                                                   */
 const char *zeta_status_string(zeta_status status);
 

@@ -553,6 +553,29 @@ zeta_status zeta_bwd(const zeta_shape* shape, const float* q, const float* k, co
                        workspace_bytes, stream);
 }
 
+zeta_status zeta_probe_row_gather(const void* table, int64_t table_rows, int32_t row_bytes,
+                                  int64_t groups, int32_t rows_per_group, uint32_t seed,
+                                  uint32_t* sink, void* stream) {
+    g_last_error.clear();
+    if (!table || !sink) return fail(ZETA_ERR_INVALID_ARGUMENT, "table or sink is NULL");
+    if (!aligned(table, 16) || !aligned(sink, 4))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "table must be 16-byte and sink 4-byte aligned");
+    if (table_rows < 1 || table_rows > (int64_t(1) << 32) || (table_rows & (table_rows - 1)) != 0)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "table_rows must be a power of two <= 2^32");
+    if (row_bytes < 16 || row_bytes > 256 || row_bytes % 16 != 0)
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "row_bytes must be a multiple of 16 in [16, 256]");
+    if (rows_per_group < 8 || rows_per_group % 8 != 0 || rows_per_group > (1 << 20))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "rows_per_group must be a multiple of 8 in [8, 2^20]");
+    if (groups < 1 || groups > (int64_t(1) << 34))
+        return fail(ZETA_ERR_INVALID_ARGUMENT, "groups must be in [1, 2^34]");
+    zeta_status st = preflight();
+    if (st != ZETA_OK) return st;
+    hipError_t e = zeta::launch_probe_row_gather(table, table_rows, row_bytes, groups,
+                                                 rows_per_group, seed, sink,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ZETA_OK : fail_hip("probe launch", e);
+}
+
 zeta_status zeta_set_stage_events(void* const* events, int32_t count) {
     g_last_error.clear();
     if (count < 0) return fail(ZETA_ERR_INVALID_ARGUMENT, "count must be >= 0");

@@ -126,6 +126,12 @@ size_t order_scratch_words(int64_t BH, int64_t N);
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
                         uint32_t* scratch, hipStream_t s);
 
+// Measurement: `groups` groups of 16 lanes each read rows_per_group rows (row_bytes bytes,
+// 16 per lane) drawn from table [table_rows] (a power of two); one word per group to sink.
+hipError_t launch_probe_row_gather(const void* table, int64_t table_rows, int row_bytes,
+                                   int64_t groups, int rows_per_group, uint32_t seed,
+                                   uint32_t* sink, hipStream_t s);
+
 struct BwdBuffers {
     float2* coef;     // [BH, N, topk] per selection slot {a_ij, c_ij}
     float* dg_row;    // [BHN] per-query dgamma contributions

@@ -37,6 +37,7 @@ ZETA_SELECT_CURVES = 2
 
 EXPORTS = (
     "zeta_workspace_bytes",
+    "zeta_probe_row_gather",
     "zeta_fwd_noalloc",
     "zeta_encode",
     "zeta_tree_levels",
@@ -133,6 +134,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeta_fwd_noalloc.restype = i32
     lib.zeta_bwd.argtypes = [sp, p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.zeta_bwd.restype = i32
+    lib.zeta_probe_row_gather.argtypes = [p, i64, i32, i64, i32, ctypes.c_uint32, p, p]
+    lib.zeta_probe_row_gather.restype = i32
     lib.zeta_set_stage_events.argtypes = [p, i32]
     lib.zeta_set_stage_events.restype = i32
     lib.zeta_status_string.argtypes = [i32]
@@ -377,6 +380,19 @@ def zeta_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Ten
                                    _ptr(idx), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                    _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv, dg
+
+
+def zeta_probe_row_gather(table: torch.Tensor, row_bytes: int, groups: int, rows_per_group: int,
+                          seed: int = 1, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement hook: scattered 16-lane row gathers from `table` (uint8 device tensor of
+    table_rows * row_bytes bytes); returns the per-group sink words."""
+    _dev(table, "table", torch.uint8)
+    rows = table.numel() // row_bytes
+    if sink is None:
+        sink = torch.empty(groups, dtype=torch.int32, device=table.device)
+    _check(load_library().zeta_probe_row_gather(_ptr(table), rows, row_bytes, groups,
+                                                rows_per_group, seed, _ptr(sink), _stream()))
+    return sink
 
 
 class ZetaAttention(torch.autograd.Function):

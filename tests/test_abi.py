@@ -145,6 +145,16 @@ def test_noalloc_validates_before_any_launch(lib):
     assert lib.zeta_workspace_bytes(ctypes.byref(fits), zeta.ZETA_WS_FWD) <= 128 << 20
 
 
+@pytest.mark.parametrize("args", [
+    (None, 1024, 256, 100, 32), (FAKE, 1000, 256, 100, 32), (FAKE, 1024, 8, 100, 32),
+    (FAKE, 1024, 272, 100, 32), (FAKE, 1024, 256, 0, 32), (FAKE, 1024, 256, 100, 12),
+    (ctypes.c_void_p(0x100008), 1024, 256, 100, 32),
+])
+def test_probe_validates_before_launch(lib, args):
+    table, rows, rb, groups, per = args
+    assert lib.zeta_probe_row_gather(table, rows, rb, groups, per, 1, FAKE, None) == 1
+
+
 def test_workspace_grows_with_shape(lib):
     a = lib.zeta_workspace_bytes(ctypes.byref(shape(N=1000)), zeta.ZETA_WS_FWD)
     b = lib.zeta_workspace_bytes(ctypes.byref(shape(N=4000)), zeta.ZETA_WS_FWD)

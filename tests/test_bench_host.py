@@ -43,10 +43,29 @@ def test_gather_bytes_closed_form():
     w = inputs.CONFIGS["long_fwd_bwd"]
     row = w.dv * (2 if w.v_dtype == inputs.BF16 else 4)
     BH = w.B * w.H
-    # per query: (m + 1) * (16 + row) -- index and key rows and value rows of m slots, plus
-    # the query point, the order entry and the output row
-    want = BH * (_sum_valid_slots(w.N, w.topk) + w.N) * (16 + row)
-    assert bench.kernel_bytes(w)["gather"] == pytest.approx(want, rel=0, abs=0.5)
+    # per query: 4m + 12 + 12m + m row + row -- index, key row and value row of each of the m
+    # selected slots, the query point and the output row
+    want = BH * (_sum_valid_slots(w.N, w.topk) * (16 + row) + w.N * (12 + row))
+    assert bench.algorithmic_bytes(w)["gather"] == pytest.approx(want, rel=0, abs=0.5)
+
+
+@pytest.mark.parametrize("name,fwd_mb", [("tiny", 10.5), ("multihead", 354), ("clustered", 11400),
+                                         ("long_fwd", 6280)])
+def test_forward_bytes_match_the_scope_table(name, fwd_mb):
+    # the forward totals of the method's byte model (encode + sort + select + gather), as
+    # tabulated per configuration: 10.5 MB, 354 MB, 11.40 GB, 6.28 GB (the table counts k
+    # slots for every query, the model here m = min(k, i+1): 1.4 % fewer bytes at N = 1024)
+    b = bench.algorithmic_bytes(inputs.CONFIGS[name])
+    got = (b["encode_order"] - 12 * inputs.CONFIGS[name].rows + b["tree"] + b["select"] +
+           b["gather"]) / 1e6
+    assert got == pytest.approx(fwd_mb, rel=0.02)
+
+
+@pytest.mark.parametrize("N,k,want", [(65536, 32, 11), (16384, 64, 8), (1024, 32, 5),
+                                      (1000, 64, 3), (100, 64, 0), (65536, 256, 8)])
+def test_stored_levels(N, k, want):
+    w = inputs.Workload("s", 1, 1, N, 8, k)
+    assert bench.stored_levels(w) == want
 
 
 def _count_bit_set(n, l):
