@@ -517,24 +517,6 @@ __device__ __forceinline__ bool make_item(uint2& rec, int64_t e, int64_t items,
     return true;
 }
 
-// Lanes of the wavefront whose 8-bit digit equals this lane's, among the valid ones: the
-// AND over the digit's bits of the ballot of that bit (or of its complement where the lane's
-// bit is 0).  Each bit's 0 / all-ones mask is a sign-extended bit field, so a bit costs a
-// compare, a field extract and an xor per 32-bit half (gfx950 folds the AND into v_bitop3).
-__device__ __forceinline__ uint64_t digit_peers(uint32_t digit, bool valid) {
-    const uint64_t v = __ballot(valid);
-    uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
-    uint32_t hi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(digit << (31 - b)) >> 31);
-        const uint64_t bal = __ballot(m != 0u);
-        lo &= ~(static_cast<uint32_t>(bal) ^ m);
-        hi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
-    }
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 // Digit counts of one tile of items.  Pass 0 takes every selection slot (items = N * topk)
 // and keeps the pairs; later passes take the first counts[bh] records.
 template <bool FIRST>
@@ -643,7 +625,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     for (int it = 0; it < kRadixItems; ++it) {
         const bool valid = (okmask >> it) & 1u;
         const uint32_t digit = valid ? (rec[it].x >> shift) & 255u : 0u;
-        const uint64_t peers = digit_peers(digit, valid);
+        const uint64_t peers = digit_peers<8>(digit, valid);
         // every lane reads the running count before the group's first lane advances it (LDS
         // operations of one wavefront take effect in program order)
         const uint32_t before = valid ? wcnt[wave][digit] : 0u;
@@ -825,7 +807,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
         for (int it = 0; it < kBucketItems; ++it) {
             const bool valid = c0 + wave * kWaveItems + it * 64 + lane < n;
             const uint32_t digit = rec[it].x >> 8;
-            const uint64_t peers = digit_peers(digit, valid);
+            const uint64_t peers = digit_peers<8>(digit, valid);
             const uint32_t before = valid ? wcnt[wave][digit] : 0u;
             if (valid && (peers & lt) == 0) wcnt[wave][digit] = before + __popcll(peers);
             lrank[it] = before + __popcll(peers & lt);

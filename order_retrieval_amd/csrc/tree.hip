@@ -16,94 +16,208 @@
 // The selection kernel walks the asc tree forward (codes >= the query) and the desc tree
 // backward (codes < the query), so both walks meet equal codes in ascending j order.
 //
-// Levels below `first` are not written (the selection reads short runs straight from the
-// codes); they are still formed in LDS on the way up.  Only the levels from
+// The keys are sorted on the curve by radix sort (rebuttal page, answer W3/A3: sorting is
+// linear by radix sort).  Build: levels up to 12 inside one workgroup per 4096-position tile
+// and tree (an LDS radix sort ranked by wavefront ballots, then every level as a stable
+// partition of the sorted tile by block), then one merge-path launch per higher level
+// (streaming: 8 B read and 8 B written per entry and tree).  Levels below `first` are not
+// written (the selection reads short runs straight from the codes).  Only the levels from
 // tree_store_base(levels, first) up are stored: level l of (b,h) sits at
 // tree + (bh * stored + l - base) * N, stored = levels - base.
-// Build: levels 0..10 inside one workgroup per 1024-entry tile (LDS rank merge: each entry
-// moves to its own index plus its rank in the sibling block; keys are unique, so this is
-// an exact merge), then one merge-path launch per higher level (streaming: 8 B read and
-// 8 B written per entry and tree).
 #include "zeta_internal.hpp"
+#include "xlane.hpp"
 
 namespace zeta {
 
-constexpr int kTileLog = 10;
+constexpr int kTileLog = 12;  // the tile stage builds levels up to 12 (4096-position tiles)
 constexpr int kTile = 1 << kTileLog;
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTile = 2048;  // merged outputs per workgroup
 constexpr int kMergePer = kMergeTile / kMergeThreads;
 static_assert(kMergeThreads == 256, "the split search runs two diagonals on 128 threads each");
 
-__device__ __forceinline__ int lds_lower_bound(const uint64_t* a, int n, uint64_t x) {
-    int lo = 0;
-    while (n > 0) {
-        int half = n >> 1;
-        if (a[lo + half] < x) {
-            lo += half + 1;
-            n -= half + 1;
-        } else {
-            n = half;
-        }
+// ---------------------------------------------------------------------------- radix tile
+// Tile stage as an LDS radix sort.  One workgroup per tile of 2^TL positions and tree.  The
+// tile's local indices are sorted by code with a stable LSD radix sort over 8-bit digits; each
+// pass ranks the items of every 64-item step of a wavefront by ballots (the lanes holding the
+// same digit, digit_peers) plus a running count per digit and wavefront, and scatters them in
+// LDS after one scan over the digits.  Stability makes the order (code, j ascending) when the
+// initial sequence is j ascending (asc tree) and (code, j descending) when it is j descending
+// (desc tree).  Level l of the tile is then the stable partition of that sorted sequence by
+// the block j >> l: the block's entries in sorted order, which is exactly the block sorted.
+// Partitions with at most 64 blocks rank by ballots the same way; levels with blocks of at
+// most 32 positions rank each entry by counting the smaller entries of its block.
+constexpr int kRTThreads = 1024;
+constexpr int kRTWaves = kRTThreads / 64;
+
+// Inclusive sum over the workgroup's first 256 threads (one value each; the others pass 0).
+// `part` holds one word per wavefront.
+__device__ __forceinline__ uint32_t tile_scan256(uint32_t v, uint32_t* part) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    return lo;
+    if (lane == 63) part[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave && w < 4; ++w) x += part[w];
+    return x;
 }
 
-template <typename CT, int S>
-__global__ void __launch_bounds__(kTile) zeta_tree_tile_kernel(const CT* __restrict__ zk,
-                                                              uint64_t* __restrict__ asc,
-                                                              uint64_t* __restrict__ desc,
-                                                              int64_t N, int stored, int top,
-                                                              int first) {
-    constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
-    __shared__ uint64_t buf[2][2][kTile];  // [tree][ping-pong][entry]
-    const int64_t bh = blockIdx.y;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
-    const int n = static_cast<int>(N - base < kTile ? N - base : kTile);
-    const CT* zrow = zk + bh * N + base;
-    // level l at (l - first) N: `first` is also the lowest stored level
-    uint64_t* tA = asc + bh * stored * N + base;
-    uint64_t* tD = desc + bh * stored * N + base;
+// digit_peers with a digit of `bits` bits (0 <= bits <= 6), decided at run time.
+__device__ __forceinline__ uint64_t group_peers(uint32_t g, int bits, bool valid) {
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
+    uint32_t hi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
+    for (int b = 0; b < bits; ++b) {
+        const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(g << (31 - b)) >> 31);
+        const uint64_t bal = __ballot(m != 0u);
+        lo &= ~(static_cast<uint32_t>(bal) ^ m);
+        hi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
+    }
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
-    for (int e = threadIdx.x; e < n; e += blockDim.x) {
-        const uint64_t j = static_cast<uint64_t>(base + e);
-        const uint64_t c = static_cast<uint64_t>(zrow[e]) << S;
-        const uint64_t ka = c | j, kd = c | (~j & kJMask);
-        buf[0][0][e] = ka;
-        buf[1][0][e] = kd;
-        if (first == 0) {
-            tA[e] = ka;
-            tD[e] = kd;
-        }
+template <typename CT, int S, int TL>
+__global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
+    const CT* __restrict__ zk, uint64_t* __restrict__ asc, uint64_t* __restrict__ desc,
+    int64_t N, int stored, int top, int first) {
+    constexpr int T = 1 << TL;
+    constexpr int kWaveItems = T / kRTWaves;  // sequence positions of one wavefront
+    constexpr int kItems = kWaveItems / 64;   // 64-item steps of one wavefront
+    constexpr int kCodeBits = S == 32 ? 30 : 36;
+    constexpr int kPasses = (kCodeBits + 7) / 8;
+    constexpr int kMaxGroups = 64;            // partitions ranked by ballots
+    constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
+    static_assert(kItems >= 1, "at least one step per wavefront");
+    static_assert(T / 64 <= kMaxGroups, "partitions of blocks above 32 entries ranked by ballots");
+    __shared__ CT zc[T];                   // codes by local index
+    __shared__ uint16_t seq[2][T];         // local indices in sequence order (ping-pong)
+    __shared__ uint16_t stage[T];          // one level of the tile, as local indices
+    __shared__ uint32_t wcnt[kRTWaves][256];
+    __shared__ uint32_t part[kRTWaves];
+    const bool dsc = blockIdx.z != 0;
+    const int64_t bh = blockIdx.y;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * T;
+    const int n = static_cast<int>(N - base < T ? N - base : T);
+    uint64_t* tree = (dsc ? desc : asc) + bh * stored * N + base;  // level l at (l - first) N
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    auto entry = [&](int i) -> uint64_t {
+        const uint64_t j = static_cast<uint64_t>(base + i);
+        return (static_cast<uint64_t>(zc[i]) << S) | (dsc ? (~j & kJMask) : j);
+    };
+
+    for (int e = tid; e < T; e += kRTThreads) {
+        zc[e] = e < n ? zk[bh * N + base + e] : CT(0);
+        seq[0][e] = static_cast<uint16_t>(e < n ? (dsc ? n - 1 - e : e) : e);
     }
     __syncthreads();
+    if (first == 0)
+        for (int e = tid; e < n; e += kRTThreads) tree[e] = entry(e);
 
+    // stable LSD radix sort of the sequence by code
     int cur = 0;
-    for (int l = 0; l < top; ++l) {
-        const int s = 1 << l;
-        for (int e = threadIdx.x; e < n; e += blockDim.x) {
-            const int run0 = e & ~(2 * s - 1);
-            const bool inB = (e & s) != 0;
-            const int own = e - run0 - (inB ? s : 0);
-            const int sib0 = inB ? run0 : run0 + s;
-            int sibLen = n - sib0;
-            sibLen = sibLen < 0 ? 0 : (sibLen > s ? s : sibLen);
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int shift = 8 * pass;
+        if (tid < 256)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint64_t x = buf[t][cur][e];
-                const int r = lds_lower_bound(&buf[t][cur][sib0], sibLen, x);
-                buf[t][cur ^ 1][run0 + own + r] = x;
+            for (int w = 0; w < kRTWaves; ++w) wcnt[w][tid] = 0;
+        __syncthreads();
+        uint16_t idx[kItems];
+        uint32_t dig[kItems], rank[kItems];
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int pos = wave * kWaveItems + it * 64 + lane;
+            const bool valid = pos < n;
+            idx[it] = seq[cur][pos];
+            dig[it] = valid ? static_cast<uint32_t>(zc[idx[it]] >> shift) & 255u : 0u;
+            const uint64_t peers = digit_peers<8>(dig[it], valid);
+            // every lane reads the running count before the group's first lane advances it
+            // (LDS operations of one wavefront take effect in program order)
+            const uint32_t before = valid ? wcnt[wave][dig[it]] : 0u;
+            if (valid && (peers & lt) == 0) wcnt[wave][dig[it]] = before + __popcll(peers);
+            rank[it] = before + __popcll(peers & lt);
+        }
+        __syncthreads();
+        {
+            uint32_t c = 0;
+            if (tid < 256)
+#pragma unroll
+                for (int w = 0; w < kRTWaves; ++w) c += wcnt[w][tid];
+            uint32_t run = tile_scan256(c, part) - c;  // digit tid's first position
+            if (tid < 256)
+#pragma unroll
+                for (int w = 0; w < kRTWaves; ++w) {
+                    const uint32_t t = wcnt[w][tid];
+                    wcnt[w][tid] = run;
+                    run += t;
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kItems; ++it)
+            if (wave * kWaveItems + it * 64 + lane < n) seq[cur ^ 1][wcnt[wave][dig[it]] + rank[it]] = idx[it];
+        __syncthreads();
+        cur ^= 1;
+    }
+
+    // levels first .. top: the stable partition of the sorted sequence by block
+    for (int l = first > 1 ? first : 1; l <= top; ++l) {
+        uint64_t* out = tree + static_cast<int64_t>(l - first) * N;
+        const int groups = T >> l;
+        if ((1 << l) <= 32) {
+            // small blocks: an entry's place is the number of smaller entries of its block
+            for (int i = tid; i < n; i += kRTThreads) {
+                const int b0 = i >> l << l;
+                const int b1 = b0 + (1 << l) < n ? b0 + (1 << l) : n;
+                const CT c = zc[i];
+                int r = 0;
+                for (int u = b0; u < b1; ++u) {
+                    const CT cu = zc[u];
+                    r += (cu < c || (cu == c && (dsc ? u > i : u < i))) ? 1 : 0;
+                }
+                out[b0 + r] = entry(i);
+            }
+            continue;
+        }
+        int bits = 0;
+        while ((1 << bits) < groups) ++bits;
+#pragma unroll
+        for (int w = 0; w < kRTWaves; ++w)
+            if (tid < kMaxGroups) wcnt[w][tid] = 0;
+        __syncthreads();
+        uint16_t idx[kItems];
+        uint32_t grp[kItems], rank[kItems];
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int pos = wave * kWaveItems + it * 64 + lane;
+            const bool valid = pos < n;
+            idx[it] = seq[cur][pos];
+            grp[it] = valid ? static_cast<uint32_t>(idx[it]) >> l : 0u;
+            const uint64_t peers = group_peers(grp[it], bits, valid);
+            const uint32_t before = valid ? wcnt[wave][grp[it]] : 0u;
+            if (valid && (peers & lt) == 0) wcnt[wave][grp[it]] = before + __popcll(peers);
+            rank[it] = before + __popcll(peers & lt);
+        }
+        __syncthreads();
+        if (tid < groups) {
+            uint32_t run = static_cast<uint32_t>(tid) << l;  // block tid starts at tid 2^l
+#pragma unroll
+            for (int w = 0; w < kRTWaves; ++w) {
+                const uint32_t t = wcnt[w][tid];
+                wcnt[w][tid] = run;
+                run += t;
             }
         }
         __syncthreads();
-        cur ^= 1;
-        if (l + 1 < first) continue;  // level not read by the caller: stays in LDS only
-        uint64_t* oA = tA + static_cast<int64_t>(l + 1 - first) * N;
-        uint64_t* oD = tD + static_cast<int64_t>(l + 1 - first) * N;
-        for (int e = threadIdx.x; e < n; e += blockDim.x) {
-            oA[e] = buf[0][cur][e];
-            oD[e] = buf[1][cur][e];
-        }
+#pragma unroll
+        for (int it = 0; it < kItems; ++it)
+            if (wave * kWaveItems + it * 64 + lane < n) stage[wcnt[wave][grp[it]] + rank[it]] = idx[it];
+        __syncthreads();
+        for (int e = tid; e < n; e += kRTThreads) out[e] = entry(stage[e]);
+        __syncthreads();
     }
 }
 
@@ -235,8 +349,10 @@ static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, con
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
     const int base = tree_store_base(levels, first);
     const int stored = levels > base ? levels - base : 0;
-    hipLaunchKernelGGL((zeta_tree_tile_kernel<CT, S>), grid, dim3(kTile), 0, s, zk, tree_asc,
-                       tree_desc, N, stored, top_tile, base);
+    // one workgroup per tile and tree (z = 0 asc, z = 1 desc)
+    dim3 g3(grid.x, grid.y, 2);
+    hipLaunchKernelGGL((zeta_tree_radix_tile_kernel<CT, S, kTileLog>), g3, dim3(kRTThreads), 0, s,
+                       zk, tree_asc, tree_desc, N, stored, top_tile, base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int l = top_tile; l + 1 < levels; ++l) {

@@ -77,4 +77,24 @@ __device__ __forceinline__ float group_sum(float x, int G) {
     return x;
 }
 
+// Lanes of the wavefront whose B-bit digit equals this lane's, among the valid ones: the AND
+// over the digit's bits of the ballot of that bit (or of its complement where the lane's bit
+// is 0).  Each bit's 0 / all-ones mask is a sign-extended bit field, so a bit costs a compare,
+// a field extract and an xor per 32-bit half (gfx950 folds the AND into v_bitop3).  With the
+// lanes below this one masked off, the popcount is the lane's stable rank among its peers.
+template <int B>
+__device__ __forceinline__ uint64_t digit_peers(uint32_t digit, bool valid) {
+    const uint64_t v = __ballot(valid);
+    uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
+    uint32_t hi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(digit << (31 - b)) >> 31);
+        const uint64_t bal = __ballot(m != 0u);
+        lo &= ~(static_cast<uint32_t>(bal) ^ m);
+        hi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
+    }
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 }  // namespace zeta
