@@ -427,8 +427,13 @@ def ceiling_summary(d: str) -> None:
         for ln in open(log):
             if ln.startswith("{"):
                 line = json.loads(ln)
-    kt = trace_kernels(d)
-    probe = kt.get("zeta_probe_row_gather_kernel")
+    durs = []  # probe dispatches in launch order: 3 warm-up then the timed ones, per table
+    for f in glob.glob(os.path.join(d, "*kernel_trace.csv")):
+        for r in csv.DictReader(open(f)):
+            if kernel_base(r["Kernel_Name"]) == "zeta_probe_row_gather_kernel":
+                durs.append((int(r["Start_Timestamp"]),
+                             (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3))
+    durs = [u for _, u in sorted(durs)]
     lines = ["# Row-gather ceiling (zeta_probe_row_gather)", "",
              "What bounds the gather and both backward passes: groups of 16 lanes each read 32 "
              "rows of 256 bytes drawn uniformly from a table, 16 bytes per lane, eight rows' "
@@ -440,13 +445,15 @@ def ceiling_summary(d: str) -> None:
              "Command (from the repository root; stdout to run.log in the same folder):", "",
              f"    {CEILING_CMD.format(d=d)}", f"    python3 bench.py --ceiling-summary {d}", ""]
     if line is not None:
-        lines += ["| table | launches timed | GB/s (HIP events) | us per launch |", "|---|---|---|---|"]
+        lines += ["| table | launches timed | GB/s (HIP events) | us per launch (HIP events) | "
+                  "us per launch (kernel trace, same launches) |", "|---|---|---|---|---|"]
+        at = 0
         for name, r in line["gather_ceiling"].items():
-            lines.append(f"| {name} | {r['launches']} | {r['GBs']:.0f} | {r['us']:.1f} |")
-    if probe is not None:
-        lines += ["", f"Kernel trace of the same run: zeta_probe_row_gather_kernel, {probe['n']} "
-                  f"dispatches, average {probe['us']:.1f} us (all table sizes together; the table "
-                  "above splits them by size).", ""]
+            n = r["launches"]
+            timed = durs[at + 3: at + 3 + n]
+            at += 3 + n
+            tr_us = f"{sum(timed) / len(timed):.1f}" if len(timed) == n else "-"
+            lines.append(f"| {name} | {n} | {r['GBs']:.0f} | {r['us']:.1f} | {tr_us} |")
     with open(os.path.join(ROOT, "profiles", "gather_ceiling.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
