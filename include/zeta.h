@@ -13,8 +13,11 @@
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers to dense row-major memory owned by the
- *     caller.  The library allocates nothing and keeps no state between calls; scratch
- *     memory is the caller's workspace (size from zeta_workspace_bytes).  Calls are
+ *     caller.  The library allocates nothing; scratch memory is the caller's workspace (size
+ *     from zeta_workspace_bytes), except for zeta_fwd_noalloc, whose scratch the library
+ *     holds per GPU.  State kept between calls: a thread-local error string, the
+ *     thread-local event list of the measurement hook zeta_set_stage_events (off unless a
+ *     caller sets it), and zeta_fwd_noalloc's per-device scratch address.  Calls are
  *     re-entrant; calls that share a workspace must not overlap.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it
  *     asynchronously; no call synchronises the host.
