@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(64) zeta_radix_scan_kernel(uint32_t* __restric
 // staged in LDS in that order and written out with consecutive lanes on consecutive slots
 // of a digit's run, so the global writes are coalesced.  Pass 0 also records the number of
 // pairs of each (b,h) in counts[bh] (the sum of the digit totals).
-template <bool FIRST>
+template <bool FIRST, bool PACK>
 __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t slots,
     uint32_t* __restrict__ counts, int64_t in_stride, int shift, int64_t tiles, PairSpec ps,
@@ -674,12 +674,18 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     __syncthreads();
 
     uint2* out = rout + bh * P;
+    uint32_t* out32 = reinterpret_cast<uint32_t*>(rout) + bh * P;
 #pragma unroll
     for (int it = 0; it < kRadixItems; ++it) {
         const int t = it * kRadixThreads + tid;  // slot in the staged tile
         if (t < static_cast<int>(tile_items)) {
             const uint2 r = stage[t];
-            out[delta[(r.x >> shift) & 255u] + t] = r;
+            // packed: the low byte of j is the bucket the record lands in, so a 4-byte record
+            // holds the high byte of j (bits 24..31) and the slot (below 2^24)
+            if constexpr (PACK)
+                out32[delta[(r.x >> shift) & 255u] + t] = ((r.x >> 8) << 24) | r.y;
+            else
+                out[delta[(r.x >> shift) & 255u] + t] = r;
         }
     }
 }
@@ -687,7 +693,9 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
 // ---------------------------------------------------------------------------- 3. segments
 // Keys below 2^16: the one global pass sorts the records stably by the low byte of j, so
 // bucket b holds the pairs of the keys j with j mod 256 = b (every bucket about 1/256 of the
-// pairs, whatever the key popularity) in ascending slot order.  One workgroup per bucket
+// pairs, whatever the key popularity) in ascending slot order.  The bucket implies the low
+// byte, so that pass writes 4-byte records: the high byte of j above a 24-bit slot.  One
+// workgroup per bucket
 // finishes the sort on the high byte of j: it counts the bucket's digits (one per key),
 // writes every key's segment [begin, end) from their exclusive scan, and scatters the records
 // stably a tile at a time (ranked by ballots and staged in LDS like a radix tile), so the
@@ -717,7 +725,7 @@ constexpr int kBucketItems = 12;
 constexpr int kBucketTile = kRadixThreads * kBucketItems;
 
 __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
-    const uint2* __restrict__ rin, const uint32_t* __restrict__ totals, int64_t N, int64_t P,
+    const uint32_t* __restrict__ rin, const uint32_t* __restrict__ totals, int64_t N, int64_t P,
     uint32_t* __restrict__ slots, uint32_t* __restrict__ begin, uint32_t* __restrict__ end) {
     static_assert(kRadixThreads == 256, "one thread per digit");
     constexpr int kWaves = kRadixThreads / 64;
@@ -744,7 +752,12 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
         __syncthreads();
     }
     const uint32_t n = s1 - s0;
-    const uint2* rb = rin + bh * P + s0;
+    const uint32_t* rb = rin + bh * P + s0;
+    // record e of the bucket as {high byte of j << 8, slot}, from its 4-byte form
+    auto rec_at = [&](uint32_t e) -> uint2 {
+        const uint32_t w = rb[e];
+        return make_uint2((w >> 24) << 8, w & 0xFFFFFFu);
+    };
 
     // digit counts over the bucket; the first tile stays in registers for the scatter
     run[tid] = 0;
@@ -756,7 +769,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
 #pragma unroll
         for (int it = 0; it < kBucketItems; ++it) {
             const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
-            rec[it] = rb[e < n ? e : n - 1];
+            rec[it] = rec_at(e < n ? e : n - 1);
         }
 #pragma unroll
         for (int it = 0; it < kBucketItems; ++it) keep(rec[it]);
@@ -772,7 +785,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_bucket_sort_kernel(
 #pragma unroll
             for (int it = 0; it < kBucketItems; ++it) {
                 const uint32_t e = c0 + wave * kWaveItems + it * 64 + lane;
-                dg[it] = rb[e < n ? e : n - 1].x;
+                dg[it] = rec_at(e < n ? e : n - 1).x;
             }
 #pragma unroll
             for (int it = 0; it < kBucketItems; ++it) keep(dg[it]);
@@ -1134,10 +1147,17 @@ size_t bwd_pairs_per_head(int64_t N, int topk, bool causal) {
 
 int64_t bwd_tiles_per_head(int64_t items) { return (items + kRadixTile - 1) / kRadixTile; }
 
+bool bwd_records_packed(int64_t N, int topk) {
+    // keys below 2^16 (the bucket holds their low byte) and slots below 2^24
+    return N <= (int64_t(1) << 16) && N * topk <= (int64_t(1) << 24);
+}
+static_assert(int64_t(1) << 16 << 8 == int64_t(1) << 24 && kMaxTopK <= 256,
+              "keys below 2^16 with at most 256 slots each have slots below 2^24");
+
 
 // items: slots of pass 0 (N * topk), else the upper bound P of the pairs per (b,h) (the
 // grid size; the kernels stop at the device-side count).
-template <bool FIRST>
+template <bool FIRST, bool PACK = false>
 static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t items,
                        int64_t stride, int shift, const PairSpec& ps, const BwdBuffers& ws,
                        uint2* rout, hipStream_t s) {
@@ -1147,7 +1167,7 @@ static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t
                        items, ws.counts, stride, shift, tiles, ps, ws.hist);
     hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64), 0, s,
                        ws.hist, tiles, ws.totals);
-    hipLaunchKernelGGL(zeta_radix_scatter_kernel<FIRST>, grid, dim3(kRadixThreads), 0, s, idx, rin,
+    hipLaunchKernelGGL((zeta_radix_scatter_kernel<FIRST, PACK>), grid, dim3(kRadixThreads), 0, s, idx, rin,
                        items, ws.counts, stride, shift, tiles, ps, ws.hist, ws.totals, ws.P, rout);
 }
 
@@ -1174,17 +1194,19 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     while ((int64_t(1) << bits) < N) ++bits;
     const PairSpec ps{topk, causal ? 1 : 0, N, make_div(static_cast<uint32_t>(topk))};
     KeySegments sg{};
-    radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
     if (bits <= 16) {
-        // one global pass on the low byte of j, then one workgroup per low-byte bucket
+        // one global pass on the low byte of j writing 4-byte records (N k <= 2^24 here,
+        // since topk <= 256), then one workgroup per low-byte bucket
+        radix_pass<true, true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
         uint32_t* sl = reinterpret_cast<uint32_t*>(ws.rec1);
         hipLaunchKernelGGL(zeta_bucket_sort_kernel,
                            dim3(static_cast<unsigned>(N < 256 ? N : 256), static_cast<unsigned>(BH)),
-                           dim3(kRadixThreads), 0, s, ws.rec0, ws.totals, N, ws.P, sl, ws.offs,
-                           ws.ends);
+                           dim3(kRadixThreads), 0, s, reinterpret_cast<const uint32_t*>(ws.rec0),
+                           ws.totals, N, ws.P, sl, ws.offs, ws.ends);
         sg = KeySegments{sl, 1, ws.offs, ws.ends};
     } else {
         // LSD passes over every byte of j, then the segment starts from the sorted keys
+        radix_pass<true>(BH, idx, nullptr, N * topk, N * topk, 0, ps, ws, ws.rec0, s);
         uint2* cur = ws.rec0;
         for (int shift = 8; shift < bits; shift += 8) {
             uint2* nxt = cur == ws.rec0 ? ws.rec1 : ws.rec0;

@@ -208,7 +208,8 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
     // bits; otherwise it takes only the final 4-byte slot list
     int key_bits = 0;
     while ((int64_t(1) << key_bits) < N) ++key_bits;
-    p.r0 = take(8 * BH * p.P);
+    // 4-byte records from the first radix pass when keys fit 16 bits, else 8-byte ones
+    p.r0 = take((zeta::bwd_records_packed(N, static_cast<int>(K)) ? 4 : 8) * BH * p.P);
     p.r1 = take((key_bits <= 16 ? 4 : 8) * BH * p.P);
     p.hist = take(sizeof(uint32_t) * BH * 256 * p.tiles);
     p.totals = take(sizeof(uint32_t) * BH * 256);

@@ -153,6 +153,8 @@ struct BwdBuffers {
 };
 size_t bwd_pairs_per_head(int64_t N, int topk, bool causal);
 int64_t bwd_tiles_per_head(int64_t P);
+// Keys below 2^16 and slots below 2^24: the first radix pass writes 4-byte records.
+bool bwd_records_packed(int64_t N, int topk);
 int64_t dgamma_chunks(int64_t B, int64_t N);
 hipError_t launch_bwd(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk, bool causal, bool bf16,
                       const float* q, const float* k, const void* v, const float* gamma,
