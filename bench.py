@@ -98,7 +98,9 @@ def variant_select_bytes(w: inputs.Workload, mode: str, causal: bool = True, chu
     return curves * one + BH * N * (curves * per * 4 + 4 * k)
 
 
-VARIANTS = [  # name, zeta_select_opts fields
+VARIANTS = [  # name, zeta_select_opts fields (topk: a wider selection of the same workload)
+    ("exact_k128", dict(mode=0, causal=True, topk=128)),
+    ("exact_k256", dict(mode=0, causal=True, topk=256)),
     ("exact_noncausal", dict(mode=0, causal=False)),
     ("exact_12bit", dict(mode=0, causal=True, bits=12)),
     ("chunked_4", dict(mode=1, chunks=4)),
@@ -533,21 +535,23 @@ def measure_variants(w, q, k, v, gamma, dout, idx_exact, hip, lib, Z, torch, ste
     out = torch.empty_like(v)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty((w.H,), dtype=torch.float32, device=q.device))
-    shape = Z.make_shape(w.B, w.H, N, w.dv, K, Z.ZETA_BF16 if v.dtype == torch.bfloat16 else Z.ZETA_F32)
     for name, f in VARIANTS:
+        KK = f.get("topk", K)  # a wider selection of the same workload
+        shape = Z.make_shape(w.B, w.H, N, w.dv, KK,
+                             Z.ZETA_BF16 if v.dtype == torch.bfloat16 else Z.ZETA_F32)
         o = Z.select_opts(f.get("mode", 0), causal=f.get("causal", True), bits=f.get("bits", 10),
                           chunks=f.get("chunks", 0), curves=f.get("curves", 0))
         ws_f = Z.workspace(shape, Z.ZETA_WS_FWD, q.device, o)
         ws_b = Z.workspace(shape, Z.ZETA_WS_BWD, q.device, o)
-        idx = torch.empty((w.B, w.H, N, K), dtype=torch.int32, device=q.device)
+        idx = torch.empty((w.B, w.H, N, KK), dtype=torch.int32, device=q.device)
         for _ in range(2):
-            Z.zeta_fwd_ex(q, k, v, gamma, K, o, ws=ws_f, out=out, idx=idx)
+            Z.zeta_fwd_ex(q, k, v, gamma, KK, o, ws=ws_f, out=out, idx=idx)
             Z.zeta_bwd_ex(q, k, v, gamma, idx, dout, o, ws=ws_b, grads=grads)
         ev = [(hip.create(6), hip.create(6)) for _ in range(steps)]
         torch.cuda.synchronize()
         for ef, eb in ev:
             lib.zeta_set_stage_events(ef, 6)
-            Z.zeta_fwd_ex(q, k, v, gamma, K, o, ws=ws_f, out=out, idx=idx)
+            Z.zeta_fwd_ex(q, k, v, gamma, KK, o, ws=ws_f, out=out, idx=idx)
             lib.zeta_set_stage_events(eb, 6)
             Z.zeta_bwd_ex(q, k, v, gamma, idx, dout, o, ws=ws_b, grads=grads)
             lib.zeta_set_stage_events(None, 0)
@@ -560,16 +564,22 @@ def measure_variants(w, q, k, v, gamma, dout, idx_exact, hip, lib, Z, torch, ste
             hip.destroy(ef)
             hip.destroy(eb)
         mode = ["exact", "chunked", "curves"][f.get("mode", 0)]
-        sb = variant_select_bytes(w, mode, f.get("causal", True), f.get("chunks", 0),
+        wk = inputs.Workload(**{**w.__dict__, "topk": KK})
+        sb = variant_select_bytes(wk, mode, f.get("causal", True), f.get("chunks", 0),
                                   f.get("curves", 0), f.get("bits", 10))
-        sel_rows = idx.reshape(BH, N, K)[:, rows]
+        sel_rows = idx.reshape(BH, N, KK)[:, rows]
         r = {"select_stages_ms": round(sel, 4), "select_kernel_ms": round(sel_k, 4),
              "fwd_ms": round(fwd, 4), "fwd_bwd_ms": round(fwd + bwd, 4),
              "select_algorithmic_GBs": round(sb / ((sel if mode == "curves" else sel_k) * 1e-3)
-                                             / 1e9, 1),
-             "recall_vs_exact_causal": round(_recall(sel_rows, exact_rows, torch), 4),
-             "recall_vs_euclidean": round(_recall(sel_rows, eu_causal if f.get("causal", True)
-                                                  else eu_all, torch), 4)}
+                                             / 1e9, 1)}
+        if KK == K:
+            r["recall_vs_exact_causal"] = round(_recall(sel_rows, exact_rows, torch), 4)
+            r["recall_vs_euclidean"] = round(_recall(sel_rows, eu_causal if f.get("causal", True)
+                                                     else eu_all, torch), 4)
+        else:  # the exact top-KK against the Euclidean top-KK of the same queries
+            r["topk"] = KK
+            r["recall_vs_euclidean"] = round(
+                _recall(sel_rows, _euclid_topk(q, k, rows, KK, True, torch), torch), 4)
         if mode == "curves":  # stage 3 spans the later curves and the merge
             r["note"] = "select_kernel_ms covers curves 2..P and the merge; GB/s over all stages"
         res[name] = r
