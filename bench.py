@@ -57,20 +57,6 @@ def valid_slots(w: inputs.Workload) -> np.ndarray:
     return np.minimum(np.arange(w.N, dtype=np.int64) + 1, w.topk)
 
 
-def select_run_bytes(w: inputs.Workload) -> float:
-    """Per (b,h), as the kernel reads them: for every query, the sorted runs of its causal
-    prefix (set bits of i+1): a binary search (floor(log2 s)+1 probes of 8 B) and two k-wide
-    windows (<= s entries of 8 B) per run, plus the query code (4 B) and the written index
-    row (4k B)."""
-    i1 = np.arange(1, w.N + 1, dtype=np.int64)
-    total = np.zeros(w.N, dtype=np.float64)
-    for l in range(int(np.log2(w.N)) + 1):
-        s = 1 << l
-        has = (i1 >> l) & 1
-        total += has * (8.0 * (l + 1) + 8.0 * min(2 * w.topk, s))
-    return float((total + 4 + 4 * w.topk).sum())
-
-
 def variant_select_bytes(w: inputs.Workload, mode: str, causal: bool = True, chunks: int = 0,
                          curves: int = 0, bits: int = 10) -> float:
     """Bytes of one selection launch (all (b,h)) of a variant, counted as the kernels read
@@ -688,10 +674,6 @@ class Run:
         self.Z.zeta_bwd(self.q, self.k, self.v, self.gamma, self.idx, self.dout, ws=self.ws_b,
                         grads=self.grads)
 
-    def tensor_bytes(self) -> int:
-        ts = (self.q, self.k, self.v, self.gamma, self.dout, self.out, self.idx) + self.grads
-        return int(sum(t.numel() * t.element_size() for t in ts))
-
 
 def time_run(r: Run, lib, hip, steps: int, warmup: int) -> dict:
     """Stage times (HIP events the library records between its stages), the fwd+bwd step
@@ -750,7 +732,7 @@ def stored_levels(w: inputs.Workload) -> int:
     return max(0, L - base)
 
 
-def summarise(r: Run, t: dict, Z) -> dict:
+def summarise(r: Run, t: dict) -> dict:
     """Per-workload figures: times, queries/s, bytes and fractions."""
     w = r.w
     alg = algorithmic_bytes(w)
@@ -788,7 +770,7 @@ def summarise(r: Run, t: dict, Z) -> dict:
     }
 
 
-def roofline(summary: dict, w: inputs.Workload, ceiling: dict) -> dict:
+def roofline(summary: dict, ceiling: dict) -> dict:
     """The dominant single-kernel stage against what bounds it.  The row kernels gather rows
     that are mostly L2 hits, so their ceiling is the measured rate of such gathers (an
     L2-resident table); the selection is bounded by VALU issue and reported against HBM."""
@@ -929,9 +911,9 @@ def main() -> int:
     r = Run(w, Z, torch)
     torch.cuda.synchronize()
     t = time_run(r, lib, hip, args.steps, args.warmup)
-    main_sum = summarise(r, t, Z)
+    main_sum = summarise(r, t)
     ceiling = measure_ceiling(Z, torch)
-    roof = roofline(main_sum, w, ceiling)
+    roof = roofline(main_sum, ceiling)
     result = {
         "metric": METRIC,
         "value": round(t["step_ms"], 4),
@@ -974,7 +956,7 @@ def main() -> int:
                 s_ = {k_: v_ for k_, v_ in main_sum.items() if k_ != "kernels"}
             else:
                 rr = Run(inputs.Workload(**{**cw.__dict__, "backward": True}), Z, torch)
-                s_ = summarise(rr, time_run(rr, lib, hip, args.steps, args.warmup), Z)
+                s_ = summarise(rr, time_run(rr, lib, hip, args.steps, args.warmup))
                 s_.pop("kernels")
                 del rr
                 torch.cuda.empty_cache()

@@ -84,7 +84,8 @@ def test_select_bytes_closed_form(name):
     for l in range(w.N.bit_length()):
         want += _count_bit_set(w.N, l) * (8.0 * (l + 1) + 8.0 * min(2 * k, 1 << l))
     want += w.N * (4 + 4 * k)
-    assert bench.select_run_bytes(w) == pytest.approx(want, rel=1e-12)
+    got = bench.variant_select_bytes(w, "exact") / (w.B * w.H)
+    assert got == pytest.approx(want, rel=1e-12)
 
 
 def test_kernel_base_names():
