@@ -16,14 +16,15 @@
 // the first k of every walk gives the exact answer.
 //
 // The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
-// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 64,
-// so a lane holds 8 or 16 entries in registers and more wavefronts fit; L = 1 below; a whole
-// 16-lane row for K = 128 and 256, 8 or 16 entries per lane).  A
+// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 8
+// for K = 64, so a lane holds 8 entries in registers and more wavefronts fit; L = 1 below; a
+// whole 16-lane row for K = 128 and 256, 8 or 16 entries per lane).  A
 // walk's K candidates are merged with one bitonic step: elementwise min against the
 // reversed candidates (each lane loads its own contiguous block of the walk) leaves a
 // bitonic sequence of the K smallest, which log2(K) compare-exchange stages sort; the stages
 // whose stride spans lanes exchange values with DPP quad permutes (lanes 4 or 8 apart: a
-// ds_swizzle, which moves data between lanes without touching LDS memory).  A walk whose first
+// ds_swizzle, which moves data between lanes without touching LDS memory; broadcasts inside
+// a group of 8 are ds_swizzles too, inside a 16-lane row DPP row broadcasts).  A walk whose first
 // candidate cannot beat the current K-th is skipped, decided from values the search already
 // holds.  The runs are taken in groups: with several lanes per query each lane
 // binary-searches its own run of the group (with one lane, kSearchGroup runs advance in
@@ -39,6 +40,7 @@ constexpr int kChunk = 8;        // candidates of a walk loaded per step (regist
 constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (chunked search)
 constexpr int kInsert = 2;       // walk candidates merged by insertion when no more can enter
 constexpr int kInsert2 = 3;      // the second insertion tier (lane groups of 4 or more lanes)
+constexpr int kLanes64 = 8;      // lanes per query of the K = 64 list (8 entries per lane)
 
 // One word of lane `lane ^ D` (D = 1, 2: a DPP quad permute that the compiler can fold into
 // the instruction consuming it; D = 4, 8: a ds_swizzle in bitmask mode, and-mask 31 with
@@ -69,6 +71,15 @@ __device__ __forceinline__ uint64_t pack64(uint32_t lo, uint32_t hi) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// One word of lane SRC of this lane's aligned group of 8 (ds_swizzle in bit-mask mode:
+// source lane = (lane & 0x18) | SRC inside the 32-lane half).
+template <int SRC>
+__device__ __forceinline__ uint32_t group8_lane32(uint32_t x) {
+    static_assert(SRC >= 0 && SRC < 8, "a group has 8 lanes");
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_ds_swizzle(static_cast<int>(x), 0x18 | (SRC << 5)));
+}
+
 // One word of lane SRC of this 16-lane row (DPP row_newbcast).
 template <int SRC>
 __device__ __forceinline__ uint32_t row_lane32(uint32_t x) {
@@ -81,9 +92,13 @@ __device__ __forceinline__ uint32_t row_lane32(uint32_t x) {
 // 16-lane row).
 template <int L>
 __device__ __forceinline__ uint64_t from_last_lane(uint64_t x) {
-    static_assert(L == 1 || L == 2 || L == 4 || L == 16, "lane groups of 1, 2, 4 or 16");
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16,
+                  "lane groups of 1, 2, 4, 8 or 16");
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 8) {
+        return pack64(group8_lane32<7>(static_cast<uint32_t>(x)),
+                      group8_lane32<7>(static_cast<uint32_t>(x >> 32)));
     } else if constexpr (L == 16) {
         return pack64(row_lane32<15>(static_cast<uint32_t>(x)),
                       row_lane32<15>(static_cast<uint32_t>(x >> 32)));
@@ -103,6 +118,9 @@ template <int L, int SRC>
 __device__ __forceinline__ uint64_t from_lane64(uint64_t x) {
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 8) {
+        return pack64(group8_lane32<SRC>(static_cast<uint32_t>(x)),
+                      group8_lane32<SRC>(static_cast<uint32_t>(x >> 32)));
     } else if constexpr (L == 16) {
         return pack64(row_lane32<SRC>(static_cast<uint32_t>(x)),
                       row_lane32<SRC>(static_cast<uint32_t>(x >> 32)));
@@ -122,6 +140,8 @@ template <int L, int SRC>
 __device__ __forceinline__ int64_t from_lane(int64_t x) {
     if constexpr (L == 1) {
         return x;
+    } else if constexpr (L == 8) {
+        return static_cast<int64_t>(group8_lane32<SRC>(static_cast<uint32_t>(x)));
     } else if constexpr (L == 16) {
         return static_cast<int64_t>(row_lane32<SRC>(static_cast<uint32_t>(x)));
     } else {
@@ -268,11 +288,13 @@ __device__ __forceinline__ void sort_blocks(uint64_t (&a)[E], int lane) {
 }
 
 // Value of the previous lane of this query's lane group (L = 2 or 4 lanes in a quad, or a
-// 16-lane row); the group's first lane reads its own (quads) or an undefined value (rows).
+// group of 8 or 16); the group's first lane reads its own (quads) or another lane's value
+// (larger groups), which the caller replaces.
 template <int L>
 __device__ __forceinline__ uint64_t from_prev_lane(uint64_t x) {
-    // quad_perm [0,0,1,2] / [0,0,2,2]; row_shr:1 for a row
-    constexpr int ctrl = L == 16 ? 0x111 : (L == 4 ? 0x90 : 0xA0);
+    // quad_perm [0,0,1,2] / [0,0,2,2]; row_shr:1 for groups of 8 or 16 (the group's first
+    // lane then reads the previous group's last lane, which the caller discards)
+    constexpr int ctrl = L >= 8 ? 0x111 : (L == 4 ? 0x90 : 0xA0);
     const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x)), ctrl, 0xF,
                                             0xF, false);
     const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(x >> 32)), ctrl,
@@ -323,11 +345,11 @@ __device__ __forceinline__ bool one_per_group(uint64_t m) {
         const uint64_t pair_both = m & (m >> 1) & 0x5555555555555555ull;
         if constexpr (L == 2) {
             return pair_both == 0;
-        } else if constexpr (L == 16) {
+        } else if constexpr (L == 8 || L == 16) {
             bool ok = true;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const uint32_t c = static_cast<uint32_t>(m >> (16 * g)) & 0xFFFFu;
+            for (int g = 0; g < 64 / L; ++g) {
+                const uint32_t c = static_cast<uint32_t>(m >> (L * g)) & ((1u << L) - 1u);
                 ok = ok && (c & (c - 1u)) == 0u;
             }
             return ok;
@@ -812,7 +834,7 @@ static hipError_t select_t(int64_t BH, int64_t N, int stored, int base, int topk
     if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 64) return launch_select_k<64, 4, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 64) return launch_select_k<64, kLanes64, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 128) return launch_select_k<128, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     return launch_select_k<256, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
 }
@@ -976,7 +998,7 @@ static hipError_t chunked_t(int64_t BH, int64_t N, int stored, int base, int lvl
     if (topk <= 8) return launch_chunked_k<8, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
     if (topk <= 16) return launch_chunked_k<16, 1, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
     if (topk <= 32) return launch_chunked_k<32, 2, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
-    if (topk <= 64) return launch_chunked_k<64, 4, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
+    if (topk <= 64) return launch_chunked_k<64, kLanes64, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
     if (topk <= 128) return launch_chunked_k<128, 16, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
     return launch_chunked_k<256, 16, CT, S>(rows, N, stored, base, lvl, topk, zq, ta, idx, s);
 }

@@ -45,8 +45,8 @@ static_assert(kMergeThreads == 256, "the split search runs two diagonals on 128 
 // initial sequence is j ascending (asc tree) and (code, j descending) when it is j descending
 // (desc tree).  Level l of the tile is then the stable partition of that sorted sequence by
 // the block j >> l: the block's entries in sorted order, which is exactly the block sorted.
-// Partitions with at most 64 blocks rank by ballots the same way; levels with blocks of at
-// most 32 positions rank each entry by counting the smaller entries of its block.
+// Partitions with at most 256 blocks rank by ballots the same way; levels with blocks of at
+// most 8 positions rank each entry by counting the smaller entries of its block.
 constexpr int kRTThreads = 1024;
 constexpr int kRTWaves = kRTThreads / 64;
 
@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t tile_scan256(uint32_t v, uint32_t* part) {
     return x;
 }
 
-// digit_peers with a digit of `bits` bits (0 <= bits <= 6), decided at run time.
+// digit_peers with a digit of `bits` bits (0 <= bits <= 8), decided at run time.
 __device__ __forceinline__ uint64_t group_peers(uint32_t g, int bits, bool valid) {
     const uint64_t v = __ballot(valid);
     uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
@@ -88,10 +88,10 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
     constexpr int kItems = kWaveItems / 64;   // 64-item steps of one wavefront
     constexpr int kCodeBits = S == 32 ? 30 : 36;
     constexpr int kPasses = (kCodeBits + 7) / 8;
-    constexpr int kMaxGroups = 64;            // partitions ranked by ballots
+    constexpr int kMaxGroups = 256;           // partitions ranked by ballots (8-bit groups)
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     static_assert(kItems >= 1, "at least one step per wavefront");
-    static_assert(T / 64 <= kMaxGroups, "partitions of blocks above 32 entries ranked by ballots");
+    static_assert(T / 16 <= kMaxGroups, "partitions of blocks of 16 entries and up ranked by ballots");
     __shared__ CT zc[T];                   // codes by local index
     __shared__ uint16_t seq[2][T];         // local indices in sequence order (ping-pong)
     __shared__ uint16_t stage[T];          // one level of the tile, as local indices
@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
     for (int l = first > 1 ? first : 1; l <= top; ++l) {
         uint64_t* out = tree + static_cast<int64_t>(l - first) * N;
         const int groups = T >> l;
-        if ((1 << l) <= 32) {
+        if (groups > kMaxGroups) {
             // small blocks: an entry's place is the number of smaller entries of its block
             for (int i = tid; i < n; i += kRTThreads) {
                 const int b0 = i >> l << l;
