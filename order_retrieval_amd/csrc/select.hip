@@ -16,9 +16,9 @@
 // the first k of every walk gives the exact answer.
 //
 // The running top-K (K = next power of two >= k) of a query is a sorted list of packed keys
-// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 32 and 8
-// for K = 64, so a lane holds 8 entries in registers and more wavefronts fit; L = 1 below; a
-// whole 16-lane row for K = 128 and 256, 8 or 16 entries per lane).  A
+// (|dz| << 32) | j spread over L consecutive lanes of a wavefront (L = 4 for K = 16, 8 for
+// K = 32 and 64, a whole 16-lane row for K = 128 and 256: 4 to 16 entries per lane, so more
+// wavefronts fit and each query's merge work is spread; L = 1 below K = 16).  A
 // walk's K candidates are merged with one bitonic step: elementwise min against the
 // reversed candidates (each lane loads its own contiguous block of the walk) leaves a
 // bitonic sequence of the K smallest, which log2(K) compare-exchange stages sort; the stages
@@ -41,6 +41,8 @@ constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (
 constexpr int kInsert = 2;       // walk candidates merged by insertion when no more can enter
 constexpr int kInsert2 = 3;      // the second insertion tier (lane groups of 4 or more lanes)
 constexpr int kLanes64 = 8;      // lanes per query of the K = 64 list (8 entries per lane)
+constexpr int kLanes32 = 8;      // lanes per query of the K = 32 list (4 entries per lane)
+constexpr int kLanes16 = 4;      // lanes per query of the K = 16 list (4 entries per lane)
 
 // One word of lane `lane ^ D` (D = 1, 2: a DPP quad permute that the compiler can fold into
 // the instruction consuming it; D = 4, 8: a ds_swizzle in bitmask mode, and-mask 31 with
@@ -832,8 +834,8 @@ static hipError_t select_t(int64_t BH, int64_t N, int stored, int base, int topk
     if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 4) return launch_select_k<4, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 8) return launch_select_k<8, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 16) return launch_select_k<16, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
-    if (topk <= 32) return launch_select_k<32, 4, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 16) return launch_select_k<16, kLanes16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
+    if (topk <= 32) return launch_select_k<32, kLanes32, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 64) return launch_select_k<64, kLanes64, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 128) return launch_select_k<128, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     return launch_select_k<256, 16, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
