@@ -609,8 +609,15 @@ __device__ __forceinline__ void fill_keys(uint64_t (&best)[K / L], const uint64_
 
 // CT, S: code type and position bits of the packed tree entries (uint32_t, 32 for 30-bit
 // codes; uint64_t, 28 for the 36-bit codes of 12-bit cells).
+// Workgroup of the exact selection: 256 threads up to K = 16; one wavefront for longer lists,
+// whose queries run for very different times (measured at N = 65536, H = 8: k = 32 / 64 / 128
+// in 0.180 / 0.345 / 0.820 ms with 256 threads, 0.176 / 0.335 / 0.771 ms with 64; k = 16 is
+// 0.120 ms either way).
+template <int K>
+constexpr int sel_threads() { return K <= 16 ? 256 : 64; }
+
 template <int K, int L, typename CT, int S, bool O32>
-__global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__ zq,
+__global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT* __restrict__ zq,
                                                            const CT* __restrict__ zk,
                                                            const uint64_t* __restrict__ tree_asc,
                                                            const uint64_t* __restrict__ tree_desc,
@@ -625,7 +632,8 @@ __global__ void __launch_bounds__(256) zeta_select_kernel(const CT* __restrict__
     const int64_t tile = xcd_tile(blockIdx.x, per_xcd);
     if (tile >= tiles) return;
     const int64_t bh = tile / tph;  // uniform: tiles never straddle two (b,h)
-    const int64_t t = (tile - bh * tph) * (256 / L) + threadIdx.x / L;  // processing position
+    constexpr int QPT = sel_threads<K>() / L;  // queries per workgroup
+    const int64_t t = (tile - bh * tph) * QPT + threadIdx.x / L;  // processing position
     const int lane = static_cast<int>(threadIdx.x % L);
     if (t >= N) return;  // uniform over the L lanes of a query
     // queries close on the curve search the same parts of the tree, so taking them in the
@@ -814,16 +822,17 @@ static hipError_t launch_select_k(int64_t rows, int64_t N, int stored, int base,
                                   const CT* zq, const CT* zk, const uint64_t* ta,
                                   const uint64_t* td, const uint32_t* order, int32_t* idx,
                                   hipStream_t s) {
-    // tiles of 256 / L queries, never straddling two (b,h)
-    const int64_t tph = (N + (256 / L) - 1) / (256 / L);
+    // tiles of sel_threads<K>() / L queries, never straddling two (b,h)
+    constexpr int QPT = sel_threads<K>() / L;
+    const int64_t tph = (N + QPT - 1) / QPT;
     const int64_t tiles = (rows / N) * tph;
     const int64_t per = xcd_per(tiles);
     const dim3 grid(static_cast<unsigned>(per * kXcds));
     if (static_cast<int64_t>(stored) * N < (int64_t(1) << 28))
-        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, true>), grid, dim3(256), 0, s, zq, zk,
+        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, true>), grid, dim3(sel_threads<K>()), 0, s, zq, zk,
                            ta, td, order, N, stored, base, topk, causal, tph, tiles, per, idx);
     else
-        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, false>), grid, dim3(256), 0, s, zq,
+        hipLaunchKernelGGL((zeta_select_kernel<K, L, CT, S, false>), grid, dim3(sel_threads<K>()), 0, s, zq,
                            zk, ta, td, order, N, stored, base, topk, causal, tph, tiles, per, idx);
     return hipGetLastError();
 }
