@@ -719,14 +719,18 @@ def time_run(r: Run, lib, hip, steps: int, warmup: int) -> dict:
 
 
 def stored_levels(w: inputs.Workload) -> int:
-    """Tree levels the forward workspace stores: from log2(2K) (K = k padded to a power of two;
-    shorter runs are read from the codes) to the top level floor(log2 N), and from the tile
-    stage's top level (12) when that is lower and merge passes build the rest from it."""
-    L = int(np.floor(np.log2(w.N))) + 1
+    """Tree levels the forward workspace stores (causal selection): from log2(2K) (K = k padded
+    to a power of two; shorter runs are read from the codes) to the top level floor(log2(N-1))
+    (a run of N keys, the last query's when N is a power of two, is read as two runs of the
+    level below; kept when that level is below log2(2K)), and from the tile stage's top level
+    (12) when that is lower and merge passes build the rest from it."""
     K = 1
     while K < w.topk:
         K *= 2
     first = int(np.log2(2 * K))
+    L = (w.N - 1).bit_length() if w.N >= 2 else 1
+    if L - 1 < first:
+        L = w.N.bit_length()
     top_tile = min(L - 1, 12)
     base = top_tile if (top_tile + 1 < L and first > top_tile) else first
     return max(0, L - base)

@@ -657,6 +657,11 @@ __global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT*
     const uint64_t m = causal ? static_cast<uint64_t>(i) + 1 : static_cast<uint64_t>(N);
     constexpr uint64_t kShort = 2 * K;
     uint64_t rem = m & ~(kShort - 1);
+    // Runs above the top stored level (only m = 2^(top+1) = N under the causal mask, when
+    // that level is not built) are taken as runs of the top level; `start` is the first
+    // position of the next run, the sum of the runs taken before it.
+    const int top = base + stored - 1;
+    uint64_t start = 0;
     // A group takes the next kRuns runs (largest first).  With several lanes per query each
     // lane binary-searches its own run(s) of the group (kPer per lane, in lock-step), and the
     // insertion positions then reach every lane of the query by a DPP quad broadcast.
@@ -673,11 +678,13 @@ __global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT*
             lv[gi] = -1;
             roff[gi] = 0;
             if (rem) {
-                const int l = 63 - __clzll(rem);
-                rem ^= uint64_t(1) << l;
+                const int hb = 63 - __clzll(rem);
+                const int l = hb < top ? hb : top;
+                rem -= uint64_t(1) << l;
                 lv[gi] = l;
                 roff[gi] = static_cast<IX>(static_cast<int64_t>(l - base) * N +
-                                           static_cast<int64_t>((m >> (l + 1)) << (l + 1)));
+                                           static_cast<int64_t>(start));
+                start += uint64_t(1) << l;
             }
         }
         // this lane's runs: gi = lane * kPer + t
@@ -843,6 +850,12 @@ static hipError_t select_t(int64_t BH, int64_t N, int stored, int base, int topk
                            const uint32_t* order, int32_t* idx, hipStream_t s) {
     const int64_t rows = BH * N;
     if (rows <= 0) return hipSuccess;
+    // Every run the kernel takes lies on a stored level: the stored levels must reach from
+    // log2(2K) (shorter runs are read from the codes) up; runs longer than the top stored
+    // level are taken as several runs of that level.
+    const int first = select_first_level(topk);
+    if ((int64_t(1) << first) <= N && (base > first || base + stored - 1 < first))
+        return hipErrorInvalidValue;
     const int c = causal ? 1 : 0;
     if (topk <= 1) return launch_select_k<1, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);
     if (topk <= 2) return launch_select_k<2, 1, CT, S>(rows, N, stored, base, topk, c, zq, zk, ta, td, order, idx, s);

@@ -38,21 +38,25 @@ static_assert(kMergeThreads == 256, "the split search runs two diagonals on 128 
 
 // ---------------------------------------------------------------------------- radix tile
 // Tile stage as an LDS radix sort.  One workgroup per tile of 2^TL positions and tree.  The
-// tile's local indices are sorted by code with a stable LSD radix sort over 8-bit digits; each
-// pass ranks the items of every 64-item step of a wavefront by ballots (the lanes holding the
-// same digit, digit_peers) plus a running count per digit and wavefront, and scatters them in
-// LDS after one scan over the digits.  Stability makes the order (code, j ascending) when the
-// initial sequence is j ascending (asc tree) and (code, j descending) when it is j descending
-// (desc tree).  Level l of the tile is then the stable partition of that sorted sequence by
-// the block j >> l: the block's entries in sorted order, which is exactly the block sorted.
-// Partitions with at most 256 blocks rank by ballots the same way; levels with blocks of at
-// most 8 positions rank each entry by counting the smaller entries of its block.
+// tile's local indices are sorted by code with a stable LSD radix sort over 10-bit digits (9
+// for 36-bit codes); each pass ranks the items of every 64-item step of a wavefront by ballots
+// (the lanes holding the same digit, digit_peers) plus a running count per digit and
+// wavefront, and scatters them in LDS after one scan over the digits.  Stability makes the
+// order (code, j ascending) when the initial sequence is j ascending (asc tree) and (code, j
+// descending) when it is j descending (desc tree).  Level l of the tile is then the stable
+// partition of that sorted sequence by the block j >> l: the block's entries in sorted order,
+// which is exactly the block sorted.  Levels with at most 256 blocks are ranked together, up
+// to kBatch of them in one pass: the block of level l is the block of level l - 1 shifted
+// right by one bit, so one ballot per position bit, taken from the top bit down, yields the
+// peers of every level on the way.  Levels with blocks of at most 8 positions rank each
+// entry by counting the smaller entries of its block; the level of the whole tile is the
+// sorted sequence itself.
 constexpr int kRTThreads = 1024;
 constexpr int kRTWaves = kRTThreads / 64;
 
-// Inclusive sum over the workgroup's first 256 threads (one value each; the others pass 0).
-// `part` holds one word per wavefront.
-__device__ __forceinline__ uint32_t tile_scan256(uint32_t v, uint32_t* part) {
+// Inclusive sum over the workgroup (one value per thread).  `part` holds one word per
+// wavefront.
+__device__ __forceinline__ uint32_t tile_scan(uint32_t v, uint32_t* part) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
     for (int off = 1; off < 64; off <<= 1) {
@@ -61,22 +65,8 @@ __device__ __forceinline__ uint32_t tile_scan256(uint32_t v, uint32_t* part) {
     }
     if (lane == 63) part[wave] = x;
     __syncthreads();
-    for (int w = 0; w < wave && w < 4; ++w) x += part[w];
+    for (int w = 0; w < wave; ++w) x += part[w];
     return x;
-}
-
-// digit_peers with a digit of `bits` bits (0 <= bits <= 8), decided at run time.
-__device__ __forceinline__ uint64_t group_peers(uint32_t g, int bits, bool valid) {
-    const uint64_t v = __ballot(valid);
-    uint32_t lo = valid ? static_cast<uint32_t>(v) : 0u;
-    uint32_t hi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
-    for (int b = 0; b < bits; ++b) {
-        const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(g << (31 - b)) >> 31);
-        const uint64_t bal = __ballot(m != 0u);
-        lo &= ~(static_cast<uint32_t>(bal) ^ m);
-        hi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
-    }
-    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 template <typename CT, int S, int TL>
@@ -87,16 +77,28 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
     constexpr int kWaveItems = T / kRTWaves;  // sequence positions of one wavefront
     constexpr int kItems = kWaveItems / 64;   // 64-item steps of one wavefront
     constexpr int kCodeBits = S == 32 ? 30 : 36;
-    constexpr int kPasses = (kCodeBits + 7) / 8;
-    constexpr int kMaxGroups = 256;           // partitions ranked by ballots (8-bit groups)
+    constexpr int kPasses = (kCodeBits + 9) / 10;
+    constexpr int kDigit = (kCodeBits + kPasses - 1) / kPasses;  // 10 bits, or 9 for 36-bit codes
+    constexpr int kBuckets = 1 << kDigit;
+    constexpr int kMaxGroups = 256;           // partitions ranked by ballots
+    constexpr int kLowBallot = TL - 8;        // lowest such level (blocks of T / 256)
+    constexpr int kBatch = 6;                 // levels ranked in one pass
+    constexpr int kLevWords = 2 * kMaxGroups; // level l's counters at (T >> l) - 2 of a wavefront's
+    constexpr int kSortWords = kRTWaves * kBuckets;
+    constexpr int kPartWords = kRTWaves * kLevWords + kBatch * T / 2;
+    constexpr int kRawWords = kSortWords > kPartWords ? kSortWords : kPartWords;
     constexpr uint64_t kJMask = (S == 32) ? 0xffffffffull : ((uint64_t(1) << S) - 1);
     static_assert(kItems >= 1, "at least one step per wavefront");
-    static_assert(T / 16 <= kMaxGroups, "partitions of blocks of 16 entries and up ranked by ballots");
-    __shared__ CT zc[T];                   // codes by local index
-    __shared__ uint16_t seq[2][T];         // local indices in sequence order (ping-pong)
-    __shared__ uint16_t stage[T];          // one level of the tile, as local indices
-    __shared__ uint32_t wcnt[kRTWaves][256];
+    static_assert(kBuckets <= kRTThreads, "one digit per thread in the scan");
+    static_assert(kLowBallot >= 1, "tiles of 512 positions and up");
+    __shared__ CT zc[T];             // codes by local index
+    __shared__ uint16_t seq[2][T];   // local indices in sequence order (ping-pong)
+    // sort: counters [wave][digit]; partitions: counters [wave][kLevWords], then the levels
+    // of a batch as local indices [kBatch][T]
+    __shared__ uint32_t raw[kRawWords];
     __shared__ uint32_t part[kRTWaves];
+    uint32_t* const cnt = raw;
+    uint16_t* const stage = reinterpret_cast<uint16_t*>(raw + kRTWaves * kLevWords);
     const bool dsc = blockIdx.z != 0;
     const int64_t bh = blockIdx.y;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * T;
@@ -112,6 +114,7 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
     for (int e = tid; e < T; e += kRTThreads) {
         zc[e] = e < n ? zk[bh * N + base + e] : CT(0);
         seq[0][e] = static_cast<uint16_t>(e < n ? (dsc ? n - 1 - e : e) : e);
+        seq[1][e] = static_cast<uint16_t>(e);  // positions past n keep a local index
     }
     __syncthreads();
     if (first == 0)
@@ -120,10 +123,8 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
     // stable LSD radix sort of the sequence by code
     int cur = 0;
     for (int pass = 0; pass < kPasses; ++pass) {
-        const int shift = 8 * pass;
-        if (tid < 256)
-#pragma unroll
-            for (int w = 0; w < kRTWaves; ++w) wcnt[w][tid] = 0;
+        const int shift = kDigit * pass;
+        for (int e = tid; e < kSortWords; e += kRTThreads) cnt[e] = 0;
         __syncthreads();
         uint16_t idx[kItems];
         uint32_t dig[kItems], rank[kItems];
@@ -132,91 +133,133 @@ __global__ void __launch_bounds__(kRTThreads) zeta_tree_radix_tile_kernel(
             const int pos = wave * kWaveItems + it * 64 + lane;
             const bool valid = pos < n;
             idx[it] = seq[cur][pos];
-            dig[it] = valid ? static_cast<uint32_t>(zc[idx[it]] >> shift) & 255u : 0u;
-            const uint64_t peers = digit_peers<8>(dig[it], valid);
+            dig[it] = valid ? static_cast<uint32_t>(zc[idx[it]] >> shift) & (kBuckets - 1) : 0u;
+            const uint64_t peers = digit_peers<kDigit>(dig[it], valid);
             // every lane reads the running count before the group's first lane advances it
             // (LDS operations of one wavefront take effect in program order)
-            const uint32_t before = valid ? wcnt[wave][dig[it]] : 0u;
-            if (valid && (peers & lt) == 0) wcnt[wave][dig[it]] = before + __popcll(peers);
+            uint32_t* const c = cnt + wave * kBuckets + dig[it];
+            const uint32_t before = valid ? *c : 0u;
+            if (valid && (peers & lt) == 0) *c = before + __popcll(peers);
             rank[it] = before + __popcll(peers & lt);
         }
         __syncthreads();
         {
             uint32_t c = 0;
-            if (tid < 256)
+            if (tid < kBuckets)
 #pragma unroll
-                for (int w = 0; w < kRTWaves; ++w) c += wcnt[w][tid];
-            uint32_t run = tile_scan256(c, part) - c;  // digit tid's first position
-            if (tid < 256)
+                for (int w = 0; w < kRTWaves; ++w) c += cnt[w * kBuckets + tid];
+            uint32_t run = tile_scan(c, part) - c;  // digit tid's first position
+            if (tid < kBuckets)
 #pragma unroll
                 for (int w = 0; w < kRTWaves; ++w) {
-                    const uint32_t t = wcnt[w][tid];
-                    wcnt[w][tid] = run;
+                    const uint32_t t = cnt[w * kBuckets + tid];
+                    cnt[w * kBuckets + tid] = run;
                     run += t;
                 }
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < kItems; ++it)
-            if (wave * kWaveItems + it * 64 + lane < n) seq[cur ^ 1][wcnt[wave][dig[it]] + rank[it]] = idx[it];
+            if (wave * kWaveItems + it * 64 + lane < n)
+                seq[cur ^ 1][cnt[wave * kBuckets + dig[it]] + rank[it]] = idx[it];
         __syncthreads();
         cur ^= 1;
     }
 
-    // levels first .. top: the stable partition of the sorted sequence by block
-    for (int l = first > 1 ? first : 1; l <= top; ++l) {
+    const int lo = first > 1 ? first : 1;
+    // levels of blocks up to 8 positions: an entry's place is the number of smaller entries
+    // of its block
+    for (int l = lo; l <= top && l < kLowBallot; ++l) {
         uint64_t* out = tree + static_cast<int64_t>(l - first) * N;
-        const int groups = T >> l;
-        if (groups > kMaxGroups) {
-            // small blocks: an entry's place is the number of smaller entries of its block
-            for (int i = tid; i < n; i += kRTThreads) {
-                const int b0 = i >> l << l;
-                const int b1 = b0 + (1 << l) < n ? b0 + (1 << l) : n;
-                const CT c = zc[i];
-                int r = 0;
-                for (int u = b0; u < b1; ++u) {
-                    const CT cu = zc[u];
-                    r += (cu < c || (cu == c && (dsc ? u > i : u < i))) ? 1 : 0;
-                }
-                out[b0 + r] = entry(i);
+        for (int i = tid; i < n; i += kRTThreads) {
+            const int b0 = i >> l << l;
+            const int b1 = b0 + (1 << l) < n ? b0 + (1 << l) : n;
+            const CT c = zc[i];
+            int r = 0;
+            for (int u = b0; u < b1; ++u) {
+                const CT cu = zc[u];
+                r += (cu < c || (cu == c && (dsc ? u > i : u < i))) ? 1 : 0;
             }
-            continue;
+            out[b0 + r] = entry(i);
         }
-        int bits = 0;
-        while ((1 << bits) < groups) ++bits;
-#pragma unroll
-        for (int w = 0; w < kRTWaves; ++w)
-            if (tid < kMaxGroups) wcnt[w][tid] = 0;
+    }
+    // the whole tile is one block: the sorted sequence itself
+    if (top >= TL && first <= TL)
+        for (int e = tid; e < n; e += kRTThreads)
+            tree[static_cast<int64_t>(TL - first) * N + e] = entry(seq[cur][e]);
+    // levels of 2 .. 256 blocks, kBatch at a time: levels la + s, s < nl
+    const int hi = top < TL - 1 ? top : TL - 1;
+    for (int la = lo > kLowBallot ? lo : kLowBallot; la <= hi; la += kBatch) {
+        const int nl = hi - la + 1 < kBatch ? hi - la + 1 : kBatch;
+        for (int e = tid; e < kRTWaves * kLevWords; e += kRTThreads) cnt[e] = 0;
         __syncthreads();
         uint16_t idx[kItems];
-        uint32_t grp[kItems], rank[kItems];
+        uint32_t rank[kItems][kBatch];
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int pos = wave * kWaveItems + it * 64 + lane;
             const bool valid = pos < n;
             idx[it] = seq[cur][pos];
-            grp[it] = valid ? static_cast<uint32_t>(idx[it]) >> l : 0u;
-            const uint64_t peers = group_peers(grp[it], bits, valid);
-            const uint32_t before = valid ? wcnt[wave][grp[it]] : 0u;
-            if (valid && (peers & lt) == 0) wcnt[wave][grp[it]] = before + __popcll(peers);
-            rank[it] = before + __popcll(peers & lt);
+            const uint32_t x = valid ? idx[it] : 0u;
+            const uint64_t v = __ballot(valid);
+            uint32_t plo = valid ? static_cast<uint32_t>(v) : 0u;
+            uint32_t phi = valid ? static_cast<uint32_t>(v >> 32) : 0u;
+            // peers in the position bits above the batch's levels
+            for (int b = TL - 1; b >= la + nl; --b) {
+                const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(x << (31 - b)) >> 31);
+                const uint64_t bal = __ballot(m != 0u);
+                plo &= ~(static_cast<uint32_t>(bal) ^ m);
+                phi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
+            }
+            // then level by level down the batch: the peers of level la + s share bits la + s up
+#pragma unroll
+            for (int s = kBatch - 1; s >= 0; --s) {
+                if (s >= nl) continue;  // uniform
+                const int b = la + s;
+                const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(x << (31 - b)) >> 31);
+                const uint64_t bal = __ballot(m != 0u);
+                plo &= ~(static_cast<uint32_t>(bal) ^ m);
+                phi &= ~(static_cast<uint32_t>(bal >> 32) ^ m);
+                const uint64_t peers = (static_cast<uint64_t>(phi) << 32) | plo;
+                uint32_t* const c = cnt + wave * kLevWords + (T >> b) - 2 + (x >> b);
+                const uint32_t before = valid ? *c : 0u;
+                if (valid && (peers & lt) == 0) *c = before + __popcll(peers);
+                rank[it][s] = before + __popcll(peers & lt);
+            }
         }
         __syncthreads();
-        if (tid < groups) {
-            uint32_t run = static_cast<uint32_t>(tid) << l;  // block tid starts at tid 2^l
+        // counter word w of a wavefront belongs to level TL - log2(w + 2), block w + 2 - 2^(..)
+        if (tid < kLevWords - 2) {
+            const int lg = 31 - __clz(tid + 2);
+            const int l = TL - lg;
+            if (l >= la && l < la + nl) {
+                uint32_t run = static_cast<uint32_t>(tid + 2 - (1 << lg)) << l;  // block start
 #pragma unroll
-            for (int w = 0; w < kRTWaves; ++w) {
-                const uint32_t t = wcnt[w][tid];
-                wcnt[w][tid] = run;
-                run += t;
+                for (int w = 0; w < kRTWaves; ++w) {
+                    const uint32_t t = cnt[w * kLevWords + tid];
+                    cnt[w * kLevWords + tid] = run;
+                    run += t;
+                }
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < kItems; ++it)
-            if (wave * kWaveItems + it * 64 + lane < n) stage[wcnt[wave][grp[it]] + rank[it]] = idx[it];
+        for (int it = 0; it < kItems; ++it) {
+            if (wave * kWaveItems + it * 64 + lane >= n) continue;
+            const uint32_t x = idx[it];
+#pragma unroll
+            for (int s = 0; s < kBatch; ++s) {
+                if (s >= nl) continue;  // uniform
+                const int b = la + s;
+                stage[s * T + cnt[wave * kLevWords + (T >> b) - 2 + (x >> b)] + rank[it][s]] =
+                    idx[it];
+            }
+        }
         __syncthreads();
-        for (int e = tid; e < n; e += kRTThreads) out[e] = entry(stage[e]);
+        for (int s = 0; s < nl; ++s) {
+            uint64_t* out = tree + static_cast<int64_t>(la + s - first) * N;
+            for (int e = tid; e < n; e += kRTThreads) out[e] = entry(stage[s * T + e]);
+        }
         __syncthreads();
     }
 }

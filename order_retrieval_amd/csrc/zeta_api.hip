@@ -123,9 +123,17 @@ int chunk_level(int64_t N, int chunks) {
 }
 
 // Tree levels a selection needs: every level of the exact search; for the chunked search
-// only up to the chunk level (which is above the top level when 2^lvl > N).
-int tree_levels(const zeta_shape* sh, const Opts& o) {
+// only up to the chunk level (which is above the top level when 2^lvl > N).  Under the
+// causal mask a query sees i + 1 <= N keys, so a run of 2^l keys needs 2^l <= N - 1 except
+// for the last query when N is a power of two; that query takes its one run of N keys as
+// two runs of the level below, and the top level (a whole merge pass) is not built.
+int tree_levels(const zeta_shape* sh, const Opts& o, int first) {
     if (o.mode == ZETA_SELECT_CHUNKED) return chunk_level(sh->N, o.chunks) + 1;
+    if (o.causal && sh->N >= 2) {
+        // N = 2K: the level below the top is shorter than the short runs, keep the top
+        const int lv = levels_of(sh->N - 1);
+        return lv - 1 >= first ? lv : levels_of(sh->N);
+    }
     return levels_of(sh->N);
 }
 
@@ -160,8 +168,8 @@ struct FwdPlan {
 FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
     const int64_t BHN = sh->B * sh->H * sh->N;
     FwdPlan p{};
-    p.levels = tree_levels(sh, o);
     p.first = tree_first(sh, o);
+    p.levels = tree_levels(sh, o, p.first);
     p.base = zeta::tree_store_base(p.levels, p.first);
     p.stored = p.levels > p.base ? p.levels - p.base : 0;
     size_t off = 0;

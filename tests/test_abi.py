@@ -221,6 +221,17 @@ def test_null_options_equal_the_plain_calls(lib):
             lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_FWD))
 
 
+def test_causal_tree_skips_the_top_level(lib):
+    # under the causal mask the level of N keys is read only by the last query when N is a
+    # power of two, which takes it as two runs of the level below: one level fewer per tree
+    for N, fewer in ((65536, 1), (4096, 1), (1000, 0), (64, 0), (128, 1)):
+        s = shape(B=2, H=2, N=N, topk=32)
+        nc = opts(causal=0)
+        causal = lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_FWD)
+        full = lib.zeta_workspace_bytes_ex(ctypes.byref(s), ctypes.byref(nc), zeta.ZETA_WS_FWD)
+        assert full - causal == fewer * 2 * 8 * 2 * 2 * N, N
+
+
 def test_variant_workspaces(lib):
     s = shape(N=1000, topk=32)
     base = lib.zeta_workspace_bytes(ctypes.byref(s), zeta.ZETA_WS_FWD)

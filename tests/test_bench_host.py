@@ -61,8 +61,9 @@ def test_forward_bytes_match_the_scope_table(name, fwd_mb):
     assert got == pytest.approx(fwd_mb, rel=0.02)
 
 
-@pytest.mark.parametrize("N,k,want", [(65536, 32, 11), (16384, 64, 8), (1024, 32, 5),
-                                      (1000, 64, 3), (100, 64, 0), (65536, 256, 8)])
+@pytest.mark.parametrize("N,k,want", [(65536, 32, 10), (16384, 64, 7), (1024, 32, 4),
+                                      (1000, 64, 3), (100, 64, 0), (65536, 256, 7),
+                                      (64, 32, 1), (128, 32, 1), (129, 32, 2)])
 def test_stored_levels(N, k, want):
     w = inputs.Workload("s", 1, 1, N, 8, k)
     assert bench.stored_levels(w) == want

@@ -155,6 +155,18 @@ def test_select_edge_shapes(B, H, N, topk, dist):
     _select_and_compare(W("e", B, H, N, 8, topk, dist=dist, seed=N + topk))
 
 
+@pytest.mark.parametrize("B,H,N,topk,dist", [
+    (1, 1, 64, 32, "normal"), (1, 2, 128, 64, "discrete"), (1, 1, 512, 256, "clustered"),
+    (1, 2, 128, 32, "normal"), (2, 1, 8192, 16, "discrete"), (1, 1, 16384, 32, "clustered"),
+])
+def test_select_power_of_two_lengths(B, H, N, topk, dist):
+    # under the causal mask the top level (one run of all N keys) is not built when N is a
+    # power of two above 2K: the last query reads its N keys as two runs of the level below;
+    # N = 2K keeps the top level (the level below is a short run)
+    log(f"select power-of-two B={B} H={H} N={N} k={topk} {dist}")
+    _select_and_compare(W("p2", B, H, N, 8, topk, dist=dist, seed=N + 3 * topk))
+
+
 @pytest.mark.parametrize("topk", [65, 96, 128, 256])
 def test_select_wide_topk_clustered_batch(topk):
     # the clustered mixture (heavy code ties) with four batch entries, selections wider than 64
