@@ -669,40 +669,41 @@ __global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT*
     constexpr int kRuns = kPer * L;
     bool fresh = true;  // the list is still empty
     while (rem) {
-        // run gi: level lv[gi], entries hA[roff[gi] .. roff[gi] + 2^lv[gi]) (same in hD);
-        // offsets (not pointers) keep every access a global-memory access
-        int lv[kRuns];
-        IX roff[kRuns];
+        // run gi: level l, entries hA[roff .. roff + 2^l) (same in hD); offsets (not
+        // pointers) keep every access a global-memory access.  Every lane peels the same
+        // runs off `rem` but keeps only its own (gi = lane * kPer + t, level mlv[t] or -1,
+        // offset mro[t]); the merges below fetch a run's level and offset from its lane, so
+        // no lane holds all of them.
+        int lv0 = -1;  // the group's first (largest) run, on every lane
+        int mlv[kPer];
+        IX mro[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            mlv[t] = -1;
+            mro[t] = 0;
+        }
 #pragma unroll
         for (int gi = 0; gi < kRuns; ++gi) {
-            lv[gi] = -1;
-            roff[gi] = 0;
             if (rem) {
                 const int hb = 63 - __clzll(rem);
                 const int l = hb < top ? hb : top;
                 rem -= uint64_t(1) << l;
-                lv[gi] = l;
-                roff[gi] = static_cast<IX>(static_cast<int64_t>(l - base) * N +
-                                           static_cast<int64_t>(start));
+                const IX ro = static_cast<IX>(static_cast<int64_t>(l - base) * N +
+                                              static_cast<int64_t>(start));
                 start += uint64_t(1) << l;
+                if (gi == 0) lv0 = l;
+                if (lane == gi / kPer) {
+                    mlv[gi % kPer] = l;
+                    mro[gi % kPer] = ro;
+                }
             }
         }
-        // this lane's runs: gi = lane * kPer + t
-        IX mro[kPer], mlen[kPer], pos[kPer];
+        IX mlen[kPer], pos[kPer];
         bool mon[kPer];
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
-            int ml = lv[t];
-            IX mr = roff[t];
-#pragma unroll
-            for (int u = 1; u < L; ++u)
-                if (lane == u) {
-                    ml = lv[u * kPer + t];
-                    mr = roff[u * kPer + t];
-                }
-            mon[t] = ml >= 0;
-            mro[t] = mr;
-            mlen[t] = ml >= 0 ? IX(1) << ml : 1;
+            mon[t] = mlv[t] >= 0;
+            mlen[t] = mlv[t] >= 0 ? IX(1) << mlv[t] : 1;
             pos[t] = 0;
         }
         // probes from clamped positions, held live together (see keep()), so the searches'
@@ -718,7 +719,7 @@ __global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT*
         uint64_t rfirst[kPer], lbound[kPer];
 #pragma unroll
         for (int t = 0; t < kPer; ++t) below[t] = 0;
-        for (IX step = (IX(1) << lv[0]) >> 1; step > 0; step >>= 1) {
+        for (IX step = (IX(1) << lv0) >> 1; step > 0; step >>= 1) {
             PV e[kPer];
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
@@ -759,21 +760,29 @@ __global__ void __launch_bounds__(sel_threads<K>()) zeta_select_kernel(const CT*
             const IX pg = static_cast<IX>(from_lane<L, src>(pos[slot]));
             const uint64_t rf = from_lane64<L, src>(rfirst[slot]);
             const uint64_t lb = from_lane64<L, src>(lbound[slot]);
-            if (lv[gi] >= 0) {
-                const IX s = IX(1) << lv[gi];
+            // the run's level and offset, from the lane that searched it
+            const int lvg = static_cast<int>(static_cast<uint32_t>(
+                from_lane<L, src>(static_cast<uint32_t>(mlv[slot]))));
+            IX rog;
+            if constexpr (O32)
+                rog = static_cast<IX>(from_lane<L, src>(static_cast<uint32_t>(mro[slot])));
+            else
+                rog = static_cast<IX>(from_lane64<L, src>(static_cast<uint64_t>(mro[slot])));
+            if (lvg >= 0) {
+                const IX s = IX(1) << lvg;
                 const bool fill = gi == 0 && fresh;  // uniform: every query's first group
                 if (fill) {
                     uint64_t c[E];
-                    fill_load<K, L, O32>(c, hA, roff[gi], pg, s, lane);
+                    fill_load<K, L, O32>(c, hA, rog, pg, s, lane);
 #pragma unroll
                     for (int t = 0; t < E; ++t) keep(c[t]);
                     fill_keys<K, L, S, O32>(best, c, pg, s, target, lane);
                 } else if (rf < from_last_lane<L>(best[E - 1])) {
-                    merge_walk<K, L, true, S, O32>(best, hA, roff[gi], pg, s, target, lane,
+                    merge_walk<K, L, true, S, O32>(best, hA, rog, pg, s, target, lane,
                                                    !(fresh && gi < 2));
                 }
                 if (lb < from_last_lane<L>(best[E - 1]))
-                    merge_walk<K, L, false, S, O32>(best, hD, roff[gi], pg, s, target, lane,
+                    merge_walk<K, L, false, S, O32>(best, hD, rog, pg, s, target, lane,
                                                     !(fresh && gi < 2));
             }
         });
