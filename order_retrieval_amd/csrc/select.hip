@@ -39,7 +39,11 @@ constexpr int kSearchGroup = 2;  // runs whose binary searches advance in lock-s
 constexpr int kChunk = 8;        // candidates of a walk loaded per step (register budget)
 constexpr int kChunkGroup = 4;   // chunks whose searches advance in lock-step (chunked search)
 constexpr int kInsert = 2;       // walk candidates merged by insertion when no more can enter
-constexpr int kInsert2 = 3;      // the second insertion tier (lane groups of 4 or more lanes)
+// The second insertion tier (lane groups of 4 or more lanes): the first three candidates, or
+// four for K = 64 on 8 lanes (measured at N = 65536, H = 8: k = 64 selection 0.334 -> 0.326
+// ms; four for K = 16 and 32 was slower, 0.126 and 0.168 against 0.119 and 0.165).
+template <int K, int L>
+constexpr int insert2_of() { return (K / L >= 8 && L == 8) ? 4 : 3; }
 // lanes per query of a list of K entries (measured at N = 65536, H = 8: K = 32 on 4 / 8 / 16
 // lanes 0.191 / 0.179 / 0.283 ms; K = 64 on 4 / 8 / 16 lanes 0.55 / 0.34 / 0.43 ms)
 constexpr int kLanes64 = 8;      // 8 entries per lane
@@ -505,7 +509,8 @@ __device__ __forceinline__ void walk_keys(uint64_t (&c)[CH], const WalkShare<K, 
 // Deep in the prefix a walk admits a few keys at most: when candidate kInsert cannot beat
 // its query's K-th for any query of the wavefront, the first kInsert candidates are merged
 // by insertion and the bitonic merge is skipped; with four or more lanes per query, failing
-// that, the first three when candidate 3 cannot enter (each choice uniform over the wavefront).
+// that, the first insert2_of<K, L>() when the candidate after them cannot enter (each choice
+// uniform over the wavefront).
 // `few` = false skips those checks for walks that nearly always admit more (the walks of a
 // query's two largest runs).
 template <int K, int L, bool RIGHT, int S, bool O32>
@@ -515,6 +520,7 @@ __device__ __forceinline__ void merge_walk(uint64_t (&best)[K / L], const uint64
                                            bool few = true) {
     constexpr int E = K / L;
     constexpr int CH = kChunk < E ? kChunk : E;
+    constexpr int kInsert2 = insert2_of<K, L>();
     const WalkShare<K, L, RIGHT, O32> w(p, s, lane);
     if constexpr (L >= 4 && kInsert > 0 && kInsert < kInsert2 && kInsert2 < L) {
         if (few) {
