@@ -304,46 +304,40 @@ __global__ void __launch_bounds__(kMergeThreads) zeta_tree_merge_kernel(uint64_t
 
     // Merge-path splits of the two diagonals d0, d1 (threads 0-127 and 128-255): the number
     // a of A entries among the first d outputs is the first a with A[a] > B[d-1-a] (keys are
-    // unique).  Each round tests 128 evenly spaced candidates of the open interval at once,
-    // so a few rounds of independent loads replace a long chain of dependent ones.
+    // unique), so the test A[a] < B[d-1-a] holds exactly for a below the split.  Each round
+    // tests 128 evenly spaced candidates of the open interval [lo, hi) at once; the count T of
+    // passing candidates (two wavefront ballots, exchanged through LDS: one barrier a round)
+    // puts the split after candidate T-1 and at or before candidate T.  Every thread keeps its
+    // diagonal's interval itself, and the number of rounds follows from the wider of the two
+    // initial intervals, so it is the same on every thread.
     {
-        __shared__ int lo_s[2], hi_s[2], lo_n[2], hi_n[2];
+        __shared__ int wtrue[2][2][2];  // [round parity][diagonal][wavefront]
         const int h = threadIdx.x >> 7;
         const int t = threadIdx.x & 127;
+        const int wv = t >> 6;
         const int d = h ? d1 : d0;
-        if (t == 0) {
-            lo_s[h] = d - nb > 0 ? d - nb : 0;
-            hi_s[h] = d < na ? d : na;
+        int lo = d - nb > 0 ? d - nb : 0;
+        int hi = d < na ? d : na;
+        const int w0 = (d0 < na ? d0 : na) - (d0 - nb > 0 ? d0 - nb : 0);
+        const int w1 = (d1 < na ? d1 : na) - (d1 - nb > 0 ? d1 - nb : 0);
+        int par = 0;
+        for (int W = w0 > w1 ? w0 : w1; W > 0; W = (W + 127) / 128 - 1) {
+            const int step = hi > lo ? (hi - lo + 127) / 128 : 1;
+            const int a = lo + t * step;
+            bool pass = false;
+            if (a < hi) pass = A[a] < B[d - 1 - a];
+            const uint64_t bal = __ballot(pass);
+            if ((threadIdx.x & 63) == 0) wtrue[par][h][wv] = __popcll(bal);
+            __syncthreads();
+            const int T = wtrue[par][h][0] + wtrue[par][h][1];
+            const int valid = hi > lo ? (hi - lo + step - 1) / step : 0;
+            const int nlo = T > 0 ? lo + (T - 1) * step + 1 : lo;
+            const int nhi = T < valid ? lo + T * step : hi;
+            lo = nlo;
+            hi = nhi;
+            par ^= 1;
         }
-        __syncthreads();
-        while (true) {
-            const int lo = lo_s[h], hi = hi_s[h];
-            const bool open0 = lo_s[0] < hi_s[0], open1 = lo_s[1] < hi_s[1];
-            if (!open0 && !open1) break;  // uniform over the workgroup
-            __syncthreads();
-            if (t == 0) {
-                lo_n[h] = lo;
-                hi_n[h] = hi;
-            }
-            __syncthreads();
-            if (lo < hi) {
-                const int step = (hi - lo + 127) / 128;
-                const int a = lo + t * step;
-                if (a < hi) {
-                    if (A[a] < B[d - 1 - a])
-                        atomicMax(&lo_n[h], a + 1);  // the split lies above a
-                    else
-                        atomicMin(&hi_n[h], a);      // the split is at most a
-                }
-            }
-            __syncthreads();
-            if (t == 0) {
-                lo_s[h] = lo_n[h];
-                hi_s[h] = hi_n[h];
-            }
-            __syncthreads();
-        }
-        if (t == 0) split[h] = lo_s[h];
+        if (t == 0) split[h] = lo;
     }
     __syncthreads();
     const int a0 = split[0], a1 = split[1];
