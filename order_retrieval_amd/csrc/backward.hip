@@ -1181,8 +1181,8 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     marks.record(0, s);
     // the key codes and order follow the query ones in memory (zk = zq + BH N, perm_k =
     // perm_q + BH N): one order build takes both as 2 BH slices
-    hipError_t e = launch_encode2_perm(q, ws.zq, k, ws.zk, rows, kPermIdentity, s);
-    if (e == hipSuccess) e = launch_order(2 * BH, N, ws.zq, ws.perm_q, ws.ohist, s);
+    hipError_t e = launch_encode_order(q, ws.zq, k, ws.zk, BH, N, kPermIdentity, true,
+                                       ws.perm_q, ws.ohist, s);
     if (e != hipSuccess) return e;
     marks.record(1, s);
     e = launch_query<BF16>(BH, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,

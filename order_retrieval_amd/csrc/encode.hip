@@ -10,39 +10,9 @@
 // Memory-bound elementwise kernel: 12 B in, 4 B out per point.  Each thread converts four
 // consecutive points with three 16-byte loads and one 16-byte store.
 #include "zeta_internal.hpp"
+#include "morton.hpp"
 
 namespace zeta {
-
-__device__ __forceinline__ uint32_t cell10(float x) {
-    if (!(x == x)) return 0u;  // NaN
-    x = fminf(fmaxf(x, -4.0f), 4.0f);
-    int c = static_cast<int>(floorf(x * 128.0f)) + 512;
-    return static_cast<uint32_t>(c > 1023 ? 1023 : c);
-}
-
-// Spread the 10 low bits of v so that bit b moves to bit 3b.
-__device__ __forceinline__ uint32_t spread3(uint32_t v) {
-    v = (v | (v << 16)) & 0x030000FFu;
-    v = (v | (v << 8)) & 0x0300F00Fu;
-    v = (v | (v << 4)) & 0x030C30C3u;
-    v = (v | (v << 2)) & 0x09249249u;
-    return v;
-}
-
-__device__ __forceinline__ uint32_t morton3(float x0, float x1, float x2) {
-    return spread3(cell10(x0)) | (spread3(cell10(x1)) << 1) | (spread3(cell10(x2)) << 2);
-}
-
-// Coordinate `a` of the curve's axis order: axis a reads coordinate (perm >> 2a) & 3.
-__device__ __forceinline__ float axis_of(float x0, float x1, float x2, int perm, int a) {
-    const int c = (perm >> (2 * a)) & 3;
-    return c == 0 ? x0 : (c == 1 ? x1 : x2);
-}
-
-__device__ __forceinline__ uint32_t morton3p(float x0, float x1, float x2, int perm) {
-    return morton3(axis_of(x0, x1, x2, perm, 0), axis_of(x0, x1, x2, perm, 1),
-                   axis_of(x0, x1, x2, perm, 2));
-}
 
 // perm packs the curve's coordinate order (several-curve variant, rebuttal page on the
 // asymmetry of interleaving: the coordinates are fed to the curve in a permuted order);

@@ -12,6 +12,7 @@
 // tile's positions after the earlier tiles' positions of the same bucket (order inside a
 // tile's bucket comes from LDS atomics and is arbitrary).
 #include "zeta_internal.hpp"
+#include "morton.hpp"
 
 namespace zeta {
 
@@ -64,6 +65,64 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_hist_kernel(
     __syncthreads();
     hist[(bh * tiles + blockIdx.x) * kOrderThreads + tid] =
         make_uint4(cnt[tid * 4], cnt[tid * 4 + 1], cnt[tid * 4 + 2], cnt[tid * 4 + 3]);
+}
+
+// Codes and bucket counts in one pass: one workgroup per tile of kOrderTile positions of a
+// (b,h) slice and point set (blockIdx.z: 0 queries, 1 keys).  Each thread encodes four
+// consecutive points (three 16-byte loads and one 16-byte store when the slice rows allow)
+// and, for a set that gets a processing order, adds their buckets to the tile's counts;
+// the counts go to slice set * BH + bh, so keys stored right after the queries are ordered
+// by the same scan and scatter as 2 BH slices.
+__global__ void __launch_bounds__(kOrderThreads) zeta_encode_hist_kernel(
+    const float* __restrict__ q, uint32_t* __restrict__ zq, const float* __restrict__ k,
+    uint32_t* __restrict__ zk, int64_t BH, int64_t N, int64_t tiles, int perm, int vec_ok,
+    int count_keys, uint4* __restrict__ hist) {
+    __shared__ uint32_t cnt[kOrderBuckets];
+    const int set = blockIdx.z;
+    const float* __restrict__ x = set ? k : q;
+    uint32_t* __restrict__ z = set ? zk : zq;
+    const bool counted = set == 0 || count_keys != 0;  // uniform over the workgroup
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    if (counted) {
+#pragma unroll
+        for (int u = 0; u < kOrderPer; ++u) cnt[tid * kOrderPer + u] = 0;
+        __syncthreads();
+    }
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kOrderTile + tid * 4;  // in the slice
+    const int64_t r0 = bh * N + p0;                                              // row
+    uint32_t c[4];
+    bool ok[4];
+    if (vec_ok && p0 + 4 <= N) {  // N % 4 == 0 and aligned bases: row r0 starts a 16-byte word
+        const float4* xv = reinterpret_cast<const float4*>(x) + 3 * (r0 / 4);
+        const float4 a = xv[0], b = xv[1], d = xv[2];
+        c[0] = morton3p(a.x, a.y, a.z, perm);
+        c[1] = morton3p(a.w, b.x, b.y, perm);
+        c[2] = morton3p(b.z, b.w, d.x, perm);
+        c[3] = morton3p(d.y, d.z, d.w, perm);
+        *reinterpret_cast<uint4*>(z + r0) = make_uint4(c[0], c[1], c[2], c[3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ok[u] = true;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            ok[u] = p0 + u < N;
+            c[u] = 0;
+            if (ok[u]) {
+                const int64_t r = r0 + u;
+                c[u] = morton3p(x[3 * r], x[3 * r + 1], x[3 * r + 2], perm);
+                z[r] = c[u];
+            }
+        }
+    }
+    if (counted) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ok[u]) atomicAdd(&cnt[order_bucket(c[u])], 1u);
+        __syncthreads();
+        hist[((set * BH + bh) * tiles + blockIdx.x) * kOrderThreads + tid] =
+            make_uint4(cnt[tid * 4], cnt[tid * 4 + 1], cnt[tid * 4 + 2], cnt[tid * 4 + 3]);
+    }
 }
 
 // Per (b,h): exclusive scan in (bucket, tile) order, in place.  Thread t owns buckets
@@ -180,6 +239,29 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
             out[pos] = static_cast<uint32_t>(t0 + it * kOrderThreads + tid);
         }
     }
+}
+
+hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
+                               int64_t BH, int64_t N, int perm, bool order_keys,
+                               uint32_t* order, uint32_t* scratch, hipStream_t s) {
+    if (BH <= 0 || N <= 0) return hipSuccess;
+    // the keys' order slices follow the queries': their codes must too
+    if (order_keys && zk != zq + BH * N) return hipErrorInvalidValue;
+    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const int vec_ok = (N % 4 == 0) && a16(q) && a16(zq) && a16(k) && a16(zk);
+    const int64_t tiles = order_tiles(N);
+    const int64_t slices = order_keys ? 2 * BH : BH;
+    uint4* hist = reinterpret_cast<uint4*>(scratch);  // the workspace carve is 256-byte aligned
+    hipLaunchKernelGGL(zeta_encode_hist_kernel,
+                       dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(BH), 2u),
+                       dim3(kOrderThreads), 0, s, q, zq, k, zk, BH, N, tiles, perm, vec_ok,
+                       order_keys ? 1 : 0, hist);
+    hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(slices)),
+                       dim3(kOrderThreads), 0, s, hist, tiles);
+    hipLaunchKernelGGL(zeta_order_scatter_kernel,
+                       dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(slices)),
+                       dim3(kOrderThreads), 0, s, zq, N, tiles, hist, order);
+    return hipGetLastError();
 }
 
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,

@@ -279,15 +279,15 @@ zeta_status run_select(const zeta_shape* sh, const Opts& o, const float* q, cons
         if (wide) {
             e = zeta::launch_encode36_perm(q, BHN, perm, zq64, s);
             if (e == hipSuccess) e = zeta::launch_encode36_perm(k, BHN, perm, zk64, s);
+        } else if (o.mode != ZETA_SELECT_CHUNKED) {
+            // the codes and the query processing order of the select (and later of the
+            // gather)
+            e = zeta::launch_encode_order(q, zq, k, zk, BH, N, perm, false,
+                                          at<uint32_t>(ws, p.perm), at<uint32_t>(ws, p.ohist), s);
         } else {
             e = zeta::launch_encode2_perm(q, zq, k, zk, BHN, perm, s);
         }
         if (e != hipSuccess) return fail_hip("encode launch", e);
-        // the query processing order of the select (and later of the gather)
-        if (!wide && o.mode != ZETA_SELECT_CHUNKED) {
-            e = zeta::launch_order(BH, N, zq, at<uint32_t>(ws, p.perm), at<uint32_t>(ws, p.ohist), s);
-            if (e != hipSuccess) return fail_hip("order launch", e);
-        }
         if (c == 0) g_marks.record(1, s);
         e = wide ? zeta::launch_build_tree36(BH, N, L, p.first, zk64, ta, td, s)
                  : zeta::launch_build_tree(BH, N, L, p.first, zk, ta, td, s);

@@ -123,6 +123,12 @@ hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk,
 // Processing order: per (b,h), positions bucketed by the top code bits (order.hip).
 // scratch: order_scratch_words(BH, N) words.
 size_t order_scratch_words(int64_t BH, int64_t N);
+// Codes of q and k (curve order `perm`) and the processing order of the queries, and of the
+// keys too when order_keys (then zk must be zq + BH N, and `order` and `scratch` hold 2 BH
+// slices), in three launches.
+hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
+                               int64_t BH, int64_t N, int perm, bool order_keys,
+                               uint32_t* order, uint32_t* scratch, hipStream_t s);
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
                         uint32_t* scratch, hipStream_t s);
 
