@@ -203,18 +203,89 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scan_kernel(uint4* _
     }
 }
 
-// Places every position of a tile at its bucket's next free slot.
+// Exclusive sum over the workgroup's 1024 threads of one value each (wavefront shuffles,
+// then the sixteen wavefront totals in wavefront 0).  `part` holds kOrderThreads / 64 words.
+__device__ __forceinline__ uint32_t order_excl_scan(uint32_t mine, uint32_t* part) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t w = lane < kOrderThreads / 64 ? part[lane] : 0u;
+        uint32_t wi = w;
+        for (int off = 1; off < kOrderThreads / 64; off <<= 1) {
+            const uint32_t y = __shfl_up(wi, off, 64);
+            if (lane >= off) wi += y;
+        }
+        if (lane < kOrderThreads / 64) part[lane] = wi - w;  // exclusive wavefront offsets
+    }
+    __syncthreads();
+    return part[wave] + incl - mine;
+}
+
+// Slices of at most kFuseTiles tiles: the scatter workgroup scans the slice's counts itself
+// (every tile's counts of the thread's four buckets, then one workgroup scan), so no scan
+// launch runs between the counts and the scatter.
+constexpr int64_t kFuseTiles = 32;
+
+// Places every position of a tile at its bucket's next free slot.  SCAN: the counts are
+// raw and the workgroup forms its tile's bucket starts from them; otherwise they were
+// scanned in place by zeta_order_scan_kernel.
+template <bool SCAN>
 __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
     const uint32_t* __restrict__ codes, int64_t N, int64_t tiles, const uint4* __restrict__ hist,
     uint32_t* __restrict__ perm) {
     __shared__ uint32_t base[kOrderBuckets];
+    __shared__ uint32_t part[kOrderThreads / 64];
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x;
-    const uint4 b4 = hist[(bh * tiles + blockIdx.x) * kOrderThreads + tid];
-    base[tid * 4] = b4.x;
-    base[tid * 4 + 1] = b4.y;
-    base[tid * 4 + 2] = b4.z;
-    base[tid * 4 + 3] = b4.w;
+    if constexpr (SCAN) {
+        // bucket 4 tid + u starts after every position of the lower buckets and this
+        // bucket's positions in the earlier tiles
+        constexpr int kLoads = 8;
+        const uint4* h = hist + bh * tiles * kOrderThreads + tid;
+        uint32_t tot[kOrderPer] = {0, 0, 0, 0}, pre[kOrderPer] = {0, 0, 0, 0};
+        for (int64_t t0 = 0; t0 < tiles; t0 += kLoads) {
+            uint4 x[kLoads];
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                const int64_t t = t0 + u < tiles ? t0 + u : tiles - 1;
+                x[u] = h[t * kOrderThreads];
+            }
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) keep(x[u]);
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                if (t0 + u < tiles) {
+                    tot[0] += x[u].x;
+                    tot[1] += x[u].y;
+                    tot[2] += x[u].z;
+                    tot[3] += x[u].w;
+                    if (t0 + u < static_cast<int64_t>(blockIdx.x)) {
+                        pre[0] += x[u].x;
+                        pre[1] += x[u].y;
+                        pre[2] += x[u].z;
+                        pre[3] += x[u].w;
+                    }
+                }
+            }
+        }
+        const uint32_t ex = order_excl_scan(tot[0] + tot[1] + tot[2] + tot[3], part);
+        base[tid * 4] = ex + pre[0];
+        base[tid * 4 + 1] = ex + tot[0] + pre[1];
+        base[tid * 4 + 2] = ex + tot[0] + tot[1] + pre[2];
+        base[tid * 4 + 3] = ex + tot[0] + tot[1] + tot[2] + pre[3];
+    } else {
+        const uint4 b4 = hist[(bh * tiles + blockIdx.x) * kOrderThreads + tid];
+        base[tid * 4] = b4.x;
+        base[tid * 4 + 1] = b4.y;
+        base[tid * 4 + 2] = b4.z;
+        base[tid * 4 + 3] = b4.w;
+    }
     __syncthreads();
     const uint32_t* c = codes + bh * N;
     uint32_t* out = perm + bh * N;
@@ -241,6 +312,24 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
     }
 }
 
+// The scan (in place, unless the scatter does it) and the scatter of `slices` slices whose
+// counts are in hist.
+static hipError_t order_scan_scatter(int64_t slices, int64_t N, int64_t tiles,
+                                     const uint32_t* codes, uint4* hist, uint32_t* perm,
+                                     hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(slices));
+    if (tiles <= kFuseTiles) {
+        hipLaunchKernelGGL(zeta_order_scatter_kernel<true>, grid, dim3(kOrderThreads), 0, s, codes,
+                           N, tiles, hist, perm);
+    } else {
+        hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(slices)),
+                           dim3(kOrderThreads), 0, s, hist, tiles);
+        hipLaunchKernelGGL(zeta_order_scatter_kernel<false>, grid, dim3(kOrderThreads), 0, s,
+                           codes, N, tiles, hist, perm);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
                                int64_t BH, int64_t N, int perm, bool order_keys,
                                uint32_t* order, uint32_t* scratch, hipStream_t s) {
@@ -256,12 +345,7 @@ hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uin
                        dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(BH), 2u),
                        dim3(kOrderThreads), 0, s, q, zq, k, zk, BH, N, tiles, perm, vec_ok,
                        order_keys ? 1 : 0, hist);
-    hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(slices)),
-                       dim3(kOrderThreads), 0, s, hist, tiles);
-    hipLaunchKernelGGL(zeta_order_scatter_kernel,
-                       dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(slices)),
-                       dim3(kOrderThreads), 0, s, zq, N, tiles, hist, order);
-    return hipGetLastError();
+    return order_scan_scatter(slices, N, tiles, zq, hist, order, s);
 }
 
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
@@ -272,11 +356,7 @@ hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* 
     uint4* hist = reinterpret_cast<uint4*>(scratch);  // the workspace carve is 256-byte aligned
     hipLaunchKernelGGL(zeta_order_hist_kernel, grid, dim3(kOrderThreads), 0, s, codes, N, tiles,
                        hist);
-    hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(BH)), dim3(kOrderThreads),
-                       0, s, hist, tiles);
-    hipLaunchKernelGGL(zeta_order_scatter_kernel, grid, dim3(kOrderThreads), 0, s, codes, N, tiles,
-                       hist, perm);
-    return hipGetLastError();
+    return order_scan_scatter(BH, N, tiles, codes, hist, perm, s);
 }
 
 }  // namespace zeta
