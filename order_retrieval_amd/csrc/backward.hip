@@ -8,16 +8,20 @@
 //     dk_j =  (2/gamma^2) sum_i c_ij (q_i - k_j)        dgamma = (2/gamma^3) sum c_ij d_ij
 //
 // Pipeline (no floating-point atomics anywhere, so results are bitwise reproducible):
-//   1. per-query pass: recompute s, gather v rows for g, write a_ij and c_ij of every
-//      selection slot, dq_i and the query's dgamma term;
+//   1. per-query pass (queries in the Z-order processing order): recompute s, gather v rows
+//      for g, write a_ij and c_ij of every selection slot and the query record {q_i, i}, both
+//      at the query's rank in that order, and dq_i and the query's dgamma term;
 //   2. selection transpose, a stable radix sort of the pairs of every (b,h) by key: a global
-//      pass on the low byte of j builds 8-byte records {j, slot} grouped by that byte;
+//      pass on the low byte of j builds 8-byte records {j, slot} grouped by that byte (the
+//      slot named by the query's rank);
 //   3. keys below 2^16: one workgroup per low-byte group sorts it on the high byte and writes
 //      every key's segment bounds, leaving the slots in contiguous per-key segments (queries
 //      ascending inside a segment); larger keys: global passes on the further bytes, then
 //      the segment starts from the sorted keys;
-//   4. per-key pass (keys in Z-order): each key gathers its pairs' {a_ij, c_ij}, q_i and dO_i
-//      rows and reduces its segment in a fixed order (dv, dk);
+//   4. per-key pass (keys in Z-order): each key gathers its pairs' {a_ij, c_ij}, query records
+//      and dO_i rows and reduces its segment in a fixed order (dv, dk).  The pairs of keys
+//      close on the curve come from queries close on the curve, whose ranks are close, so the
+//      rank layout keeps those gathers inside a few cache lines;
 //   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
 // g_ij = dO_i . v_j is formed once, on the query side, which owns dO_i; the key side only
 // scales and adds rows.
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t N, int64_t H,
     int dv, int topk, int causal, int64_t tph, int64_t tiles, int64_t per_xcd,
-    float2* __restrict__ coef, float* __restrict__ dq, float* __restrict__ dg_row) {
+    float2* __restrict__ coef, float4* __restrict__ qrec, float* __restrict__ dq,
+    float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -255,7 +260,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
     const float D = group_sum(tsum, kRowLanes) * inv_S;
 
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, ag = 0.0f;
-    float2* cr = coef + row * topk;
+    float2* cr = coef + (bh * N + pp) * topk;  // slots of the query's rank
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (sel[u]) {
@@ -278,6 +283,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_kernel(
         dq[3 * row + 1] = f * a1;
         dq[3 * row + 2] = f * a2;
         dg_row[row] = 2.0f * inv_g2 / g * ag;
+        qrec[bh * N + pp] = make_float4(q0, q1, q2, __uint_as_float(static_cast<uint32_t>(i)));
     }
 }
 
@@ -296,7 +302,8 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_wide_kernel(
     const float* __restrict__ gamma, const int32_t* __restrict__ idx,
     const void* __restrict__ dout, const uint32_t* __restrict__ order, int64_t N, int64_t H,
     int dv, int topk, int causal, int64_t tph, int64_t tiles, int64_t per_xcd,
-    float2* __restrict__ coef, float* __restrict__ dq, float* __restrict__ dg_row) {
+    float2* __restrict__ coef, float4* __restrict__ qrec, float* __restrict__ dq,
+    float* __restrict__ dg_row) {
     using IO = VecIO<BF16>;
     using T = typename IO::elem_t;
     constexpr int E = IO::kElems;
@@ -319,7 +326,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_wide_kernel(
     const int32_t* ir = idx + row * topk;
     const float* kh = k + bh * N * 3;
     const T* vh = static_cast<const T*>(v) + bh * N * dv;
-    float2* cr = coef + row * topk;
+    float2* cr = coef + (bh * N + pp) * topk;  // slots of the query's rank
 
     float go[CPL][E];
     int coff[CPL];  // element offset of the lane's chunks (clamped; chunks past the row meet go = 0)
@@ -437,6 +444,7 @@ __global__ void __launch_bounds__(kQueryThreads) zeta_bwd_query_wide_kernel(
         dq[3 * row + 1] = f * a1;
         dq[3 * row + 2] = f * a2;
         dg_row[row] = 2.0f * inv_g2 / g * ag;
+        qrec[bh * N + pp] = make_float4(q0, q1, q2, __uint_as_float(static_cast<uint32_t>(i)));
     }
 }
 
@@ -444,8 +452,8 @@ template <bool BF16, bool O32, int CPL>
 static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int topk,
                                  int causal, const float* q, const float* k, const void* v,
                                  const float* gamma, const int32_t* idx, const void* dout,
-                                 const uint32_t* order, float2* coef, float* dq, float* dg_row,
-                                 hipStream_t s) {
+                                 const uint32_t* order, float2* coef, float4* qrec, float* dq,
+                                 float* dg_row, hipStream_t s) {
     const int64_t tph = (N + kQueryRows - 1) / kQueryRows;
     const int64_t tiles = BH * tph;
     const int64_t per = xcd_per(tiles);
@@ -456,8 +464,8 @@ static hipError_t launch_query_c(int64_t BH, int64_t N, int64_t H, int dv, int t
                        : zeta_bwd_query_wide_kernel<BF16, O32, CPL>;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kQueryThreads), 0, s,
                        q, k, v,
-                       gamma, idx, dout, order, N, H, dv, topk, causal, tph, tiles, per, coef, dq,
-                       dg_row);
+                       gamma, idx, dout, order, N, H, dv, topk, causal, tph, tiles, per, coef,
+                       qrec, dq, dg_row);
     return hipGetLastError();
 }
 
@@ -465,31 +473,32 @@ template <bool BF16, int CPL>
 static hipError_t launch_query_o(int64_t BH, int64_t N, int64_t H, int dv, int topk,
                                  int causal, const float* q, const float* k, const void* v,
                                  const float* gamma, const int32_t* idx, const void* dout,
-                                 const uint32_t* order, float2* coef, float* dq, float* dg_row,
-                                 hipStream_t s) {
+                                 const uint32_t* order, float2* coef, float4* qrec, float* dq,
+                                 float* dg_row, hipStream_t s) {
     if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
-        return launch_query_c<BF16, true, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
-    return launch_query_c<BF16, false, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+        return launch_query_c<BF16, true, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
+    return launch_query_c<BF16, false, CPL>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
 }
 
 template <bool BF16>
 static hipError_t launch_query(int64_t BH, int64_t N, int64_t H, int dv, int topk, int causal,
                                const float* q, const float* k, const void* v, const float* gamma,
                                const int32_t* idx, const void* dout, const uint32_t* order,
-                               float2* coef, float* dq, float* dg_row, hipStream_t s) {
+                               float2* coef, float4* qrec, float* dq, float* dg_row,
+                               hipStream_t s) {
     const int cpl = (dv / VecIO<BF16>::kElems + kRowLanes - 1) / kRowLanes;
     if (cpl <= 1)
-        return launch_query_o<BF16, 1>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+        return launch_query_o<BF16, 1>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
     if (cpl <= 2)
-        return launch_query_o<BF16, 2>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+        return launch_query_o<BF16, 2>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
     if (BF16 || cpl <= 4)  // bf16 rows have <= 64 chunks
-        return launch_query_o<BF16, 4>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
-    return launch_query_o<BF16, BF16 ? 4 : 8>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, dq, dg_row, s);
+        return launch_query_o<BF16, 4>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
+    return launch_query_o<BF16, BF16 ? 4 : 8>(BH, N, H, dv, topk, causal, q, k, v, gamma, idx, dout, order, coef, qrec, dq, dg_row, s);
 }
 
 // ---------------------------------------------------------------------------- 2. transpose
-// Every pair travels through the sort as one 8-byte record {j, p}, p = i * topk + r the
-// pair's selection slot.  Pass 0 reads the
+// Every pair travels through the sort as one 8-byte record {j, p}, p = rank(i) * topk + r
+// the pair's slot in the per-query pass's rank-ordered coefficients.  Pass 0 reads the
 // selection in pair order (coalesced) and builds the records; later passes move records.
 // The key kernel then reads each key's pairs as one contiguous run of records.
 // A tile's items are loaded from clamped positions (item min(e, items - 1); with no items at
@@ -584,7 +593,7 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     const int32_t* __restrict__ idx, const uint2* __restrict__ rin, int64_t slots,
     uint32_t* __restrict__ counts, int64_t in_stride, int shift, int64_t tiles, PairSpec ps,
     const uint32_t* __restrict__ hist, const uint32_t* __restrict__ totals, int64_t P,
-    uint2* __restrict__ rout) {
+    const uint32_t* __restrict__ rank_of, uint2* __restrict__ rout) {
     constexpr int kWaves = kRadixThreads / 64;
     constexpr int kWaveItems = kRadixTile / kWaves;
     __shared__ uint2 stage[kRadixTile];
@@ -603,14 +612,35 @@ __global__ void __launch_bounds__(kRadixThreads) zeta_radix_scatter_kernel(
     uint32_t okmask = 0;
     {
         const int64_t off = bh * in_stride;
+        // pass 0: the rank of the slot's query in the processing order (slot e belongs to
+        // query e / topk; clamped positions, in flight with the indices)
+        uint32_t rk[kRadixItems];
 #pragma unroll
-        for (int it = 0; it < kRadixItems; ++it)
+        for (int it = 0; it < kRadixItems; ++it) {
             rec[it] = load_item<FIRST>(idx + off, rin + off, t0 + it * 64 + lane, items);
+            if constexpr (FIRST) {
+                const int64_t e = t0 + it * 64 + lane;
+                const int64_t ec = e < items ? e : (items > 0 ? items - 1 : 0);
+                rk[it] = rank_of[bh * ps.N + div_u32(static_cast<uint32_t>(ec), ps.by_topk)];
+            }
+        }
 #pragma unroll
-        for (int it = 0; it < kRadixItems; ++it) keep(rec[it]);
+        for (int it = 0; it < kRadixItems; ++it) {
+            keep(rec[it]);
+            if constexpr (FIRST) keep(rk[it]);
+        }
 #pragma unroll
-        for (int it = 0; it < kRadixItems; ++it)
-            if (make_item<FIRST>(rec[it], t0 + it * 64 + lane, items, ps)) okmask |= 1u << it;
+        for (int it = 0; it < kRadixItems; ++it) {
+            if (make_item<FIRST>(rec[it], t0 + it * 64 + lane, items, ps)) {
+                okmask |= 1u << it;
+                if constexpr (FIRST) {
+                    // the record names the slot r of the query's rank: rank * topk + r
+                    const uint32_t e = rec[it].y;
+                    const uint32_t r = e - div_u32(e, ps.by_topk) * static_cast<uint32_t>(ps.topk);
+                    rec[it].y = rk[it] * static_cast<uint32_t>(ps.topk) + r;
+                }
+            }
+        }
     }
 
 #pragma unroll
@@ -889,8 +919,9 @@ __global__ void __launch_bounds__(256) zeta_segment_offsets_kernel(const uint2* 
 // processing order: the queries that selected a key are near it on the curve, so keys that
 // run together read overlapping dO rows and L2 serves the repeats.  A key's pairs are a
 // contiguous run of records, taken 16 at a time: lane l of the row owns record l of the batch
-// (its slot is loaded one batch ahead) and loads the slot's {a_ij, c_ij} (written by the
-// per-query pass) and q_i.  The row then walks the batch's records in order: i and a_ij come from the owning lane
+// (its slot is loaded two batches ahead) and loads the slot's {a_ij, c_ij} and its query's
+// record {q_i, i} one batch ahead (both written by the per-query pass at the query's rank).
+// The row then walks the batch's records in order: i and a_ij come from the owning lane
 // by a DPP row broadcast, every lane loads its chunks of the dO_i row (the loads of kKeyLoads
 // records are issued together) and adds a_ij dO_i to its chunks of dv_j; the owning lane adds
 // c_ij (q_i - k_j) to the dk sum.  No LDS traffic; the trip counts are uniform over the
@@ -928,8 +959,9 @@ __device__ __forceinline__ void key_records(const typename VecIO<BF16>::elem_t* 
 
 template <bool BF16, bool O32, int CPL>
 __global__ void __launch_bounds__(kKeyThreads) zeta_bwd_key_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ gamma,
+    const float* __restrict__ k, const float* __restrict__ gamma,
     const void* __restrict__ dout, const float2* __restrict__ coef,
+    const float4* __restrict__ qrec,
     const uint32_t* __restrict__ slots, int slot_stride, const uint32_t* __restrict__ seg_lo,
     const uint32_t* __restrict__ seg_hi, const uint32_t* __restrict__ order, int64_t N,
     int64_t H, int dv, int topk, DivU32 slot_div,
@@ -978,7 +1010,7 @@ __global__ void __launch_bounds__(kKeyThreads) zeta_bwd_key_kernel(
     const uint32_t seg0 = seg_lo[bh * (N + 1) + j];
     const int cnt = live ? static_cast<int>(seg_hi[bh * (N + 1) + j] - seg0) : 0;
     const uint32_t* rh = slots + (bh * P + seg0) * slot_stride;
-    const float* qh = q + bh * N * 3;
+    const float4* qrh = qrec + bh * N;
     const float2* cf = coef + bh * N * topk;
     const T* doh = static_cast<const T*>(dout) + bh * N * dv;
 
@@ -1003,19 +1035,26 @@ __global__ void __launch_bounds__(kKeyThreads) zeta_bwd_key_kernel(
     auto slot_at = [&](int p) -> uint32_t {
         return cnt > 0 ? rh[(p < last ? p : last) * slot_stride] : 0u;
     };
+    // two-deep: while a batch's dO rows load, the next batch's {a, c} and query record and
+    // the slot after it are in flight
     uint32_t slot_next = slot_at(lrow);
+    float2 ac_next = cf[slot_next];
+    float4 q_next = qrh[div_u32(slot_next, slot_div)];  // the slot's query: q_i and i
+    if (kKeyRow < most) slot_next = slot_at(lrow + kKeyRow);
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
     for (int first = 0; first < most; first += kKeyRow) {  // batches of 16 records
         const int p = first + lrow;
         const bool own = p < cnt;
-        const uint32_t slot = slot_next;
-        if (first + kKeyRow < most) slot_next = slot_at(p + kKeyRow);  // in flight meanwhile
-        const uint32_t io = div_u32(slot, slot_div);
-        const float2 ac = cf[slot];
-        const Point3 qi = load_point(qh, io);
+        const float2 ac = ac_next;
+        const float4 qi = q_next;
+        if (first + kKeyRow < most) {  // uniform
+            ac_next = cf[slot_next];
+            q_next = qrh[div_u32(slot_next, slot_div)];
+            if (first + 2 * kKeyRow < most) slot_next = slot_at(p + 2 * kKeyRow);
+        }
         const float dx = qi.x - k0, dy = qi.y - k1, dz = qi.z - k2;
         const float ao = own ? ac.x : 0.0f;
-        const uint32_t nm = RowRef<BF16, O32>::name(io, dv);
+        const uint32_t nm = RowRef<BF16, O32>::name(__float_as_uint(qi.w), dv);
         static_for<0, kKeyRow / kKeyLoads>([&](auto bc) {
             constexpr int b = decltype(bc)::value * kKeyLoads;
             if (first + b < most)  // uniform
@@ -1061,7 +1100,7 @@ struct KeySegments {
 
 template <bool BF16, bool O32>
 static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int topk,
-                               const float* q, const float* k, const float* gamma,
+                               const float* k, const float* gamma,
                                const void* dout, const BwdBuffers& ws, const KeySegments& sg,
                                const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     const int chunks = dv / VecIO<BF16>::kElems;
@@ -1073,8 +1112,8 @@ static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int top
               : cpl <= 2 ? zeta_bwd_key_kernel<BF16, O32, 2>
               : cpl <= 4 ? zeta_bwd_key_kernel<BF16, O32, 4>
                          : zeta_bwd_key_kernel<BF16, O32, BF16 ? 4 : 8>;  // bf16: <= 64 chunks
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kKeyThreads), 0, s, q, k,
-                       gamma, dout, ws.coef, sg.slots, sg.stride, sg.lo, sg.hi, order, N, H, dv,
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(per * kXcds)), dim3(kKeyThreads), 0, s, k,
+                       gamma, dout, ws.coef, ws.qrec, sg.slots, sg.stride, sg.lo, sg.hi, order, N, H, dv,
                        topk,
                        make_div(static_cast<uint32_t>(topk)), ws.P, tph, tiles, per, dk, dvout);
     return hipGetLastError();
@@ -1082,12 +1121,12 @@ static hipError_t launch_key_o(int64_t BH, int64_t H, int64_t N, int dv, int top
 
 template <bool BF16>
 static hipError_t launch_key(int64_t BH, int64_t H, int64_t N, int dv, int topk,
-                             const float* q, const float* k, const float* gamma,
+                             const float* k, const float* gamma,
                              const void* dout, const BwdBuffers& ws, const KeySegments& sg,
                              const uint32_t* order, float* dk, void* dvout, hipStream_t s) {
     if (rows_fit_32(N, dv, sizeof(typename VecIO<BF16>::elem_t)))
-        return launch_key_o<BF16, true>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, order, dk, dvout, s);
-    return launch_key_o<BF16, false>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, order, dk, dvout, s);
+        return launch_key_o<BF16, true>(BH, H, N, dv, topk, k, gamma, dout, ws, sg, order, dk, dvout, s);
+    return launch_key_o<BF16, false>(BH, H, N, dv, topk, k, gamma, dout, ws, sg, order, dk, dvout, s);
 }
 
 // ---------------------------------------------------------------------------- 5. dgamma
@@ -1168,7 +1207,7 @@ static void radix_pass(int64_t BH, const int32_t* idx, const uint2* rin, int64_t
     hipLaunchKernelGGL(zeta_radix_scan_kernel, dim3(256, static_cast<unsigned>(BH)), dim3(64), 0, s,
                        ws.hist, tiles, ws.totals);
     hipLaunchKernelGGL((zeta_radix_scatter_kernel<FIRST, PACK>), grid, dim3(kRadixThreads), 0, s, idx, rin,
-                       items, ws.counts, stride, shift, tiles, ps, ws.hist, ws.totals, ws.P, rout);
+                       items, ws.counts, stride, shift, tiles, ps, ws.hist, ws.totals, ws.P, ws.rank_q, rout);
 }
 
 template <bool BF16>
@@ -1182,11 +1221,11 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     // the key codes and order follow the query ones in memory (zk = zq + BH N, perm_k =
     // perm_q + BH N): one order build takes both as 2 BH slices
     hipError_t e = launch_encode_order(q, ws.zq, k, ws.zk, BH, N, kPermIdentity, true,
-                                       ws.perm_q, ws.ohist, s);
+                                       ws.perm_q, ws.ohist, s, ws.rank_q);
     if (e != hipSuccess) return e;
     marks.record(1, s);
     e = launch_query<BF16>(BH, N, H, dv, topk, causal ? 1 : 0, q, k, v, gamma, idx, dout,
-                           ws.perm_q, ws.coef, dq, ws.dg_row, s);
+                           ws.perm_q, ws.coef, ws.qrec, dq, ws.dg_row, s);
     if (e != hipSuccess) return e;
     marks.record(2, s);
 
@@ -1221,7 +1260,7 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     marks.record(3, s);
-    e = launch_key<BF16>(BH, H, N, dv, topk, q, k, gamma, dout, ws, sg, ws.perm_k, dk, dvout, s);
+    e = launch_key<BF16>(BH, H, N, dv, topk, k, gamma, dout, ws, sg, ws.perm_k, dk, dvout, s);
     if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);

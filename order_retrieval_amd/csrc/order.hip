@@ -238,7 +238,7 @@ constexpr int64_t kFuseTiles = 32;
 template <bool SCAN>
 __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
     const uint32_t* __restrict__ codes, int64_t N, int64_t tiles, const uint4* __restrict__ hist,
-    uint32_t* __restrict__ perm) {
+    uint32_t* __restrict__ perm, uint32_t* __restrict__ rank_of, int64_t rank_slices) {
     __shared__ uint32_t base[kOrderBuckets];
     __shared__ uint32_t part[kOrderThreads / 64];
     const int64_t bh = blockIdx.y;
@@ -308,6 +308,8 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
         if (bk[it] < kOrderBuckets) {
             const uint32_t pos = atomicAdd(&base[bk[it]], 1u);
             out[pos] = static_cast<uint32_t>(t0 + it * kOrderThreads + tid);
+            // the inverse, position -> rank (consecutive threads write consecutive positions)
+            if (bh < rank_slices) rank_of[bh * N + t0 + it * kOrderThreads + tid] = pos;
         }
     }
 }
@@ -316,23 +318,24 @@ __global__ void __launch_bounds__(kOrderThreads) zeta_order_scatter_kernel(
 // counts are in hist.
 static hipError_t order_scan_scatter(int64_t slices, int64_t N, int64_t tiles,
                                      const uint32_t* codes, uint4* hist, uint32_t* perm,
-                                     hipStream_t s) {
+                                     uint32_t* rank_of, int64_t rank_slices, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(slices));
     if (tiles <= kFuseTiles) {
         hipLaunchKernelGGL(zeta_order_scatter_kernel<true>, grid, dim3(kOrderThreads), 0, s, codes,
-                           N, tiles, hist, perm);
+                           N, tiles, hist, perm, rank_of, rank_slices);
     } else {
         hipLaunchKernelGGL(zeta_order_scan_kernel, dim3(static_cast<unsigned>(slices)),
                            dim3(kOrderThreads), 0, s, hist, tiles);
         hipLaunchKernelGGL(zeta_order_scatter_kernel<false>, grid, dim3(kOrderThreads), 0, s,
-                           codes, N, tiles, hist, perm);
+                           codes, N, tiles, hist, perm, rank_of, rank_slices);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
                                int64_t BH, int64_t N, int perm, bool order_keys,
-                               uint32_t* order, uint32_t* scratch, hipStream_t s) {
+                               uint32_t* order, uint32_t* scratch, hipStream_t s,
+                               uint32_t* rank_of) {
     if (BH <= 0 || N <= 0) return hipSuccess;
     // the keys' order slices follow the queries': their codes must too
     if (order_keys && zk != zq + BH * N) return hipErrorInvalidValue;
@@ -345,7 +348,7 @@ hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uin
                        dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(BH), 2u),
                        dim3(kOrderThreads), 0, s, q, zq, k, zk, BH, N, tiles, perm, vec_ok,
                        order_keys ? 1 : 0, hist);
-    return order_scan_scatter(slices, N, tiles, zq, hist, order, s);
+    return order_scan_scatter(slices, N, tiles, zq, hist, order, rank_of, rank_of ? BH : 0, s);
 }
 
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
@@ -356,7 +359,7 @@ hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* 
     uint4* hist = reinterpret_cast<uint4*>(scratch);  // the workspace carve is 256-byte aligned
     hipLaunchKernelGGL(zeta_order_hist_kernel, grid, dim3(kOrderThreads), 0, s, codes, N, tiles,
                        hist);
-    return order_scan_scatter(BH, N, tiles, codes, hist, perm, s);
+    return order_scan_scatter(BH, N, tiles, codes, hist, perm, nullptr, 0, s);
 }
 
 }  // namespace zeta

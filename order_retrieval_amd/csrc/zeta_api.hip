@@ -194,7 +194,8 @@ FwdPlan plan_fwd(const zeta_shape* sh, const Opts& o) {
 }
 
 struct BwdPlan {
-    size_t qs, dg, dgp, r0, r1, hist, totals, counts, offs, ends, zq, pq, zk, pk, ohist, total;
+    size_t qs, qr, rq, dg, dgp, r0, r1, hist, totals, counts, offs, ends, zq, pq, zk, pk, ohist,
+        total;
     int64_t P, tiles;
 };
 
@@ -210,6 +211,8 @@ BwdPlan plan_bwd(const zeta_shape* sh, const Opts& o) {
         return at;
     };
     p.qs = take(2 * sizeof(float) * BH * N * K);
+    p.qr = take(4 * sizeof(float) * BH * N);
+    p.rq = take(sizeof(uint32_t) * BH * N);
     p.dg = take(sizeof(float) * BH * N);
     p.dgp = take(sizeof(float) * sh->H * zeta::dgamma_chunks(sh->B, N));
     // rec1: the second radix ping-pong buffer of 8-byte records when keys need more than 16
@@ -531,6 +534,8 @@ zeta_status zeta_bwd_ex(const zeta_shape* shape, const zeta_select_opts* opts, c
     if ((st = preflight()) != ZETA_OK) return st;
     zeta::BwdBuffers b{};
     b.coef = at<float2>(workspace, p.qs);
+    b.qrec = at<float4>(workspace, p.qr);
+    b.rank_q = at<uint32_t>(workspace, p.rq);
     b.dg_row = at<float>(workspace, p.dg);
     b.dg_part = at<float>(workspace, p.dgp);
     b.rec0 = at<uint2>(workspace, p.r0);

@@ -125,10 +125,12 @@ hipError_t launch_gather(int64_t BH, int64_t H, int64_t N, int64_t dv, int topk,
 size_t order_scratch_words(int64_t BH, int64_t N);
 // Codes of q and k (curve order `perm`) and the processing order of the queries, and of the
 // keys too when order_keys (then zk must be zq + BH N, and `order` and `scratch` hold 2 BH
-// slices), in three launches.
+// slices), in three launches.  rank_of, when not null, takes the inverse of the queries'
+// order: rank_of[bh N + i] = the rank of query i ([BHN] words).
 hipError_t launch_encode_order(const float* q, uint32_t* zq, const float* k, uint32_t* zk,
                                int64_t BH, int64_t N, int perm, bool order_keys,
-                               uint32_t* order, uint32_t* scratch, hipStream_t s);
+                               uint32_t* order, uint32_t* scratch, hipStream_t s,
+                               uint32_t* rank_of = nullptr);
 hipError_t launch_order(int64_t BH, int64_t N, const uint32_t* codes, uint32_t* perm,
                         uint32_t* scratch, hipStream_t s);
 
@@ -139,7 +141,9 @@ hipError_t launch_probe_row_gather(const void* table, int64_t table_rows, int ro
                                    uint32_t* sink, hipStream_t s);
 
 struct BwdBuffers {
-    float2* coef;     // [BH, N, topk] per selection slot {a_ij, c_ij}
+    float2* coef;     // [BH][N][topk] per selection slot {a_ij, c_ij}, queries in processing order
+    float4* qrec;     // [BH][N] per query in processing order: {q_i, i}
+    uint32_t* rank_q; // [BH][N] rank of each query in its processing order
     float* dg_row;    // [BHN] per-query dgamma contributions
     float* dg_part;   // [H][dgamma_chunks] partial sums
     uint2* rec0;      // [BH][P] radix-sort ping-pong records {j, p}; with keys below 2^16
