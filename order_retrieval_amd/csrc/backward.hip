@@ -106,9 +106,9 @@ static_assert(kRowLoads == 8 && kRowLanes == 16, "two 8-slot reduce-scatters per
 __device__ __forceinline__ int query_slot_of_lane(int l) { return (l & 1) * 8 + (l >> 1); }
 constexpr int query_lane_of_slot(int s) { return (s & 7) * 2 + (s >> 3); }
 // Workgroup sizes (measured): more curve neighbours per workgroup share a CU's L1 in the
-// per-query pass; the per-key pass keeps 256 (its rows are ordered by pair count within a
-// workgroup, and more VGPRs per lane limit larger workgroups to fewer waves per SIMD).
-constexpr int kQueryThreads = 512;  // workgroup of the per-query pass
+// per-query pass (64 queries: 0.290 ms, 32: 0.297, 16: 0.315); the per-key pass keeps 256
+// (8 keys: the same; 20 or 40 keys: 0.45 and 0.49 ms against 0.384).
+constexpr int kQueryThreads = 1024;  // workgroup of the per-query pass
 constexpr int kKeyThreads = 256;    // workgroup of the per-key pass
 constexpr int kQueryRows = kQueryThreads / kRowLanes;  // queries per workgroup (one (b,h))
 constexpr int kKeyRows = kKeyThreads / kRowLanes;      // keys per workgroup (one (b,h))
