@@ -22,7 +22,8 @@
 //      and dO_i rows and reduces its segment in a fixed order (dv, dk).  The pairs of keys
 //      close on the curve come from queries close on the curve, whose ranks are close, so the
 //      rank layout keeps those gathers inside a few cache lines;
-//   5. dgamma: two-level fixed-order reduction per head over the batch and the queries.
+//   5. dgamma: fixed-order reduction per head over the batch and the queries (one workgroup
+//      per head, or two levels for long heads).
 // g_ij = dO_i . v_j is formed once, on the query side, which owns dO_i; the key side only
 // scales and adds rows.
 #include "zeta_internal.hpp"
@@ -1175,6 +1176,41 @@ __global__ void __launch_bounds__(64) zeta_dgamma_final_kernel(const float* __re
     if (threadIdx.x == 0) dgamma[h] = acc;
 }
 
+// Up to kDgHeadMax terms per head: one workgroup per head sums them all (each thread its
+// strided share, eight loads in flight, then an LDS tree), one launch instead of two.
+constexpr int kDgHeadThreads = 1024;
+constexpr int64_t kDgHeadMax = int64_t(1) << 18;
+__global__ void __launch_bounds__(kDgHeadThreads) zeta_dgamma_head_kernel(
+    const float* __restrict__ dg_row, int64_t B, int64_t H, int64_t N, float* __restrict__ dgamma) {
+    __shared__ float red[kDgHeadThreads];
+    const int64_t h = blockIdx.x;
+    const int tid = threadIdx.x;
+    float acc = 0.0f;
+    for (int64_t b = 0; b < B; ++b) {
+        const float* row = dg_row + (b * H + h) * N;
+        for (int64_t i0 = 0; i0 < N; i0 += 8 * kDgHeadThreads) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {  // clamped positions: the loads issue together
+                const int64_t i = i0 + u * kDgHeadThreads + tid;
+                x[u] = row[i < N ? i : N - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) keep(x[u]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * kDgHeadThreads + tid < N) acc += x[u];
+        }
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int w = kDgHeadThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) dgamma[h] = red[0];
+}
+
 int64_t dgamma_chunks(int64_t B, int64_t N) { return (B * N + kDgChunk - 1) / kDgChunk; }
 
 // ---------------------------------------------------------------------------- host
@@ -1264,11 +1300,16 @@ static hipError_t launch_bwd_t(int64_t BH, int64_t H, int64_t N, int dv, int top
     if (e != hipSuccess) return e;
     marks.record(4, s);
     const int64_t dch = dgamma_chunks(BH / H, N);
-    hipLaunchKernelGGL(zeta_dgamma_partial_kernel,
-                       dim3(static_cast<unsigned>(dch), static_cast<unsigned>(H)), dim3(256), 0, s,
-                       ws.dg_row, BH / H, H, N, dch, ws.dg_part);
-    hipLaunchKernelGGL(zeta_dgamma_final_kernel, dim3(static_cast<unsigned>(H)), dim3(64), 0, s,
-                       ws.dg_part, dch, dgamma);
+    if ((BH / H) * N <= kDgHeadMax) {
+        hipLaunchKernelGGL(zeta_dgamma_head_kernel, dim3(static_cast<unsigned>(H)),
+                           dim3(kDgHeadThreads), 0, s, ws.dg_row, BH / H, H, N, dgamma);
+    } else {
+        hipLaunchKernelGGL(zeta_dgamma_partial_kernel,
+                           dim3(static_cast<unsigned>(dch), static_cast<unsigned>(H)), dim3(256), 0,
+                           s, ws.dg_row, BH / H, H, N, dch, ws.dg_part);
+        hipLaunchKernelGGL(zeta_dgamma_final_kernel, dim3(static_cast<unsigned>(H)), dim3(64), 0, s,
+                           ws.dg_part, dch, dgamma);
+    }
     marks.record(5, s);
     return hipGetLastError();
 }
