@@ -386,10 +386,18 @@ static hipError_t build_tree_t(int64_t BH, int64_t N, int levels, int first, con
     dim3 grid(static_cast<unsigned>((N + kTile - 1) / kTile), static_cast<unsigned>(BH));
     const int base = tree_store_base(levels, first);
     const int stored = levels > base ? levels - base : 0;
-    // one workgroup per tile and tree (z = 0 asc, z = 1 desc)
+    // one workgroup per tile and tree (z = 0 asc, z = 1 desc); a sequence of at most 1024 or
+    // 2048 keys takes a tile of that size (one workgroup per tree, a quarter or half the work)
     dim3 g3(grid.x, grid.y, 2);
-    hipLaunchKernelGGL((zeta_tree_radix_tile_kernel<CT, S, kTileLog>), g3, dim3(kRTThreads), 0, s,
-                       zk, tree_asc, tree_desc, N, stored, top_tile, base);
+    if (N <= 1024)
+        hipLaunchKernelGGL((zeta_tree_radix_tile_kernel<CT, S, 10>), g3, dim3(kRTThreads), 0, s,
+                           zk, tree_asc, tree_desc, N, stored, top_tile, base);
+    else if (N <= 2048)
+        hipLaunchKernelGGL((zeta_tree_radix_tile_kernel<CT, S, 11>), g3, dim3(kRTThreads), 0, s,
+                           zk, tree_asc, tree_desc, N, stored, top_tile, base);
+    else
+        hipLaunchKernelGGL((zeta_tree_radix_tile_kernel<CT, S, kTileLog>), g3, dim3(kRTThreads), 0,
+                           s, zk, tree_asc, tree_desc, N, stored, top_tile, base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     for (int l = top_tile; l + 1 < levels; ++l) {
