@@ -277,7 +277,8 @@ def waves_by_lds(lds: int, wg: int) -> int:
     wgs = LDS_BYTES_PER_CU // lds if lds > 0 else 64
     return min(8, (wgs * waves_wg) // SIMDS_PER_CU)
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
-             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants --no-configs")
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-variants --no-configs"
+             "{wl}")
 CEILING_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o tr -- "
                "python3 bench.py --gather-ceiling")
 
@@ -449,6 +450,7 @@ def ceiling_summary(d: str) -> None:
 def trace_summary(d: str, workload: str) -> None:
     """Per-kernel durations from a rocprofv3 --kernel-trace --stats run, next to the bench line
     the same run printed (its stage_ms come from HIP events on the launch stream)."""
+    wl = "" if workload == "long_fwd_bwd" else f" --workload {workload}"
     stats = glob.glob(os.path.join(d, "*kernel_stats.csv"))
     if not stats:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -461,7 +463,8 @@ def trace_summary(d: str, workload: str) -> None:
                 bench_line = json.loads(ln)
     lines = [f"# Kernel durations, {workload} (rocprofv3 --kernel-trace --stats)", "",
              "Command (from the repository root; stdout to run.log in the same folder):", "",
-             f"    {TRACE_CMD.format(d=d)}", f"    python3 bench.py --trace-summary {d}", "",
+             f"    {TRACE_CMD.format(d=d, wl=wl)}",
+             f"    python3 bench.py --trace-summary {d}{wl}", "",
              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
